@@ -1,0 +1,346 @@
+// ft_api.cpp -- the C ABI of libft.so: argument validation, the per-format
+// capability table, the per-stream grow-only scratch pool and dispatch.
+//
+// Refusal happens on the host before anything is enqueued, and the capability
+// table is the one the dispatcher uses (vllm.cpp PR #523, review and rework:
+// per-dtype availability instead of a boolean; refuse before the first
+// forward).  Scratch comes from a per-stream pool that only grows and retires
+// buffers instead of freeing them while work may be in flight (same PR: a
+// grow-only per-stream pool, no per-call malloc/free/synchronize).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "ft.h"
+#include "ft_internal.h"
+
+namespace {
+
+constexpr int kElems[8] = {32, 32, 256, 256, 256, 32, 32, 256};
+constexpr int kBytes[8] = {18, 34, 144, 176, 210, 17, 36, 292};
+
+bool is_weight(int t) { return t >= FT_Q4_0 && t <= FT_MXFP4; }
+bool is_act(int t) { return t == FT_Q8_1 || t == FT_Q8_K; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+int64_t row_bytes_of(int type, int64_t k) { return k / kElems[type] * kBytes[type]; }
+
+hipStream_t hs(ft_stream_t s) { return (hipStream_t)s; }
+
+ft_status hip_status(hipError_t e) { return e == hipSuccess ? FT_OK : FT_ERR_HIP; }
+
+// --------------------------------------------------------------------------
+// scratch pool
+// --------------------------------------------------------------------------
+struct Pool {
+  void* ptr = nullptr;
+  size_t size = 0;
+  std::vector<void*> retired;
+};
+std::mutex g_pool_mu;
+std::unordered_map<hipStream_t, Pool> g_pools;
+
+ft_status pool_get(hipStream_t st, size_t bytes, void** out) {
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  Pool& p = g_pools[st];
+  if (p.size >= bytes) {
+    *out = p.ptr;
+    return FT_OK;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return FT_ERR_HIP;
+  if (cs != hipStreamCaptureStatusNone) return FT_ERR_NO_SCRATCH;
+  size_t want = std::max(bytes, 2 * p.size);
+  want = (want + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+  void* np = nullptr;
+  if (hipMalloc(&np, want) != hipSuccess) return FT_ERR_HIP;
+  if (p.ptr) p.retired.push_back(p.ptr);  // work already enqueued may still use it
+  p.ptr = np;
+  p.size = want;
+  *out = np;
+  return FT_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// scratch layout of ft_moe_q_vec
+struct MoeScratch {
+  size_t xq, h, hq, d, total;
+};
+MoeScratch moe_layout(int w, int act, int64_t hidden, int64_t inter, int64_t t, int topk) {
+  (void)w;
+  MoeScratch s;
+  size_t off = 0;
+  s.xq = off;
+  off += align256((size_t)t * row_bytes_of(act, hidden));
+  s.h = off;
+  off += align256((size_t)t * topk * inter * sizeof(float));
+  s.hq = off;
+  off += align256((size_t)t * topk * row_bytes_of(act, inter));
+  s.d = off;
+  off += align256((size_t)t * topk * hidden * sizeof(float));
+  s.total = off;
+  return s;
+}
+
+// scratch layout of the grouped GEMM's sort
+struct SortScratch {
+  size_t counts, offsets, pairs, total;
+};
+SortScratch sort_layout(int64_t n_expert, int64_t t, int topk) {
+  SortScratch s;
+  size_t off = 0;
+  s.counts = off;
+  off += align256((size_t)n_expert * 4);
+  s.offsets = off;
+  off += align256((size_t)(n_expert + 1) * 4);
+  s.pairs = off;
+  off += align256((size_t)t * topk * 4);
+  s.total = off;
+  return s;
+}
+
+bool mmvq_pair(int w, int a) {
+  return a == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K);
+}
+bool moe_pair(int w, int a) { return (w == FT_Q4_K && a == FT_Q8_1) || (w == FT_MXFP4 && a == FT_Q8_K); }
+bool grouped_pair(int w, int a) {
+  return a == FT_Q8_K && (w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ft_block_elems(ft_type t) { return ((int)t >= 0 && (int)t < 8) ? kElems[t] : 0; }
+size_t ft_block_bytes(ft_type t) { return ((int)t >= 0 && (int)t < 8) ? (size_t)kBytes[t] : 0; }
+
+const char* ft_version(void) { return "ft 0.1 (gfx950)"; }
+
+int ft_supported(ft_op op, ft_type w, ft_type act) {
+  switch (op) {
+    case FT_OP_QUANTIZE: return is_act(act);
+    case FT_OP_DEQUANT: return is_weight(w);
+    case FT_OP_MMVQ: return mmvq_pair(w, act);
+    case FT_OP_MOE_VEC: return moe_pair(w, act);
+    case FT_OP_GROUPED: return grouped_pair(w, act);
+    case FT_OP_BLOCK_DOTS: return is_weight(w) && is_act(act);
+  }
+  return 0;
+}
+
+const char* ft_status_str(ft_status s) {
+  switch (s) {
+    case FT_OK: return "ok";
+    case FT_ERR_INVALID_ARG: return "invalid argument";
+    case FT_ERR_UNSUPPORTED: return "unsupported format combination";
+    case FT_ERR_SHAPE: return "shape not supported (block multiple, topk or size limit)";
+    case FT_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case FT_ERR_NO_SCRATCH: return "scratch pool too small while capturing";
+    case FT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+ft_status ft_quantize_act(ft_type act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
+                          ft_stream_t stream) {
+  if (!is_act(act)) return FT_ERR_UNSUPPORTED;
+  if (rows < 0 || k < 0 || ldx < k) return FT_ERR_INVALID_ARG;
+  if (k % kElems[act]) return FT_ERR_SHAPE;
+  if (rows == 0 || k == 0) return FT_OK;
+  if (!x || !xq) return FT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(xq)) return FT_ERR_ALIGNMENT;
+  return hip_status(ftk_launch_quantize(act, x, rows, k, ldx, xq, hs(stream)));
+}
+
+ft_status ft_dequant(ft_type w, const void* blocks, int64_t rows, int64_t k, float* out, ft_stream_t stream) {
+  if (!is_weight(w)) return FT_ERR_UNSUPPORTED;
+  if (rows < 0 || k < 0) return FT_ERR_INVALID_ARG;
+  if (k % kElems[w]) return FT_ERR_SHAPE;
+  if (rows == 0 || k == 0) return FT_OK;
+  if (!blocks || !out) return FT_ERR_INVALID_ARG;
+  if (!aligned16(blocks) || !aligned16(out)) return FT_ERR_ALIGNMENT;
+  return hip_status(ftk_launch_dequant(w, blocks, rows, k, out, hs(stream)));
+}
+
+ft_status ft_mul_mat_vec_q(ft_type w, const void* W, int64_t n, int64_t k, ft_type act, const void* xq, int64_t t,
+                           float* y, int64_t ldy, ft_stream_t stream) {
+  if (!is_weight(w) || !is_act(act) || !mmvq_pair(w, act)) return FT_ERR_UNSUPPORTED;
+  if (n < 0 || k < 0 || t < 0 || ldy < n) return FT_ERR_INVALID_ARG;
+  if (k % kElems[w] || k % kElems[act]) return FT_ERR_SHAPE;
+  if (k > 32768 || n > ((int64_t)1 << 31) / 2) return FT_ERR_SHAPE;
+  if (n == 0 || t == 0) return FT_OK;
+  if (!W || !xq || !y) return FT_ERR_INVALID_ARG;
+  if (k == 0) return FT_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(xq) || !aligned16(y)) return FT_ERR_ALIGNMENT;
+  MmvqArgs a;
+  a.w = w;
+  a.act = act;
+  a.W = W;
+  a.n = n;
+  a.row_bytes = (int)row_bytes_of(w, k);
+  a.units_per_row = 0;
+  a.xrow_bytes = (int)row_bytes_of(act, k);
+  a.ldy = ldy;
+  for (int64_t t0 = 0; t0 < t; t0 += 8) {
+    a.t = (int)std::min<int64_t>(8, t - t0);
+    a.xq = (const uint8_t*)xq + t0 * a.xrow_bytes;
+    a.y = y + t0 * ldy;
+    const hipError_t e = ftk_launch_mmvq(a, k, hs(stream));
+    if (e != hipSuccess) return FT_ERR_HIP;
+  }
+  return FT_OK;
+}
+
+ft_status ft_moe_route(const float* logits, int64_t t, int64_t n_expert, int topk, int32_t* ids, float* w,
+                       ft_stream_t stream) {
+  if (t < 0 || n_expert < 1 || n_expert > 1024) return FT_ERR_SHAPE;
+  if (topk < 1 || topk > 8 || topk > n_expert) return FT_ERR_SHAPE;
+  if (t == 0) return FT_OK;
+  if (!logits || !ids || !w) return FT_ERR_INVALID_ARG;
+  return hip_status(ftk_launch_route(logits, t, n_expert, topk, ids, w, hs(stream)));
+}
+
+ft_status ft_moe_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert, int32_t* counts, int32_t* offsets,
+                      int32_t* pairs, ft_stream_t stream) {
+  if (t < 0 || n_expert < 1 || n_expert > 8192 || topk < 1 || topk > 8) return FT_ERR_SHAPE;
+  if (!counts || !offsets || (t > 0 && (!ids || !pairs))) return FT_ERR_INVALID_ARG;
+  return hip_status(ftk_launch_sort(ids, t, topk, n_expert, counts, offsets, pairs, hs(stream)));
+}
+
+size_t ft_moe_scratch_bytes(ft_type w, ft_type act, int64_t n_expert, int64_t hidden, int64_t inter, int64_t t,
+                            int topk) {
+  (void)n_expert;
+  if (!is_act(act) || t < 0 || topk < 0) return 0;
+  return moe_layout(w, act, hidden, inter, t, topk).total;
+}
+
+size_t ft_grouped_scratch_bytes(int64_t n_expert, int64_t t, int topk) {
+  return sort_layout(n_expert, t, topk).total;
+}
+
+ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const void* w_down, int64_t n_expert,
+                       int64_t hidden, int64_t inter, ft_type act, const float* x, int64_t t,
+                       const int32_t* expert_ids, const float* expert_w, int topk, float* y, const ft_moe_opts* opts,
+                       ft_stream_t stream) {
+  if (!is_weight(w) || !is_act(act) || !moe_pair(w, act)) return FT_ERR_UNSUPPORTED;
+  if (n_expert < 1 || hidden < 0 || inter < 0 || t < 0) return FT_ERR_INVALID_ARG;
+  if (topk < 1 || topk > 8 || topk > n_expert) return FT_ERR_SHAPE;
+  if (hidden % kElems[w] || hidden % kElems[act] || inter % kElems[w] || inter % kElems[act]) return FT_ERR_SHAPE;
+  if (hidden == 0 || inter == 0 || hidden > 16384 || inter > 16384) return FT_ERR_SHAPE;
+  if (t == 0) return FT_OK;
+  if (!w_gate || !w_up || !w_down || !x || !expert_ids || !expert_w || !y) return FT_ERR_INVALID_ARG;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(x) || !aligned16(y))
+    return FT_ERR_ALIGNMENT;
+  ft_moe_opts o = {};
+  if (opts) o = *opts;
+  if (o.route < 0 || o.route > 2) return FT_ERR_INVALID_ARG;
+  if (o.route == 2) return FT_ERR_UNSUPPORTED;  // sorted-tile route not provided by this build
+  if ((o.tap_g && !aligned16(o.tap_g)) || (o.tap_u && !aligned16(o.tap_u)) || (o.tap_h && !aligned16(o.tap_h)) ||
+      (o.tap_hq && !aligned16(o.tap_hq)) || (o.tap_down && !aligned16(o.tap_down)) ||
+      (o.in_hq && !aligned16(o.in_hq)))
+    return FT_ERR_ALIGNMENT;
+
+  hipStream_t st = hs(stream);
+  const MoeScratch L = moe_layout(w, act, hidden, inter, t, topk);
+  void* base = nullptr;
+  ft_status s = pool_get(st, L.total, &base);
+  if (s != FT_OK) return s;
+  uint8_t* b = (uint8_t*)base;
+
+  MoeArgs a;
+  a.w = w;
+  a.act = act;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.n_expert = n_expert;
+  a.hidden = hidden;
+  a.inter = inter;
+  a.t = t;
+  a.topk = topk;
+  a.ids = expert_ids;
+  a.ew = expert_w;
+  a.xq = b + L.xq;
+  a.h = o.tap_h ? o.tap_h : (float*)(b + L.h);
+  a.g_tap = o.tap_g;
+  a.u_tap = o.tap_u;
+  a.hq = o.in_hq ? const_cast<void*>(o.in_hq) : (o.tap_hq ? o.tap_hq : (void*)(b + L.hq));
+  a.dpair = o.tap_down ? o.tap_down : (float*)(b + L.d);
+  a.y = y;
+
+  hipError_t e = ftk_launch_quantize(act, x, t, hidden, hidden, (void*)a.xq, st);
+  if (e == hipSuccess) e = ftk_launch_moe_gate_up(a, st);
+  if (e == hipSuccess && !o.in_hq) e = ftk_launch_quantize(act, a.h, t * topk, inter, inter, a.hq, st);
+  if (e == hipSuccess && o.in_hq && o.tap_hq)
+    e = hipMemcpyAsync(o.tap_hq, o.in_hq, (size_t)t * topk * row_bytes_of(act, inter), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) e = ftk_launch_moe_down(a, st);
+  if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
+  return hip_status(e);
+}
+
+ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t n, int64_t k, ft_type act,
+                            const void* xq, int x_per_pair, const int32_t* expert_ids, int64_t t, int topk, float* y,
+                            ft_stream_t stream) {
+  if (!is_weight(w) || !is_act(act) || !grouped_pair(w, act)) return FT_ERR_UNSUPPORTED;
+  if (n_expert < 1 || n < 0 || k < 0 || t < 0) return FT_ERR_INVALID_ARG;
+  if (topk < 1 || topk > 8 || topk > n_expert || n_expert > 8192) return FT_ERR_SHAPE;
+  if (k % kElems[w] || k % kElems[act] || k == 0 || k > 16384) return FT_ERR_SHAPE;
+  if (n == 0 || t == 0) return FT_OK;
+  if (!W || !xq || !expert_ids || !y) return FT_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(xq) || !aligned16(y)) return FT_ERR_ALIGNMENT;
+  hipStream_t st = hs(stream);
+  const SortScratch L = sort_layout(n_expert, t, topk);
+  void* base = nullptr;
+  ft_status s = pool_get(st, L.total, &base);
+  if (s != FT_OK) return s;
+  uint8_t* b = (uint8_t*)base;
+  GroupedArgs a;
+  a.w = w;
+  a.act = act;
+  a.W = W;
+  a.n_expert = n_expert;
+  a.n = n;
+  a.k = k;
+  a.xq = xq;
+  a.x_per_pair = x_per_pair ? 1 : 0;
+  a.t = t;
+  a.topk = topk;
+  a.counts = (const int32_t*)(b + L.counts);
+  a.offsets = (const int32_t*)(b + L.offsets);
+  a.pairs = (const int32_t*)(b + L.pairs);
+  a.y = y;
+  hipError_t e = ftk_launch_sort(expert_ids, t, topk, n_expert, (int32_t*)(b + L.counts), (int32_t*)(b + L.offsets),
+                                 (int32_t*)(b + L.pairs), st);
+  if (e == hipSuccess) e = ftk_launch_grouped(a, st);
+  return hip_status(e);
+}
+
+ft_status ft_debug_block_dots(ft_type w, const void* W, int64_t n, int64_t k, ft_type act, const void* xq, int64_t t,
+                              int32_t* partials, ft_stream_t stream) {
+  if (!is_weight(w) || !is_act(act)) return FT_ERR_UNSUPPORTED;
+  if (n < 0 || k < 0 || t < 0) return FT_ERR_INVALID_ARG;
+  if (k % kElems[w] || k % kElems[act]) return FT_ERR_SHAPE;
+  if (n == 0 || t == 0 || k == 0) return FT_OK;
+  if (!W || !xq || !partials) return FT_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(xq)) return FT_ERR_ALIGNMENT;
+  return hip_status(ftk_launch_block_dots(w, W, n, k, act, xq, t, partials, hs(stream)));
+}
+
+ft_status ft_scratch_reserve(ft_stream_t stream, size_t bytes) {
+  void* p = nullptr;
+  return pool_get(hs(stream), bytes, &p);
+}
+
+void ft_shutdown(void) {
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  for (auto& kv : g_pools) {
+    if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    for (void* r : kv.second.retired) (void)hipFree(r);
+  }
+  g_pools.clear();
+}
+
+}  // extern "C"

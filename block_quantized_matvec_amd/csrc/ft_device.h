@@ -1,0 +1,447 @@
+// ft_device.h -- device-side building blocks shared by the gfx950 kernels:
+// block format traits, the per-unit unpack + int8 dot4 core, activation preload
+// and 64-lane reductions.
+//
+// A "unit" is the work of one lane on one row: 32 weights of one block (64 for
+// Q4_K / Q5_K, whose lanes take both 32-element sub-blocks of one 64-element
+// chunk so that one scale decode and one combine serve 64 weights).  The lane
+// holds the matching activation codes (NW dwords of int8x4) in VGPRs, unpacks
+// the unit's weight codes into the same dword order and takes integer dots with
+// v_dot4_i32_i8.  A unit is cut into S "segments" whose elements share one
+// weight scale and one activation block; the fp32 combine is, per segment,
+//   acc += d_x * (wscale * I - wmin * B)
+// with I the integer dot of raw codes and B the sum of the activation codes.
+// (Q4_0's -8 and Q6_K's -32 code offsets enter through wmin.)  This is the
+// keep-quant scheme of vllm.cpp PR #523 "grouped + non-grouped keep-quant expert
+// GEMM" (What changed: superblock dots on an integer dot4 core), laid out for
+// 64-lane wavefronts.  Block byte layouts are the public GGUF formats.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ft.h"
+
+namespace ftk {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// format traits
+//   BLK, BB   elements and bytes per block
+//   UPB       units per block;  NW activation dwords per unit (4 codes each)
+//   S         segments per unit; SUB elements per exported integer partial
+//   act_elem(ui, j)  element (within the block) of the first code of dword j
+//   seg_of(j)        segment of dword j
+// ---------------------------------------------------------------------------
+template <int F> struct Fmt;
+
+// Q4_0: fp16 d @0, qs[16] @2; element e<16 low nibble of qs[e], else high nibble
+// of qs[e-16]; w = d*(n-8).  One unit, one segment.
+template <> struct Fmt<FT_Q4_0> {
+  static constexpr int BLK = 32, BB = 18, UPB = 1, NW = 8, S = 1, SUB = 32;
+  static constexpr bool HAS_MIN = true;   // the -8 offset, as wmin = 8d
+  static constexpr int CODE_OFF = 8;      // exported partials use n - 8
+  __device__ static int act_elem(int, int j) { return 4 * j; }
+  __device__ static constexpr int seg_of(int) { return 0; }
+};
+// Q8_0: fp16 d @0, int8 qs[32] @2; w = d*q.
+template <> struct Fmt<FT_Q8_0> {
+  static constexpr int BLK = 32, BB = 34, UPB = 1, NW = 8, S = 1, SUB = 32;
+  static constexpr bool HAS_MIN = false;
+  static constexpr int CODE_OFF = 0;
+  __device__ static int act_elem(int, int j) { return 4 * j; }
+  __device__ static constexpr int seg_of(int) { return 0; }
+};
+// MXFP4: E8M0 e @0, qs[16] @1 (nibble order as Q4_0); w = v2 * 2^(e-128) with v2
+// twice the E2M1 value (an integer in [-12, 12]).
+template <> struct Fmt<FT_MXFP4> {
+  static constexpr int BLK = 32, BB = 17, UPB = 1, NW = 8, S = 1, SUB = 32;
+  static constexpr bool HAS_MIN = false;
+  static constexpr int CODE_OFF = 0;
+  __device__ static int act_elem(int, int j) { return 4 * j; }
+  __device__ static constexpr int seg_of(int) { return 0; }
+};
+// Q4_K: d @0, dmin @2, scales[12] @4, qs[128] @16.  Element e = 64c + 32h + l is
+// nibble h of qs[32c+l]; sub-block j = 2c+h.  Unit c covers qs[32c .. 32c+31]:
+// dwords 0-7 are its low nibbles (sub-block 2c), dwords 8-15 its high nibbles
+// (sub-block 2c+1).
+template <> struct Fmt<FT_Q4_K> {
+  static constexpr int BLK = 256, BB = 144, UPB = 4, NW = 16, S = 2, SUB = 32;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int CODE_OFF = 0;
+  __device__ static int act_elem(int ui, int j) { return 64 * ui + (j < 8 ? 4 * j : 32 + 4 * (j - 8)); }
+  __device__ static constexpr int seg_of(int j) { return j >> 3; }
+};
+// Q5_K: d @0, dmin @2, scales[12] @4, qh[32] @16, qs[128] @48; as Q4_K with the
+// fifth bit of element 64c+32h+l in bit (2c+h) of qh[l].
+template <> struct Fmt<FT_Q5_K> {
+  static constexpr int BLK = 256, BB = 176, UPB = 4, NW = 16, S = 2, SUB = 32;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int CODE_OFF = 0;
+  __device__ static int act_elem(int ui, int j) { return Fmt<FT_Q4_K>::act_elem(ui, j); }
+  __device__ static constexpr int seg_of(int j) { return j >> 3; }
+};
+// Q6_K: ql[128] @0, qh[64] @128, int8 scales[16] @192, fp16 d @208.  Element
+// e = 128g + 32r + l: low 4 bits from ql[64g + 32(r&1) + l] (low nibble for r<2,
+// high for r>=2), top 2 bits = bits 2r..2r+1 of qh[32g + l]; w = d*sc[e/16]*(q6-32).
+// Unit ui = 4g + (l0/8) covers l in [l0, l0+8) for all four r: dwords 2r, 2r+1.
+template <> struct Fmt<FT_Q6_K> {
+  static constexpr int BLK = 256, BB = 210, UPB = 8, NW = 8, S = 4, SUB = 16;
+  static constexpr bool HAS_MIN = true;   // the -32 offset, as wmin = 32*d*sc
+  static constexpr int CODE_OFF = 32;
+  __device__ static int act_elem(int ui, int j) {
+    return 128 * (ui >> 2) + 32 * (j >> 1) + 8 * (ui & 3) + 4 * (j & 1);
+  }
+  __device__ static constexpr int seg_of(int j) { return j >> 1; }
+};
+
+template <int A> struct Act;
+template <> struct Act<FT_Q8_1> { static constexpr int BLK = 32, BB = 36; };
+template <> struct Act<FT_Q8_K> { static constexpr int BLK = 256, BB = 292; };
+
+// units in a row of k elements (host and device)
+template <int F>
+__host__ __device__ constexpr int64_t units_in_row(int64_t k) {
+  return k / Fmt<F>::BLK * Fmt<F>::UPB;
+}
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  _Float16 h;
+  uint16_t b = (uint16_t)bits16;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+__device__ __forceinline__ uint32_t f2h_bits(float f) {  // round to nearest even
+  _Float16 h = (_Float16)f;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+// 2^(e-128) for an E8M0 byte, built from its bits (exact, subnormals for e < 2)
+__device__ __forceinline__ float e8m0_half(uint32_t e) {
+  uint32_t bits = e >= 2 ? (e - 1) << 23 : (0x00400000u >> (1 - e));
+  return __uint_as_float(bits);
+}
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// ---------------------------------------------------------------------------
+// byte-addressed readers over a dword array (LDS tile or global blocks).
+// u32(off) returns the 4 bytes at any byte offset.
+// ---------------------------------------------------------------------------
+template <typename P>
+struct Reader {
+  P base;  // const uint32_t* in LDS (address space inferred) or global
+  __device__ __forceinline__ uint32_t u32(uint32_t off) const {
+    uint32_t lo = base[off >> 2], hi = base[(off >> 2) + 1];
+    return __builtin_amdgcn_alignbyte(hi, lo, off & 3);
+  }
+  template <int N>
+  __device__ __forceinline__ void dwords(uint32_t off, uint32_t (&o)[N]) const {
+    const uint32_t w0 = off >> 2, sh = off & 3;
+    uint32_t prev = base[w0];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      uint32_t nx = base[w0 + i + 1];
+      o[i] = __builtin_amdgcn_alignbyte(nx, prev, sh);
+      prev = nx;
+    }
+  }
+  // off must be 16-byte aligned; N a multiple of 4
+  template <int N>
+  __device__ __forceinline__ void dwords16(uint32_t off, uint32_t (&o)[N]) const {
+    const u32x4* b = (const u32x4*)base;
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const u32x4 v = b[(off >> 4) + i];
+      o[4 * i] = v.x;
+      o[4 * i + 1] = v.y;
+      o[4 * i + 2] = v.z;
+      o[4 * i + 3] = v.w;
+    }
+  }
+  __device__ __forceinline__ uint32_t u16(uint32_t off) const { return (u32(off)) & 0xFFFFu; }
+  __device__ __forceinline__ uint32_t u8(uint32_t off) const {
+    return (base[off >> 2] >> (8 * (off & 3))) & 0xFFu;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// unit unpack: weight codes in activation dword order + per-segment scale/min
+// ---------------------------------------------------------------------------
+template <int F> struct Unit {
+  uint32_t w[Fmt<F>::NW];
+  float ws[Fmt<F>::S];
+  float wm[Fmt<F>::S];
+};
+
+// K-quant 6-bit scale and min of sub-block j from the three header dwords
+// h0 = scales[0..3], h1 = scales[4..7], h2 = scales[8..11] (element-wise use).
+__device__ __forceinline__ void kq_scale_min(uint32_t h0, uint32_t h1, uint32_t h2, int j,
+                                             uint32_t& sc, uint32_t& m) {
+  if (j < 4) {
+    sc = (h0 >> (8 * j)) & 63;
+    m = (h1 >> (8 * j)) & 63;
+  } else {
+    const int jj = j - 4;
+    const uint32_t b8 = (h2 >> (8 * jj)) & 0xFF;
+    sc = (b8 & 15) | (((h0 >> (8 * jj + 6)) & 3) << 4);
+    m = (b8 >> 4) | (((h1 >> (8 * jj + 6)) & 3) << 4);
+  }
+}
+
+// All eight 6-bit scales and mins of a K-quant superblock, four per dword:
+// sc_lo bytes = sc_0..3, sc_hi = sc_4..7, m_lo = m_0..3, m_hi = m_4..7.
+// (Sub-blocks 4-7 keep their low four bits in bytes 8-11 -- scale in the low
+// nibble, min in the high nibble -- and their top two bits in the spare top bits
+// of bytes 0-3 (scale) and 4-7 (min).)
+__device__ __forceinline__ void kq_unpack_scales(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t& sc_lo,
+                                                 uint32_t& sc_hi, uint32_t& m_lo, uint32_t& m_hi) {
+  sc_lo = h0 & 0x3F3F3F3Fu;
+  m_lo = h1 & 0x3F3F3F3Fu;
+  sc_hi = (h2 & 0x0F0F0F0Fu) | ((h0 >> 2) & 0x30303030u);
+  m_hi = ((h2 >> 4) & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+}
+
+// K-quant header (d|dmin, scales) -> wscale / wmin of the two sub-blocks 2c, 2c+1
+// of unit c: bytes 2(c&1), 2(c&1)+1 of the lo (c < 2) or hi (c >= 2) packed dwords.
+__device__ __forceinline__ void kq_header(uint32_t h_ddm, uint32_t h0, uint32_t h1, uint32_t h2, int c,
+                                          float (&ws)[2], float (&wm)[2]) {
+  const float d = h2f(h_ddm & 0xFFFF), dmin = h2f(h_ddm >> 16);
+  uint32_t sc_lo, sc_hi, m_lo, m_hi;
+  kq_unpack_scales(h0, h1, h2, sc_lo, sc_hi, m_lo, m_hi);
+  const uint32_t sh = 16u * (uint32_t)(c & 1);
+  const uint32_t sc = (c >= 2 ? sc_hi : sc_lo) >> sh;
+  const uint32_t m = (c >= 2 ? m_hi : m_lo) >> sh;
+  ws[0] = d * (float)(sc & 0xFF);
+  ws[1] = d * (float)((sc >> 8) & 0xFF);
+  wm[0] = dmin * (float)(m & 0xFF);
+  wm[1] = dmin * (float)((m >> 8) & 0xFF);
+}
+
+// E2M1 codes (one per byte, 0..15) -> twice their value as int8, via byte permutes:
+// magnitudes 0,1,2,3,4,6,8,12 for codes 0..7; codes 8..15 are the negatives.
+__device__ __forceinline__ uint32_t e2m1x2_bytes(uint32_t c) {
+  const uint32_t sel = c & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, sel);
+  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, sel);
+  const uint32_t sb = c & 0x08080808u;
+  const uint32_t mask = (sb << 5) - (sb >> 3);  // 0xFF in every byte whose code is negative
+  return (neg & mask) | (pos & ~mask);
+}
+
+// A16: the block's offset is 16-byte aligned in the reader (K-quant rows always
+// are: 144- and 176-byte blocks in 16-byte-aligned rows).
+template <int F, bool A16, typename R>
+__device__ __forceinline__ void unpack_unit(const R& rd, uint32_t bo, int ui, Unit<F>& u) {
+  if constexpr (F == FT_Q4_0) {
+    const float d = h2f(rd.u16(bo));
+    uint32_t q[4];
+    rd.template dwords<4>(bo + 2, q);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      u.w[m] = q[m] & 0x0F0F0F0Fu;
+      u.w[4 + m] = (q[m] >> 4) & 0x0F0F0F0Fu;
+    }
+    u.ws[0] = d;
+    u.wm[0] = 8.0f * d;
+  } else if constexpr (F == FT_Q8_0) {
+    u.ws[0] = h2f(rd.u16(bo));
+    u.wm[0] = 0.0f;
+    rd.template dwords<8>(bo + 2, u.w);
+  } else if constexpr (F == FT_MXFP4) {
+    u.ws[0] = e8m0_half(rd.u8(bo));
+    u.wm[0] = 0.0f;
+    uint32_t q[4];
+    rd.template dwords<4>(bo + 1, q);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      u.w[m] = e2m1x2_bytes(q[m] & 0x0F0F0F0Fu);
+      u.w[4 + m] = e2m1x2_bytes((q[m] >> 4) & 0x0F0F0F0Fu);
+    }
+  } else if constexpr (F == FT_Q4_K || F == FT_Q5_K) {
+    uint32_t h[4], q[8];
+    constexpr uint32_t QOFF = F == FT_Q4_K ? 16 : 48;
+    if constexpr (A16) {
+      rd.template dwords16<4>(bo, h);
+      rd.template dwords16<8>(bo + QOFF + 32 * ui, q);
+    } else {
+      rd.template dwords<4>(bo, h);
+      rd.template dwords<8>(bo + QOFF + 32 * ui, q);
+    }
+    kq_header(h[0], h[1], h[2], h[3], ui, u.ws, u.wm);
+    if constexpr (F == FT_Q4_K) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        u.w[m] = q[m] & 0x0F0F0F0Fu;
+        u.w[8 + m] = (q[m] >> 4) & 0x0F0F0F0Fu;
+      }
+    } else {
+      uint32_t qh[8];
+      if constexpr (A16) rd.template dwords16<8>(bo + 16, qh);
+      else rd.template dwords<8>(bo + 16, qh);
+      const uint32_t hb = 2u * (uint32_t)ui;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        u.w[m] = (q[m] & 0x0F0F0F0Fu) | (((qh[m] >> hb) & 0x01010101u) << 4);
+        u.w[8 + m] = ((q[m] >> 4) & 0x0F0F0F0Fu) | (((qh[m] >> (hb + 1)) & 0x01010101u) << 4);
+      }
+    }
+  } else {  // Q6_K
+    const int g = ui >> 2, l0 = 8 * (ui & 3);
+    uint32_t qa[2], qb[2], qh[2];
+    rd.template dwords<2>(bo + 64 * g + l0, qa);        // r = 0 (low nibbles), r = 2 (high)
+    rd.template dwords<2>(bo + 64 * g + 32 + l0, qb);   // r = 1 (low nibbles), r = 3 (high)
+    rd.template dwords<2>(bo + 128 + 32 * g + l0, qh);
+    const float d = h2f(rd.u16(bo + 208));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      u.w[0 + m] = (qa[m] & 0x0F0F0F0Fu) | ((qh[m] & 0x03030303u) << 4);
+      u.w[2 + m] = (qb[m] & 0x0F0F0F0Fu) | (((qh[m] >> 2) & 0x03030303u) << 4);
+      u.w[4 + m] = ((qa[m] >> 4) & 0x0F0F0F0Fu) | (((qh[m] >> 4) & 0x03030303u) << 4);
+      u.w[6 + m] = ((qb[m] >> 4) & 0x0F0F0F0Fu) | (((qh[m] >> 6) & 0x03030303u) << 4);
+    }
+    // scales of the four segments: sc[8g + 2r + l0/16]
+    const uint32_t sbase = bo + 192 + 8 * g + (l0 >> 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sc = (float)(int8_t)rd.u8(sbase + 2 * r);
+      u.ws[r] = d * sc;
+      u.wm[r] = 32.0f * u.ws[r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// activations of one unit position, held in VGPRs
+// ---------------------------------------------------------------------------
+template <int F> struct ActUnit {
+  uint32_t x[Fmt<F>::NW];      // int8x4 codes, dword j <-> Fmt<F>::act_elem(ui, j)
+  float dx[Fmt<F>::S];         // activation scale of each segment
+  float dxb[Fmt<F>::S];        // dx * (sum of the segment's codes)
+  int bsum[Fmt<F>::S];         // sum of the segment's codes
+};
+
+// first dword of segment s
+template <int F>
+__device__ __forceinline__ constexpr int seg_first(int s) {
+  int j0 = 0;
+  for (int j = Fmt<F>::NW - 1; j >= 0; --j)
+    if (Fmt<F>::seg_of(j) == s) j0 = j;
+  return j0;
+}
+
+// Load the activation codes of unit (block b, unit ui) of one token row.
+// xrow: that token's activation blocks (dword aligned).
+template <int F, int A>
+__device__ __forceinline__ void load_act_unit(const uint8_t* __restrict__ xrow, int b, int ui, ActUnit<F>& a) {
+  constexpr int S = Fmt<F>::S, NW = Fmt<F>::NW;
+#pragma unroll
+  for (int s = 0; s < S; ++s) a.bsum[s] = 0;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int e = b * Fmt<F>::BLK + Fmt<F>::act_elem(ui, j);
+    const int ab = e / Act<A>::BLK, pos = e % Act<A>::BLK;
+    a.x[j] = *(const uint32_t*)(xrow + (size_t)ab * Act<A>::BB + 4 + pos);
+    a.bsum[Fmt<F>::seg_of(j)] = dot4(a.x[j], 0x01010101u, a.bsum[Fmt<F>::seg_of(j)]);
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = b * Fmt<F>::BLK + Fmt<F>::act_elem(ui, seg_first<F>(s));
+    const uint8_t* ab = xrow + (size_t)(e / Act<A>::BLK) * Act<A>::BB;
+    float dx;
+    if (A == FT_Q8_1) dx = h2f(*(const uint16_t*)ab);
+    else dx = *(const float*)ab;
+    a.dx[s] = dx;
+    a.dxb[s] = dx * (float)a.bsum[s];
+  }
+}
+
+template <int F>
+__device__ __forceinline__ void zero_act_unit(ActUnit<F>& a) {
+#pragma unroll
+  for (int j = 0; j < Fmt<F>::NW; ++j) a.x[j] = 0;
+#pragma unroll
+  for (int s = 0; s < Fmt<F>::S; ++s) { a.dx[s] = 0.f; a.dxb[s] = 0.f; a.bsum[s] = 0; }
+}
+
+// Integer dot of each segment of a unit against one token's codes.
+template <int F>
+__device__ __forceinline__ void unit_dots(const Unit<F>& u, const ActUnit<F>& a, int (&I)[Fmt<F>::S]) {
+#pragma unroll
+  for (int s = 0; s < Fmt<F>::S; ++s) I[s] = 0;
+#pragma unroll
+  for (int j = 0; j < Fmt<F>::NW; ++j) I[Fmt<F>::seg_of(j)] = dot4(u.w[j], a.x[j], I[Fmt<F>::seg_of(j)]);
+}
+
+// fp32 combine of one unit for one token.
+template <int F>
+__device__ __forceinline__ float unit_combine(const Unit<F>& u, const ActUnit<F>& a, float acc) {
+  int I[Fmt<F>::S];
+  unit_dots<F>(u, a, I);
+#pragma unroll
+  for (int s = 0; s < Fmt<F>::S; ++s) {
+    acc = fmaf(a.dx[s] * (float)I[s], u.ws[s], acc);
+    if (Fmt<F>::HAS_MIN) acc = fmaf(-u.wm[s], a.dxb[s], acc);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// 64-lane reductions
+// ---------------------------------------------------------------------------
+// value of the partner lane at xor-distance S (S = 1, 2: quad permutes; 4, 8:
+// half-row / row mirrors, which pair lanes across the same bit; 16, 32: LDS
+// permute).
+template <int S>
+__device__ __forceinline__ float xchg(float v) {
+  const int i = __float_as_int(v);
+  int r;
+  if constexpr (S == 1) r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
+  else if constexpr (S == 2) r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  else if constexpr (S == 4) r = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, false); // row_half_mirror
+  else if constexpr (S == 8) r = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, false); // row_mirror
+  else r = __shfl_xor(i, S, 64);
+  return __int_as_float(r);
+}
+
+// Reduce M values per lane over the lanes of an aligned group of L lanes
+// (L a power of two <= 64, M <= L).  Afterwards value index i's group total sits
+// in v[0] of lanes (i * L/M) .. (i * L/M + L/M - 1) of the group: each exchange
+// step keeps the half of the values selected by the lane bit it pairs across.
+template <int M, int S>
+__device__ __forceinline__ void reduce_level(float (&v)[M], int& m, int lane) {
+  if (m > 1) {
+    const bool upper = (lane & S) != 0;
+#pragma unroll
+    for (int i = 0; i < M / 2; ++i) {
+      if (i < m / 2) {
+        const float keep = upper ? v[i + m / 2] : v[i];
+        const float send = upper ? v[i] : v[i + m / 2];
+        v[i] = keep + xchg<S>(send);
+      }
+    }
+    m >>= 1;
+  } else {
+    v[0] += xchg<S>(v[0]);
+  }
+}
+
+template <int M, int L>
+__device__ __forceinline__ void group_reduce_multi(float (&v)[M], int lane) {
+  static_assert(M <= L && L <= 64, "");
+  int m = M;
+  if constexpr (L >= 64) reduce_level<M, 32>(v, m, lane);
+  if constexpr (L >= 32) reduce_level<M, 16>(v, m, lane);
+  if constexpr (L >= 16) reduce_level<M, 8>(v, m, lane);
+  if constexpr (L >= 8) reduce_level<M, 4>(v, m, lane);
+  if constexpr (L >= 4) reduce_level<M, 2>(v, m, lane);
+  if constexpr (L >= 2) reduce_level<M, 1>(v, m, lane);
+}
+
+}  // namespace ftk

@@ -1,0 +1,78 @@
+// ft_internal.h -- host-side launcher interface between the C ABI (ft_api.cpp)
+// and the kernel translation units.  Launchers assume validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ft.h"
+
+struct MmvqArgs {
+  int w, act;
+  const void* W;
+  int64_t n;
+  int row_bytes, units_per_row;  // units_per_row is set by the launcher
+  const void* xq;
+  int xrow_bytes;
+  int t;  // 1..8
+  float* y;
+  int64_t ldy;
+};
+
+struct MmvqPlan {
+  int tslot;          // token slots of the kernel (1, 2, 4, 8)
+  int lr, p;          // lanes per row, units per lane
+  int cpl;            // 16-byte chunks per lane per tile
+  int rows_per_tile, rows_per_wg, grid;
+};
+int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out);
+hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
+
+hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
+                               hipStream_t st);
+hipError_t ftk_launch_dequant(int w, const void* blocks, int64_t rows, int64_t k, float* out,
+                              hipStream_t st);
+hipError_t ftk_launch_block_dots(int w, const void* W, int64_t n, int64_t k, int act, const void* xq,
+                                 int64_t t, int32_t* partials, hipStream_t st);
+
+hipError_t ftk_launch_route(const float* logits, int64_t t, int64_t n_expert, int topk, int32_t* ids,
+                            float* w, hipStream_t st);
+hipError_t ftk_launch_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert, int32_t* counts,
+                           int32_t* offsets, int32_t* pairs, hipStream_t st);
+
+// routed-MoE vector path (direct route): per-stage launchers
+struct MoeArgs {
+  int w, act;
+  const void *w_gate, *w_up, *w_down;
+  int64_t n_expert, hidden, inter;
+  int64_t t;
+  int topk;
+  const int32_t* ids;
+  const float* ew;
+  const void* xq;      // quantized x [t][hidden/blk_a]
+  float* h;            // [t*topk][inter]
+  float* g_tap;        // nullable
+  float* u_tap;        // nullable
+  void* hq;            // quantized h [t*topk][inter/blk_a]
+  float* dpair;        // [t*topk][hidden] per-pair down projections
+  float* y;            // [t][hidden]
+};
+hipError_t ftk_launch_moe_gate_up(const MoeArgs& a, hipStream_t st);
+hipError_t ftk_launch_moe_down(const MoeArgs& a, hipStream_t st);
+hipError_t ftk_launch_moe_combine(const MoeArgs& a, hipStream_t st);
+
+// grouped GEMM over expert-sorted pairs
+struct GroupedArgs {
+  int w, act;
+  const void* W;
+  int64_t n_expert, n, k;
+  const void* xq;
+  int x_per_pair;
+  int64_t t;
+  int topk;
+  const int32_t* counts;   // [E]   (device, from the sort)
+  const int32_t* offsets;  // [E+1]
+  const int32_t* pairs;    // [t*topk]
+  float* y;                // [t*topk][n]
+};
+hipError_t ftk_launch_grouped(const GroupedArgs& a, hipStream_t st);

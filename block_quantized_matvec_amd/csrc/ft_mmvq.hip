@@ -1,0 +1,281 @@
+// ft_mmvq.hip -- quantized matvec y[t][n] = W[n][:] . xhat[t][:] on gfx950.
+//
+// The operation is the int8-dot matvec of FreeToken PR #136 (Summary: production
+// matvec with quantized activations) and the non-grouped keep-quant op of
+// vllm.cpp PR #523 (What changed).  Design for MI355X:
+//  * Each workgroup (4 waves) owns a contiguous, equal share of the rows and walks
+//    it in tiles of whole rows.  A tile's bytes are contiguous in HBM and are
+//    fetched with fully coalesced 16-byte loads (lane i of the workgroup reads
+//    bytes 16i..16i+15 of each 4 KiB slice), into VGPRs for tile t+1 while tile t
+//    is computed from LDS; then one ds_write_b128 per slice publishes it.  Any
+//    block size or alignment works because lanes read their units back from LDS
+//    at byte granularity.
+//  * Each lane owns fixed 32-weight units of a row and keeps the matching
+//    activation codes and scales in VGPRs for the whole kernel, so LDS carries
+//    only weight bytes.  Nibble / 6-bit / high-bit unpack happens in registers;
+//    dots use v_dot4_i32_i8.
+//  * Rows of a tile are spread over the row groups of the workgroup; each group
+//    reduces its rows over its lanes with a multi-value butterfly (M values cost
+//    M-1 + log2(L/M) shuffles instead of M*log2(L)).
+#include <stdlib.h>
+
+#include "ft_device.h"
+#include "ft_internal.h"
+
+namespace ftk {
+
+constexpr int MMVQ_THREADS = 256;
+
+// LR: lanes per row (64, 128 or 256); P: units per lane; T: token slots;
+// CPL: 16-byte chunks per lane per tile (tile <= CPL * 4 KiB).
+template <int F, int A, int T, int LR, int P, int CPL>
+__global__ void __launch_bounds__(MMVQ_THREADS)
+mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_per_row, int rows_per_wg,
+            int rows_per_tile, const uint8_t* __restrict__ xq, int xrow_bytes, int t_real,
+            float* __restrict__ y, int64_t ldy) {
+  using FT = Fmt<F>;
+  constexpr int G = MMVQ_THREADS / LR;        // row groups in the workgroup
+  constexpr int RA = T >= 2 ? 1 : 2;          // rows per group per reduction step
+  constexpr int M = RA * T;                   // values reduced per step
+  constexpr int WPR = LR / 64;                // waves per row
+  extern __shared__ u32x4 smem4[];
+  const uint32_t* smem = (const uint32_t*)smem4;
+  float* red = (float*)(smem4 + CPL * MMVQ_THREADS + 1);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = tid / LR, gl = tid % LR;
+
+  const int64_t wr0 = (int64_t)blockIdx.x * rows_per_wg;
+  if (wr0 >= n) return;
+  const int wrows = (int)min<int64_t>(rows_per_wg, n - wr0);
+  const int ntiles = (wrows + rows_per_tile - 1) / rows_per_tile;
+
+  u32x4 pre[CPL];
+  auto fetch = [&](int tile) {
+    const int64_t r0 = wr0 + (int64_t)tile * rows_per_tile;
+    const int nr = min(rows_per_tile, (int)(wr0 + wrows - r0));
+    const int64_t start = r0 * row_bytes, a0 = start & ~(int64_t)15;
+    const int nch = (int)((start + (int64_t)nr * row_bytes - a0 + 15) >> 4);
+    const u32x4* src = (const u32x4*)(W + a0);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = i * MMVQ_THREADS + tid;
+      if (c < nch) pre[i] = __builtin_nontemporal_load(src + c);
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) smem4[i * MMVQ_THREADS + tid] = pre[i];
+  };
+
+  fetch(0);
+
+  // activations of this lane's units (VGPR-resident for the whole kernel)
+  ActUnit<F> act[P][T];
+  uint32_t ub[P];
+  int uu[P];
+  bool uv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int u0 = gl + p * LR;
+    uv[p] = u0 < units_per_row;
+    const int u = uv[p] ? u0 : 0;   // idle lanes read a real unit, against zero activations
+    ub[p] = (uint32_t)(u / FT::UPB) * FT::BB;
+    uu[p] = u % FT::UPB;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (uv[p] && t < t_real) load_act_unit<F, A>(xq + (size_t)t * xrow_bytes, u / FT::UPB, uu[p], act[p][t]);
+      else zero_act_unit<F>(act[p][t]);
+    }
+  }
+  commit();
+  __syncthreads();
+
+  const Reader<const uint32_t*> rd{smem};
+  int parity = 0;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    if (tile + 1 < ntiles) fetch(tile + 1);
+    const int64_t r0 = wr0 + (int64_t)tile * rows_per_tile;
+    const int nr = min(rows_per_tile, (int)(wr0 + wrows - r0));
+    const uint32_t shift = (uint32_t)((r0 * row_bytes) & 15);
+
+    for (int rb = 0; rb < nr; rb += G * RA) {
+      float v[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) v[i] = 0.0f;
+#pragma unroll
+      for (int ra = 0; ra < RA; ++ra) {
+        const int r = rb + ra * G + grp;
+        if (r < nr) {
+          const uint32_t rowoff = shift + (uint32_t)r * row_bytes;
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            Unit<F> un;
+            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, rowoff + ub[p], uu[p], un);
+#pragma unroll
+            for (int t = 0; t < T; ++t) v[ra * T + t] = unit_combine<F>(un, act[p][t], v[ra * T + t]);
+          }
+        }
+      }
+      group_reduce_multi<M, (LR < 64 ? LR : 64)>(v, LR < 64 ? gl : lane);
+      constexpr int L = LR < 64 ? LR : 64;
+      const int idx = (LR < 64 ? gl : lane) / (L / M);
+      const bool leader = ((LR < 64 ? gl : lane) % (L / M)) == 0;
+      if (WPR <= 1) {
+        if (leader) {
+          const int ra = idx / T, t = idx % T;
+          const int r = rb + ra * G + grp;
+          if (r < nr && t < t_real) y[(int64_t)t * ldy + r0 + r] = v[0];
+        }
+      } else {
+        float* rp = red + parity * (MMVQ_THREADS / 64) * M;
+        if (leader) rp[wave * M + idx] = v[0];
+        __syncthreads();
+        if (gl < M) {
+          const int ra = gl / T, t = gl % T;
+          const int r = rb + ra * G + grp;
+          float s = 0.0f;
+#pragma unroll
+          for (int w = 0; w < WPR; ++w) s += rp[(grp * WPR + w) * M + gl];
+          if (r < nr && t < t_real) y[(int64_t)t * ldy + r0 + r] = s;
+        }
+        parity ^= 1;
+      }
+    }
+    if (tile + 1 < ntiles) {
+      __syncthreads();   // every wave is done reading the tile
+      commit();
+      __syncthreads();
+    }
+  }
+}
+
+// host side -------------------------------------------------------------------
+
+int g_num_cus = 0;
+
+static int num_cus() {
+  if (g_num_cus > 0) return g_num_cus;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    g_num_cus = cus;
+  else
+    g_num_cus = 256;
+  return g_num_cus;
+}
+
+template <int F, int A, int T, int LR, int P, int CPL>
+static hipError_t launch_mmvq_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
+  const size_t lds = (size_t)CPL * MMVQ_THREADS * 16 + 16 + 2 * (MMVQ_THREADS / 64) * 64 * sizeof(float);
+  hipLaunchKernelGGL((mmvq_kernel<F, A, T, LR, P, CPL>), dim3((unsigned)pl.grid), dim3(MMVQ_THREADS), lds, st,
+                     (const uint8_t*)a.W, a.n, a.row_bytes, a.units_per_row, pl.rows_per_wg, pl.rows_per_tile,
+                     (const uint8_t*)a.xq, a.xrow_bytes, a.t, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+template <int F, int A, int T, int CPL>
+static hipError_t dispatch_lp(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
+#define FT_LP(LRV, PV)                                                             \
+  if constexpr (PV * T <= 16)                                                     \
+    if (pl.lr == LRV && pl.p == PV) return launch_mmvq_t<F, A, T, LRV, PV, CPL>(a, pl, st);
+  FT_LP(64, 1) FT_LP(64, 2) FT_LP(64, 4) FT_LP(64, 8)
+  FT_LP(128, 1) FT_LP(128, 2) FT_LP(128, 4) FT_LP(128, 8)
+  FT_LP(256, 1) FT_LP(256, 2) FT_LP(256, 4) FT_LP(256, 8)
+#undef FT_LP
+  return hipErrorInvalidValue;
+}
+
+template <int F, int A, int T>
+static hipError_t dispatch_c(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
+  if (pl.cpl == 4) return dispatch_lp<F, A, T, 4>(a, pl, st);
+  if (pl.cpl == 8) return dispatch_lp<F, A, T, 8>(a, pl, st);
+  return hipErrorInvalidValue;
+}
+
+template <int F, int A>
+static hipError_t dispatch_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
+  switch (pl.tslot) {
+    case 1: return dispatch_c<F, A, 1>(a, pl, st);
+    case 2: return dispatch_c<F, A, 2>(a, pl, st);
+    case 4: return dispatch_c<F, A, 4>(a, pl, st);
+    case 8: return dispatch_c<F, A, 8>(a, pl, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ftk
+
+// Launch plan: lanes per row (LR) and units per lane (P) cover a row with the
+// fewest idle lanes, at most 16 unit-token activation sets per lane; a tile is
+// as many whole rows as fit in CPL * 4 KiB and must give every row group a row;
+// the grid is a few workgroups per CU, each owning an equal share of rows.
+// FT_MMVQ_PLAN="lr,p,cpl,wgs_per_cu" forces a plan (tuning sweeps).
+int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out) {
+  MmvqPlan best{};
+  double best_cost = 1e30;
+  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0;
+  if (const char* e = getenv("FT_MMVQ_PLAN")) sscanf(e, "%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs);
+  for (int cpl = 4; cpl <= 8; cpl += 4) {
+    if (force_cpl && cpl != force_cpl) continue;
+    const int rt = (cpl * 4096 - 15) / row_bytes;
+    if (rt < 1) continue;
+    for (int L = 64; L <= 256; L *= 2) {
+      if (force_lr && L != force_lr) continue;
+      const int G = ftk::MMVQ_THREADS / L;
+      if (G > rt) continue;
+      for (int P = 1; P <= 8; P *= 2) {
+        if (force_p && P != force_p) continue;
+        if (P * L < units_per_row || P * tslot > 16) continue;
+        const double waste = (double)(P * L - units_per_row) / (P * L);
+        const int rows_per_group = rt / G;
+        const double idle_groups = (double)(rt % G) / rt;
+        double cost = waste + 0.5 * idle_groups + 0.04 * (L / 64 - 1) + (P * tslot > 8 ? 0.3 : 0.0);
+        cost += rows_per_group < 2 ? 0.05 : 0.0;
+        cost += cpl == 8 ? 0.02 : 0.0;
+        if (cost < best_cost) {
+          best_cost = cost;
+          best.lr = L;
+          best.p = P;
+          best.cpl = cpl;
+          best.rows_per_tile = rt;
+        }
+      }
+    }
+  }
+  if (!best.lr) return 0;
+  best.tslot = tslot;
+  const int wgs_per_cu = force_wgs ? force_wgs : 2;
+  const int64_t slots = (int64_t)ftk::num_cus() * wgs_per_cu;
+  const int64_t tiles = (n + best.rows_per_tile - 1) / best.rows_per_tile;
+  const int64_t grid = tiles < slots ? tiles : slots;
+  best.rows_per_wg = (int)((n + grid - 1) / grid);
+  best.grid = (int)((n + best.rows_per_wg - 1) / best.rows_per_wg);
+  *out = best;
+  return 1;
+}
+
+namespace ftk {
+template <int F, int A>
+static hipError_t launch_fa(MmvqArgs a, int64_t k, hipStream_t st) {
+  const int tslot = a.t <= 1 ? 1 : a.t <= 2 ? 2 : a.t <= 4 ? 4 : 8;
+  a.units_per_row = (int)units_in_row<F>(k);
+  MmvqPlan pl;
+  if (!ftk_mmvq_plan(a.units_per_row, tslot, a.row_bytes, a.n, &pl)) return hipErrorInvalidValue;
+  return dispatch_t<F, A>(a, pl, st);
+}
+}  // namespace ftk
+
+hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
+  using namespace ftk;
+  if (a.act == FT_Q8_1) {
+    switch (a.w) {
+      case FT_Q4_0: return launch_fa<FT_Q4_0, FT_Q8_1>(a, k, st);
+      case FT_Q8_0: return launch_fa<FT_Q8_0, FT_Q8_1>(a, k, st);
+      case FT_Q4_K: return launch_fa<FT_Q4_K, FT_Q8_1>(a, k, st);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}

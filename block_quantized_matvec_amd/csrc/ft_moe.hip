@@ -1,0 +1,510 @@
+// ft_moe.hip -- routed-MoE vector path: router, token->expert sort, and the
+// direct-route expert kernels (gate/up + SwiGLU, down, weighted combine).
+//
+// ds4 PR #656 "Add ROCm MXFP4 routed expert kernels" (Summary): resident
+// MXFP4 x Q8_K routed gate/up and down kernels with SwiGLU between them,
+// coalesced weight reads with register unpack, and tiny batches (2-4 tokens)
+// sent through direct kernels instead of partly filled expert-sorted tiles.
+// FreeToken PR #136 (Summary): the routed MoE vector kernel with two-expert
+// routing.  MI355X design:
+//  * one workgroup per (distinct selected expert, tile of output rows); the
+//    expert's rows are streamed into LDS once with 16-byte global_load_lds and
+//    applied to every token that selected it (duplicates across tokens are read
+//    once; the first slot naming an expert owns it);
+//  * activation codes of all tokens sit in VGPRs; a wave-uniform token mask skips
+//    tokens that did not pick the expert;
+//  * gate and up share the activations; SwiGLU is applied right after the
+//    64-lane reduction, before h leaves registers.
+#include "ft_device.h"
+#include "ft_internal.h"
+
+namespace ftk {
+
+constexpr int MOE_THREADS = 256;
+
+// ---------------------------------------------------------------------------
+// router: one wave per token
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk, int32_t* __restrict__ ids,
+             float* __restrict__ w) {
+  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= t) return;
+  const float* l = logits + tok * n_expert;
+  constexpr int MAXE = 1024 / 64;
+  float v[MAXE];
+  bool taken[MAXE];
+#pragma unroll
+  for (int i = 0; i < MAXE; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < n_expert ? l[e] : 0.0f;
+    taken[i] = e >= n_expert;
+  }
+  float selv[8];
+  int seli[8];
+  for (int k = 0; k < topk; ++k) {
+    // lane-local best (lower index wins ties: ascending scan with strict >)
+    float bv = 0.0f;
+    int bi = -1;
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i)
+      if (!taken[i] && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = lane + 64 * i; }
+    // wave argmax; candidates with index -1 lose
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oi = __shfl_xor(bi, m, 64);
+      const bool better = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
+      if (better) { bv = ov; bi = oi; }
+    }
+    selv[k] = bv;
+    seli[k] = bi;
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i)
+      if (lane + 64 * i == bi) taken[i] = true;
+  }
+  if (lane == 0) {
+    const float lmax = selv[0];
+    float den = 0.0f, ex[8];
+    for (int k = 0; k < topk; ++k) {
+      ex[k] = expf(selv[k] - lmax);
+      den += ex[k];
+    }
+    for (int k = 0; k < topk; ++k) {
+      ids[tok * topk + k] = seli[k];
+      w[tok * topk + k] = ex[k] / den;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// stable counting sort of (token, slot) pairs by expert: one workgroup
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+sort_kernel(const int32_t* __restrict__ ids, int64_t npairs, int n_expert, int32_t* __restrict__ counts,
+            int32_t* __restrict__ offsets, int32_t* __restrict__ pairs) {
+  extern __shared__ int32_t sh[];
+  int32_t* cnt = sh;                 // [n_expert]
+  int32_t* chunk = sh + n_expert;    // [256]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n_expert; e += 256) cnt[e] = 0;
+  __syncthreads();
+  for (int64_t p = tid; p < npairs; p += 256) {
+    int e = ids[p];
+    e = e < 0 ? 0 : (e >= n_expert ? n_expert - 1 : e);
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix sum (n_expert is small)
+    int run = 0;
+    for (int e = 0; e < n_expert; ++e) {
+      const int c = cnt[e];
+      counts[e] = c;
+      offsets[e] = run;
+      cnt[e] = run;  // becomes the running insert position
+      run += c;
+    }
+    offsets[n_expert] = run;
+  }
+  __syncthreads();
+  for (int64_t base = 0; base < npairs; base += 256) {
+    const int64_t p = base + tid;
+    int e = -1;
+    if (p < npairs) {
+      e = ids[p];
+      e = e < 0 ? 0 : (e >= n_expert ? n_expert - 1 : e);
+    }
+    chunk[tid] = e;
+    __syncthreads();
+    if (e >= 0) {
+      int rank = 0;
+      for (int j = 0; j < tid; ++j) rank += chunk[j] == e;
+      pairs[cnt[e] + rank] = (int32_t)p;
+    }
+    __syncthreads();
+    if (e >= 0) {
+      // the last pair of this expert in the chunk advances the insert position
+      bool last = true;
+      for (int j = tid + 1; j < 256; ++j)
+        if (chunk[j] == e) { last = false; break; }
+      if (last) {
+        int c = 0;
+        for (int j = 0; j <= tid; ++j) c += chunk[j] == e;
+        cnt[e] += c;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// helpers shared by the expert kernels
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int clamp_id(int e, int64_t n_expert) {
+  return e < 0 ? 0 : (e >= n_expert ? (int)n_expert - 1 : e);
+}
+
+// stream nbytes starting at src (any alignment) into LDS at dst; returns the
+// shift (src & 15) at which byte 0 landed.  Every thread of the workgroup calls it.
+__device__ __forceinline__ uint32_t stage_bytes(const uint8_t* src, int64_t nbytes, uint32_t* dst, int tid,
+                                                int nthreads) {
+  const uintptr_t a = (uintptr_t)src;
+  const uint8_t* a0 = (const uint8_t*)(a & ~(uintptr_t)15);
+  const uint32_t shift = (uint32_t)(a & 15);
+  const int nchunks = (int)((shift + nbytes + 15) >> 4);
+  const int wave = tid >> 6;
+  for (int base = 0; base < nchunks; base += nthreads) {
+    const int c = base + tid;
+    if (c < nchunks)
+      __builtin_amdgcn_global_load_lds((const void*)(a0 + 16 * (int64_t)c),
+                                       (__attribute__((address_space(3))) void*)(dst + 4 * (base + wave * 64)),
+                                       16, 0, 0);
+  }
+  return shift;
+}
+
+// Decide which tokens picked expert e (and at which slot); returns false if an
+// earlier slot already names e (that workgroup owns the expert).
+template <int T>
+__device__ __forceinline__ bool expert_tokens(const int32_t* __restrict__ ids, int slot, int t_real, int topk,
+                                              int64_t n_expert, int& e, uint32_t& mask, int (&pair)[T]) {
+  e = clamp_id(ids[slot], n_expert);
+  for (int s2 = 0; s2 < slot; ++s2)
+    if (clamp_id(ids[s2], n_expert) == e) return false;
+  mask = 0;
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    pair[i] = 0;
+    if (i < t_real) {
+      for (int k = 0; k < topk; ++k)
+        if (clamp_id(ids[i * topk + k], n_expert) == e) {
+          mask |= 1u << i;
+          pair[i] = i * topk + k;
+          break;
+        }
+    }
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// gate/up + SwiGLU (direct route)
+// grid: x = row tiles of inter, y = (token, slot) pairs of this token chunk
+// ---------------------------------------------------------------------------
+template <int F, int A, int T, int LR, int P>
+__global__ void __launch_bounds__(MOE_THREADS)
+moe_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t n_expert,
+                   int64_t inter, int row_bytes, int units_per_row, int rows_per_tile,
+                   const uint8_t* __restrict__ xq, int xrow_bytes, int t_real, const int32_t* __restrict__ ids,
+                   int topk, float* __restrict__ h, float* __restrict__ gtap, float* __restrict__ utap) {
+  using FT = Fmt<F>;
+  constexpr int G = MOE_THREADS / LR;
+  constexpr int RA = T >= 4 ? 1 : 4 / T;
+  constexpr int M = 2 * RA * T;   // g values then u values
+  static_assert(M <= LR, "");
+  extern __shared__ uint32_t smem[];
+  const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
+
+  int e, pair[T];
+  uint32_t mask;
+  if (!expert_tokens<T>(ids, blockIdx.y, t_real, topk, n_expert, e, mask, pair)) return;
+
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_tile;
+  const int nrows = (int)min<int64_t>(rows_per_tile, inter - r0);
+  const int64_t tile_bytes = (int64_t)nrows * row_bytes;
+  const uint32_t tile_words = (uint32_t)(((tile_bytes + 15 + 15) >> 4) << 2);
+  const uint32_t sg = stage_bytes(wg + ((int64_t)e * inter + r0) * row_bytes, tile_bytes, smem, tid, MOE_THREADS);
+  const uint32_t su = stage_bytes(wu + ((int64_t)e * inter + r0) * row_bytes, tile_bytes, smem + tile_words, tid,
+                                  MOE_THREADS);
+
+  ActUnit<F> act[P][T];
+  int ub[P], uu[P];
+  bool uv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int u = gl + p * LR;
+    uv[p] = u < units_per_row;
+    ub[p] = u / FT::UPB;
+    uu[p] = u % FT::UPB;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      if (uv[p] && ((mask >> i) & 1)) load_act_unit<F, A>(xq + (size_t)i * xrow_bytes, ub[p], uu[p], act[p][i]);
+      else zero_act_unit<F>(act[p][i]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const Reader<const uint32_t*> rg{smem}, ru{smem + tile_words};
+  for (int rb = 0; rb < nrows; rb += G * RA) {
+    float v[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] = 0.0f;
+#pragma unroll
+    for (int ra = 0; ra < RA; ++ra) {
+      const int r = rb + ra * G + grp;
+      if (r < nrows) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          if (uv[p]) {
+            const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)ub[p] * FT::BB;
+            Unit<F> ug, uup;
+            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rg, sg + off, uu[p], ug);
+            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(ru, su + off, uu[p], uup);
+#pragma unroll
+            for (int i = 0; i < T; ++i) {
+              if ((mask >> i) & 1) {
+                v[ra * T + i] = unit_combine<F>(ug, act[p][i], v[ra * T + i]);
+                v[M / 2 + ra * T + i] = unit_combine<F>(uup, act[p][i], v[M / 2 + ra * T + i]);
+              }
+            }
+          }
+        }
+      }
+    }
+    group_reduce_multi<M, LR>(v, gl);
+    const int idx = gl / (LR / M);
+    const bool leader = (gl % (LR / M)) == 0;
+    const float other = __shfl_xor(v[0], LR / 2, 64);   // the up value of the same (row, token)
+    if (leader && idx < M / 2) {
+      const int ra = idx / T, i = idx % T;
+      const int r = rb + ra * G + grp;
+      if (r < nrows && ((mask >> i) & 1)) {
+        const float g = v[0], u = other;
+        const int64_t o = (int64_t)pair[i] * inter + r0 + r;
+        h[o] = g / (1.0f + expf(-g)) * u;
+        if (gtap) gtap[o] = g;
+        if (utap) utap[o] = u;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down projection (direct route): per pair d = W_down[e] . hhat(pair)
+// ---------------------------------------------------------------------------
+template <int F, int A, int T, int LR, int P>
+__global__ void __launch_bounds__(MOE_THREADS)
+moe_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int row_bytes,
+                int units_per_row, int rows_per_tile, const uint8_t* __restrict__ hq, int hrow_bytes,
+                int t_real, const int32_t* __restrict__ ids, int topk, float* __restrict__ dpair) {
+  using FT = Fmt<F>;
+  constexpr int G = MOE_THREADS / LR;
+  constexpr int RA = T >= 8 ? 1 : 8 / T;
+  constexpr int M = RA * T;
+  static_assert(M <= LR, "");
+  extern __shared__ uint32_t smem[];
+  const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
+
+  int e, pair[T];
+  uint32_t mask;
+  if (!expert_tokens<T>(ids, blockIdx.y, t_real, topk, n_expert, e, mask, pair)) return;
+
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_tile;
+  const int nrows = (int)min<int64_t>(rows_per_tile, hidden - r0);
+  const uint32_t sd = stage_bytes(wd + ((int64_t)e * hidden + r0) * row_bytes, (int64_t)nrows * row_bytes, smem,
+                                  tid, MOE_THREADS);
+  ActUnit<F> act[P][T];
+  int ub[P], uu[P];
+  bool uv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int u = gl + p * LR;
+    uv[p] = u < units_per_row;
+    ub[p] = u / FT::UPB;
+    uu[p] = u % FT::UPB;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      if (uv[p] && ((mask >> i) & 1))
+        load_act_unit<F, A>(hq + (size_t)pair[i] * hrow_bytes, ub[p], uu[p], act[p][i]);
+      else zero_act_unit<F>(act[p][i]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const Reader<const uint32_t*> rd{smem};
+  for (int rb = 0; rb < nrows; rb += G * RA) {
+    float v[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] = 0.0f;
+#pragma unroll
+    for (int ra = 0; ra < RA; ++ra) {
+      const int r = rb + ra * G + grp;
+      if (r < nrows) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          if (uv[p]) {
+            Unit<F> un;
+            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, sd + (uint32_t)r * row_bytes + (uint32_t)ub[p] * FT::BB, uu[p], un);
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+              if ((mask >> i) & 1) v[ra * T + i] = unit_combine<F>(un, act[p][i], v[ra * T + i]);
+          }
+        }
+      }
+    }
+    group_reduce_multi<M, LR>(v, gl);
+    const int idx = gl / (LR / M);
+    if ((gl % (LR / M)) == 0) {
+      const int ra = idx / T, i = idx % T;
+      const int r = rb + ra * G + grp;
+      if (r < nrows && ((mask >> i) & 1)) dpair[(int64_t)pair[i] * hidden + r0 + r] = v[0];
+    }
+  }
+}
+
+// y[t][c] = sum_k w[t][k] * d[t*topk+k][c], slot order
+__global__ void __launch_bounds__(256)
+moe_combine_kernel(const float* __restrict__ d, const float* __restrict__ w, int64_t t, int topk, int64_t hidden,
+                   float* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= t * hidden) return;
+  const int64_t tok = i / hidden, c = i % hidden;
+  float s = 0.0f;
+  for (int k = 0; k < topk; ++k) s = fmaf(w[tok * topk + k], d[(tok * topk + k) * hidden + c], s);
+  y[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// launch planning
+// ---------------------------------------------------------------------------
+struct MoePlan { int lr, p, rows_per_tile; };
+
+static MoePlan moe_plan(int units_per_row, int row_bytes, int tiles, int tslot) {
+  MoePlan pl;
+  if (units_per_row <= 64) {
+    pl.p = 1;
+    pl.lr = 16;
+    while (pl.lr < units_per_row) pl.lr *= 2;
+  } else {
+    pl.lr = 64;
+    pl.p = 1;
+    while (pl.p * 64 < units_per_row) pl.p *= 2;
+  }
+  (void)tslot;
+  const int G = MOE_THREADS / pl.lr;
+  int rpt = (40 * 1024) / (tiles * row_bytes);
+  if (rpt > G) rpt = rpt / G * G;
+  if (rpt < 1) rpt = 1;
+  pl.rows_per_tile = rpt;
+  return pl;
+}
+
+template <int F, int A, int T, int LR, int P>
+static hipError_t launch_gate_up_t(const MoeArgs& a, const MoePlan& pl, int row_bytes, int units, int chunk0,
+                                   int tchunk, hipStream_t st) {
+  const int xrb = (int)(a.hidden / Act<A>::BLK * Act<A>::BB);
+  const size_t tile = ((size_t)pl.rows_per_tile * row_bytes + 32) & ~(size_t)15;
+  const dim3 grid((unsigned)((a.inter + pl.rows_per_tile - 1) / pl.rows_per_tile), (unsigned)(tchunk * a.topk));
+  hipLaunchKernelGGL((moe_gate_up_kernel<F, A, T, LR, P>), grid, dim3(MOE_THREADS), 2 * tile + 64, st,
+                     (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, row_bytes, units,
+                     pl.rows_per_tile, (const uint8_t*)a.xq + (size_t)chunk0 * xrb, xrb, tchunk,
+                     a.ids + (size_t)chunk0 * a.topk, a.topk, a.h + (size_t)chunk0 * a.topk * a.inter,
+                     a.g_tap ? a.g_tap + (size_t)chunk0 * a.topk * a.inter : nullptr,
+                     a.u_tap ? a.u_tap + (size_t)chunk0 * a.topk * a.inter : nullptr);
+  return hipGetLastError();
+}
+
+template <int F, int A, int T, int LR, int P>
+static hipError_t launch_down_t(const MoeArgs& a, const MoePlan& pl, int row_bytes, int units, int chunk0,
+                                int tchunk, hipStream_t st) {
+  const int hrb = (int)(a.inter / Act<A>::BLK * Act<A>::BB);
+  const size_t tile = ((size_t)pl.rows_per_tile * row_bytes + 32) & ~(size_t)15;
+  const dim3 grid((unsigned)((a.hidden + pl.rows_per_tile - 1) / pl.rows_per_tile), (unsigned)(tchunk * a.topk));
+  // pair indices inside the chunk are relative to the chunk's first pair
+  hipLaunchKernelGGL((moe_down_kernel<F, A, T, LR, P>), grid, dim3(MOE_THREADS), tile + 64, st,
+                     (const uint8_t*)a.w_down, a.n_expert, a.hidden, row_bytes, units, pl.rows_per_tile,
+                     (const uint8_t*)a.hq + (size_t)chunk0 * a.topk * hrb, hrb, tchunk,
+                     a.ids + (size_t)chunk0 * a.topk, a.topk, a.dpair + (size_t)chunk0 * a.topk * a.hidden);
+  return hipGetLastError();
+}
+
+template <int F, int A, int T>
+static hipError_t gate_up_lp(const MoeArgs& a, const MoePlan& pl, int rb, int units, int c0, int tc,
+                             hipStream_t st) {
+#define FT_GU(LRV, PV) \
+  if (pl.lr == LRV && pl.p == PV) return launch_gate_up_t<F, A, T, LRV, PV>(a, pl, rb, units, c0, tc, st);
+  if constexpr (2 * (T >= 4 ? 1 : 4 / T) * T <= 16) { FT_GU(16, 1) }
+  if constexpr (2 * (T >= 4 ? 1 : 4 / T) * T <= 32) { FT_GU(32, 1) }
+  FT_GU(64, 1) FT_GU(64, 2) FT_GU(64, 4)
+  if constexpr (T <= 2) { FT_GU(64, 8) }
+#undef FT_GU
+  return hipErrorInvalidValue;
+}
+
+template <int F, int A, int T>
+static hipError_t down_lp(const MoeArgs& a, const MoePlan& pl, int rb, int units, int c0, int tc, hipStream_t st) {
+#define FT_DN(LRV, PV) \
+  if (pl.lr == LRV && pl.p == PV) return launch_down_t<F, A, T, LRV, PV>(a, pl, rb, units, c0, tc, st);
+  if constexpr ((T >= 8 ? 1 : 8 / T) * T <= 16) { FT_DN(16, 1) }
+  FT_DN(32, 1) FT_DN(64, 1) FT_DN(64, 2) FT_DN(64, 4)
+  if constexpr (T <= 2) { FT_DN(64, 8) }
+#undef FT_DN
+  return hipErrorInvalidValue;
+}
+
+template <int F, int A>
+static hipError_t moe_stage(const MoeArgs& a, bool gate, hipStream_t st) {
+  const int64_t k = gate ? a.hidden : a.inter;
+  const int row_bytes = (int)(k / Fmt<F>::BLK * Fmt<F>::BB);
+  const int units = (int)units_in_row<F>(k);
+  for (int64_t c0 = 0; c0 < a.t; c0 += 4) {
+    const int tc = (int)(a.t - c0 < 4 ? a.t - c0 : 4);
+    const int tslot = tc <= 1 ? 1 : tc <= 2 ? 2 : 4;
+    const MoePlan pl = moe_plan(units, row_bytes, gate ? 2 : 1, tslot);
+    hipError_t err = hipErrorInvalidValue;
+    if (gate) {
+      if (tslot == 1) err = gate_up_lp<F, A, 1>(a, pl, row_bytes, units, (int)c0, tc, st);
+      else if (tslot == 2) err = gate_up_lp<F, A, 2>(a, pl, row_bytes, units, (int)c0, tc, st);
+      else err = gate_up_lp<F, A, 4>(a, pl, row_bytes, units, (int)c0, tc, st);
+    } else {
+      if (tslot == 1) err = down_lp<F, A, 1>(a, pl, row_bytes, units, (int)c0, tc, st);
+      else if (tslot == 2) err = down_lp<F, A, 2>(a, pl, row_bytes, units, (int)c0, tc, st);
+      else err = down_lp<F, A, 4>(a, pl, row_bytes, units, (int)c0, tc, st);
+    }
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace ftk
+
+using namespace ftk;
+
+hipError_t ftk_launch_route(const float* logits, int64_t t, int64_t n_expert, int topk, int32_t* ids, float* w,
+                            hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)((t + 3) / 4)), dim3(256), 0, st, logits, t, (int)n_expert, topk,
+                     ids, w);
+  return hipGetLastError();
+}
+
+hipError_t ftk_launch_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert, int32_t* counts,
+                           int32_t* offsets, int32_t* pairs, hipStream_t st) {
+  const size_t lds = ((size_t)n_expert + 256) * sizeof(int32_t);
+  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(256), lds, st, ids, t * topk, (int)n_expert, counts, offsets,
+                     pairs);
+  return hipGetLastError();
+}
+
+hipError_t ftk_launch_moe_gate_up(const MoeArgs& a, hipStream_t st) {
+  if (a.w == FT_Q4_K && a.act == FT_Q8_1) return moe_stage<FT_Q4_K, FT_Q8_1>(a, true, st);
+  if (a.w == FT_MXFP4 && a.act == FT_Q8_K) return moe_stage<FT_MXFP4, FT_Q8_K>(a, true, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t ftk_launch_moe_down(const MoeArgs& a, hipStream_t st) {
+  if (a.w == FT_Q4_K && a.act == FT_Q8_1) return moe_stage<FT_Q4_K, FT_Q8_1>(a, false, st);
+  if (a.w == FT_MXFP4 && a.act == FT_Q8_K) return moe_stage<FT_MXFP4, FT_Q8_K>(a, false, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t ftk_launch_moe_combine(const MoeArgs& a, hipStream_t st) {
+  const int64_t n = a.t * a.hidden;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dpair, a.ew, a.t,
+                     a.topk, a.hidden, a.y);
+  return hipGetLastError();
+}

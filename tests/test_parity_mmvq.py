@@ -1,0 +1,105 @@
+"""GPU parity: integer block partials (bit-exact) and the quantized matvec
+(fp32, normwise 1e-5 / NMSE 1e-9) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_quantized_matvec_amd import ft, synth
+from tests.gpu_util import check_fp32, dev, host, log, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(w, a) for w in synth.WEIGHT_FORMATS for a in synth.ACT_FORMATS]
+MMVQ = [("Q4_0", "Q8_1"), ("Q8_0", "Q8_1"), ("Q4_K", "Q8_1")]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("w,a", PAIRS)
+def test_block_dots_bit_exact(w, a):
+    n, k, t = 37, 1536, 3
+    log(f"block_dots {w}x{a}")
+    g = synth.rng(200, synth.WEIGHT_FORMATS.index(w))
+    W = synth.weights(w, n, k, g)
+    xq = oracle.quantize(a, synth.activations(t, k, g))
+    got = host(ft.debug_block_dots(w, dev(W), n, k, a, dev(xq), t))
+    ref = oracle.block_dots(w, W, n, k, a, xq, t)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("w,a", PAIRS)
+def test_block_dots_extreme_codes(w, a):
+    # all-ones weight bytes (every code at its maximum) against activation codes
+    # alternating -128 / +127
+    n, k, t = 3, 512, 1
+    be, bb = synth.BLOCK[w]
+    W = np.full((n, k // be * bb), 0xFF, np.uint8)
+    abe, abb = synth.BLOCK[a]
+    xq = np.zeros((t, k // abe, abb), np.uint8)
+    xq[:, :, 0:4] = 0x3C
+    xq[:, :, 4:4 + abe] = np.where(np.arange(abe) % 2 == 0, 0x80, 0x7F).astype(np.uint8)
+    got = host(ft.debug_block_dots(w, dev(W), n, k, a, dev(xq.reshape(t, -1)), t))
+    assert np.array_equal(got, oracle.block_dots(w, W, n, k, a, xq, t))
+
+
+@pytest.mark.parametrize("w,a", MMVQ)
+@pytest.mark.parametrize("n,k", [(1, 256), (45, 512), (301, 2048), (130, 4352)])
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 5, 8, 9])
+def test_mmvq_small(w, a, n, k, t):
+    log(f"mmvq {w} n={n} k={k} t={t}")
+    g = synth.rng(201, n, k, t)
+    W = synth.weights(w, n, k, g)
+    xq = oracle.quantize(a, synth.activations(t, k, g))
+    y = host(ft.mul_mat_vec_q(w, dev(W), n, k, a, dev(xq), t))
+    check_fp32(y, oracle.matvec(w, W, n, k, a, xq, t), f"{w} n={n} k={k} t={t}")
+
+
+@pytest.mark.parametrize("w,a", MMVQ)
+def test_mmvq_ldy_and_row_tail(w, a):
+    n, k, t = 1000, 1024, 3
+    g = synth.rng(202)
+    W = synth.weights(w, n, k, g)
+    xq = oracle.quantize(a, synth.activations(t, k, g))
+    out = torch.full((t, n + 24), 7.0, device="cuda")
+    dW, dxq = dev(W), dev(xq)          # keep the device copies alive across the call
+    st = ft.lib().ft_mul_mat_vec_q(ft.TYPES[w], ft._ptr(dW), n, k, ft.TYPES[a], ft._ptr(dxq), t,
+                                   ft._ptr(out), n + 24, ft._stream())
+    assert st == 0
+    o = host(out)
+    check_fp32(o[:, :n], oracle.matvec(w, W, n, k, a, xq, t))
+    assert np.all(o[:, n:] == 7.0)
+
+
+def test_q4_0_matvec_full_size():
+    n = k = 2048
+    g = synth.rng(203)
+    W = synth.weights("Q4_0", n, k, g)
+    x = synth.activations(1, k, g)
+    xq_gpu = ft.quantize_act("Q8_1", dev(x))
+    xq = oracle.quantize("Q8_1", x)
+    assert np.array_equal(host(xq_gpu), xq)
+    y = host(ft.mul_mat_vec_q("Q4_0", dev(W), n, k, "Q8_1", xq_gpu, 1))
+    check_fp32(y, oracle.matvec("Q4_0", W, n, k, "Q8_1", xq, 1))
+
+
+@pytest.mark.parametrize("w", ["Q8_0", "Q4_K"])
+@pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_dense_decode_full_size_sampled(w, n, k, t):
+    """Full dense-decode shapes in the bench's launch configuration; the oracle
+    computes a sample of rows (every row of two tiles plus scattered rows)."""
+    log(f"dense decode {w} {n}x{k} t={t}")
+    g = synth.rng(204, n, k, t)
+    W = synth.weights(w, n, k, g)
+    x = synth.activations(t, k, g)
+    xq_gpu = ft.quantize_act("Q8_1", dev(x))
+    xq = oracle.quantize("Q8_1", x)
+    assert np.array_equal(host(xq_gpu), xq)
+    y = host(ft.mul_mat_vec_q(w, dev(W), n, k, "Q8_1", xq_gpu, t))
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 40, n), g.choice(n, 200, replace=False)]))
+    ref = oracle.matvec(w, np.ascontiguousarray(W[rows]), len(rows), k, "Q8_1", xq, t)
+    check_fp32(y[:, rows], ref, f"{w} {n}x{k} t={t}")
