@@ -22,6 +22,33 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 256 << 20         # calibration copy for the FETCH_SIZE / WRITE_SIZE counters
+
+
+def _src_hash():
+    """Hash of the kernel sources: traffic figures are void once the kernels change."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_matvec_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(key):
+    """HBM bytes per launch measured with rocprofv3 counters (null if absent or stale)."""
+    try:
+        d = json.load(open(TRAFFIC_PATH))
+    except (OSError, ValueError):
+        return None
+    e = d.get(key)
+    if not e or e.get("src_hash") != _src_hash():
+        return None
+    return e["bytes_per_launch"]
 
 
 def _args():
@@ -30,15 +57,21 @@ def _args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_decode",
-                    choices=["dense_decode", "q4_0_matvec", "moe_q4k", "moe_mxfp4", "grouped_kq"])
+                    choices=["dense_decode", "q4_0_matvec", "moe_q4k", "moe_mxfp4", "grouped_kq", "counters"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies per matrix (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=str, default="", help="comma list overriding the token counts")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs of `--workload counters` into "
+                         "profiles/traffic.json and exit")
     return ap.parse_args()
 
 
 def main():
     args = _args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "layout is a design note, not a measured path.", file=sys.stderr)
@@ -52,7 +85,7 @@ def main():
         sys.exit(1)
     ft.lib()
     fn = {"dense_decode": bench_dense, "q4_0_matvec": bench_q4_0, "moe_q4k": bench_moe,
-          "moe_mxfp4": bench_moe, "grouped_kq": bench_grouped}[args.workload]
+          "moe_mxfp4": bench_moe, "grouped_kq": bench_grouped, "counters": run_counters}[args.workload]
     out = fn(args, np, torch, ft, synth)
     print(json.dumps(out), flush=True)
 
@@ -60,53 +93,55 @@ def main():
 # ---------------------------------------------------------------------------
 # helpers
 # ---------------------------------------------------------------------------
-class Timer:
-    """Per-launch HIP events on the launching (current) stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def start(self, key):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def stop(self, key, e0):
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e1.record()
-        self.pairs.setdefault(key, []).append((e0, e1))
-
-    def times_us(self, key):
-        return sorted(1000.0 * a.elapsed_time(b) for a, b in self.pairs.get(key, []))
-
-    def avg_us(self, key):
-        ts = self.times_us(key)
-        return sum(ts) / max(len(ts), 1)
-
-    def median_us(self, key):
-        ts = self.times_us(key)
-        return ts[len(ts) // 2] if ts else 0.0
+_CAPTURE_STREAM = None
 
 
-def _cpu_baseline(fn, sample_desc, unit, work):
+def _graph(torch, fn):
+    """Capture fn() into a HIP graph on one dedicated stream.  fn runs once on that
+    stream first, so the library's per-stream scratch pool is grown before capture."""
+    global _CAPTURE_STREAM
+    if _CAPTURE_STREAM is None:
+        _CAPTURE_STREAM = torch.cuda.Stream()
+    s = _CAPTURE_STREAM
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_graph(torch, g, reps):
+    """Average replay time (s) of graph g, replayed `reps` times between two events."""
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def _cpu_baseline(fn, sample_desc, unit, work, min_seconds=10.0):
+    """Time the oracle (as it stands) on the host cores: repeat fn until about
+    min_seconds of CPU work, report work per second."""
     import oracle
+    reps = 0
     t0 = time.perf_counter()
-    fn()
-    dt = time.perf_counter() - t0
-    return {"value": work / dt, "unit": unit, "cores": oracle.threads(), "kind": "oracle",
-            "sample": sample_desc, "seconds": round(dt, 3)}
-
-
-def _timed(torch, steps, warmup, step_fn, timer=None):
-    for i in range(warmup):
-        step_fn(i, None)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step_fn(warmup + i, timer)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(reps * work / dt, 4), "unit": unit, "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{reps} x {sample_desc}", "seconds": round(dt, 2)}
 
 
 # ---------------------------------------------------------------------------
@@ -136,33 +171,46 @@ def bench_dense(args, np, torch, ft, synth):
           for (k, t) in xs}
     cases = [(fmt, n, k, t) for (fmt, n, k) in mats for t in tokens]
     ys = {c: torch.empty((c[3], c[1]), dtype=torch.float32, device="cuda") for c in cases}
-    use = {}
 
-    def step(i, timer):
-        for ci, (fmt, n, k, t) in enumerate(cases):
-            j = use.get((fmt, n, k), 0)
-            use[(fmt, n, k)] = (j + 1) % copies
+    def step(j):
+        """one pass of the path over every case, weight copy j"""
+        for (fmt, n, k, t) in cases:
             ft.quantize_act("Q8_1", dxs[(k, t)], out=xq[(k, t)])
-            e0 = timer.start(ci) if timer else None
             ft.mul_mat_vec_q(fmt, dev[(fmt, n, k)][j], n, k, "Q8_1", xq[(k, t)], t, out=ys[(fmt, n, k, t)])
-            if timer:
-                timer.stop(ci, e0)
 
-    timer = Timer(torch)
-    sec = _timed(torch, args.steps, args.warmup, step, timer)
+    # one graph holds `copies` consecutive steps (step j reads weight copy j)
+    g_steps = _graph(torch, lambda: [step(j) for j in range(copies)])
+    for _ in range(max(1, args.warmup // copies)):
+        g_steps.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // copies))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g_steps.replay()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / (reps * copies)
+    steps_done = reps * copies
+
+    # per-case kernel duration: a graph of R back-to-back launches of that case's
+    # matvec over the rotating copies, timed with two events on the same stream
+    R = 8 * copies
     wbytes = {c: mats[c[:3]].nbytes for c in cases}
     abytes = {c: c[3] * ft.row_bytes("Q8_1", c[2]) + 4 * c[3] * c[1] for c in cases}
-    per_case = []
-    for ci, c in enumerate(cases):
-        us = timer.avg_us(ci)
+    per_case, kus = [], {}
+    for c in cases:
+        fmt, n, k, t = c
+        gk = _graph(torch, lambda: [ft.mul_mat_vec_q(fmt, dev[(fmt, n, k)][i % copies], n, k, "Q8_1",
+                                                     xq[(k, t)], t, out=ys[c]) for i in range(R)])
+        us = _time_graph(torch, gk, 3) / R * 1e6
+        kus[c] = us
         alg = wbytes[c] + abytes[c]
-        per_case.append({"case": f"{c[0]} {c[1]}x{c[2]} t={c[3]}", "kernel_us": round(us, 2),
-                         "median_us": round(timer.median_us(ci), 2),
+        per_case.append({"case": f"{fmt} {n}x{k} t={t}", "kernel_us": round(us, 2),
                          "weight_GBps": round(wbytes[c] / us / 1e3, 1),
                          "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del gk
     head = cases.index(("Q4_K", 14336, 4096, 1)) if ("Q4_K", 14336, 4096, 1) in cases else 0
     hc = cases[head]
-    h_us = timer.avg_us(head)
+    h_us = kus[hc]
     h_alg = wbytes[hc] + abytes[hc]
     achieved = h_alg / h_us / 1e3
     total_w = sum(wbytes.values())
@@ -170,19 +218,19 @@ def bench_dense(args, np, torch, ft, synth):
         "metric": "Q-matvec effective weight GB/s",
         "value": round(total_w / sec / 1e9, 2),
         "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": steps_done, "warmup": args.warmup,
         "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 dot4 -> i32, f32 scale combine",
         "data": "synthetic (seeded GGUF blocks, N(0,1) activations)",
         "config": {"workload": "dense decode matvec: Q8_0 and Q4_K, W 14336x4096 and 4096x14336, "
                                f"batch {'/'.join(map(str, tokens))}, Q8_1 activations; step = quantize + "
-                               "matvec for all cases",
+                               "matvec for all cases, replayed as a HIP graph",
                    "cases": len(cases), "weight_copies_per_matrix": copies,
                    "weight_bytes_per_step": total_w},
         "roofline": {"bound": "hbm", "kernel": f"mmvq {hc[0]} {hc[1]}x{hc[2]} t={hc[3]}",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("mmvq_q4k_14336x4096_t1"),
                      "kernel_us": round(h_us, 3), "alg_bytes_per_launch": h_alg},
         "cases": per_case,
     }
@@ -206,56 +254,52 @@ def bench_q4_0(args, np, torch, ft, synth):
     n, k = c["n"], c["k"]
     g = synth.rng(7, 0)
     W = synth.weights("Q4_0", n, k, g)
-    copies = args.copies or 1024
+    copies = args.copies or 256          # 2.36 MB each: 600 MB rotated
     dW = torch.from_numpy(W).cuda()
     dWs = [dW] + [dW.clone() for _ in range(copies - 1)]
     x = torch.from_numpy(synth.activations(1, k, g)).cuda()
     xq = torch.empty((1, ft.row_bytes("Q8_1", k)), dtype=torch.uint8, device="cuda")
     y = torch.empty((1, n), device="cuda")
     deq = torch.empty((n, k), device="cuda")
+    R = 64
 
-    def step(i, timer):
-        Wc = dWs[i % copies]
-        ft.quantize_act("Q8_1", x, out=xq)
-        e0 = timer.start("mmvq") if timer else None
-        ft.mul_mat_vec_q("Q4_0", Wc, n, k, "Q8_1", xq, 1, out=y)
-        if timer:
-            timer.stop("mmvq", e0)
-            e1 = timer.start("deq")
-        ft.dequant("Q4_0", Wc, n, k, out=deq)
-        if timer:
-            timer.stop("deq", e1)
+    def steps():
+        for j in range(R):
+            ft.quantize_act("Q8_1", x, out=xq)
+            ft.mul_mat_vec_q("Q4_0", dWs[j % copies], n, k, "Q8_1", xq, 1, out=y)
+            ft.dequant("Q4_0", dWs[j % copies], n, k, out=deq)
 
-    timer = Timer(torch)
-    sec = _timed(torch, args.steps, args.warmup, step, timer)
-    us = timer.avg_us("mmvq")
+    gs = _graph(torch, steps)
+    sec = _time_graph(torch, gs, max(1, args.steps // R)) / R
+    gm = _graph(torch, lambda: [ft.mul_mat_vec_q("Q4_0", dWs[j % copies], n, k, "Q8_1", xq, 1, out=y)
+                                for j in range(R)])
+    us = _time_graph(torch, gm, 3) / R * 1e6
+    gd = _graph(torch, lambda: [ft.dequant("Q4_0", dWs[j % copies], n, k, out=deq) for j in range(R)])
+    dus = _time_graph(torch, gd, 3) / R * 1e6
     alg = W.nbytes + ft.row_bytes("Q8_1", k) + 4 * n
     out = {
         "metric": "Q-matvec effective weight GB/s", "value": round(W.nbytes / sec / 1e9, 2), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
+        "n_gpus": 1, "steps": R * max(1, args.steps // R), "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 dot4 -> i32, f32 scale combine", "data": "synthetic",
-        "config": {"workload": "Q4_0 2048x2048: Q8_1 quantize + dequant + single-token matvec",
+        "config": {"workload": "Q4_0 2048x2048: Q8_1 quantize + single-token matvec + dequant, HIP graph",
                    "weight_copies": copies},
         "roofline": {"bound": "hbm", "kernel": "mmvq Q4_0 2048x2048 t=1", "achieved": round(alg / us / 1e3, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel_us": round(us, 3), "alg_bytes_per_launch": alg,
-                     "dequant_us": round(timer.avg_us("deq"), 3)},
+                     "dequant_us": round(dus, 3),
+                     "dequant_GBps": round((W.nbytes + 4 * n * k) / dus / 1e3, 1)},
     }
     if not args.no_cpu_baseline:
         import oracle
         xqn = oracle.quantize("Q8_1", x.cpu().numpy())
-
-        def run():
-            for _ in range(20):
-                oracle.matvec("Q4_0", W, n, k, "Q8_1", xqn, 1)
-        out["cpu_baseline"] = _cpu_baseline(run, "20 single-token Q4_0 2048x2048 matvecs", "GB/s",
-                                            20 * W.nbytes / 1e9)
+        out["cpu_baseline"] = _cpu_baseline(lambda: oracle.matvec("Q4_0", W, n, k, "Q8_1", xqn, 1),
+                                            "single-token Q4_0 2048x2048 matvec", "GB/s", W.nbytes / 1e9)
     return out
 
 
 # ---------------------------------------------------------------------------
-# routed MoE vector layer (direct route), tokens/s
+# routed MoE layer, tokens/s
 # ---------------------------------------------------------------------------
 def bench_moe(args, np, torch, ft, synth):
     c = synth.MOE_Q4K if args.workload == "moe_q4k" else synth.MOE_MXFP4
@@ -272,42 +316,43 @@ def bench_moe(args, np, torch, ft, synth):
         banks.append(tuple(b.clone() for b in banks[0]))
     per_expert = layer_bytes // E
     results = []
-    steps_logits = args.steps + args.warmup
+    G = 2 * layers                       # steps per graph: each reads another layer's bank
     for t in tokens:
         x = torch.from_numpy(synth.activations(t, H, g)).cuda()
-        logits = torch.from_numpy(np.stack([synth.logits(t, E, g) for _ in range(steps_logits)])).cuda()
+        logits = torch.from_numpy(np.stack([synth.logits(t, E, g) for _ in range(G)])).cuda()
+        ids = torch.empty((G, t, topk), dtype=torch.int32, device="cuda")
+        w = torch.empty((G, t, topk), dtype=torch.float32, device="cuda")
         y = torch.empty((t, H), device="cuda")
         ft.scratch_reserve(ft.moe_scratch_bytes(fmt, act, E, H, I, t, topk))
-        uniq = []
 
-        def step(i, timer):
-            wgb, wub, wdb = banks[i % layers]
-            ids, w = ft.moe_route(logits[i], topk)
-            e0 = timer.start("layer") if timer else None
-            ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, ids, w, out=y)
-            if timer:
-                timer.stop("layer", e0)
-                uniq.append(ids)
+        def steps():
+            for i in range(G):
+                wgb, wub, wdb = banks[i % layers]
+                ft.moe_route(logits[i], topk, ids=ids[i], w=w[i])
+                ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, ids[i], w[i], out=y)
 
-        timer = Timer(torch)
-        sec = _timed(torch, args.steps, args.warmup, step, timer)
-        u = np.mean([len(np.unique(i.cpu().numpy())) for i in uniq])
-        us = timer.avg_us("layer")
+        gs = _graph(torch, steps)
+        sec = _time_graph(torch, gs, max(1, args.steps // G)) / G
+        idh = ids.cpu().numpy()
+        u = float(np.mean([len(np.unique(idh[i])) for i in range(G)]))
         results.append({"tokens": t, "tok_per_s": round(t / sec, 1), "layer_us": round(sec * 1e6, 2),
-                        "moe_vec_us": round(us, 2), "unique_experts": round(float(u), 2),
-                        "weight_GBps": round(u * per_expert / us / 1e3, 1),
-                        "hbm_frac": round(u * per_expert / us / 1e3 / HBM_PEAK_GBS, 4)})
+                        "unique_experts": round(u, 2),
+                        "weight_GBps": round(u * per_expert / sec / 1e9, 1),
+                        "hbm_frac": round(u * per_expert / sec / 1e9 / HBM_PEAK_GBS, 4)})
+        del gs
     head = results[0]
     out = {
         "metric": "routed-MoE layer tokens/s", "value": head["tok_per_s"], "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["layer_us"] / 1e3,
+        "n_gpus": 1, "steps": G * max(1, args.steps // G), "warmup": args.warmup,
+        "ms_per_step": round(head["layer_us"] / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 dot4 -> i32, f32 scale combine", "data": "synthetic (router logits redrawn every step)",
-        "config": {"workload": f"routed MoE layer {fmt} x {act}: hidden {H}, {E} experts of {I}, top-{topk}, "
-                               f"direct route; step = route + quantize + gate/up+SwiGLU + quantize + down + combine",
+        "config": {"workload": f"routed MoE layer {fmt} x {act}: hidden {H}, {E} experts of {I}, top-{topk}; "
+                               "step = route + quantize + gate/up+SwiGLU + quantize + down + combine, HIP graph",
                    "tokens": tokens, "layer_banks": layers},
-        "roofline": {"bound": "hbm", "kernel": "moe_q_vec (all stages)", "achieved": head["weight_GBps"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["hbm_frac"], "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "whole MoE layer (unique experts' weight bytes / layer time)",
+                     "achieved": head["weight_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["hbm_frac"], "traffic": None},
         "per_tokens": results,
     }
     return out
@@ -331,39 +376,94 @@ def bench_grouped(args, np, torch, ft, synth):
             per_pair = proj == "down"
             x = torch.from_numpy(synth.activations(T * topk if per_pair else T, k, g)).cuda()
             xq = ft.quantize_act("Q8_K", x)
-            ids_pool = [torch.from_numpy(synth.expert_ids(T, E, topk, g)).cuda() for _ in range(4)]
+            ids_pool = [torch.from_numpy(synth.expert_ids(T, E, topk, g)).cuda() for _ in range(copies)]
             y = torch.empty((T * topk, n), device="cuda")
             ft.scratch_reserve(1 << 20)
-
-            def step(i, timer):
-                e0 = timer.start("g") if timer else None
-                ft.grouped_gemm_q(fmt, dWs[i % copies], E, n, k, "Q8_K", xq, per_pair, ids_pool[i % 4], out=y)
-                if timer:
-                    timer.stop("g", e0)
-
-            timer = Timer(torch)
-            _timed(torch, args.steps, args.warmup, step, timer)
-            us = timer.avg_us("g")
+            gg = _graph(torch, lambda: [ft.grouped_gemm_q(fmt, dWs[i], E, n, k, "Q8_K", xq, per_pair, ids_pool[i], out=y)
+                                        for i in range(copies)])
+            us = _time_graph(torch, gg, max(1, args.steps // copies)) / copies * 1e6
             ops = 2.0 * T * topk * n * k
             alg = W.nbytes + xq.numel() + y.numel() * 4
             results.append({"case": f"{fmt} {proj} {n}x{k}", "us": round(us, 2),
                             "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
                             "int8_TOPS": round(ops / us / 1e6, 2),
                             "mfma_frac": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)})
-            del dWs, dW
+            del dWs, dW, gg
     head = results[0]
     out = {
         "metric": "grouped expert GEMM int8 TOP/s", "value": head["int8_TOPS"], "unit": "TOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["us"] / 1e3,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us"] / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 dot4 -> i32, f32 scale combine", "data": "synthetic",
+        "dtype": "i8 -> i32, f32 scale combine", "data": "synthetic",
         "config": {"workload": f"grouped keep-quant GEMM: {T} tokens, hidden {H}, {E} experts of {I}, "
-                               f"top-{topk}, Q5_K/Q6_K x Q8_K"},
+                               f"top-{topk}, Q5_K/Q6_K x Q8_K (sort + GEMM per launch), HIP graph"},
         "roofline": {"bound": "hbm", "kernel": head["case"], "achieved": round(head["hbm_frac"] * HBM_PEAK_GBS, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["hbm_frac"], "traffic": None},
         "cases": results,
     }
     return out
+
+
+# ---------------------------------------------------------------------------
+# counter runs: a device copy of known size (calibration) and the headline kernel
+# ---------------------------------------------------------------------------
+def run_counters(args, np, torch, ft, synth):
+    a = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    n, k = 14336, 4096
+    g = synth.rng(7, 1)
+    W = torch.from_numpy(synth.weights("Q4_K", n, k, g)).cuda()
+    Ws = [W] + [W.clone() for _ in range(7)]
+    xq = ft.quantize_act("Q8_1", torch.from_numpy(synth.activations(1, k, g)).cuda())
+    y = torch.empty((1, n), device="cuda")
+    for i in range(20):
+        ft.mul_mat_vec_q("Q4_K", Ws[i % 8], n, k, "Q8_1", xq, 1, out=y)
+    torch.cuda.synchronize()
+    return {"counters_run": "copy 256 MiB x3, mmvq Q4_K 14336x4096 t=1 x20"}
+
+
+def traffic_from(fetch_csv, write_csv):
+    import csv
+    import statistics
+
+    def rows(path, counter):
+        return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+    def calib(rs):
+        # run_counters issues the three 256 MiB calibration copies before anything
+        # else that copies (the weight clones come after them)
+        cp = sorted((r for r in rs if "copyBuffer" in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+        return [float(r["Counter_Value"]) for r in cp[:3]]
+
+    rf, rw = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
+    copy_f, copy_w = calib(rf), calib(rw)
+    f = {}
+    w = {}
+    for r in rf:
+        f.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    for r in rw:
+        w.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    # counters report KiB; the copy reads and writes COPY_BYTES each
+    fscale = COPY_BYTES / (statistics.median(copy_f) * 1024)
+    wscale = COPY_BYTES / (statistics.median(copy_w) * 1024)
+    mf = [v for kname, vs in f.items() if "mmvq" in kname for v in vs]
+    mw = [v for kname, vs in w.items() if "mmvq" in kname for v in vs]
+    fetch = statistics.mean(mf) * 1024 * fscale
+    write = statistics.mean(mw) * 1024 * wscale
+    try:
+        d = json.load(open(TRAFFIC_PATH))
+    except (OSError, ValueError):
+        d = {}
+    d["mmvq_q4k_14336x4096_t1"] = {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
+                                   "write_bytes": round(write), "fetch_scale": round(fscale, 4),
+                                   "write_scale": round(wscale, 4), "launches": len(mf),
+                                   "src_hash": _src_hash()}
+    os.makedirs(os.path.dirname(TRAFFIC_PATH), exist_ok=True)
+    json.dump(d, open(TRAFFIC_PATH, "w"), indent=1)
+    print(json.dumps(d["mmvq_q4k_14336x4096_t1"]))
 
 
 if __name__ == "__main__":

@@ -40,6 +40,7 @@ template <int F> struct Fmt;
 // of qs[e-16]; w = d*(n-8).  One unit, one segment.
 template <> struct Fmt<FT_Q4_0> {
   static constexpr int BLK = 32, BB = 18, UPB = 1, NW = 8, S = 1, SUB = 32;
+  static constexpr bool XF1 = false;      // see Fmt<FT_Q4_K>
   static constexpr bool HAS_MIN = true;   // the -8 offset, as wmin = 8d
   static constexpr int CODE_OFF = 8;      // exported partials use n - 8
   __device__ static int act_elem(int, int j) { return 4 * j; }
@@ -48,6 +49,7 @@ template <> struct Fmt<FT_Q4_0> {
 // Q8_0: fp16 d @0, int8 qs[32] @2; w = d*q.
 template <> struct Fmt<FT_Q8_0> {
   static constexpr int BLK = 32, BB = 34, UPB = 1, NW = 8, S = 1, SUB = 32;
+  static constexpr bool XF1 = false;
   static constexpr bool HAS_MIN = false;
   static constexpr int CODE_OFF = 0;
   __device__ static int act_elem(int, int j) { return 4 * j; }
@@ -57,6 +59,7 @@ template <> struct Fmt<FT_Q8_0> {
 // twice the E2M1 value (an integer in [-12, 12]).
 template <> struct Fmt<FT_MXFP4> {
   static constexpr int BLK = 32, BB = 17, UPB = 1, NW = 8, S = 1, SUB = 32;
+  static constexpr bool XF1 = false;
   static constexpr bool HAS_MIN = false;
   static constexpr int CODE_OFF = 0;
   __device__ static int act_elem(int, int j) { return 4 * j; }
@@ -65,9 +68,13 @@ template <> struct Fmt<FT_MXFP4> {
 // Q4_K: d @0, dmin @2, scales[12] @4, qs[128] @16.  Element e = 64c + 32h + l is
 // nibble h of qs[32c+l]; sub-block j = 2c+h.  Unit c covers qs[32c .. 32c+31]:
 // dwords 0-7 are its low nibbles (sub-block 2c), dwords 8-15 its high nibbles
-// (sub-block 2c+1).
+// (sub-block 2c+1).  XF1: the high nibbles are taken as the int8 bytes
+// (q & 0xF0) ^ 0x80 = 16*hi - 128 (one bitwise op per dword); their dot D relates
+// to the true one by I = (D + 128*B)/16, folded into the activation scale (dx/16)
+// and the min term (wmin - 8*wscale).
 template <> struct Fmt<FT_Q4_K> {
   static constexpr int BLK = 256, BB = 144, UPB = 4, NW = 16, S = 2, SUB = 32;
+  static constexpr bool XF1 = true;
   static constexpr bool HAS_MIN = true;
   static constexpr int CODE_OFF = 0;
   __device__ static int act_elem(int ui, int j) { return 64 * ui + (j < 8 ? 4 * j : 32 + 4 * (j - 8)); }
@@ -77,6 +84,7 @@ template <> struct Fmt<FT_Q4_K> {
 // fifth bit of element 64c+32h+l in bit (2c+h) of qh[l].
 template <> struct Fmt<FT_Q5_K> {
   static constexpr int BLK = 256, BB = 176, UPB = 4, NW = 16, S = 2, SUB = 32;
+  static constexpr bool XF1 = false;
   static constexpr bool HAS_MIN = true;
   static constexpr int CODE_OFF = 0;
   __device__ static int act_elem(int ui, int j) { return Fmt<FT_Q4_K>::act_elem(ui, j); }
@@ -88,6 +96,7 @@ template <> struct Fmt<FT_Q5_K> {
 // Unit ui = 4g + (l0/8) covers l in [l0, l0+8) for all four r: dwords 2r, 2r+1.
 template <> struct Fmt<FT_Q6_K> {
   static constexpr int BLK = 256, BB = 210, UPB = 8, NW = 8, S = 4, SUB = 16;
+  static constexpr bool XF1 = false;
   static constexpr bool HAS_MIN = true;   // the -32 offset, as wmin = 32*d*sc
   static constexpr int CODE_OFF = 32;
   __device__ static int act_elem(int ui, int j) {
@@ -235,6 +244,29 @@ __device__ __forceinline__ uint32_t e2m1x2_bytes(uint32_t c) {
   return (neg & mask) | (pos & ~mask);
 }
 
+// K-quant unit c from registers: header h (d|dmin, 12 scale bytes), the 32 nibble
+// bytes q of chunk c and, for Q5_K, the 32 fifth-bit bytes qh.
+template <int F>
+__device__ __forceinline__ void kq_unit(const uint32_t (&h)[4], const uint32_t (&q)[8], const uint32_t (&qh)[8],
+                                        int c, Unit<F>& u) {
+  kq_header(h[0], h[1], h[2], h[3], c, u.ws, u.wm);
+  if constexpr (F == FT_Q4_K) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      u.w[m] = q[m] & 0x0F0F0F0Fu;
+      u.w[8 + m] = (q[m] & 0xF0F0F0F0u) ^ 0x80808080u;   // 16*hi - 128 as int8
+    }
+    u.wm[1] = fmaf(-8.0f, u.ws[1], u.wm[1]);
+  } else {
+    const uint32_t hb = 2u * (uint32_t)c;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      u.w[m] = (q[m] & 0x0F0F0F0Fu) | (((qh[m] >> hb) & 0x01010101u) << 4);
+      u.w[8 + m] = ((q[m] >> 4) & 0x0F0F0F0Fu) | (((qh[m] >> (hb + 1)) & 0x01010101u) << 4);
+    }
+  }
+}
+
 // A16: the block's offset is 16-byte aligned in the reader (K-quant rows always
 // are: 144- and 176-byte blocks in 16-byte-aligned rows).
 template <int F, bool A16, typename R>
@@ -265,33 +297,18 @@ __device__ __forceinline__ void unpack_unit(const R& rd, uint32_t bo, int ui, Un
       u.w[4 + m] = e2m1x2_bytes((q[m] >> 4) & 0x0F0F0F0Fu);
     }
   } else if constexpr (F == FT_Q4_K || F == FT_Q5_K) {
-    uint32_t h[4], q[8];
+    uint32_t h[4], q[8], qh[8];
     constexpr uint32_t QOFF = F == FT_Q4_K ? 16 : 48;
     if constexpr (A16) {
       rd.template dwords16<4>(bo, h);
       rd.template dwords16<8>(bo + QOFF + 32 * ui, q);
+      if constexpr (F == FT_Q5_K) rd.template dwords16<8>(bo + 16, qh);
     } else {
       rd.template dwords<4>(bo, h);
       rd.template dwords<8>(bo + QOFF + 32 * ui, q);
+      if constexpr (F == FT_Q5_K) rd.template dwords<8>(bo + 16, qh);
     }
-    kq_header(h[0], h[1], h[2], h[3], ui, u.ws, u.wm);
-    if constexpr (F == FT_Q4_K) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        u.w[m] = q[m] & 0x0F0F0F0Fu;
-        u.w[8 + m] = (q[m] >> 4) & 0x0F0F0F0Fu;
-      }
-    } else {
-      uint32_t qh[8];
-      if constexpr (A16) rd.template dwords16<8>(bo + 16, qh);
-      else rd.template dwords<8>(bo + 16, qh);
-      const uint32_t hb = 2u * (uint32_t)ui;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        u.w[m] = (q[m] & 0x0F0F0F0Fu) | (((qh[m] >> hb) & 0x01010101u) << 4);
-        u.w[8 + m] = ((q[m] >> 4) & 0x0F0F0F0Fu) | (((qh[m] >> (hb + 1)) & 0x01010101u) << 4);
-      }
-    }
+    kq_unit<F>(h, q, qh, ui, u);
   } else {  // Q6_K
     const int g = ui >> 2, l0 = 8 * (ui & 3);
     uint32_t qa[2], qb[2], qh[2];
@@ -322,8 +339,8 @@ __device__ __forceinline__ void unpack_unit(const R& rd, uint32_t bo, int ui, Un
 // ---------------------------------------------------------------------------
 template <int F> struct ActUnit {
   uint32_t x[Fmt<F>::NW];      // int8x4 codes, dword j <-> Fmt<F>::act_elem(ui, j)
-  float dx[Fmt<F>::S];         // activation scale of each segment
-  float dxb[Fmt<F>::S];        // dx * (sum of the segment's codes)
+  float dx[Fmt<F>::S];         // activation scale of each segment (dx/16 for XF1's segment 1)
+  float dxb[Fmt<F>::S];        // true dx * (sum of the segment's codes)
   int bsum[Fmt<F>::S];         // sum of the segment's codes
 };
 
@@ -357,9 +374,15 @@ __device__ __forceinline__ void load_act_unit(const uint8_t* __restrict__ xrow, 
     float dx;
     if (A == FT_Q8_1) dx = h2f(*(const uint16_t*)ab);
     else dx = *(const float*)ab;
-    a.dx[s] = dx;
     a.dxb[s] = dx * (float)a.bsum[s];
+    a.dx[s] = (Fmt<F>::XF1 && s == 1) ? dx * 0.0625f : dx;
   }
+}
+
+// true integer dot of segment s from the raw dot D of the unpacked codes
+template <int F>
+__device__ __forceinline__ int seg_true_dot(int s, int D, int bsum) {
+  return (Fmt<F>::XF1 && s == 1) ? (D + 128 * bsum) >> 4 : D;
 }
 
 template <int F>

@@ -20,12 +20,15 @@ struct MmvqArgs {
 };
 
 struct MmvqPlan {
+  int direct;         // 1: LDS-free variant (aligned K-quants), rows_per_wg = rows per wave
   int tslot;          // token slots of the kernel (1, 2, 4, 8)
   int lr, p;          // lanes per row, units per lane
-  int cpl;            // 16-byte chunks per lane per tile
+  int cpl;            // 16-byte chunks per lane per tile (LDS variant)
+  int rb;             // rows per register batch (direct variant)
   int rows_per_tile, rows_per_wg, grid;
 };
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out);
+int ftk_mmvq_plan_fmt(int units_per_row, int tslot, int row_bytes, int64_t n, bool aligned_kquant, MmvqPlan* out);
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
 
 hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,

@@ -176,7 +176,7 @@ block_dots_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, const uin
 #pragma unroll
     for (int s = 0; s < FT::S; ++s) {
       const int sub = FT::act_elem(ui, seg_first<F>(s)) / FT::SUB;
-      const int val = I[s] - FT::CODE_OFF * au.bsum[s];
+      const int val = seg_true_dot<F>(s, I[s], au.bsum[s]) - FT::CODE_OFF * au.bsum[s];
 #pragma unroll
       for (int i = 0; i < NSUB; ++i)
         if (i == sub) acc[i] += val;

@@ -157,11 +157,14 @@ def mul_mat_vec_q(w: str, W: torch.Tensor, n: int, k: int, act: str, xq: torch.T
     return out
 
 
-def moe_route(logits: torch.Tensor, topk: int, stream=None):
+def moe_route(logits: torch.Tensor, topk: int, ids: torch.Tensor | None = None, w: torch.Tensor | None = None,
+              stream=None):
     _dev(logits, "logits")
     t, e = logits.shape
-    ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
-    w = torch.empty((t, topk), dtype=torch.float32, device=logits.device)
+    if ids is None:
+        ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((t, topk), dtype=torch.float32, device=logits.device)
     _check(lib().ft_moe_route(_ptr(logits), t, e, topk, _ptr(ids), _ptr(w), _stream(stream)), "ft_moe_route")
     return ids, w
 
