@@ -28,6 +28,8 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE fp32 divide (the quantizers decide integers from x/d)
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-ffp-contract=fast",
+    # MFMA results in VGPRs (no AGPR copies back for the integer scale combine)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]

@@ -1,146 +1,427 @@
-// ft_grouped.hip -- grouped keep-quant expert GEMM over expert-sorted pairs.
+// ft_grouped.hip -- grouped keep-quant expert GEMM over expert-sorted pairs, on
+// int8 MFMA.
 //
 // vllm.cpp PR #523 "grouped + non-grouped keep-quant expert GEMM" (What changed:
-// the keep-quant op grouped over expert_ids) and ds4 PR #656 (Summary: larger
-// batches on expert-sorted tiles).  y[p] = W[ids[p]] . xhat_row(p) with
-// p = token*topk + slot.  The token->expert sort (ft_moe.hip) gives each expert
-// its contiguous list of pairs; a workgroup owns (expert, tile of output rows),
-// streams that tile of the expert's weights into LDS once with 16-byte
-// global_load_lds, and applies it to every pair of the expert, four pairs per
-// pass with the activation codes in VGPRs.  Rows never mix across pairs, so the
-// order inside the sort cannot change any result.
+// the keep-quant op grouped over expert_ids, with a superblock integer dot core)
+// and ds4 PR #656 (Summary: larger batches on expert-sorted tiles).
+// y[p] = W[ids[p]] . xhat_row(p), p = token*topk + slot.  The token->expert sort
+// (ft_moe.hip) gives each expert its contiguous list of pairs.
+//
+// Contraction on gfx950 (wave64, v_mfma_i32_16x16x32_i8):
+//  * A workgroup owns (expert, 128 output rows; 64 for Q6_K); each of its four
+//    waves owns 32 rows as two 16-row MFMA B operands that share every A-operand
+//    read (16 rows for Q6_K, whose two MFMAs and two scales per group need the
+//    registers), and every pair of the expert passes through it in tiles of 16
+//    pairs (the A operand).  The expert's weight bytes are read from HBM once.
+//  * Lane l of an MFMA holds weight row l%16 and the 8 codes 8(l/16)..8(l/16)+7 of
+//    every 32-element group; the int32 result of one group is scaled by that
+//    row's integer sub-block scale in the same lane (one v_mad_i32_i24 per output
+//    and sub-block).  Q6_K's 16-element sub-blocks take two MFMAs per group whose
+//    A operands are zero in the other half's lanes (those lanes read an all-zero
+//    LDS tile).
+//  * The K-quant min term sum_j m_j*B_j (B_j = sum of the activation codes of
+//    sub-block j) and Q6_K's -32 offset term run on v_mfma_f32_16x16x16_f16 over
+//    the 16-element code sums, which are exact in fp16 (|sum| <= 2032) and whose
+//    products and sums are exact in fp32.
+//  * MXFP4 blocks are 32-element groups with a power-of-two scale: each group's
+//    int32 result is converted and scaled in fp32.
+//  * Per 256-element superblock the workgroup stages the activations of up to PT
+//    pair tiles into LDS, in MFMA A-operand order, with the 16-element code sums
+//    computed from the codes; each wave stages its rows' weight bytes into its own
+//    LDS slots with 16-byte loads.  Both are fetched into VGPRs one superblock
+//    ahead and published to LDS between two barriers.
+//  * Workgroups are numbered so that all row tiles of one expert run on one XCD
+//    (dispatch goes round-robin over the eight XCDs), so an expert's activation
+//    rows are fetched into one L2.
+// Rows never mix across pairs, so the order inside the sort cannot change any
+// result.
+#include <math.h>
+
 #include "ft_device.h"
 #include "ft_internal.h"
 
 namespace ftk {
 
-constexpr int GRP_THREADS = 256;
-constexpr int GRP_T = 4;  // pairs per pass
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int F, int A, int LR, int P>
-__global__ void __launch_bounds__(GRP_THREADS)
-grouped_dot4_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_per_row,
-                    int rows_per_tile, const uint8_t* __restrict__ xq, int xrow_bytes, int x_per_pair,
-                    int topk, const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
-                    float* __restrict__ y) {
-  using FT = Fmt<F>;
-  constexpr int T = GRP_T;
-  constexpr int G = GRP_THREADS / LR;
-  constexpr int RA = 2;
-  constexpr int M = RA * T;
-  static_assert(M <= LR, "");
-  extern __shared__ uint32_t smem[];
-  const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
-  const int e = blockIdx.y;
+constexpr int GM_WAVES = 4;
+constexpr int GM_THREADS = 64 * GM_WAVES;
+// 16-row MFMA groups per wave (they share every A-operand read); Q6_K's two
+// MFMAs and two scales per group need the registers of a second group
+template <int F> struct GRg { static constexpr int RG = F == FT_Q6_K ? 1 : 2; };
+template <int F> constexpr int gm_rows() { return 16 * GRg<F>::RG * GM_WAVES; }   // rows per workgroup
+
+// One 256-element superblock of a weight row: BYTES in HBM; SLOT bytes in LDS
+// (room for a misaligned start; SLOT/16 odd keeps the 16 rows of an MFMA group on
+// distinct LDS banks).
+template <int F> struct GSb;
+template <> struct GSb<FT_Q4_K> { static constexpr int BYTES = 144, SLOT = 144; static constexpr bool ALIGNED = true; };
+template <> struct GSb<FT_Q5_K> { static constexpr int BYTES = 176, SLOT = 176; static constexpr bool ALIGNED = true; };
+template <> struct GSb<FT_Q6_K> { static constexpr int BYTES = 210, SLOT = 240; static constexpr bool ALIGNED = false; };
+template <> struct GSb<FT_MXFP4> { static constexpr int BYTES = 136, SLOT = 176; static constexpr bool ALIGNED = false; };
+
+// LDS layout (bytes) for PT pair tiles: one superblock's buffer of BUF bytes, then
+// the all-zero tile of the Q6_K half masks.
+template <int F, int PT> struct GLds {
+  static constexpr int GSTR = 544;                       // bytes per 32-element group (512 + bank pad)
+  static constexpr int TSTR = 8 * GSTR;                  // bytes per pair tile
+  static constexpr int CODES = 0;                        // [PT][8 groups][64 lanes] x 8 B (+ pad)
+  static constexpr int BSUM = CODES + PT * TSTR;         // [PT][64 lanes] x 4 fp16
+  static constexpr int DX = BSUM + PT * 512;             // [PT][16 pairs] fp32
+  static constexpr int WT = DX + PT * 64;                // [waves][16*RG rows][SLOT]
+  static constexpr int BUF = WT + GM_WAVES * 16 * GRg<F>::RG * GSb<F>::SLOT;
+  static constexpr int ZTILE = BUF;                      // the zero tile
+  static constexpr int TOTAL = ZTILE + (F == FT_Q6_K ? TSTR : 0);
+};
+
+// Weight operands of one 16-row group for one superblock, in one lane.
+template <int F> struct GW {
+  uint64_t b[8];    // int8 codes of the lane's 8 elements of each 32-element group
+  int sc[8];        // integer sub-block scales (Q4_K/Q5_K)
+  uint32_t scp[4];  // Q6_K: the 16 int8 sub-block scales, packed
+  float s[8];       // MXFP4: 2^(e-128) per block
+  v4h mb;           // f16 MFMA B operand of the min / offset term
+  float d, dmin;
+};
+
+__device__ __forceinline__ uint64_t pk64(uint32_t lo, uint32_t hi) { return (uint64_t)lo | ((uint64_t)hi << 32); }
+
+// Decode the lane's share of one superblock from its row slot (LDS).  o: byte
+// offset of the superblock in the slot (0 for the 16-byte-aligned formats).
+template <int F>
+__device__ __forceinline__ void gw_decode(const uint8_t* sl, uint32_t o, int q, GW<F>& w) {
+  if constexpr (F == FT_Q4_K || F == FT_Q5_K) {
+    const u32x4 h = *(const u32x4*)sl;
+    uint32_t sc_lo, sc_hi, m_lo, m_hi;
+    kq_unpack_scales(h.y, h.z, h.w, sc_lo, sc_hi, m_lo, m_hi);
+    w.d = h2f(h.x & 0xFFFFu);
+    w.dmin = h2f(h.x >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w.sc[j] = (int)((sc_lo >> (8 * j)) & 0xFFu);
+      w.sc[4 + j] = (int)((sc_hi >> (8 * j)) & 0xFFu);
+    }
+    // min operand: lane quarter q covers code sums 4q..4q+3 = sub-blocks 2q, 2q+1
+    const uint32_t mm = ((q < 2) ? m_lo : m_hi) >> (16 * (q & 1));
+    const _Float16 ma = (_Float16)(float)(mm & 0xFFu), mb = (_Float16)(float)((mm >> 8) & 0xFFu);
+    w.mb = (v4h){ma, ma, mb, mb};
+    uint32_t e0 = 0, e1 = 0;
+    if constexpr (F == FT_Q5_K) {
+      const u32x2 e = *(const u32x2*)(sl + 16 + 8 * q);
+      e0 = e.x;
+      e1 = e.y;
+    }
+    constexpr int QO = F == FT_Q4_K ? 16 : 48;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x2 v = *(const u32x2*)(sl + QO + 32 * c + 8 * q);
+      uint32_t l0 = v.x & 0x0F0F0F0Fu, l1 = v.y & 0x0F0F0F0Fu;
+      uint32_t h0 = (v.x >> 4) & 0x0F0F0F0Fu, h1 = (v.y >> 4) & 0x0F0F0F0Fu;
+      if constexpr (F == FT_Q5_K) {
+        l0 |= ((e0 >> (2 * c)) & 0x01010101u) << 4;
+        l1 |= ((e1 >> (2 * c)) & 0x01010101u) << 4;
+        h0 |= ((e0 >> (2 * c + 1)) & 0x01010101u) << 4;
+        h1 |= ((e1 >> (2 * c + 1)) & 0x01010101u) << 4;
+      }
+      w.b[2 * c] = pk64(l0, l1);
+      w.b[2 * c + 1] = pk64(h0, h1);
+    }
+  } else if constexpr (F == FT_Q6_K) {
+    const Reader<const uint32_t*> rd{(const uint32_t*)sl};
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      uint32_t a[2], bq[2], hq[2];
+      rd.template dwords<2>(o + 64 * g + 8 * q, a);        // groups r = 0 (low nibbles), 2 (high)
+      rd.template dwords<2>(o + 64 * g + 32 + 8 * q, bq);  // groups r = 1, 3
+      rd.template dwords<2>(o + 128 + 32 * g + 8 * q, hq); // top two bits of all four
+      uint32_t c[4][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        c[0][m] = (a[m] & 0x0F0F0F0Fu) | ((hq[m] << 4) & 0x30303030u);
+        c[1][m] = (bq[m] & 0x0F0F0F0Fu) | ((hq[m] << 2) & 0x30303030u);
+        c[2][m] = ((a[m] >> 4) & 0x0F0F0F0Fu) | (hq[m] & 0x30303030u);
+        c[3][m] = ((bq[m] >> 4) & 0x0F0F0F0Fu) | ((hq[m] >> 2) & 0x30303030u);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w.b[4 * g + r] = pk64(c[r][0], c[r][1]);
+    }
+    uint32_t s4[4];
+    rd.template dwords<4>(o + 192, s4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w.scp[i] = s4[i];   // int8 scales stay packed (register pressure)
+    const uint32_t sq = q == 0 ? s4[0] : q == 1 ? s4[1] : q == 2 ? s4[2] : s4[3];
+    w.mb = (v4h){(_Float16)(float)(int8_t)(sq & 0xFFu), (_Float16)(float)(int8_t)((sq >> 8) & 0xFFu),
+                 (_Float16)(float)(int8_t)((sq >> 16) & 0xFFu), (_Float16)(float)(int8_t)(sq >> 24)};
+    w.d = h2f(rd.u16(o + 208));
+    w.dmin = 0.0f;
+  } else {  // MXFP4: 8 blocks of 17 bytes
+    const Reader<const uint32_t*> rd{(const uint32_t*)sl};
+    const uint32_t nsh = 4u * (uint32_t)(q >> 1);   // quarters 2, 3 take the high nibbles
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      const uint32_t bo = o + 17 * jb;
+      uint32_t v[2];
+      rd.template dwords<2>(bo + 1 + 8 * (q & 1), v);
+      w.b[jb] = pk64(e2m1x2_bytes((v[0] >> nsh) & 0x0F0F0F0Fu), e2m1x2_bytes((v[1] >> nsh) & 0x0F0F0F0Fu));
+      w.s[jb] = e8m0_half(rd.u8(bo));
+    }
+    w.d = 0.0f;
+    w.dmin = 0.0f;
+  }
+}
+
+template <int F, int PT>
+__global__ void __launch_bounds__(GM_THREADS)
+grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes, int nsb,
+                    const uint8_t* __restrict__ xq, int64_t xrow_bytes, int x_per_pair, int topk,
+                    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
+                    float* __restrict__ y, int64_t row_tiles, int64_t total, int64_t per_xcd) {
+  using SB = GSb<F>;
+  using LY = GLds<F, PT>;
+  constexpr int NCH = SB::SLOT / 16;                   // 16-byte chunks per row slot
+  constexpr int RG = GRg<F>::RG;
+  constexpr int WROWS = 16 * RG;                       // rows per wave
+  constexpr int NWI = (WROWS * NCH + 63) / 64;         // weight chunks per lane
+  constexpr int NAI = (PT * 256 + GM_THREADS - 1) / GM_THREADS;   // activation chunks per thread
+  constexpr bool MINT = F != FT_MXFP4;                 // has a code-sum term
+  constexpr bool KQ = F == FT_Q4_K || F == FT_Q5_K;
+  extern __shared__ u32x4 gsm[];
+  uint8_t* L = (uint8_t*)gsm;
+
+  // XCD-aware numbering: consecutive (expert, row tile) items on one XCD
+  const int64_t bid = blockIdx.x;
+  const int64_t item = (bid & 7) * per_xcd + (bid >> 3);
+  if (item >= total) return;
+  const int e = (int)(item / row_tiles);
+  const int64_t tile = item % row_tiles;
   const int p0 = offsets[e], p1 = offsets[e + 1];
   if (p0 >= p1) return;
 
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_tile;
-  const int nrows = (int)min<int64_t>(rows_per_tile, n - r0);
-  const uint8_t* src = W + ((int64_t)e * n + r0) * row_bytes;
-  const uintptr_t sa = (uintptr_t)src;
-  const uint8_t* a0 = (const uint8_t*)(sa & ~(uintptr_t)15);
-  const uint32_t shift = (uint32_t)(sa & 15);
-  const int nchunks = (int)((shift + (int64_t)nrows * row_bytes + 15) >> 4);
-  for (int base = 0; base < nchunks; base += GRP_THREADS) {
-    const int c = base + tid;
-    if (c < nchunks)
-      __builtin_amdgcn_global_load_lds((const void*)(a0 + 16 * (int64_t)c),
-                                       (__attribute__((address_space(3))) void*)(smem + 4 * (base + (tid >> 6) * 64)),
-                                       16, 0, 0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4, rl = lane & 15;
+  const int64_t wrow0 = tile * gm_rows<F>() + (int64_t)wave * WROWS;   // first row of this wave
+  const uint8_t* wexp = W + (int64_t)e * n * row_bytes;
+  const int wslot = LY::WT + wave * WROWS * SB::SLOT;   // this wave's weight rows in a buffer
+  const v4f zf = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (F == FT_Q6_K) {   // published by the first barrier of the superblock loop
+    for (int i = tid; i < LY::TSTR / 16; i += GM_THREADS) ((u32x4*)(L + LY::ZTILE))[i] = (u32x4){0u, 0u, 0u, 0u};
   }
 
-  int ub[P], uu[P];
-  bool uv[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int u = gl + p * LR;
-    uv[p] = u < units_per_row;
-    ub[p] = u / FT::UPB;
-    uu[p] = u % FT::UPB;
-  }
-  const Reader<const uint32_t*> rd{smem};
+  for (int g0 = p0; g0 < p1; g0 += PT * 16) {
+    const int gm = min(PT * 16, p1 - g0);
+    const int npt = (gm + 15) >> 4;
 
-  for (int c0 = p0; c0 < p1; c0 += T) {
-    const int tc = min(T, p1 - c0);
-    int pr[T];
-    ActUnit<F> act[P][T];
+    // activation staging: item it = tid + GM_THREADS*i is chunk su = it&15 (16 codes)
+    // of pair slot it>>4 of the group
+    const uint8_t* xr[NAI];
 #pragma unroll
-    for (int i = 0; i < T; ++i) {
-      pr[i] = i < tc ? pairs[c0 + i] : 0;
-      const int64_t xrow = x_per_pair ? pr[i] : pr[i] / topk;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (uv[p] && i < tc) load_act_unit<F, A>(xq + xrow * xrow_bytes, ub[p], uu[p], act[p][i]);
-        else zero_act_unit<F>(act[p][i]);
+    for (int i = 0; i < NAI; ++i) {
+      const int pi = (tid + GM_THREADS * i) >> 4;
+      xr[i] = nullptr;
+      if (pi < gm) {
+        const int pr = pairs[g0 + pi];
+        xr[i] = xq + (int64_t)(x_per_pair ? pr : pr / topk) * xrow_bytes;
       }
     }
-    if (c0 == p0) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-    for (int rb = 0; rb < nrows; rb += G * RA) {
-      float v[M];
+    const int su = tid & 15;
+
+    u32x4 pa[NAI];
+    float pdx[NAI];
+    u32x4 pw[NWI];
+    auto fetch = [&](int sb) {
 #pragma unroll
-      for (int i = 0; i < M; ++i) v[i] = 0.0f;
+      for (int i = 0; i < NAI; ++i) {
+        pa[i] = (u32x4){0u, 0u, 0u, 0u};
+        pdx[i] = 0.0f;
+        if (xr[i]) {
+          const uint32_t* src = (const uint32_t*)(xr[i] + (int64_t)sb * 292 + 4 + 16 * su);
+          pa[i] = (u32x4){src[0], src[1], src[2], src[3]};
+          if (su == 0) pdx[i] = *(const float*)(xr[i] + (int64_t)sb * 292);
+        }
+      }
 #pragma unroll
-      for (int ra = 0; ra < RA; ++ra) {
-        const int r = rb + ra * G + grp;
-        if (r < nrows) {
+      for (int i = 0; i < NWI; ++i) {
+        const int c = lane + 64 * i;
+        const int r = c / NCH, ch = c % NCH;
+        const int64_t row = wrow0 + r;
+        if (r < WROWS && row < n) {
+          const int64_t off = row * row_bytes + (int64_t)sb * SB::BYTES;
+          const int sh = SB::ALIGNED ? 0 : (int)((uintptr_t)(wexp + off) & 15);
+          const int nch = (sh + SB::BYTES + 15) >> 4;
+          if (ch < nch) pw[i] = __builtin_nontemporal_load((const u32x4*)(wexp + (off - sh)) + ch);
+        }
+      }
+    };
+    auto commit = [&](uint8_t* B) {
 #pragma unroll
-          for (int p = 0; p < P; ++p) {
-            if (uv[p]) {
-              Unit<F> un;
-              unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, shift + (uint32_t)r * row_bytes + (uint32_t)ub[p] * FT::BB, uu[p], un);
-#pragma unroll
-              for (int i = 0; i < T; ++i)
-                if (i < tc) v[ra * T + i] = unit_combine<F>(un, act[p][i], v[ra * T + i]);
+      for (int i = 0; i < NAI; ++i) {
+        const int it = tid + GM_THREADS * i;
+        if (it < PT * 256) {   // uniform per wave
+          const int pi = it >> 4, m = pi >> 4, spl = pi & 15;
+          const int j = su >> 1, qa = 2 * (su & 1);
+          uint64_t* cd = (uint64_t*)(B + LY::CODES + m * LY::TSTR + j * LY::GSTR);
+          cd[qa * 16 + spl] = pk64(pa[i].x, pa[i].y);
+          cd[(qa + 1) * 16 + spl] = pk64(pa[i].z, pa[i].w);
+          if constexpr (MINT) {
+            // code sum of this 16-element group; the quad su&~3 .. su|3 holds the
+            // four sums one A-operand slot needs, gathered into its first lane
+            const int s0 = dot4(pa[i].x, 0x01010101u, dot4(pa[i].y, 0x01010101u,
+                           dot4(pa[i].z, 0x01010101u, dot4(pa[i].w, 0x01010101u, 0))));
+            const float f0 = (float)s0;
+            const float f1 = xchg<1>(f0), f2 = xchg<2>(f0);
+            const float f3 = xchg<2>(f1);
+            if ((su & 3) == 0) {
+              const v4h hv = {(_Float16)f0, (_Float16)f1, (_Float16)f2, (_Float16)f3};
+              *(v4h*)(B + LY::BSUM + m * 512 + 8 * ((su >> 2) * 16 + spl)) = hv;
             }
+          }
+          if (su == 0) ((float*)(B + LY::DX))[m * 16 + spl] = pdx[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NWI; ++i) {
+        const int c = lane + 64 * i;
+        const int r = c / NCH, ch = c % NCH;
+        if (r < WROWS && wrow0 + r < n) *(u32x4*)(B + wslot + r * SB::SLOT + 16 * ch) = pw[i];
+      }
+    };
+
+    v4f acc[PT][RG];
+#pragma unroll
+    for (int m = 0; m < PT; ++m)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) acc[m][rg] = zf;
+
+    fetch(0);
+    for (int sb = 0; sb < nsb; ++sb) {
+      __syncthreads();   // the previous superblock's LDS reads are done
+      commit(L);
+      if (sb + 1 < nsb) fetch(sb + 1);
+      __syncthreads();
+      uint8_t* cur = L;
+
+      GW<F> w[RG];
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const int r = rg * 16 + rl;
+        uint32_t o = 0;
+        if constexpr (!SB::ALIGNED)
+          o = (uint32_t)((uintptr_t)(wexp + (wrow0 + r) * row_bytes + (int64_t)sb * SB::BYTES) & 15);
+        gw_decode<F>(cur + wslot + r * SB::SLOT, o, q, w[rg]);
+      }
+      // the occupied pair tiles against the lane's decoded row groups (the helper
+      // arrays stay in registers only when this code is written inline)
+      const v4i zi = {0, 0, 0, 0};
+    #pragma unroll
+      for (int m = 0; m < PT; ++m) {
+        if (m < npt) {
+          const uint8_t* ac = cur + LY::CODES + m * LY::TSTR + 8 * lane;
+          // Q6_K: the low half of a 32-element group (quarters 0, 1) is one sub-block
+          // and the high half the next; each of its two MFMAs reads zeros in the other
+          // half's lanes (an all-zero LDS tile)
+          const uint8_t* az = L + LY::ZTILE + 8 * lane;
+          const uint8_t* a0p = (F == FT_Q6_K && q >= 2) ? az : ac;
+          const uint8_t* a1p = (F == FT_Q6_K && q < 2) ? az : ac;
+          v4i isc[RG];
+          v4f ys[RG];
+    #pragma unroll
+          for (int rg = 0; rg < RG; ++rg) {
+            isc[rg] = zi;
+            ys[rg] = zf;
+          }
+    #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const long a0 = *(const long*)(a0p + j * LY::GSTR);
+            long a1 = 0;
+            if constexpr (F == FT_Q6_K) a1 = *(const long*)(a1p + j * LY::GSTR);
+    #pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+              const v4i dv = __builtin_amdgcn_mfma_i32_16x16x32_i8(a0, (long)w[rg].b[j], zi, 0, 0, 0);
+              if constexpr (KQ) {
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) isc[rg][r] += __mul24(dv[r], w[rg].sc[j]);
+              } else if constexpr (F == FT_Q6_K) {
+                const v4i dh = __builtin_amdgcn_mfma_i32_16x16x32_i8(a1, (long)w[rg].b[j], zi, 0, 0, 0);
+                const int s0 = (int)(int8_t)((w[rg].scp[j >> 1] >> (16 * (j & 1))) & 0xFFu);
+                const int s1 = (int)(int8_t)((w[rg].scp[j >> 1] >> (16 * (j & 1) + 8)) & 0xFFu);
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) isc[rg][r] += __mul24(dv[r], s0) + __mul24(dh[r], s1);
+              } else {
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) ys[rg][r] = fmaf((float)dv[r], w[rg].s[j], ys[rg][r]);
+              }
+            }
+          }
+          const v4f dx4 = *(const v4f*)(cur + LY::DX + m * 64 + 16 * q);
+          if constexpr (F != FT_MXFP4) {
+            const v4h ba = *(const v4h*)(cur + LY::BSUM + m * 512 + 8 * lane);
+    #pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+              const v4f dm = __builtin_amdgcn_mfma_f32_16x16x16f16(ba, w[rg].mb, zf, 0, 0, 0);
+    #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float t;
+                if constexpr (KQ) t = fmaf(-w[rg].dmin, dm[r], w[rg].d * (float)isc[rg][r]);
+                else t = w[rg].d * fmaf(-32.0f, dm[r], (float)isc[rg][r]);
+                acc[m][rg][r] = fmaf(dx4[r], t, acc[m][rg][r]);
+              }
+            }
+          } else {
+    #pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+    #pragma unroll
+              for (int r = 0; r < 4; ++r) acc[m][rg][r] = fmaf(dx4[r], ys[rg][r], acc[m][rg][r]);
           }
         }
       }
-      group_reduce_multi<M, LR>(v, gl);
-      const int idx = gl / (LR / M);
-      if ((gl % (LR / M)) == 0) {
-        const int ra = idx / T, i = idx % T;
-        const int r = rb + ra * G + grp;
-        if (r < nrows && i < tc) y[(int64_t)pr[i] * n + r0 + r] = v[0];
+    }
+
+    // lane holds rows wrow0 + 16rg + rl for pairs 16m + 4q + r of the group
+#pragma unroll
+    for (int m = 0; m < PT; ++m) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pi = 16 * m + 4 * q + r;
+        if (pi < gm) {
+          const int64_t pr = pairs[g0 + pi];
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg) {
+            const int64_t row = wrow0 + 16 * rg + rl;
+            if (row < n) y[pr * n + row] = acc[m][rg][r];
+          }
+        }
       }
     }
   }
 }
 
-template <int F, int A, int LR, int P>
-static hipError_t launch_grouped_t(const GroupedArgs& a, int row_bytes, int units, int rpt, hipStream_t st) {
-  const size_t lds = (((size_t)rpt * row_bytes + 32) & ~(size_t)15) + 64;
-  const dim3 grid((unsigned)((a.n + rpt - 1) / rpt), (unsigned)a.n_expert);
-  hipLaunchKernelGGL((grouped_dot4_kernel<F, A, LR, P>), grid, dim3(GRP_THREADS), lds, st, (const uint8_t*)a.W,
-                     a.n, row_bytes, units, rpt, (const uint8_t*)a.xq, (int)(a.k / Act<A>::BLK * Act<A>::BB),
-                     a.x_per_pair, a.topk, a.offsets, a.pairs, a.y);
+template <int F, int PT>
+static hipError_t launch_gm(const GroupedArgs& a, hipStream_t st) {
+  const int64_t row_tiles = (a.n + gm_rows<F>() - 1) / gm_rows<F>();
+  const int64_t total = row_tiles * a.n_expert;
+  const int64_t per = (total + 7) / 8;
+  const int64_t row_bytes = a.k / 256 * GSb<F>::BYTES;
+  const size_t lds = (size_t)GLds<F, PT>::TOTAL;
+  hipLaunchKernelGGL((grouped_mfma_kernel<F, PT>), dim3((unsigned)(per * 8)), dim3(GM_THREADS), lds, st, (const uint8_t*)a.W, a.n, row_bytes, (int)(a.k / 256),
+                     (const uint8_t*)a.xq, (int64_t)(a.k / 256 * 292), a.x_per_pair, a.topk, a.offsets, a.pairs,
+                     a.y, row_tiles, total, per);
   return hipGetLastError();
 }
 
-template <int F, int A>
-static hipError_t grouped_fa(const GroupedArgs& a, hipStream_t st) {
-  const int row_bytes = (int)(a.k / Fmt<F>::BLK * Fmt<F>::BB);
-  const int units = (int)units_in_row<F>(a.k);
-  int lr, p = 1;
-  if (units <= 64) {
-    lr = 16;
-    while (lr < units) lr *= 2;
-  } else {
-    lr = 64;
-    while (p * 64 < units) p *= 2;
-  }
-  const int G = GRP_THREADS / lr;
-  int rpt = (32 * 1024) / row_bytes;
-  if (rpt > G) rpt = rpt / G * G;
-  if (rpt < 1) rpt = 1;
-#define FT_G(LRV, PV) \
-  if (lr == LRV && p == PV) return launch_grouped_t<F, A, LRV, PV>(a, row_bytes, units, rpt, st);
-  FT_G(16, 1) FT_G(32, 1) FT_G(64, 1) FT_G(64, 2) FT_G(64, 4) FT_G(64, 8)
-#undef FT_G
-  return hipErrorInvalidValue;
+// Pair tiles held per pass: room for an expert 2.5 standard deviations above the
+// mean pairs per expert of this batch (uniform routing gives a near-binomial
+// spread); a larger group takes a second pass over its weights.
+template <int F>
+static hipError_t grouped_f(const GroupedArgs& a, hipStream_t st) {
+  const double avg = (double)a.t * a.topk / (double)a.n_expert;
+  const double hi = avg + 2.5 * sqrt(avg);
+  if (hi <= 16.0) return launch_gm<F, 1>(a, st);
+  if (hi <= 32.0) return launch_gm<F, 2>(a, st);
+  if (hi <= 48.0) return launch_gm<F, 3>(a, st);
+  return launch_gm<F, 4>(a, st);
 }
 
 }  // namespace ftk
@@ -148,13 +429,12 @@ static hipError_t grouped_fa(const GroupedArgs& a, hipStream_t st) {
 using namespace ftk;
 
 hipError_t ftk_launch_grouped(const GroupedArgs& a, hipStream_t st) {
-  if (a.act != FT_Q8_K) return hipErrorInvalidValue;
-  if (a.k / 32 > 512) return hipErrorInvalidValue;
+  if (a.act != FT_Q8_K || a.k % 256) return hipErrorInvalidValue;
   switch (a.w) {
-    case FT_Q4_K: return grouped_fa<FT_Q4_K, FT_Q8_K>(a, st);
-    case FT_Q5_K: return grouped_fa<FT_Q5_K, FT_Q8_K>(a, st);
-    case FT_Q6_K: return grouped_fa<FT_Q6_K, FT_Q8_K>(a, st);
-    case FT_MXFP4: return grouped_fa<FT_MXFP4, FT_Q8_K>(a, st);
+    case FT_Q4_K: return grouped_f<FT_Q4_K>(a, st);
+    case FT_Q5_K: return grouped_f<FT_Q5_K>(a, st);
+    case FT_Q6_K: return grouped_f<FT_Q6_K>(a, st);
+    case FT_MXFP4: return grouped_f<FT_MXFP4>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -79,63 +79,135 @@ route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk
 }
 
 // ---------------------------------------------------------------------------
-// stable counting sort of (token, slot) pairs by expert: one workgroup
+// stable counting sort of (token, slot) pairs by expert: one workgroup of 1024
+//  1. histogram of all pairs (LDS atomics) and a block-wide exclusive scan ->
+//     offsets; counts[] serves as the per-expert insert cursor until the end;
+//  2. pairs are taken in chunks of at most `chunk` in pair order; a chunk is
+//     histogrammed again (two 16-bit counters per LDS word), scanned, and its pairs
+//     dropped into their expert's segment of an LDS list with atomics (any order);
+//     each pair then counts the smaller pair indices in its own segment, which is
+//     its stable rank, and lands at cursor[e] + rank;
+//  3. counts[] = offsets[e+1] - offsets[e].
+// Work per pair is O(its expert's share of the chunk); LDS use is
+// 4*E + 4*chunk bytes.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-sort_kernel(const int32_t* __restrict__ ids, int64_t npairs, int n_expert, int32_t* __restrict__ counts,
-            int32_t* __restrict__ offsets, int32_t* __restrict__ pairs) {
-  extern __shared__ int32_t sh[];
-  int32_t* cnt = sh;                 // [n_expert]
-  int32_t* chunk = sh + n_expert;    // [256]
-  const int tid = threadIdx.x;
-  for (int e = tid; e < n_expert; e += 256) cnt[e] = 0;
+constexpr int SORT_THREADS = 1024;
+
+__device__ __forceinline__ int clamp_e(int e, int n_expert) {
+  return e < 0 ? 0 : (e >= n_expert ? n_expert - 1 : e);
+}
+
+// Exclusive scan over n values get(i) in index order; put(i, prefix) for each i.
+// Returns the total in every thread.  Needs wsum[SORT_THREADS / 64 + 1] in LDS.
+template <typename G, typename P>
+__device__ __forceinline__ int block_exclusive_scan(int n, int* wsum, G get, P put) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = SORT_THREADS / 64;
+  const int per = (n + SORT_THREADS - 1) / SORT_THREADS;
+  const int i0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (i0 + i < n) local += get(i0 + i);
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  for (int64_t p = tid; p < npairs; p += 256) {
-    int e = ids[p];
-    e = e < 0 ? 0 : (e >= n_expert ? n_expert - 1 : e);
-    atomicAdd(&cnt[e], 1);
+  if (wave == 0) {
+    const int v = lane < NW ? wsum[lane] : 0;
+    int sc = v;
+#pragma unroll
+    for (int d = 1; d < NW; d <<= 1) {
+      const int u = __shfl_up(sc, d, 64);
+      if (lane >= d) sc += u;
+    }
+    if (lane < NW) wsum[lane] = sc - v;
+    if (lane == NW - 1) wsum[NW] = sc;
   }
   __syncthreads();
-  if (tid == 0) {  // exclusive prefix sum (n_expert is small)
-    int run = 0;
-    for (int e = 0; e < n_expert; ++e) {
-      const int c = cnt[e];
-      counts[e] = c;
-      offsets[e] = run;
-      cnt[e] = run;  // becomes the running insert position
+  int run = wsum[wave] + incl - local;
+  for (int i = 0; i < per; ++i)
+    if (i0 + i < n) {
+      const int c = get(i0 + i);
+      put(i0 + i, run);
       run += c;
     }
-    offsets[n_expert] = run;
-  }
+  const int total = wsum[NW];
   __syncthreads();
-  for (int64_t base = 0; base < npairs; base += 256) {
-    const int64_t p = base + tid;
-    int e = -1;
-    if (p < npairs) {
-      e = ids[p];
-      e = e < 0 ? 0 : (e >= n_expert ? n_expert - 1 : e);
-    }
-    chunk[tid] = e;
+  return total;
+}
+
+__global__ void __launch_bounds__(SORT_THREADS)
+sort_kernel(const int32_t* __restrict__ ids, int npairs, int n_expert, int chunk, int32_t* __restrict__ counts,
+            int32_t* __restrict__ offsets, int32_t* __restrict__ pairs) {
+  extern __shared__ int32_t sh[];
+  __shared__ int wsum[SORT_THREADS / 64 + 1];
+  const int tid = threadIdx.x;
+  const int E = n_expert;
+
+  // 1. global histogram and offsets
+  int32_t* hist = sh;   // [E]
+  for (int e = tid; e < E; e += SORT_THREADS) hist[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < npairs; p += SORT_THREADS) atomicAdd(&hist[clamp_e(ids[p], E)], 1);
+  __syncthreads();
+  const int total = block_exclusive_scan(
+      E, wsum, [&](int e) { return hist[e]; },
+      [&](int e, int v) {
+        offsets[e] = v;
+        counts[e] = v;   // insert cursor
+      });
+  if (tid == 0) offsets[E] = total;
+
+  // 2. chunks in pair order
+  uint32_t* lc = (uint32_t*)sh;                 // [(E+1)/2] packed 16-bit counts, then cursors
+  uint16_t* lo = (uint16_t*)(lc + (E + 1) / 2);  // [E+1] chunk-local offsets
+  int32_t* lst = (int32_t*)(lc + (E + 1) / 2 + (E + 2) / 2);  // [chunk]
+  for (int c0 = 0; c0 < npairs; c0 += chunk) {
+    const int cn = min(chunk, npairs - c0);
+    for (int i = tid; i < (E + 1) / 2; i += SORT_THREADS) lc[i] = 0;
     __syncthreads();
-    if (e >= 0) {
+    for (int p = c0 + tid; p < c0 + cn; p += SORT_THREADS) {
+      const int e = clamp_e(ids[p], E);
+      atomicAdd(&lc[e >> 1], 1u << (16 * (e & 1)));
+    }
+    __syncthreads();
+    block_exclusive_scan(
+        E, wsum, [&](int e) { return (int)((lc[e >> 1] >> (16 * (e & 1))) & 0xFFFFu); },
+        [&](int e, int v) { lo[e] = (uint16_t)v; });
+    if (tid == 0) lo[E] = (uint16_t)cn;
+    __syncthreads();
+    // cursors start at the chunk-local offsets (each thread rewrites whole words)
+    for (int i = tid; i < (E + 1) / 2; i += SORT_THREADS) {
+      const uint32_t a = lo[2 * i], b = 2 * i + 1 < E ? lo[2 * i + 1] : 0u;
+      lc[i] = a | (b << 16);
+    }
+    __syncthreads();
+    for (int p = c0 + tid; p < c0 + cn; p += SORT_THREADS) {
+      const int e = clamp_e(ids[p], E);
+      const uint32_t old = atomicAdd(&lc[e >> 1], 1u << (16 * (e & 1)));
+      lst[(old >> (16 * (e & 1))) & 0xFFFFu] = p;
+    }
+    __syncthreads();
+    for (int s = tid; s < cn; s += SORT_THREADS) {
+      const int p = lst[s];
+      const int e = clamp_e(ids[p], E);
+      const int b0 = lo[e], b1 = lo[e + 1];
       int rank = 0;
-      for (int j = 0; j < tid; ++j) rank += chunk[j] == e;
-      pairs[cnt[e] + rank] = (int32_t)p;
+      for (int s2 = b0; s2 < b1; ++s2) rank += lst[s2] < p;
+      pairs[counts[e] + rank] = p;
     }
     __syncthreads();
-    if (e >= 0) {
-      // the last pair of this expert in the chunk advances the insert position
-      bool last = true;
-      for (int j = tid + 1; j < 256; ++j)
-        if (chunk[j] == e) { last = false; break; }
-      if (last) {
-        int c = 0;
-        for (int j = 0; j <= tid; ++j) c += chunk[j] == e;
-        cnt[e] += c;
-      }
-    }
+    for (int e = tid; e < E; e += SORT_THREADS) counts[e] += lo[e + 1] - lo[e];
     __syncthreads();
   }
+
+  // 3. counts
+  __syncthreads();
+  for (int e = tid; e < E; e += SORT_THREADS) counts[e] = offsets[e + 1] - offsets[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -483,9 +555,17 @@ hipError_t ftk_launch_route(const float* logits, int64_t t, int64_t n_expert, in
 
 hipError_t ftk_launch_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert, int32_t* counts,
                            int32_t* offsets, int32_t* pairs, hipStream_t st) {
-  const size_t lds = ((size_t)n_expert + 256) * sizeof(int32_t);
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(256), lds, st, ids, t * topk, (int)n_expert, counts, offsets,
-                     pairs);
+  // LDS: max(4E, 2*ceil(E/2) + 2*(E+2) + 4*chunk) bytes, kept within 64 KiB
+  const int64_t npairs = t * topk;
+  const int64_t fixed = 4 * ((n_expert + 1) / 2) + 4 * ((n_expert + 2) / 2);
+  int64_t chunk = (65536 - fixed) / 4;
+  if (chunk > 65535) chunk = 65535;
+  if (chunk < 1024 || npairs > INT32_MAX) return hipErrorInvalidValue;
+  if (chunk > npairs) chunk = npairs < 1 ? 1 : npairs;
+  size_t lds = (size_t)(fixed + 4 * chunk);
+  if (lds < (size_t)(4 * n_expert)) lds = (size_t)(4 * n_expert);
+  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(SORT_THREADS), lds, st, ids, (int)npairs, (int)n_expert, (int)chunk,
+                     counts, offsets, pairs);
   return hipGetLastError();
 }
 

@@ -37,7 +37,8 @@ def test_route_ties():
     check_fp32(host(w), rw, rel=1e-6, nmse=1e-12)
 
 
-@pytest.mark.parametrize("t,e,topk", [(1, 128, 8), (5, 256, 8), (512, 128, 8), (700, 64, 3), (4096, 256, 8)])
+@pytest.mark.parametrize("t,e,topk", [(1, 128, 8), (5, 256, 8), (512, 128, 8), (700, 64, 3), (4096, 256, 8),
+                                      (1, 1, 1), (3000, 8, 8), (2048, 8192, 8)])
 def test_sort(t, e, topk):
     ids = synth.expert_ids(t, e, topk, synth.rng(301, t))
     c, o, p = ft.moe_sort(dev(ids), e)
