@@ -106,6 +106,7 @@ bool mmvq_pair(int w, int a) {
   return a == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K);
 }
 bool moe_pair(int w, int a) { return (w == FT_Q4_K && a == FT_Q8_1) || (w == FT_MXFP4 && a == FT_Q8_K); }
+bool moe_tile_pair(int w, int a) { return w == FT_MXFP4 && a == FT_Q8_K; }
 bool grouped_pair(int w, int a) {
   return a == FT_Q8_K && (w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4);
 }
@@ -212,9 +213,10 @@ ft_status ft_moe_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert,
 
 size_t ft_moe_scratch_bytes(ft_type w, ft_type act, int64_t n_expert, int64_t hidden, int64_t inter, int64_t t,
                             int topk) {
-  (void)n_expert;
-  if (!is_act(act) || t < 0 || topk < 0) return 0;
-  return moe_layout(w, act, hidden, inter, t, topk).total;
+  if (!is_act(act) || t < 0 || topk < 0 || n_expert < 1) return 0;
+  // the sorted-tile route also needs the sort's buffers
+  return moe_layout(w, act, hidden, inter, t, topk).total +
+         (moe_tile_pair(w, act) ? sort_layout(n_expert, t, topk).total : 0);
 }
 
 size_t ft_grouped_scratch_bytes(int64_t n_expert, int64_t t, int topk) {
@@ -236,8 +238,12 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
     return FT_ERR_ALIGNMENT;
   ft_moe_opts o = {};
   if (opts) o = *opts;
-  if (o.route < 0 || o.route > 2) return FT_ERR_INVALID_ARG;
-  if (o.route == 2) return FT_ERR_UNSUPPORTED;  // sorted-tile route not provided by this build
+  if (o.route < 0 || o.route > 2 || o.direct_max_t < 0) return FT_ERR_INVALID_ARG;
+  // sorted-tile route: token->expert sort + grouped MFMA GEMMs (MXFP4 x Q8_K)
+  const bool tile_ok = moe_tile_pair(w, act);
+  if (o.route == 2 && !tile_ok) return FT_ERR_UNSUPPORTED;
+  const int64_t dmax = o.direct_max_t > 0 ? o.direct_max_t : 4;
+  const bool tiles = o.route == 2 || (o.route == 0 && tile_ok && t > dmax);
   if ((o.tap_g && !aligned16(o.tap_g)) || (o.tap_u && !aligned16(o.tap_u)) || (o.tap_h && !aligned16(o.tap_h)) ||
       (o.tap_hq && !aligned16(o.tap_hq)) || (o.tap_down && !aligned16(o.tap_down)) ||
       (o.in_hq && !aligned16(o.in_hq)))
@@ -245,8 +251,9 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
 
   hipStream_t st = hs(stream);
   const MoeScratch L = moe_layout(w, act, hidden, inter, t, topk);
+  const SortScratch S = sort_layout(n_expert, t, topk);
   void* base = nullptr;
-  ft_status s = pool_get(st, L.total, &base);
+  ft_status s = pool_get(st, L.total + (tiles ? S.total : 0), &base);
   if (s != FT_OK) return s;
   uint8_t* b = (uint8_t*)base;
 
@@ -272,6 +279,48 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
   a.y = y;
 
   hipError_t e = ftk_launch_quantize(act, x, t, hidden, hidden, (void*)a.xq, st);
+  if (tiles) {
+    uint8_t* sb = b + L.total;
+    int32_t* counts = (int32_t*)(sb + S.counts);
+    int32_t* offsets = (int32_t*)(sb + S.offsets);
+    int32_t* pairs = (int32_t*)(sb + S.pairs);
+    if (e == hipSuccess) e = ftk_launch_sort(expert_ids, t, topk, n_expert, counts, offsets, pairs, st);
+    GroupedArgs gu = {};
+    gu.w = w;
+    gu.act = act;
+    gu.W = w_gate;
+    gu.W2 = w_up;
+    gu.g_tap = o.tap_g;
+    gu.u_tap = o.tap_u;
+    gu.n_expert = n_expert;
+    gu.n = inter;
+    gu.k = hidden;
+    gu.xq = a.xq;
+    gu.x_per_pair = 0;
+    gu.t = t;
+    gu.topk = topk;
+    gu.counts = counts;
+    gu.offsets = offsets;
+    gu.pairs = pairs;
+    gu.y = a.h;
+    if (e == hipSuccess) e = ftk_launch_grouped(gu, st);
+    if (e == hipSuccess && !o.in_hq) e = ftk_launch_quantize(act, a.h, t * topk, inter, inter, a.hq, st);
+    if (e == hipSuccess && o.in_hq && o.tap_hq)
+      e = hipMemcpyAsync(o.tap_hq, o.in_hq, (size_t)t * topk * row_bytes_of(act, inter), hipMemcpyDeviceToDevice,
+                         st);
+    GroupedArgs dn = gu;
+    dn.W = w_down;
+    dn.W2 = nullptr;
+    dn.g_tap = dn.u_tap = nullptr;
+    dn.n = hidden;
+    dn.k = inter;
+    dn.xq = a.hq;
+    dn.x_per_pair = 1;
+    dn.y = a.dpair;
+    if (e == hipSuccess) e = ftk_launch_grouped(dn, st);
+    if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
+    return hip_status(e);
+  }
   if (e == hipSuccess) e = ftk_launch_moe_gate_up(a, st);
   if (e == hipSuccess && !o.in_hq) e = ftk_launch_quantize(act, a.h, t * topk, inter, inter, a.hq, st);
   if (e == hipSuccess && o.in_hq && o.tap_hq)
@@ -297,7 +346,7 @@ ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t 
   ft_status s = pool_get(st, L.total, &base);
   if (s != FT_OK) return s;
   uint8_t* b = (uint8_t*)base;
-  GroupedArgs a;
+  GroupedArgs a = {};
   a.w = w;
   a.act = act;
   a.W = W;

@@ -52,7 +52,6 @@ constexpr int GM_THREADS = 64 * GM_WAVES;
 // 16-row MFMA groups per wave (they share every A-operand read); Q6_K's two
 // MFMAs and two scales per group need the registers of a second group
 template <int F> struct GRg { static constexpr int RG = F == FT_Q6_K ? 1 : 2; };
-template <int F> constexpr int gm_rows() { return 16 * GRg<F>::RG * GM_WAVES; }   // rows per workgroup
 
 // One 256-element superblock of a weight row: BYTES in HBM; SLOT bytes in LDS
 // (room for a misaligned start; SLOT/16 odd keeps the 16 rows of an MFMA group on
@@ -173,17 +172,23 @@ __device__ __forceinline__ void gw_decode(const uint8_t* sl, uint32_t o, int q, 
   }
 }
 
-template <int F, int PT>
+// GLU: W is the gate bank and W2 the up bank of the same shape; a wave's two row
+// groups are the gate and up rows of the same 16 outputs, and y receives
+// h = silu(g) * u (g, u also written to g_tap / u_tap when those are non-null).
+template <int F, int PT, bool GLU>
 __global__ void __launch_bounds__(GM_THREADS)
-grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes, int nsb,
-                    const uint8_t* __restrict__ xq, int64_t xrow_bytes, int x_per_pair, int topk,
+grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W2, int64_t n, int64_t row_bytes,
+                    int nsb, const uint8_t* __restrict__ xq, int64_t xrow_bytes, int x_per_pair, int topk,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
-                    float* __restrict__ y, int64_t row_tiles, int64_t total, int64_t per_xcd) {
+                    float* __restrict__ y, float* __restrict__ g_tap, float* __restrict__ u_tap,
+                    int64_t row_tiles, int64_t total, int64_t per_xcd) {
   using SB = GSb<F>;
   using LY = GLds<F, PT>;
   constexpr int NCH = SB::SLOT / 16;                   // 16-byte chunks per row slot
   constexpr int RG = GRg<F>::RG;
-  constexpr int WROWS = 16 * RG;                       // rows per wave
+  static_assert(!GLU || RG == 2, "the fused gate/up form takes two row groups");
+  constexpr int WROWS = 16 * RG;                       // weight rows per wave
+  constexpr int OROWS = GLU ? 16 : WROWS;              // output rows per wave
   constexpr int NWI = (WROWS * NCH + 63) / 64;         // weight chunks per lane
   constexpr int NAI = (PT * 256 + GM_THREADS - 1) / GM_THREADS;   // activation chunks per thread
   constexpr bool MINT = F != FT_MXFP4;                 // has a code-sum term
@@ -202,8 +207,12 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes,
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, rl = lane & 15;
-  const int64_t wrow0 = tile * gm_rows<F>() + (int64_t)wave * WROWS;   // first row of this wave
+  const int64_t wrow0 = tile * (OROWS * GM_WAVES) + (int64_t)wave * OROWS;   // first output row of this wave
   const uint8_t* wexp = W + (int64_t)e * n * row_bytes;
+  const uint8_t* wexp2 = GLU ? W2 + (int64_t)e * n * row_bytes : wexp;
+  // weight slot r of this wave: its bank and output row
+  auto slot_src = [&](int r) { return (GLU && r >= 16) ? wexp2 : wexp; };
+  auto slot_row = [&](int r) { return wrow0 + (GLU ? (r & 15) : r); };
   const int wslot = LY::WT + wave * WROWS * SB::SLOT;   // this wave's weight rows in a buffer
   const v4f zf = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (F == FT_Q6_K) {   // published by the first barrier of the superblock loop
@@ -246,12 +255,13 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes,
       for (int i = 0; i < NWI; ++i) {
         const int c = lane + 64 * i;
         const int r = c / NCH, ch = c % NCH;
-        const int64_t row = wrow0 + r;
+        const int64_t row = slot_row(r);
         if (r < WROWS && row < n) {
+          const uint8_t* src = slot_src(r);
           const int64_t off = row * row_bytes + (int64_t)sb * SB::BYTES;
-          const int sh = SB::ALIGNED ? 0 : (int)((uintptr_t)(wexp + off) & 15);
+          const int sh = SB::ALIGNED ? 0 : (int)((uintptr_t)(src + off) & 15);
           const int nch = (sh + SB::BYTES + 15) >> 4;
-          if (ch < nch) pw[i] = __builtin_nontemporal_load((const u32x4*)(wexp + (off - sh)) + ch);
+          if (ch < nch) pw[i] = __builtin_nontemporal_load((const u32x4*)(src + (off - sh)) + ch);
         }
       }
     };
@@ -285,7 +295,7 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes,
       for (int i = 0; i < NWI; ++i) {
         const int c = lane + 64 * i;
         const int r = c / NCH, ch = c % NCH;
-        if (r < WROWS && wrow0 + r < n) *(u32x4*)(B + wslot + r * SB::SLOT + 16 * ch) = pw[i];
+        if (r < WROWS && slot_row(r) < n) *(u32x4*)(B + wslot + r * SB::SLOT + 16 * ch) = pw[i];
       }
     };
 
@@ -309,7 +319,7 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes,
         const int r = rg * 16 + rl;
         uint32_t o = 0;
         if constexpr (!SB::ALIGNED)
-          o = (uint32_t)((uintptr_t)(wexp + (wrow0 + r) * row_bytes + (int64_t)sb * SB::BYTES) & 15);
+          o = (uint32_t)((uintptr_t)(slot_src(r) + slot_row(r) * row_bytes + (int64_t)sb * SB::BYTES) & 15);
         gw_decode<F>(cur + wslot + r * SB::SLOT, o, q, w[rg]);
       }
       // the occupied pair tiles against the lane's decoded row groups (the helper
@@ -379,7 +389,7 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes,
       }
     }
 
-    // lane holds rows wrow0 + 16rg + rl for pairs 16m + 4q + r of the group
+    // lane holds weight slots 16rg + rl for pairs 16m + 4q + r of the group
 #pragma unroll
     for (int m = 0; m < PT; ++m) {
 #pragma unroll
@@ -387,10 +397,20 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes,
         const int pi = 16 * m + 4 * q + r;
         if (pi < gm) {
           const int64_t pr = pairs[g0 + pi];
+          if constexpr (GLU) {
+            const int64_t row = wrow0 + rl;
+            if (row < n) {
+              const float g = acc[m][0][r], u = acc[m][1][r];
+              y[pr * n + row] = g / (1.0f + expf(-g)) * u;
+              if (g_tap) g_tap[pr * n + row] = g;
+              if (u_tap) u_tap[pr * n + row] = u;
+            }
+          } else {
 #pragma unroll
-          for (int rg = 0; rg < RG; ++rg) {
-            const int64_t row = wrow0 + 16 * rg + rl;
-            if (row < n) y[pr * n + row] = acc[m][rg][r];
+            for (int rg = 0; rg < RG; ++rg) {
+              const int64_t row = wrow0 + 16 * rg + rl;
+              if (row < n) y[pr * n + row] = acc[m][rg][r];
+            }
           }
         }
       }
@@ -398,30 +418,32 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t row_bytes,
   }
 }
 
-template <int F, int PT>
+template <int F, int PT, bool GLU>
 static hipError_t launch_gm(const GroupedArgs& a, hipStream_t st) {
-  const int64_t row_tiles = (a.n + gm_rows<F>() - 1) / gm_rows<F>();
+  const int rows = (GLU ? 16 : 16 * GRg<F>::RG) * GM_WAVES;
+  const int64_t row_tiles = (a.n + rows - 1) / rows;
   const int64_t total = row_tiles * a.n_expert;
   const int64_t per = (total + 7) / 8;
   const int64_t row_bytes = a.k / 256 * GSb<F>::BYTES;
   const size_t lds = (size_t)GLds<F, PT>::TOTAL;
-  hipLaunchKernelGGL((grouped_mfma_kernel<F, PT>), dim3((unsigned)(per * 8)), dim3(GM_THREADS), lds, st, (const uint8_t*)a.W, a.n, row_bytes, (int)(a.k / 256),
+  hipLaunchKernelGGL((grouped_mfma_kernel<F, PT, GLU>), dim3((unsigned)(per * 8)), dim3(GM_THREADS), lds, st,
+                     (const uint8_t*)a.W, (const uint8_t*)a.W2, a.n, row_bytes, (int)(a.k / 256),
                      (const uint8_t*)a.xq, (int64_t)(a.k / 256 * 292), a.x_per_pair, a.topk, a.offsets, a.pairs,
-                     a.y, row_tiles, total, per);
+                     a.y, a.g_tap, a.u_tap, row_tiles, total, per);
   return hipGetLastError();
 }
 
 // Pair tiles held per pass: room for an expert 2.5 standard deviations above the
 // mean pairs per expert of this batch (uniform routing gives a near-binomial
 // spread); a larger group takes a second pass over its weights.
-template <int F>
+template <int F, bool GLU>
 static hipError_t grouped_f(const GroupedArgs& a, hipStream_t st) {
   const double avg = (double)a.t * a.topk / (double)a.n_expert;
   const double hi = avg + 2.5 * sqrt(avg);
-  if (hi <= 16.0) return launch_gm<F, 1>(a, st);
-  if (hi <= 32.0) return launch_gm<F, 2>(a, st);
-  if (hi <= 48.0) return launch_gm<F, 3>(a, st);
-  return launch_gm<F, 4>(a, st);
+  if (hi <= 16.0) return launch_gm<F, 1, GLU>(a, st);
+  if (hi <= 32.0) return launch_gm<F, 2, GLU>(a, st);
+  if (hi <= 48.0) return launch_gm<F, 3, GLU>(a, st);
+  return launch_gm<F, 4, GLU>(a, st);
 }
 
 }  // namespace ftk
@@ -430,11 +452,15 @@ using namespace ftk;
 
 hipError_t ftk_launch_grouped(const GroupedArgs& a, hipStream_t st) {
   if (a.act != FT_Q8_K || a.k % 256) return hipErrorInvalidValue;
+  if (a.W2) {   // fused gate/up + SwiGLU
+    if (a.w == FT_MXFP4) return grouped_f<FT_MXFP4, true>(a, st);
+    return hipErrorInvalidValue;
+  }
   switch (a.w) {
-    case FT_Q4_K: return grouped_f<FT_Q4_K>(a, st);
-    case FT_Q5_K: return grouped_f<FT_Q5_K>(a, st);
-    case FT_Q6_K: return grouped_f<FT_Q6_K>(a, st);
-    case FT_MXFP4: return grouped_f<FT_MXFP4>(a, st);
+    case FT_Q4_K: return grouped_f<FT_Q4_K, false>(a, st);
+    case FT_Q5_K: return grouped_f<FT_Q5_K, false>(a, st);
+    case FT_Q6_K: return grouped_f<FT_Q6_K, false>(a, st);
+    case FT_MXFP4: return grouped_f<FT_MXFP4, false>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -64,10 +64,14 @@ hipError_t ftk_launch_moe_gate_up(const MoeArgs& a, hipStream_t st);
 hipError_t ftk_launch_moe_down(const MoeArgs& a, hipStream_t st);
 hipError_t ftk_launch_moe_combine(const MoeArgs& a, hipStream_t st);
 
-// grouped GEMM over expert-sorted pairs
+// grouped GEMM over expert-sorted pairs.  With W2 set (MXFP4 only) W and W2 are
+// the gate and up banks and y receives silu(g) * u.
 struct GroupedArgs {
   int w, act;
   const void* W;
+  const void* W2;          // nullable
+  float* g_tap;            // nullable (W2 form)
+  float* u_tap;            // nullable (W2 form)
   int64_t n_expert, n, k;
   const void* xq;
   int x_per_pair;

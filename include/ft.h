@@ -138,8 +138,10 @@ ft_status ft_moe_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert,
 
 /* Options of ft_moe_q_vec; pass NULL for defaults. */
 typedef struct {
-  int route;          /* 0 auto, 1 force the direct route, 2 force sorted tiles */
-  int direct_max_t;   /* auto route: direct for t <= direct_max_t (0 = default 4) */
+  int route;          /* 0 auto, 1 force the direct route, 2 force sorted tiles
+                         (tiles: (MXFP4, Q8_K) only, else FT_ERR_UNSUPPORTED) */
+  int direct_max_t;   /* auto route: direct for t <= direct_max_t (0 = default 4),
+                         sorted tiles above it where supported */
   float* tap_g;       /* nullable [t*topk][inter] fp32: gate projections */
   float* tap_u;       /* nullable [t*topk][inter] fp32: up projections */
   float* tap_h;       /* nullable [t*topk][inter] fp32: silu(g)*u */
@@ -156,7 +158,12 @@ typedef struct {
      h = silu(g)*u, hhat = act-quantized h, d = W_down[e].hhat,
    and y[i] = sum over s (in slot order) of expert_w[i][s] * d.  y: [t][hidden] fp32.
    The topk ids of one token must be distinct (as top-k routing makes them).
-   Supported (w, act): (Q4_K, Q8_1), (MXFP4, Q8_K).  topk 1..8. */
+   Supported (w, act): (Q4_K, Q8_1), (MXFP4, Q8_K).  topk 1..8.
+   Routes [P4 Summary: tiny batches direct, larger ones on expert-sorted tiles]:
+   direct = one workgroup per selected expert and row tile, tokens in VGPRs;
+   sorted tiles = token->expert sort, one fused gate/up + SwiGLU grouped MFMA GEMM,
+   h quantize, grouped down GEMM, slot-order combine.  Both give the same result
+   up to fp32 rounding order. */
 ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const void* w_down,
                        int64_t n_expert, int64_t hidden, int64_t inter,
                        ft_type act, const float* x, int64_t t,

@@ -108,6 +108,24 @@ def test_shape_and_pointer_checks():
                           fake, None, None) == ST["FT_ERR_SHAPE"]
 
 
+def test_moe_route_options_refused_on_host():
+    """Forced sorted tiles need Q8_K activations; bad options are refused before
+    anything is launched (no GPU needed)."""
+    L = ft.lib()
+    T = ft.TYPES
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(w, a, route, dmax=0):
+        o = ft._MoeOpts(route, dmax, None, None, None, None, None, None)
+        return L.ft_moe_q_vec(T[w], fake, fake, fake, 4, 256, 256, T[a], fake, 1, fake, fake, 2, fake,
+                              ctypes.byref(o), None)
+
+    assert call("Q4_K", "Q8_1", 2) == ST["FT_ERR_UNSUPPORTED"]
+    assert call("Q4_K", "Q8_1", 3) == ST["FT_ERR_INVALID_ARG"]
+    assert call("MXFP4", "Q8_K", -1) == ST["FT_ERR_INVALID_ARG"]
+    assert call("MXFP4", "Q8_K", 0, dmax=-2) == ST["FT_ERR_INVALID_ARG"]
+
+
 def test_status_strings():
     for code in range(7):
         assert ft.lib().ft_status_str(code)

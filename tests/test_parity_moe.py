@@ -129,6 +129,61 @@ def test_moe_mxfp4_direct(t):
     _run_stages("mxfp4", t, route=0)
 
 
+@pytest.mark.parametrize("t", [1, 3, 5, 9, 40])
+def test_moe_mxfp4_small_tiles(t):
+    """Sorted-tile route forced at every t (stage taps against the oracle)."""
+    log(f"moe mxfp4_small tiles t={t}")
+    _run_stages("mxfp4_small", t, route=2)
+
+
+def test_moe_mxfp4_small_tiles_shared_experts():
+    _run_stages("mxfp4_small", 6, route=2, dup=True)
+
+
+@pytest.mark.parametrize("t,route", [(1, 2), (4, 2), (5, 0), (9, 0)])
+def test_moe_mxfp4_tiles(t, route):
+    """Full-size MXFP4 bank (hidden 4096, 256 experts of 2048): route 0 takes the
+    tiles above 4 tokens."""
+    log(f"moe mxfp4 tiles t={t} route={route}")
+    _run_stages("mxfp4", t, route=route)
+
+
+@pytest.mark.parametrize("t", [32, 128, 512])
+def test_moe_mxfp4_tiles_sampled(t):
+    """Sorted tiles at 32-512 tokens on the full bank; the oracle checks a sample of
+    pairs stage by stage (g, u, h, quantized h, down) and the whole combine."""
+    c = CASES["mxfp4"]
+    wg, wu, wd, dwg, dwu, dwd = _bank("mxfp4")
+    g = synth.rng(305, t)
+    H, I, E, K = c["hidden"], c["inter"], c["E"], c["topk"]
+    x = synth.activations(t, H, g)
+    ids = synth.expert_ids(t, E, K, g)
+    ew = synth.expert_weights(t, K, g)
+    np_ = t * K
+    taps = {"g": torch.empty(np_, I, device="cuda"), "u": torch.empty(np_, I, device="cuda"),
+            "h": torch.empty(np_, I, device="cuda"),
+            "hq": torch.empty(np_, ft.row_bytes(c["a"], I), dtype=torch.uint8, device="cuda"),
+            "down": torch.empty(np_, H, device="cuda")}
+    log(f"moe mxfp4 tiles sampled t={t}")
+    y = host(ft.moe_q_vec(c["w"], dwg, dwu, dwd, E, H, I, c["a"], dev(x), dev(ids), dev(ew), route=0, taps=taps))
+    gg, uu, hh, hq, dd = (host(taps[k]) for k in ("g", "u", "h", "hq", "down"))
+    xq = oracle.quantize(c["a"], x)
+    flat = ids.reshape(-1)
+    pairs = np.unique(np.concatenate([np.arange(4), np.arange(np_ - 4, np_), g.choice(np_, 12, replace=False)]))
+    for p in pairs:
+        e = flat[p]
+        rg = oracle.matvec(c["w"], np.ascontiguousarray(wg[e]), I, H, c["a"], xq[p // K][None], 1)[0]
+        ru = oracle.matvec(c["w"], np.ascontiguousarray(wu[e]), I, H, c["a"], xq[p // K][None], 1)[0]
+        check_fp32(gg[p], rg, f"g pair {p}")
+        check_fp32(uu[p], ru, f"u pair {p}")
+        rh = (rg / (1.0 + np.exp(-rg)) * ru)
+        check_fp32(hh[p], rh, f"h pair {p}")
+        assert np.array_equal(hq[p], oracle.quantize(c["a"], hh[p][None])[0]), f"hq pair {p}"
+        rd = oracle.matvec(c["w"], np.ascontiguousarray(wd[e]), H, I, c["a"], hq[p][None], 1)[0]
+        check_fp32(dd[p], rd, f"down pair {p}")
+    check_fp32(y, oracle.moe_combine(dd, ew), "combine")
+
+
 def test_moe_end_to_end_reported():
     """End to end from fp32 x (not gated on exact h codes): the GPU output stays
     close to the oracle's own end-to-end result."""
