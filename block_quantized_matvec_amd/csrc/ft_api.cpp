@@ -85,11 +85,12 @@ MoeScratch moe_layout(int w, int act, int64_t hidden, int64_t inter, int64_t t, 
   return s;
 }
 
-// scratch layout of the grouped GEMM's sort
+// scratch layout of the grouped GEMM: the sort, then (MXFP4) the FP8 halves of
+// the activation rows (512 bytes per row and superblock)
 struct SortScratch {
-  size_t counts, offsets, pairs, total;
+  size_t counts, offsets, pairs, xf8, total;
 };
-SortScratch sort_layout(int64_t n_expert, int64_t t, int topk) {
+SortScratch sort_layout(int64_t n_expert, int64_t t, int topk, size_t xf8_bytes = 0) {
   SortScratch s;
   size_t off = 0;
   s.counts = off;
@@ -98,15 +99,23 @@ SortScratch sort_layout(int64_t n_expert, int64_t t, int topk) {
   off += align256((size_t)(n_expert + 1) * 4);
   s.pairs = off;
   off += align256((size_t)t * topk * 4);
+  s.xf8 = off;
+  off += align256(xf8_bytes);
   s.total = off;
   return s;
 }
+size_t xf8_bytes_of(int w, int64_t rows, int64_t k) { return w == FT_MXFP4 ? (size_t)rows * (k / 256) * 512 : 0; }
 
 bool mmvq_pair(int w, int a) {
   return a == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K);
 }
 bool moe_pair(int w, int a) { return (w == FT_Q4_K && a == FT_Q8_1) || (w == FT_MXFP4 && a == FT_Q8_K); }
 bool moe_tile_pair(int w, int a) { return w == FT_MXFP4 && a == FT_Q8_K; }
+// the tile route splits x, then h, into FP8 halves in one buffer
+size_t moe_xf8_bytes(int w, int64_t hidden, int64_t inter, int64_t t, int topk) {
+  const size_t a = xf8_bytes_of(w, t, hidden), b = xf8_bytes_of(w, t * topk, inter);
+  return a > b ? a : b;
+}
 bool grouped_pair(int w, int a) {
   return a == FT_Q8_K && (w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4);
 }
@@ -216,11 +225,12 @@ size_t ft_moe_scratch_bytes(ft_type w, ft_type act, int64_t n_expert, int64_t hi
   if (!is_act(act) || t < 0 || topk < 0 || n_expert < 1) return 0;
   // the sorted-tile route also needs the sort's buffers
   return moe_layout(w, act, hidden, inter, t, topk).total +
-         (moe_tile_pair(w, act) ? sort_layout(n_expert, t, topk).total : 0);
+         (moe_tile_pair(w, act) ? sort_layout(n_expert, t, topk, moe_xf8_bytes(w, hidden, inter, t, topk)).total : 0);
 }
 
-size_t ft_grouped_scratch_bytes(int64_t n_expert, int64_t t, int topk) {
-  return sort_layout(n_expert, t, topk).total;
+size_t ft_grouped_scratch_bytes(ft_type w, int64_t n_expert, int64_t k, int64_t t, int topk, int x_per_pair) {
+  if (n_expert < 1 || k < 0 || t < 0 || topk < 1) return 0;
+  return sort_layout(n_expert, t, topk, xf8_bytes_of(w, x_per_pair ? t * topk : t, k)).total;
 }
 
 ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const void* w_down, int64_t n_expert,
@@ -251,13 +261,13 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
 
   hipStream_t st = hs(stream);
   const MoeScratch L = moe_layout(w, act, hidden, inter, t, topk);
-  const SortScratch S = sort_layout(n_expert, t, topk);
+  const SortScratch S = sort_layout(n_expert, t, topk, moe_xf8_bytes(w, hidden, inter, t, topk));
   void* base = nullptr;
   ft_status s = pool_get(st, L.total + (tiles ? S.total : 0), &base);
   if (s != FT_OK) return s;
   uint8_t* b = (uint8_t*)base;
 
-  MoeArgs a;
+  MoeArgs a = {};
   a.w = w;
   a.act = act;
   a.w_gate = w_gate;
@@ -270,21 +280,27 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
   a.topk = topk;
   a.ids = expert_ids;
   a.ew = expert_w;
+  a.x = x;
   a.xq = b + L.xq;
   a.h = o.tap_h ? o.tap_h : (float*)(b + L.h);
   a.g_tap = o.tap_g;
   a.u_tap = o.tap_u;
   a.hq = o.in_hq ? const_cast<void*>(o.in_hq) : (o.tap_hq ? o.tap_hq : (void*)(b + L.hq));
+  a.hq_tap = o.tap_hq;
+  a.in_hq = o.in_hq;
   a.dpair = o.tap_down ? o.tap_down : (float*)(b + L.d);
   a.y = y;
 
-  hipError_t e = ftk_launch_quantize(act, x, t, hidden, hidden, (void*)a.xq, st);
+  hipError_t e = hipSuccess;
   if (tiles) {
+    e = ftk_launch_quantize(act, x, t, hidden, hidden, (void*)a.xq, st);
     uint8_t* sb = b + L.total;
     int32_t* counts = (int32_t*)(sb + S.counts);
     int32_t* offsets = (int32_t*)(sb + S.offsets);
     int32_t* pairs = (int32_t*)(sb + S.pairs);
+    void* xf8 = sb + S.xf8;
     if (e == hipSuccess) e = ftk_launch_sort(expert_ids, t, topk, n_expert, counts, offsets, pairs, st);
+    if (e == hipSuccess && w == FT_MXFP4) e = ftk_launch_fp8_split(a.xq, t, hidden, xf8, st);
     GroupedArgs gu = {};
     gu.w = w;
     gu.act = act;
@@ -296,6 +312,7 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
     gu.n = inter;
     gu.k = hidden;
     gu.xq = a.xq;
+    gu.xf8 = w == FT_MXFP4 ? xf8 : nullptr;
     gu.x_per_pair = 0;
     gu.t = t;
     gu.topk = topk;
@@ -308,6 +325,7 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
     if (e == hipSuccess && o.in_hq && o.tap_hq)
       e = hipMemcpyAsync(o.tap_hq, o.in_hq, (size_t)t * topk * row_bytes_of(act, inter), hipMemcpyDeviceToDevice,
                          st);
+    if (e == hipSuccess && w == FT_MXFP4) e = ftk_launch_fp8_split(a.hq, t * topk, inter, xf8, st);
     GroupedArgs dn = gu;
     dn.W = w_down;
     dn.W2 = nullptr;
@@ -315,16 +333,16 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
     dn.n = hidden;
     dn.k = inter;
     dn.xq = a.hq;
+    dn.xf8 = w == FT_MXFP4 ? xf8 : nullptr;
     dn.x_per_pair = 1;
     dn.y = a.dpair;
     if (e == hipSuccess) e = ftk_launch_grouped(dn, st);
     if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
     return hip_status(e);
   }
-  if (e == hipSuccess) e = ftk_launch_moe_gate_up(a, st);
-  if (e == hipSuccess && !o.in_hq) e = ftk_launch_quantize(act, a.h, t * topk, inter, inter, a.hq, st);
-  if (e == hipSuccess && o.in_hq && o.tap_hq)
-    e = hipMemcpyAsync(o.tap_hq, o.in_hq, (size_t)t * topk * row_bytes_of(act, inter), hipMemcpyDeviceToDevice, st);
+  // direct route: gate/up (quantizes x itself), down (quantizes each expert's h
+  // rows itself, or reads in_hq), slot-order combine
+  e = ftk_launch_moe_gate_up(a, st);
   if (e == hipSuccess) e = ftk_launch_moe_down(a, st);
   if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
   return hip_status(e);
@@ -341,7 +359,7 @@ ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t 
   if (!W || !xq || !expert_ids || !y) return FT_ERR_INVALID_ARG;
   if (!aligned16(W) || !aligned16(xq) || !aligned16(y)) return FT_ERR_ALIGNMENT;
   hipStream_t st = hs(stream);
-  const SortScratch L = sort_layout(n_expert, t, topk);
+  const SortScratch L = sort_layout(n_expert, t, topk, xf8_bytes_of(w, x_per_pair ? t * topk : t, k));
   void* base = nullptr;
   ft_status s = pool_get(st, L.total, &base);
   if (s != FT_OK) return s;
@@ -361,8 +379,10 @@ ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t 
   a.offsets = (const int32_t*)(b + L.offsets);
   a.pairs = (const int32_t*)(b + L.pairs);
   a.y = y;
+  a.xf8 = w == FT_MXFP4 ? (const void*)(b + L.xf8) : nullptr;
   hipError_t e = ftk_launch_sort(expert_ids, t, topk, n_expert, (int32_t*)(b + L.counts), (int32_t*)(b + L.offsets),
                                  (int32_t*)(b + L.pairs), st);
+  if (e == hipSuccess && w == FT_MXFP4) e = ftk_launch_fp8_split(xq, x_per_pair ? t * topk : t, k, b + L.xf8, st);
   if (e == hipSuccess) e = ftk_launch_grouped(a, st);
   return hip_status(e);
 }

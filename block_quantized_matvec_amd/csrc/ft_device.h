@@ -416,6 +416,60 @@ __device__ __forceinline__ float unit_combine(const Unit<F>& u, const ActUnit<F>
 }
 
 // ---------------------------------------------------------------------------
+// activation quantizers, one block per call (shared by the standalone quantize
+// kernels and the fused prologues of the MoE kernels, so both are bit-identical).
+// amax, d = amax/127 (fp16 for Q8_1, fp32 for Q8_K), q = clamp(round half away
+// from zero of x/d against the stored d, +-127), IEEE correctly rounded division.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int q8_code(float v, float d) {
+  if (d == 0.0f) return 0;
+  const float rq = roundf(v / d);
+  return rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
+}
+
+// Q8_1: a half-wave per 32-element block, lane l (0..31) holds element l; every
+// lane of the wave must call it.  ob: the 36-byte block.
+__device__ __forceinline__ void q8_1_block(float v, int l, uint8_t* ob) {
+  float a = fabsf(v);
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 32));
+  uint32_t dh = f2h_bits(a / 127.0f);
+  const float d = h2f(dh);
+  const int q = q8_code(v, d);
+  int s = q;
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) s += __shfl_xor(s, m, 32);
+  ob[4 + l] = (uint8_t)(int8_t)q;
+  if (l == 0) {
+    if (d == 0.0f) dh = 0;
+    const uint32_t sh = f2h_bits(d * (float)s);
+    *(uint32_t*)ob = dh | (sh << 16);
+  }
+}
+
+// Q8_K: a wave per 256-element block, lane holds elements 4*lane .. 4*lane+3;
+// every lane of the wave must call it.  ob: the 292-byte block.
+__device__ __forceinline__ void q8_k_block(const float (&v)[4], int lane, uint8_t* ob) {
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
+  const float d = a / 127.0f;
+  uint32_t packed = 0;
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = q8_code(v[i], d);
+    s += q;
+    packed |= ((uint32_t)(uint8_t)(int8_t)q) << (8 * i);
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);  // 16-element group: lanes 4g .. 4g+3
+  *(uint32_t*)(ob + 4 + 4 * lane) = packed;
+  if ((lane & 3) == 0) *(int16_t*)(ob + 260 + 2 * (lane >> 2)) = (int16_t)s;
+  if (lane == 0) *(float*)ob = d;
+}
+
+// ---------------------------------------------------------------------------
 // 64-lane reductions
 // ---------------------------------------------------------------------------
 // value of the partner lane at xor-distance S (S = 1, 2: quad permutes; 4, 8:

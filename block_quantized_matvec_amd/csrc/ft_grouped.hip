@@ -23,8 +23,11 @@
 //    sub-block j) and Q6_K's -32 offset term run on v_mfma_f32_16x16x16_f16 over
 //    the 16-element code sums, which are exact in fp16 (|sum| <= 2032) and whose
 //    products and sums are exact in fp32.
-//  * MXFP4 blocks are 32-element groups with a power-of-two scale: each group's
-//    int32 result is converted and scaled in fp32.
+//  * MXFP4 runs on the block-scaled v_mfma_scale_f32_16x16x128_f8f6f4: the weights'
+//    qs bytes are the FP4 B operand as stored and their E8M0 bytes the B scales;
+//    the Q8_K codes enter as two exact FP8 halves x = 16*hi + lo (split once per
+//    activation row beforehand), lo with scale 1 and hi with scale 2^4 chained in
+//    one accumulator.  No E2M1 decode and no per-block scaling in the VALU.
 //  * Per 256-element superblock the workgroup stages the activations of up to PT
 //    pair tiles into LDS, in MFMA A-operand order, with the 16-element code sums
 //    computed from the codes; each wave stages its rows' weight bytes into its own
@@ -46,6 +49,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int GM_WAVES = 4;
 constexpr int GM_THREADS = 64 * GM_WAVES;
@@ -64,12 +68,15 @@ template <> struct GSb<FT_MXFP4> { static constexpr int BYTES = 136, SLOT = 176;
 
 // LDS layout (bytes) for PT pair tiles: one superblock's buffer of BUF bytes, then
 // the all-zero tile of the Q6_K half masks.
+// MXFP4 tiles hold the FP8 halves instead: [PT][2 k-steps][lo, hi][2 16-byte
+// halves][64 lanes] x 16 B, and need no code sums.
 template <int F, int PT> struct GLds {
+  static constexpr bool FP4 = F == FT_MXFP4;
   static constexpr int GSTR = 544;                       // bytes per 32-element group (512 + bank pad)
-  static constexpr int TSTR = 8 * GSTR;                  // bytes per pair tile
+  static constexpr int TSTR = FP4 ? 8192 : 8 * GSTR;     // bytes per pair tile
   static constexpr int CODES = 0;                        // [PT][8 groups][64 lanes] x 8 B (+ pad)
   static constexpr int BSUM = CODES + PT * TSTR;         // [PT][64 lanes] x 4 fp16
-  static constexpr int DX = BSUM + PT * 512;             // [PT][16 pairs] fp32
+  static constexpr int DX = BSUM + (FP4 ? 0 : PT * 512); // [PT][16 pairs] fp32
   static constexpr int WT = DX + PT * 64;                // [waves][16*RG rows][SLOT]
   static constexpr int BUF = WT + GM_WAVES * 16 * GRg<F>::RG * GSb<F>::SLOT;
   static constexpr int ZTILE = BUF;                      // the zero tile
@@ -81,7 +88,8 @@ template <int F> struct GW {
   uint64_t b[8];    // int8 codes of the lane's 8 elements of each 32-element group
   int sc[8];        // integer sub-block scales (Q4_K/Q5_K)
   uint32_t scp[4];  // Q6_K: the 16 int8 sub-block scales, packed
-  float s[8];       // MXFP4: 2^(e-128) per block
+  u32x4 fq[2];      // MXFP4: the raw qs bytes of block 4s + q (FP4 MFMA B operand), k-step s
+  int e8[2];        // MXFP4: their E8M0 scale bytes
   v4h mb;           // f16 MFMA B operand of the min / offset term
   float d, dmin;
 };
@@ -156,16 +164,15 @@ __device__ __forceinline__ void gw_decode(const uint8_t* sl, uint32_t o, int q, 
                  (_Float16)(float)(int8_t)((sq >> 16) & 0xFFu), (_Float16)(float)(int8_t)(sq >> 24)};
     w.d = h2f(rd.u16(o + 208));
     w.dmin = 0.0f;
-  } else {  // MXFP4: 8 blocks of 17 bytes
+  } else {  // MXFP4: lane quarter q takes block 4s + q of k-step s (17 bytes: E8M0, qs[16])
     const Reader<const uint32_t*> rd{(const uint32_t*)sl};
-    const uint32_t nsh = 4u * (uint32_t)(q >> 1);   // quarters 2, 3 take the high nibbles
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) {
-      const uint32_t bo = o + 17 * jb;
-      uint32_t v[2];
-      rd.template dwords<2>(bo + 1 + 8 * (q & 1), v);
-      w.b[jb] = pk64(e2m1x2_bytes((v[0] >> nsh) & 0x0F0F0F0Fu), e2m1x2_bytes((v[1] >> nsh) & 0x0F0F0F0Fu));
-      w.s[jb] = e8m0_half(rd.u8(bo));
+    for (int st = 0; st < 2; ++st) {
+      const uint32_t bo = o + 17 * (4 * st + q);
+      uint32_t v[4];
+      rd.template dwords<4>(bo + 1, v);
+      w.fq[st] = (u32x4){v[0], v[1], v[2], v[3]};
+      w.e8[st] = (int)rd.u8(bo);
     }
     w.d = 0.0f;
     w.dmin = 0.0f;
@@ -178,7 +185,8 @@ __device__ __forceinline__ void gw_decode(const uint8_t* sl, uint32_t o, int q, 
 template <int F, int PT, bool GLU>
 __global__ void __launch_bounds__(GM_THREADS)
 grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W2, int64_t n, int64_t row_bytes,
-                    int nsb, const uint8_t* __restrict__ xq, int64_t xrow_bytes, int x_per_pair, int topk,
+                    int nsb, const uint8_t* __restrict__ xq, int64_t xrow_bytes, const uint8_t* __restrict__ xf8,
+                    int x_per_pair, int topk,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
                     float* __restrict__ y, float* __restrict__ g_tap, float* __restrict__ u_tap,
                     int64_t row_tiles, int64_t total, int64_t per_xcd) {
@@ -190,8 +198,10 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
   constexpr int WROWS = 16 * RG;                       // weight rows per wave
   constexpr int OROWS = GLU ? 16 : WROWS;              // output rows per wave
   constexpr int NWI = (WROWS * NCH + 63) / 64;         // weight chunks per lane
-  constexpr int NAI = (PT * 256 + GM_THREADS - 1) / GM_THREADS;   // activation chunks per thread
-  constexpr bool MINT = F != FT_MXFP4;                 // has a code-sum term
+  constexpr bool FP4 = F == FT_MXFP4;                  // block-scaled FP4 x FP8 MFMA path
+  constexpr int CPP = FP4 ? 32 : 16;                   // 16-byte activation chunks per pair and superblock
+  constexpr int NAI = (PT * 16 * CPP + GM_THREADS - 1) / GM_THREADS;   // activation chunks per thread
+  constexpr bool MINT = !FP4;                          // has a code-sum term
   constexpr bool KQ = F == FT_Q4_K || F == FT_Q5_K;
   extern __shared__ u32x4 gsm[];
   uint8_t* L = (uint8_t*)gsm;
@@ -223,19 +233,22 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
     const int gm = min(PT * 16, p1 - g0);
     const int npt = (gm + 15) >> 4;
 
-    // activation staging: item it = tid + GM_THREADS*i is chunk su = it&15 (16 codes)
-    // of pair slot it>>4 of the group
+    // activation staging: item it = tid + GM_THREADS*i is chunk su = it % CPP of pair
+    // slot it / CPP of the group (16 codes, or an FP8 chunk of the MXFP4 path)
     const uint8_t* xr[NAI];
+    const uint8_t* xr8[NAI];
 #pragma unroll
     for (int i = 0; i < NAI; ++i) {
-      const int pi = (tid + GM_THREADS * i) >> 4;
+      const int pi = (tid + GM_THREADS * i) / CPP;
       xr[i] = nullptr;
+      xr8[i] = nullptr;
       if (pi < gm) {
-        const int pr = pairs[g0 + pi];
-        xr[i] = xq + (int64_t)(x_per_pair ? pr : pr / topk) * xrow_bytes;
+        const int64_t row = x_per_pair ? pairs[g0 + pi] : pairs[g0 + pi] / topk;
+        xr[i] = xq + row * xrow_bytes;
+        if constexpr (FP4) xr8[i] = xf8 + row * (int64_t)nsb * 512;
       }
     }
-    const int su = tid & 15;
+    const int su = tid % CPP;
 
     u32x4 pa[NAI];
     float pdx[NAI];
@@ -246,8 +259,12 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
         pa[i] = (u32x4){0u, 0u, 0u, 0u};
         pdx[i] = 0.0f;
         if (xr[i]) {
-          const uint32_t* src = (const uint32_t*)(xr[i] + (int64_t)sb * 292 + 4 + 16 * su);
-          pa[i] = (u32x4){src[0], src[1], src[2], src[3]};
+          if constexpr (FP4) {
+            pa[i] = *(const u32x4*)(xr8[i] + (int64_t)sb * 512 + 16 * su);
+          } else {
+            const uint32_t* src = (const uint32_t*)(xr[i] + (int64_t)sb * 292 + 4 + 16 * su);
+            pa[i] = (u32x4){src[0], src[1], src[2], src[3]};
+          }
           if (su == 0) pdx[i] = *(const float*)(xr[i] + (int64_t)sb * 292);
         }
       }
@@ -269,7 +286,15 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
 #pragma unroll
       for (int i = 0; i < NAI; ++i) {
         const int it = tid + GM_THREADS * i;
-        if (it < PT * 256) {   // uniform per wave
+        if (FP4 && it < PT * 16 * CPP) {   // uniform per wave
+          // chunk su = 16p + 2j + h -> A operand of k-step j/4, part p: lane quarter
+          // 2(j&1) + h, byte half (j&2)/2
+          const int pi = it / CPP, m = pi >> 4, spl = pi & 15;
+          const int pp = su >> 4, j = (su >> 1) & 7, hh = su & 1;
+          const int st = j >> 2, jj = j & 3, qa = 2 * (jj & 1) + hh, bh = jj >> 1;
+          *(u32x4*)(B + LY::CODES + m * LY::TSTR + (st * 2 + pp) * 2048 + bh * 1024 + (qa * 16 + spl) * 16) = pa[i];
+          if (su == 0) ((float*)(B + LY::DX))[m * 16 + spl] = pdx[i];
+        } else if (!FP4 && it < PT * 16 * CPP) {   // uniform per wave
           const int pi = it >> 4, m = pi >> 4, spl = pi & 15;
           const int j = su >> 1, qa = 2 * (su & 1);
           uint64_t* cd = (uint64_t*)(B + LY::CODES + m * LY::TSTR + j * LY::GSTR);
@@ -327,7 +352,35 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
       const v4i zi = {0, 0, 0, 0};
     #pragma unroll
       for (int m = 0; m < PT; ++m) {
-        if (m < npt) {
+        if (FP4 && m < npt) {
+          // two k-steps x (lo, hi) chained in one accumulator: the hi half carries
+          // scale 2^4 (E8M0 131), the weights their block's E8M0 byte
+          const uint8_t* ab = cur + LY::CODES + m * LY::TSTR + 16 * lane;
+          const v4f dx4 = *(const v4f*)(cur + LY::DX + m * 64 + 16 * q);
+          v4f dd[RG];
+    #pragma unroll
+          for (int rg = 0; rg < RG; ++rg) dd[rg] = zf;
+    #pragma unroll
+          for (int st = 0; st < 2; ++st) {
+    #pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const u32x4 a0 = *(const u32x4*)(ab + (st * 2 + pp) * 2048);
+              const u32x4 a1 = *(const u32x4*)(ab + (st * 2 + pp) * 2048 + 1024);
+              const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    #pragma unroll
+              for (int rg = 0; rg < RG; ++rg) {
+                const v8i bw = {(int)w[rg].fq[st].x, (int)w[rg].fq[st].y, (int)w[rg].fq[st].z, (int)w[rg].fq[st].w,
+                                0, 0, 0, 0};
+                dd[rg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw, dd[rg], 0, 4, 0, pp ? 131 : 127, 0,
+                                                                          w[rg].e8[st]);
+              }
+            }
+          }
+    #pragma unroll
+          for (int rg = 0; rg < RG; ++rg)
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][rg][r] = fmaf(dx4[r], dd[rg][r], acc[m][rg][r]);
+        } else if (!FP4 && m < npt) {
           const uint8_t* ac = cur + LY::CODES + m * LY::TSTR + 8 * lane;
           // Q6_K: the low half of a 32-element group (quarters 0, 1) is one sub-block
           // and the high half the next; each of its two MFMAs reads zeros in the other
@@ -361,7 +414,7 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
                 for (int r = 0; r < 4; ++r) isc[rg][r] += __mul24(dv[r], s0) + __mul24(dh[r], s1);
               } else {
     #pragma unroll
-                for (int r = 0; r < 4; ++r) ys[rg][r] = fmaf((float)dv[r], w[rg].s[j], ys[rg][r]);
+                for (int r = 0; r < 4; ++r) ys[rg][r] += (float)dv[r];   // not reached (MXFP4 takes the FP4 path)
               }
             }
           }
@@ -428,7 +481,8 @@ static hipError_t launch_gm(const GroupedArgs& a, hipStream_t st) {
   const size_t lds = (size_t)GLds<F, PT>::TOTAL;
   hipLaunchKernelGGL((grouped_mfma_kernel<F, PT, GLU>), dim3((unsigned)(per * 8)), dim3(GM_THREADS), lds, st,
                      (const uint8_t*)a.W, (const uint8_t*)a.W2, a.n, row_bytes, (int)(a.k / 256),
-                     (const uint8_t*)a.xq, (int64_t)(a.k / 256 * 292), a.x_per_pair, a.topk, a.offsets, a.pairs,
+                     (const uint8_t*)a.xq, (int64_t)(a.k / 256 * 292), (const uint8_t*)a.xf8, a.x_per_pair, a.topk,
+                     a.offsets, a.pairs,
                      a.y, a.g_tap, a.u_tap, row_tiles, total, per);
   return hipGetLastError();
 }
@@ -452,6 +506,7 @@ using namespace ftk;
 
 hipError_t ftk_launch_grouped(const GroupedArgs& a, hipStream_t st) {
   if (a.act != FT_Q8_K || a.k % 256) return hipErrorInvalidValue;
+  if (a.w == FT_MXFP4 && !a.xf8) return hipErrorInvalidValue;   // needs the FP8 halves
   if (a.W2) {   // fused gate/up + SwiGLU
     if (a.w == FT_MXFP4) return grouped_f<FT_MXFP4, true>(a, st);
     return hipErrorInvalidValue;

@@ -7,6 +7,8 @@
 
 #include "ft.h"
 
+int ftk_num_cus();   // compute units of the current device
+
 struct MmvqArgs {
   int w, act;
   const void* W;
@@ -33,6 +35,8 @@ hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
 
 hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
                                hipStream_t st);
+// Q8_K rows [rows][k/256] -> FP8 halves for the FP4 MFMA, 512 bytes per superblock
+hipError_t ftk_launch_fp8_split(const void* xq, int64_t rows, int64_t k, void* out, hipStream_t st);
 hipError_t ftk_launch_dequant(int w, const void* blocks, int64_t rows, int64_t k, float* out,
                               hipStream_t st);
 hipError_t ftk_launch_block_dots(int w, const void* W, int64_t n, int64_t k, int act, const void* xq,
@@ -52,11 +56,14 @@ struct MoeArgs {
   int topk;
   const int32_t* ids;
   const float* ew;
-  const void* xq;      // quantized x [t][hidden/blk_a]
+  const float* x;      // [t][hidden] fp32 (the direct route quantizes it in its gate/up prologue)
+  const void* xq;      // quantized x [t][hidden/blk_a] (sorted-tile route)
   float* h;            // [t*topk][inter]
   float* g_tap;        // nullable
   float* u_tap;        // nullable
-  void* hq;            // quantized h [t*topk][inter/blk_a]
+  void* hq;            // quantized h [t*topk][inter/blk_a] (sorted-tile route)
+  void* hq_tap;        // nullable: the direct route writes quantized h here
+  const void* in_hq;   // nullable: the direct route's down stage reads these blocks instead
   float* dpair;        // [t*topk][hidden] per-pair down projections
   float* y;            // [t][hidden]
 };
@@ -74,6 +81,7 @@ struct GroupedArgs {
   float* u_tap;            // nullable (W2 form)
   int64_t n_expert, n, k;
   const void* xq;
+  const void* xf8;         // MXFP4: FP8 halves of xq (ftk_launch_fp8_split), 512 B per superblock
   int x_per_pair;
   int64_t t;
   int topk;

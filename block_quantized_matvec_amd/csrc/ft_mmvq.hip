@@ -273,18 +273,7 @@ mmvq_direct_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int 
 
 // host side -------------------------------------------------------------------
 
-int g_num_cus = 0;
-
-static int num_cus() {
-  if (g_num_cus > 0) return g_num_cus;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-    g_num_cus = cus;
-  else
-    g_num_cus = 256;
-  return g_num_cus;
-}
+static int num_cus() { return ftk_num_cus(); }
 
 template <int F, int A, int T, int LR, int P, int CPL>
 static hipError_t launch_mmvq_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
@@ -441,6 +430,19 @@ static hipError_t launch_fa(MmvqArgs a, int64_t k, hipStream_t st) {
   return dispatch_t<F, A>(a, pl, st);
 }
 }  // namespace ftk
+
+// compute units of the current device (cached; every device of one node is the same part)
+int ftk_num_cus() {
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    cached = cus;
+  else
+    cached = 256;
+  return cached;
+}
 
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;

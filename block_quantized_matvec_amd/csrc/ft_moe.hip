@@ -15,6 +15,8 @@
 //    tokens that did not pick the expert;
 //  * gate and up share the activations; SwiGLU is applied right after the
 //    64-lane reduction, before h leaves registers.
+#include <stdlib.h>
+
 #include "ft_device.h"
 #include "ft_internal.h"
 
@@ -25,6 +27,7 @@ constexpr int MOE_THREADS = 256;
 // ---------------------------------------------------------------------------
 // router: one wave per token
 // ---------------------------------------------------------------------------
+template <int MAXE>   // logits per lane (n_expert <= 64 * MAXE)
 __global__ void __launch_bounds__(256)
 route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk, int32_t* __restrict__ ids,
              float* __restrict__ w) {
@@ -32,7 +35,6 @@ route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk
   const int lane = threadIdx.x & 63;
   if (tok >= t) return;
   const float* l = logits + tok * n_expert;
-  constexpr int MAXE = 1024 / 64;
   float v[MAXE];
   bool taken[MAXE];
 #pragma unroll
@@ -50,14 +52,18 @@ route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk
 #pragma unroll
     for (int i = 0; i < MAXE; ++i)
       if (!taken[i] && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = lane + 64 * i; }
-    // wave argmax; candidates with index -1 lose
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, 64);
-      const int oi = __shfl_xor(bi, m, 64);
+    // wave argmax (all lanes end with the winner); candidates with index -1 lose.
+    // Levels 1-8 pair lanes with DPP moves, 16 and 32 with LDS permutes.
+    auto level = [&](float ov, int oi) {
       const bool better = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
       if (better) { bv = ov; bi = oi; }
-    }
+    };
+    level(xchg<1>(bv), __float_as_int(xchg<1>(__int_as_float(bi))));
+    level(xchg<2>(bv), __float_as_int(xchg<2>(__int_as_float(bi))));
+    level(xchg<4>(bv), __float_as_int(xchg<4>(__int_as_float(bi))));
+    level(xchg<8>(bv), __float_as_int(xchg<8>(__int_as_float(bi))));
+    level(xchg<16>(bv), __float_as_int(xchg<16>(__int_as_float(bi))));
+    level(xchg<32>(bv), __float_as_int(xchg<32>(__int_as_float(bi))));
     selv[k] = bv;
     seli[k] = bi;
 #pragma unroll
@@ -217,25 +223,6 @@ __device__ __forceinline__ int clamp_id(int e, int64_t n_expert) {
   return e < 0 ? 0 : (e >= n_expert ? (int)n_expert - 1 : e);
 }
 
-// stream nbytes starting at src (any alignment) into LDS at dst; returns the
-// shift (src & 15) at which byte 0 landed.  Every thread of the workgroup calls it.
-__device__ __forceinline__ uint32_t stage_bytes(const uint8_t* src, int64_t nbytes, uint32_t* dst, int tid,
-                                                int nthreads) {
-  const uintptr_t a = (uintptr_t)src;
-  const uint8_t* a0 = (const uint8_t*)(a & ~(uintptr_t)15);
-  const uint32_t shift = (uint32_t)(a & 15);
-  const int nchunks = (int)((shift + nbytes + 15) >> 4);
-  const int wave = tid >> 6;
-  for (int base = 0; base < nchunks; base += nthreads) {
-    const int c = base + tid;
-    if (c < nchunks)
-      __builtin_amdgcn_global_load_lds((const void*)(a0 + 16 * (int64_t)c),
-                                       (__attribute__((address_space(3))) void*)(dst + 4 * (base + wave * 64)),
-                                       16, 0, 0);
-  }
-  return shift;
-}
-
 // Decide which tokens picked expert e (and at which slot); returns false if an
 // earlier slot already names e (that workgroup owns the expert).
 template <int T>
@@ -261,168 +248,282 @@ __device__ __forceinline__ bool expert_tokens(const int32_t* __restrict__ ids, i
 }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU (direct route)
-// grid: x = row tiles of inter, y = (token, slot) pairs of this token chunk
+// Direct-route expert kernels.  grid: x = workgroups per slot, y = the (token,
+// slot) pairs of this token chunk; the workgroup of the first slot naming an
+// expert owns it (later duplicates exit).  Each workgroup takes a contiguous share
+// of the expert's rows and walks it in tiles of whole rows: tile i+1 is fetched
+// into VGPRs with 16-byte loads while tile i is computed from LDS (as the matvec
+// does).  The activation rows the expert needs are quantized by the workgroup
+// itself into LDS first (x for gate/up; the expert's h rows for down), with the
+// same per-block arithmetic as ft_quantize_act.
 // ---------------------------------------------------------------------------
-template <int F, int A, int T, int LR, int P>
-__global__ void __launch_bounds__(MOE_THREADS)
-moe_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t n_expert,
-                   int64_t inter, int row_bytes, int units_per_row, int rows_per_tile,
-                   const uint8_t* __restrict__ xq, int xrow_bytes, int t_real, const int32_t* __restrict__ ids,
-                   int topk, float* __restrict__ h, float* __restrict__ gtap, float* __restrict__ utap) {
-  using FT = Fmt<F>;
-  constexpr int G = MOE_THREADS / LR;
-  constexpr int RA = T >= 4 ? 1 : 4 / T;
-  constexpr int M = 2 * RA * T;   // g values then u values
-  static_assert(M <= LR, "");
-  extern __shared__ uint32_t smem[];
-  const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
-
-  int e, pair[T];
-  uint32_t mask;
-  if (!expert_tokens<T>(ids, blockIdx.y, t_real, topk, n_expert, e, mask, pair)) return;
-
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_tile;
-  const int nrows = (int)min<int64_t>(rows_per_tile, inter - r0);
-  const int64_t tile_bytes = (int64_t)nrows * row_bytes;
-  const uint32_t tile_words = (uint32_t)(((tile_bytes + 15 + 15) >> 4) << 2);
-  const uint32_t sg = stage_bytes(wg + ((int64_t)e * inter + r0) * row_bytes, tile_bytes, smem, tid, MOE_THREADS);
-  const uint32_t su = stage_bytes(wu + ((int64_t)e * inter + r0) * row_bytes, tile_bytes, smem + tile_words, tid,
-                                  MOE_THREADS);
-
-  ActUnit<F> act[P][T];
-  int ub[P], uu[P];
-  bool uv[P];
+template <int CPL>
+struct TileFetch {
+  u32x4 pre[CPL];
+  int nch;
+  __device__ __forceinline__ uint32_t fetch(const uint8_t* src, int64_t nbytes, int tid) {
+    const uintptr_t a = (uintptr_t)src;
+    const uint32_t shift = (uint32_t)(a & 15);
+    nch = (int)((shift + nbytes + 15) >> 4);
+    const u32x4* s4 = (const u32x4*)(src - shift);
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int u = gl + p * LR;
-    uv[p] = u < units_per_row;
-    ub[p] = u / FT::UPB;
-    uu[p] = u % FT::UPB;
+    for (int i = 0; i < CPL; ++i) {
+      const int c = i * MOE_THREADS + tid;
+      if (c < nch) pre[i] = __builtin_nontemporal_load(s4 + c);
+    }
+    return shift;
+  }
+  __device__ __forceinline__ void commit(u32x4* dst, int tid) const {
 #pragma unroll
-    for (int i = 0; i < T; ++i) {
-      if (uv[p] && ((mask >> i) & 1)) load_act_unit<F, A>(xq + (size_t)i * xrow_bytes, ub[p], uu[p], act[p][i]);
-      else zero_act_unit<F>(act[p][i]);
+    for (int i = 0; i < CPL; ++i) {
+      const int c = i * MOE_THREADS + tid;
+      if (c < nch) dst[c] = pre[i];
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+};
 
-  const Reader<const uint32_t*> rg{smem}, ru{smem + tile_words};
-  for (int rb = 0; rb < nrows; rb += G * RA) {
-    float v[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) v[i] = 0.0f;
-#pragma unroll
-    for (int ra = 0; ra < RA; ++ra) {
-      const int r = rb + ra * G + grp;
-      if (r < nrows) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          if (uv[p]) {
-            const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)ub[p] * FT::BB;
-            Unit<F> ug, uup;
-            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rg, sg + off, uu[p], ug);
-            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(ru, su + off, uu[p], uup);
-#pragma unroll
-            for (int i = 0; i < T; ++i) {
-              if ((mask >> i) & 1) {
-                v[ra * T + i] = unit_combine<F>(ug, act[p][i], v[ra * T + i]);
-                v[M / 2 + ra * T + i] = unit_combine<F>(uup, act[p][i], v[M / 2 + ra * T + i]);
-              }
-            }
-          }
-        }
-      }
+// quantize `rows` fp32 rows of length k (row i at src + i*lds_src) into act
+// blocks at dst (row i at dst + i*rowb) with the whole workgroup
+template <int A>
+__device__ __forceinline__ void quantize_rows(const float* __restrict__ src, int64_t lds_src, int rows, int64_t k,
+                                              uint8_t* dst, int rowb, int tid) {
+  if constexpr (A == FT_Q8_1) {
+    const int nb = (int)(k / 32), l = tid & 31;
+    for (int gb = tid >> 5; gb < rows * nb; gb += MOE_THREADS / 32) {   // uniform per half-wave
+      const int r = gb / nb, b = gb % nb;
+      q8_1_block(src[r * lds_src + b * 32 + l], l, dst + r * rowb + b * 36);
     }
-    group_reduce_multi<M, LR>(v, gl);
-    const int idx = gl / (LR / M);
-    const bool leader = (gl % (LR / M)) == 0;
-    const float other = __shfl_xor(v[0], LR / 2, 64);   // the up value of the same (row, token)
-    if (leader && idx < M / 2) {
-      const int ra = idx / T, i = idx % T;
-      const int r = rb + ra * G + grp;
-      if (r < nrows && ((mask >> i) & 1)) {
-        const float g = v[0], u = other;
-        const int64_t o = (int64_t)pair[i] * inter + r0 + r;
-        h[o] = g / (1.0f + expf(-g)) * u;
-        if (gtap) gtap[o] = g;
-        if (utap) utap[o] = u;
-      }
+  } else {
+    const int nb = (int)(k / 256), lane = tid & 63;
+    for (int gb = tid >> 6; gb < rows * nb; gb += MOE_THREADS / 64) {   // uniform per wave
+      const int r = gb / nb, b = gb % nb;
+      const float* xp = src + r * lds_src + b * 256 + 4 * lane;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = xp[i];
+      q8_k_block(v, lane, dst + r * rowb + b * 292);
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// down projection (direct route): per pair d = W_down[e] . hhat(pair)
-// ---------------------------------------------------------------------------
-template <int F, int A, int T, int LR, int P>
+// gate/up + SwiGLU: h[pair][r] = silu(g) * u for the rows of this workgroup's share
+template <int F, int A, int T, int LR, int P, int CPL>
 __global__ void __launch_bounds__(MOE_THREADS)
-moe_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int row_bytes,
-                int units_per_row, int rows_per_tile, const uint8_t* __restrict__ hq, int hrow_bytes,
-                int t_real, const int32_t* __restrict__ ids, int topk, float* __restrict__ dpair) {
+moe_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t n_expert,
+                   int64_t inter, int row_bytes, int units_per_row, int rows_per_wg, int rows_per_tile,
+                   const float* __restrict__ x, int64_t hidden, int t_real, const int32_t* __restrict__ ids,
+                   int topk, float* __restrict__ h, float* __restrict__ gtap, float* __restrict__ utap) {
   using FT = Fmt<F>;
   constexpr int G = MOE_THREADS / LR;
-  constexpr int RA = T >= 8 ? 1 : 8 / T;
-  constexpr int M = RA * T;
+  constexpr int M = 2 * T;   // g values then u values of one row per group
   static_assert(M <= LR, "");
-  extern __shared__ uint32_t smem[];
+  extern __shared__ u32x4 smem4[];
   const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
 
   int e, pair[T];
   uint32_t mask;
   if (!expert_tokens<T>(ids, blockIdx.y, t_real, topk, n_expert, e, mask, pair)) return;
+  const int64_t wr0 = (int64_t)blockIdx.x * rows_per_wg;
+  if (wr0 >= inter) return;
+  const int wrows = (int)min<int64_t>(rows_per_wg, inter - wr0);
+  const int ntiles = (wrows + rows_per_tile - 1) / rows_per_tile;
+  const uint8_t* gbase = wg + ((int64_t)e * inter + wr0) * row_bytes;
+  const uint8_t* ubase = wu + ((int64_t)e * inter + wr0) * row_bytes;
 
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_tile;
-  const int nrows = (int)min<int64_t>(rows_per_tile, hidden - r0);
-  const uint32_t sd = stage_bytes(wd + ((int64_t)e * hidden + r0) * row_bytes, (int64_t)nrows * row_bytes, smem,
-                                  tid, MOE_THREADS);
+  u32x4* tg = smem4;
+  u32x4* tu = smem4 + CPL * MOE_THREADS + 1;
+  uint8_t* xql = (uint8_t*)(smem4 + 2 * (CPL * MOE_THREADS + 1));
+  const int xrb = (int)(hidden / Act<A>::BLK * Act<A>::BB);
+
+  TileFetch<CPL> fg, fu;
+  auto tile_rows = [&](int tile) { return min(rows_per_tile, wrows - tile * rows_per_tile); };
+  uint32_t sg = fg.fetch(gbase, (int64_t)tile_rows(0) * row_bytes, tid);
+  uint32_t su = fu.fetch(ubase, (int64_t)tile_rows(0) * row_bytes, tid);
+
+  quantize_rows<A>(x, hidden, t_real, hidden, xql, xrb, tid);
+  __syncthreads();
   ActUnit<F> act[P][T];
   int ub[P], uu[P];
   bool uv[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    const int u = gl + p * LR;
-    uv[p] = u < units_per_row;
+    const int u0 = gl + p * LR;
+    uv[p] = u0 < units_per_row;
+    const int u = uv[p] ? u0 : 0;
     ub[p] = u / FT::UPB;
     uu[p] = u % FT::UPB;
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      if (uv[p] && ((mask >> i) & 1))
-        load_act_unit<F, A>(hq + (size_t)pair[i] * hrow_bytes, ub[p], uu[p], act[p][i]);
+      if (uv[p] && ((mask >> i) & 1)) load_act_unit<F, A>(xql + i * xrb, ub[p], uu[p], act[p][i]);
       else zero_act_unit<F>(act[p][i]);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  fg.commit(tg, tid);
+  fu.commit(tu, tid);
   __syncthreads();
 
-  const Reader<const uint32_t*> rd{smem};
-  for (int rb = 0; rb < nrows; rb += G * RA) {
-    float v[M];
+  const Reader<const uint32_t*> rg{(const uint32_t*)tg}, ru{(const uint32_t*)tu};
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int nr = tile_rows(tile);
+    const uint32_t cg = sg, cu = su;
+    if (tile + 1 < ntiles) {
+      const int64_t off = (int64_t)(tile + 1) * rows_per_tile * row_bytes;
+      sg = fg.fetch(gbase + off, (int64_t)tile_rows(tile + 1) * row_bytes, tid);
+      su = fu.fetch(ubase + off, (int64_t)tile_rows(tile + 1) * row_bytes, tid);
+    }
+    for (int rb = 0; rb < nr; rb += G) {
+      float v[M];
 #pragma unroll
-    for (int i = 0; i < M; ++i) v[i] = 0.0f;
-#pragma unroll
-    for (int ra = 0; ra < RA; ++ra) {
-      const int r = rb + ra * G + grp;
-      if (r < nrows) {
+      for (int i = 0; i < M; ++i) v[i] = 0.0f;
+      const int r = rb + grp;
+      if (r < nr) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          if (uv[p]) {
-            Unit<F> un;
-            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, sd + (uint32_t)r * row_bytes + (uint32_t)ub[p] * FT::BB, uu[p], un);
+          const uint32_t off = (uint32_t)r * row_bytes + (uint32_t)ub[p] * FT::BB;
+          Unit<F> ug, uup;
+          unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rg, cg + off, uu[p], ug);
+          unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(ru, cu + off, uu[p], uup);
 #pragma unroll
-            for (int i = 0; i < T; ++i)
-              if ((mask >> i) & 1) v[ra * T + i] = unit_combine<F>(un, act[p][i], v[ra * T + i]);
+          for (int i = 0; i < T; ++i) {
+            if ((mask >> i) & 1) {
+              v[i] = unit_combine<F>(ug, act[p][i], v[i]);
+              v[T + i] = unit_combine<F>(uup, act[p][i], v[T + i]);
+            }
           }
         }
       }
+      group_reduce_multi<M, LR>(v, gl);
+      const int idx = gl / (LR / M);
+      const bool leader = (gl % (LR / M)) == 0;
+      const float other = __shfl_xor(v[0], LR / 2, 64);   // the u value of the same token
+      if (leader && idx < T) {
+        const int i = idx;
+        if (r < nr && ((mask >> i) & 1)) {
+          const float g = v[0], u = other;
+          const int64_t o = (int64_t)pair[i] * inter + wr0 + (int64_t)tile * rows_per_tile + r;
+          h[o] = g / (1.0f + expf(-g)) * u;
+          if (gtap) gtap[o] = g;
+          if (utap) utap[o] = u;
+        }
+      }
     }
-    group_reduce_multi<M, LR>(v, gl);
-    const int idx = gl / (LR / M);
-    if ((gl % (LR / M)) == 0) {
-      const int ra = idx / T, i = idx % T;
-      const int r = rb + ra * G + grp;
-      if (r < nrows && ((mask >> i) & 1)) dpair[(int64_t)pair[i] * hidden + r0 + r] = v[0];
+    if (tile + 1 < ntiles) {
+      __syncthreads();   // every wave is done reading the tile
+      fg.commit(tg, tid);
+      fu.commit(tu, tid);
+      __syncthreads();
+    }
+  }
+}
+
+// down projection: dpair[pair][r] = W_down[e][r] . hhat(pair) for this workgroup's
+// share of rows; hhat of the expert's pairs is quantized here (or read from
+// in_hq), and the first workgroup of the slot writes it to hq_tap.
+template <int F, int A, int T, int LR, int P, int CPL>
+__global__ void __launch_bounds__(MOE_THREADS)
+moe_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int row_bytes,
+                int units_per_row, int rows_per_wg, int rows_per_tile, const float* __restrict__ h,
+                const uint8_t* __restrict__ in_hq, uint8_t* __restrict__ hq_tap, int64_t inter, int t_real,
+                const int32_t* __restrict__ ids, int topk, float* __restrict__ dpair) {
+  using FT = Fmt<F>;
+  constexpr int G = MOE_THREADS / LR;
+  constexpr int M = T;
+  static_assert(M <= LR, "");
+  extern __shared__ u32x4 smem4[];
+  const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
+
+  int e, pair[T];
+  uint32_t mask;
+  if (!expert_tokens<T>(ids, blockIdx.y, t_real, topk, n_expert, e, mask, pair)) return;
+  const int64_t wr0 = (int64_t)blockIdx.x * rows_per_wg;
+  if (wr0 >= hidden) return;
+  const int wrows = (int)min<int64_t>(rows_per_wg, hidden - wr0);
+  const int ntiles = (wrows + rows_per_tile - 1) / rows_per_tile;
+  const uint8_t* dbase = wd + ((int64_t)e * hidden + wr0) * row_bytes;
+
+  u32x4* td = smem4;
+  uint8_t* hql = (uint8_t*)(smem4 + CPL * MOE_THREADS + 1);
+  const int hrb = (int)(inter / Act<A>::BLK * Act<A>::BB);
+
+  TileFetch<CPL> fd;
+  auto tile_rows = [&](int tile) { return min(rows_per_tile, wrows - tile * rows_per_tile); };
+  uint32_t sd = fd.fetch(dbase, (int64_t)tile_rows(0) * row_bytes, tid);
+
+  // hhat of this expert's pairs (token slot i -> LDS row i)
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    if ((mask >> i) & 1) {
+      uint8_t* dst = hql + i * hrb;
+      if (in_hq) {
+        const uint8_t* srcq = in_hq + (int64_t)pair[i] * hrb;
+        for (int b = tid; b < hrb; b += MOE_THREADS) dst[b] = srcq[b];
+      } else {
+        quantize_rows<A>(h + (int64_t)pair[i] * inter, inter, 1, inter, dst, hrb, tid);
+      }
+    }
+  }
+  __syncthreads();
+  if (hq_tap && blockIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      if ((mask >> i) & 1)
+        for (int b = tid; b < hrb; b += MOE_THREADS) hq_tap[(int64_t)pair[i] * hrb + b] = hql[i * hrb + b];
+  }
+
+  ActUnit<F> act[P][T];
+  int ub[P], uu[P];
+  bool uv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int u0 = gl + p * LR;
+    uv[p] = u0 < units_per_row;
+    const int u = uv[p] ? u0 : 0;
+    ub[p] = u / FT::UPB;
+    uu[p] = u % FT::UPB;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      if (uv[p] && ((mask >> i) & 1)) load_act_unit<F, A>(hql + i * hrb, ub[p], uu[p], act[p][i]);
+      else zero_act_unit<F>(act[p][i]);
+    }
+  }
+  fd.commit(td, tid);
+  __syncthreads();
+
+  const Reader<const uint32_t*> rd{(const uint32_t*)td};
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int nr = tile_rows(tile);
+    const uint32_t cd = sd;
+    if (tile + 1 < ntiles)
+      sd = fd.fetch(dbase + (int64_t)(tile + 1) * rows_per_tile * row_bytes, (int64_t)tile_rows(tile + 1) * row_bytes,
+                    tid);
+    for (int rb = 0; rb < nr; rb += G) {
+      float v[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) v[i] = 0.0f;
+      const int r = rb + grp;
+      if (r < nr) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          Unit<F> un;
+          unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, cd + (uint32_t)r * row_bytes + (uint32_t)ub[p] * FT::BB,
+                                                         uu[p], un);
+#pragma unroll
+          for (int i = 0; i < T; ++i)
+            if ((mask >> i) & 1) v[i] = unit_combine<F>(un, act[p][i], v[i]);
+        }
+      }
+      group_reduce_multi<M, LR>(v, gl);
+      const int idx = gl / (LR / M);
+      if ((gl % (LR / M)) == 0) {
+        const int i = idx;
+        if (r < nr && ((mask >> i) & 1))
+          dpair[(int64_t)pair[i] * hidden + wr0 + (int64_t)tile * rows_per_tile + r] = v[0];
+      }
+    }
+    if (tile + 1 < ntiles) {
+      __syncthreads();
+      fd.commit(td, tid);
+      __syncthreads();
     }
   }
 }
@@ -440,12 +541,14 @@ moe_combine_kernel(const float* __restrict__ d, const float* __restrict__ w, int
 }
 
 // ---------------------------------------------------------------------------
-// launch planning
+// launch planning: lanes per row / units per lane as for the matvec (LR <= 64),
+// tiles of whole rows in 16 KiB, and about two workgroups per CU over all slots,
+// each owning an equal share of its expert's rows.
 // ---------------------------------------------------------------------------
-struct MoePlan { int lr, p, rows_per_tile; };
+constexpr int MOE_CPL = 4;
+struct MoePlan { int lr, p, rows_per_tile, rows_per_wg, wgs; };
 
-static MoePlan moe_plan(int units_per_row, int row_bytes, int tiles, int tslot) {
-  MoePlan pl;
+static bool moe_plan(int units_per_row, int row_bytes, int64_t rows, int slots, MoePlan& pl) {
   if (units_per_row <= 64) {
     pl.p = 1;
     pl.lr = 16;
@@ -455,24 +558,30 @@ static MoePlan moe_plan(int units_per_row, int row_bytes, int tiles, int tslot) 
     pl.p = 1;
     while (pl.p * 64 < units_per_row) pl.p *= 2;
   }
-  (void)tslot;
-  const int G = MOE_THREADS / pl.lr;
-  int rpt = (40 * 1024) / (tiles * row_bytes);
-  if (rpt > G) rpt = rpt / G * G;
-  if (rpt < 1) rpt = 1;
-  pl.rows_per_tile = rpt;
-  return pl;
+  if (pl.p > 8) return false;
+  pl.rows_per_tile = (MOE_CPL * 4096 - 15) / row_bytes;
+  if (pl.rows_per_tile < 1) return false;
+  int wpc = 2;   // FT_MOE_WPC overrides (tuning sweeps)
+  if (const char* ev = getenv("FT_MOE_WPC")) wpc = atoi(ev) > 0 ? atoi(ev) : 2;
+  const int64_t target = (int64_t)wpc * ftk_num_cus();
+  int64_t x = (target + slots - 1) / slots;
+  if (x < 1) x = 1;
+  int64_t rpw = (rows + x - 1) / x;
+  if (rpw < 1) rpw = 1;
+  pl.rows_per_wg = (int)rpw;
+  pl.wgs = (int)((rows + rpw - 1) / rpw);
+  return true;
 }
 
 template <int F, int A, int T, int LR, int P>
 static hipError_t launch_gate_up_t(const MoeArgs& a, const MoePlan& pl, int row_bytes, int units, int chunk0,
                                    int tchunk, hipStream_t st) {
   const int xrb = (int)(a.hidden / Act<A>::BLK * Act<A>::BB);
-  const size_t tile = ((size_t)pl.rows_per_tile * row_bytes + 32) & ~(size_t)15;
-  const dim3 grid((unsigned)((a.inter + pl.rows_per_tile - 1) / pl.rows_per_tile), (unsigned)(tchunk * a.topk));
-  hipLaunchKernelGGL((moe_gate_up_kernel<F, A, T, LR, P>), grid, dim3(MOE_THREADS), 2 * tile + 64, st,
+  const size_t lds = 2 * (size_t)(MOE_CPL * MOE_THREADS + 1) * 16 + (size_t)T * xrb;
+  const dim3 grid((unsigned)pl.wgs, (unsigned)(tchunk * a.topk));
+  hipLaunchKernelGGL((moe_gate_up_kernel<F, A, T, LR, P, MOE_CPL>), grid, dim3(MOE_THREADS), lds, st,
                      (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, row_bytes, units,
-                     pl.rows_per_tile, (const uint8_t*)a.xq + (size_t)chunk0 * xrb, xrb, tchunk,
+                     pl.rows_per_wg, pl.rows_per_tile, a.x + (size_t)chunk0 * a.hidden, a.hidden, tchunk,
                      a.ids + (size_t)chunk0 * a.topk, a.topk, a.h + (size_t)chunk0 * a.topk * a.inter,
                      a.g_tap ? a.g_tap + (size_t)chunk0 * a.topk * a.inter : nullptr,
                      a.u_tap ? a.u_tap + (size_t)chunk0 * a.topk * a.inter : nullptr);
@@ -483,13 +592,15 @@ template <int F, int A, int T, int LR, int P>
 static hipError_t launch_down_t(const MoeArgs& a, const MoePlan& pl, int row_bytes, int units, int chunk0,
                                 int tchunk, hipStream_t st) {
   const int hrb = (int)(a.inter / Act<A>::BLK * Act<A>::BB);
-  const size_t tile = ((size_t)pl.rows_per_tile * row_bytes + 32) & ~(size_t)15;
-  const dim3 grid((unsigned)((a.hidden + pl.rows_per_tile - 1) / pl.rows_per_tile), (unsigned)(tchunk * a.topk));
+  const size_t lds = (size_t)(MOE_CPL * MOE_THREADS + 1) * 16 + (size_t)T * hrb;
+  const dim3 grid((unsigned)pl.wgs, (unsigned)(tchunk * a.topk));
   // pair indices inside the chunk are relative to the chunk's first pair
-  hipLaunchKernelGGL((moe_down_kernel<F, A, T, LR, P>), grid, dim3(MOE_THREADS), tile + 64, st,
-                     (const uint8_t*)a.w_down, a.n_expert, a.hidden, row_bytes, units, pl.rows_per_tile,
-                     (const uint8_t*)a.hq + (size_t)chunk0 * a.topk * hrb, hrb, tchunk,
-                     a.ids + (size_t)chunk0 * a.topk, a.topk, a.dpair + (size_t)chunk0 * a.topk * a.hidden);
+  const size_t p0 = (size_t)chunk0 * a.topk;
+  hipLaunchKernelGGL((moe_down_kernel<F, A, T, LR, P, MOE_CPL>), grid, dim3(MOE_THREADS), lds, st,
+                     (const uint8_t*)a.w_down, a.n_expert, a.hidden, row_bytes, units, pl.rows_per_wg,
+                     pl.rows_per_tile, a.h + p0 * a.inter, a.in_hq ? (const uint8_t*)a.in_hq + p0 * hrb : nullptr,
+                     a.hq_tap ? (uint8_t*)a.hq_tap + p0 * hrb : nullptr, a.inter, tchunk, a.ids + p0, a.topk,
+                     a.dpair + p0 * a.hidden);
   return hipGetLastError();
 }
 
@@ -498,9 +609,8 @@ static hipError_t gate_up_lp(const MoeArgs& a, const MoePlan& pl, int rb, int un
                              hipStream_t st) {
 #define FT_GU(LRV, PV) \
   if (pl.lr == LRV && pl.p == PV) return launch_gate_up_t<F, A, T, LRV, PV>(a, pl, rb, units, c0, tc, st);
-  if constexpr (2 * (T >= 4 ? 1 : 4 / T) * T <= 16) { FT_GU(16, 1) }
-  if constexpr (2 * (T >= 4 ? 1 : 4 / T) * T <= 32) { FT_GU(32, 1) }
-  FT_GU(64, 1) FT_GU(64, 2) FT_GU(64, 4)
+  if constexpr (2 * T <= 16) { FT_GU(16, 1) }
+  FT_GU(32, 1) FT_GU(64, 1) FT_GU(64, 2) FT_GU(64, 4)
   if constexpr (T <= 2) { FT_GU(64, 8) }
 #undef FT_GU
   return hipErrorInvalidValue;
@@ -510,8 +620,7 @@ template <int F, int A, int T>
 static hipError_t down_lp(const MoeArgs& a, const MoePlan& pl, int rb, int units, int c0, int tc, hipStream_t st) {
 #define FT_DN(LRV, PV) \
   if (pl.lr == LRV && pl.p == PV) return launch_down_t<F, A, T, LRV, PV>(a, pl, rb, units, c0, tc, st);
-  if constexpr ((T >= 8 ? 1 : 8 / T) * T <= 16) { FT_DN(16, 1) }
-  FT_DN(32, 1) FT_DN(64, 1) FT_DN(64, 2) FT_DN(64, 4)
+  FT_DN(16, 1) FT_DN(32, 1) FT_DN(64, 1) FT_DN(64, 2) FT_DN(64, 4)
   if constexpr (T <= 2) { FT_DN(64, 8) }
 #undef FT_DN
   return hipErrorInvalidValue;
@@ -520,12 +629,14 @@ static hipError_t down_lp(const MoeArgs& a, const MoePlan& pl, int rb, int units
 template <int F, int A>
 static hipError_t moe_stage(const MoeArgs& a, bool gate, hipStream_t st) {
   const int64_t k = gate ? a.hidden : a.inter;
+  const int64_t rows = gate ? a.inter : a.hidden;
   const int row_bytes = (int)(k / Fmt<F>::BLK * Fmt<F>::BB);
   const int units = (int)units_in_row<F>(k);
   for (int64_t c0 = 0; c0 < a.t; c0 += 4) {
     const int tc = (int)(a.t - c0 < 4 ? a.t - c0 : 4);
     const int tslot = tc <= 1 ? 1 : tc <= 2 ? 2 : 4;
-    const MoePlan pl = moe_plan(units, row_bytes, gate ? 2 : 1, tslot);
+    MoePlan pl;
+    if (!moe_plan(units, row_bytes, rows, tc * a.topk, pl)) return hipErrorInvalidValue;
     hipError_t err = hipErrorInvalidValue;
     if (gate) {
       if (tslot == 1) err = gate_up_lp<F, A, 1>(a, pl, row_bytes, units, (int)c0, tc, st);
@@ -547,10 +658,15 @@ using namespace ftk;
 
 hipError_t ftk_launch_route(const float* logits, int64_t t, int64_t n_expert, int topk, int32_t* ids, float* w,
                             hipStream_t st) {
-  if (t == 0) return hipSuccess;
-  hipLaunchKernelGGL(route_kernel, dim3((unsigned)((t + 3) / 4)), dim3(256), 0, st, logits, t, (int)n_expert, topk,
-                     ids, w);
-  return hipGetLastError();
+  const dim3 grid((unsigned)((t + 3) / 4));
+#define FT_RT(ME)                                                                                          \
+  if (n_expert <= 64 * ME) {                                                                               \
+    hipLaunchKernelGGL(route_kernel<ME>, grid, dim3(256), 0, st, logits, t, (int)n_expert, topk, ids, w); \
+    return hipGetLastError();                                                                              \
+  }
+  FT_RT(1) FT_RT(2) FT_RT(4) FT_RT(8) FT_RT(16)
+#undef FT_RT
+  return hipErrorInvalidValue;
 }
 
 hipError_t ftk_launch_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert, int32_t* counts,

@@ -24,27 +24,7 @@ quant_q8_1_kernel(const float* __restrict__ x, int64_t total_blocks, int64_t nb,
   const int l = threadIdx.x & 31;
   if (gb >= total_blocks) return;  // uniform over the half-wave
   const int64_t r = gb / nb, b = gb % nb;
-  const float v = x[r * ldx + b * 32 + l];
-  float a = fabsf(v);
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 32));
-  uint32_t dh = f2h_bits(a / 127.0f);
-  const float d = h2f(dh);
-  int q = 0;
-  if (d != 0.0f) {
-    const float rq = roundf(v / d);
-    q = rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
-  }
-  int s = q;
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) s += __shfl_xor(s, m, 32);
-  uint8_t* ob = xq + gb * 36;
-  ob[4 + l] = (uint8_t)(int8_t)q;
-  if (l == 0) {
-    if (d == 0.0f) dh = 0;
-    const uint32_t sh = f2h_bits(d * (float)s);
-    *(uint32_t*)ob = dh | (sh << 16);
-  }
+  q8_1_block(x[r * ldx + b * 32 + l], l, xq + gb * 36);
 }
 
 // ---------------------------------------------------------------------------
@@ -61,28 +41,56 @@ quant_q8_k_kernel(const float* __restrict__ x, int64_t total_blocks, int64_t nb,
   float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = xp[i];
-  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  q8_k_block(v, lane, xq + gb * 292);
+}
+
+// ---------------------------------------------------------------------------
+// Q8_K codes -> exact FP8 halves for the block-scaled FP4 MFMA.
+// Each code x in [-127, 127] is x = 16*hi + lo with hi = x >> 4 in [-8, 7] and
+// lo = x & 15 in [0, 15]; both are exact OCP E4M3 values.  For every 256-element
+// superblock the output holds 32 chunks of 16 bytes, chunk c = 16p + 2j + h
+// (p = 0: lo, 1: hi; j = 32-element block; h = half): the FP8 codes of elements
+// 8h..8h+7 and 16+8h..16+8h+7 of block j, interleaved (a0 b0 a1 b1 ...) so that
+// byte i of the chunk multiplies nibble 16h + i of an MXFP4 block's qs bytes
+// (nibble n is byte n/2, low nibble first: element n/2 + 16*(n&1)).
+// ---------------------------------------------------------------------------
+// FP8 codes of the 4-bit values in each byte of v (tables: entries 0-7 and 8-15)
+__device__ __forceinline__ uint32_t fp8_lut(uint32_t v, uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
+  const uint32_t sel = v & 0x07070707u;
+  const uint32_t a = __builtin_amdgcn_perm(t1, t0, sel);
+  const uint32_t b = __builtin_amdgcn_perm(t3, t2, sel);
+  const uint32_t m = ((v >> 3) & 0x01010101u) * 0xFFu;   // 0xFF in bytes whose value is >= 8
+  return (a & ~m) | (b & m);
+}
+
+__global__ void __launch_bounds__(256)
+fp8_split_kernel(const uint8_t* __restrict__ xq, int64_t total_chunks, uint8_t* __restrict__ out) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total_chunks) return;
+  const int c = (int)(gid & 31);
+  const int64_t rs = gid >> 5;   // (row, superblock)
+  const int p = c >> 4, j = (c >> 1) & 7, h = c & 1;
+  const uint32_t* blk = (const uint32_t*)(xq + rs * 292 + 4 + 32 * j);
+  const uint32_t ra[2] = {blk[2 * h], blk[2 * h + 1]};           // elements 8h .. 8h+7
+  const uint32_t rb[2] = {blk[4 + 2 * h], blk[5 + 2 * h]};       // elements 16+8h .. 16+8h+7
+  // lo: x & 15 -> 0 1 2 3 4 5 6 7 | 8 .. 15;  hi: (x >> 4) as 4-bit two's complement
+  const uint32_t t0 = 0x44403800u, t1 = 0x4E4C4A48u;             // 0, 1, 2, 3 | 4, 5, 6, 7
+  const uint32_t t2 = p ? 0xCACCCED0u : 0x53525150u;             // hi: -8 -7 -6 -5 | lo: 8 9 10 11
+  const uint32_t t3 = p ? 0xB8C0C4C8u : 0x57565554u;             // hi: -4 -3 -2 -1 | lo: 12 .. 15
+  uint32_t ca[2], cb[2];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
-  const float d = a / 127.0f;
-  uint32_t packed = 0;
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int q = 0;
-    if (d != 0.0f) {
-      const float rq = roundf(v[i] / d);
-      q = rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
-    }
-    s += q;
-    packed |= ((uint32_t)(uint8_t)(int8_t)q) << (8 * i);
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t va = p ? (ra[i] >> 4) & 0x0F0F0F0Fu : ra[i] & 0x0F0F0F0Fu;
+    const uint32_t vb = p ? (rb[i] >> 4) & 0x0F0F0F0Fu : rb[i] & 0x0F0F0F0Fu;
+    ca[i] = fp8_lut(va, t0, t1, t2, t3);
+    cb[i] = fp8_lut(vb, t0, t1, t2, t3);
   }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);  // 16-element group: lanes 4g .. 4g+3
-  uint8_t* ob = xq + gb * 292;
-  *(uint32_t*)(ob + 4 + 4 * lane) = packed;
-  if ((lane & 3) == 0) *(int16_t*)(ob + 260 + 2 * (lane >> 2)) = (int16_t)s;
-  if (lane == 0) *(float*)ob = d;
+  u32x4 o;
+  o.x = __builtin_amdgcn_perm(cb[0], ca[0], 0x05010400u);
+  o.y = __builtin_amdgcn_perm(cb[0], ca[0], 0x07030602u);
+  o.z = __builtin_amdgcn_perm(cb[1], ca[1], 0x05010400u);
+  o.w = __builtin_amdgcn_perm(cb[1], ca[1], 0x07030602u);
+  *(u32x4*)(out + gid * 16) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -213,6 +221,14 @@ static hipError_t launch_dequant_t(const void* blocks, int64_t rows, int64_t k, 
   if (groups == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel<F>, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st,
                      (const uint8_t*)blocks, rows, k, out);
+  return hipGetLastError();
+}
+
+hipError_t ftk_launch_fp8_split(const void* xq, int64_t rows, int64_t k, void* out, hipStream_t st) {
+  const int64_t chunks = rows * (k / 256) * 32;
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_split_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st,
+                     (const uint8_t*)xq, chunks, (uint8_t*)out);
   return hipGetLastError();
 }
 

@@ -64,7 +64,8 @@ EXPORTS = {
     "ft_scratch_reserve": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t]),
     "ft_moe_scratch_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
-    "ft_grouped_scratch_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+    "ft_grouped_scratch_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                    ctypes.c_int, ctypes.c_int]),
     "ft_shutdown": (None, []),
 }
 

@@ -198,7 +198,7 @@ ft_status ft_scratch_reserve(ft_stream_t stream, size_t bytes);
 /* Scratch bytes ft_moe_q_vec / ft_grouped_gemm_q need for a problem size. */
 size_t ft_moe_scratch_bytes(ft_type w, ft_type act, int64_t n_expert, int64_t hidden,
                             int64_t inter, int64_t t, int topk);
-size_t ft_grouped_scratch_bytes(int64_t n_expert, int64_t t, int topk);
+size_t ft_grouped_scratch_bytes(ft_type w, int64_t n_expert, int64_t k, int64_t t, int topk, int x_per_pair);
 
 /* Release every scratch buffer.  No call may be in flight. */
 void ft_shutdown(void);
