@@ -51,7 +51,10 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-constexpr int GM_WAVES = 4;
+#ifndef GM_WAVES_OPT
+#define GM_WAVES_OPT 4
+#endif
+constexpr int GM_WAVES = GM_WAVES_OPT;
 constexpr int GM_THREADS = 64 * GM_WAVES;
 // 16-row MFMA groups per wave (they share every A-operand read); Q6_K's two
 // MFMAs and two scales per group need the registers of a second group
@@ -233,19 +236,45 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
     const int gm = min(PT * 16, p1 - g0);
     const int npt = (gm + 15) >> 4;
 
-    // activation staging: item it = tid + GM_THREADS*i is chunk su = it % CPP of pair
-    // slot it / CPP of the group (16 codes, or an FP8 chunk of the MXFP4 path)
+    // activation staging: item it = tid + GM_THREADS*i.  Codes: chunk su = it % 16 (16
+    // codes) of pair slot it / 16.  MXFP4: it = 512m + 64r + 16qa + spl is the 16-byte
+    // slot of lane (qa, spl) in region r of tile m, so a wave writes 1 KB contiguously.
+    auto fp4_item = [&](int it, int& m, int& r, int& qa, int& spl) {
+      m = it >> 9;
+      r = (it >> 6) & 7;
+      qa = (it >> 4) & 3;
+      spl = it & 15;
+    };
     const uint8_t* xr[NAI];
     const uint8_t* xr8[NAI];
 #pragma unroll
     for (int i = 0; i < NAI; ++i) {
-      const int pi = (tid + GM_THREADS * i) / CPP;
+      int pi = (tid + GM_THREADS * i) / CPP;
+      if constexpr (FP4) {
+        int m, r, qa, spl;
+        fp4_item(tid + GM_THREADS * i, m, r, qa, spl);
+        pi = 16 * m + spl;
+      }
       xr[i] = nullptr;
       xr8[i] = nullptr;
       if (pi < gm) {
         const int64_t row = x_per_pair ? pairs[g0 + pi] : pairs[g0 + pi] / topk;
         xr[i] = xq + row * xrow_bytes;
         if constexpr (FP4) xr8[i] = xf8 + row * (int64_t)nsb * 512;
+      }
+    }
+    // chunk of the item: codes: su; MXFP4: the FP8 chunk c = 16p + 2j + h of region r
+    // (r = 4*st + 2*pp + bh) and lane quarter qa: j = 4st + 2bh + (qa>>1), h = qa & 1
+    int sui[NAI];
+#pragma unroll
+    for (int i = 0; i < NAI; ++i) {
+      if constexpr (FP4) {
+        int m, r, qa, spl;
+        fp4_item(tid + GM_THREADS * i, m, r, qa, spl);
+        const int st = r >> 2, pp = (r >> 1) & 1, bh = r & 1;
+        sui[i] = 16 * pp + 2 * (4 * st + 2 * bh + (qa >> 1)) + (qa & 1);
+      } else {
+        sui[i] = tid % CPP;
       }
     }
     const int su = tid % CPP;
@@ -260,12 +289,12 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
         pdx[i] = 0.0f;
         if (xr[i]) {
           if constexpr (FP4) {
-            pa[i] = *(const u32x4*)(xr8[i] + (int64_t)sb * 512 + 16 * su);
+            pa[i] = *(const u32x4*)(xr8[i] + (int64_t)sb * 512 + 16 * sui[i]);
           } else {
             const uint32_t* src = (const uint32_t*)(xr[i] + (int64_t)sb * 292 + 4 + 16 * su);
             pa[i] = (u32x4){src[0], src[1], src[2], src[3]};
           }
-          if (su == 0) pdx[i] = *(const float*)(xr[i] + (int64_t)sb * 292);
+          if (sui[i] == 0) pdx[i] = *(const float*)(xr[i] + (int64_t)sb * 292);
         }
       }
 #pragma unroll
@@ -278,7 +307,8 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
           const int64_t off = row * row_bytes + (int64_t)sb * SB::BYTES;
           const int sh = SB::ALIGNED ? 0 : (int)((uintptr_t)(src + off) & 15);
           const int nch = (sh + SB::BYTES + 15) >> 4;
-          if (ch < nch) pw[i] = __builtin_nontemporal_load((const u32x4*)(src + (off - sh)) + ch);
+          // plain loads: the line that straddles two superblocks is read again by the next step
+          if (ch < nch) pw[i] = *((const u32x4*)(src + (off - sh)) + ch);
         }
       }
     };
@@ -287,13 +317,11 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
       for (int i = 0; i < NAI; ++i) {
         const int it = tid + GM_THREADS * i;
         if (FP4 && it < PT * 16 * CPP) {   // uniform per wave
-          // chunk su = 16p + 2j + h -> A operand of k-step j/4, part p: lane quarter
-          // 2(j&1) + h, byte half (j&2)/2
-          const int pi = it / CPP, m = pi >> 4, spl = pi & 15;
-          const int pp = su >> 4, j = (su >> 1) & 7, hh = su & 1;
-          const int st = j >> 2, jj = j & 3, qa = 2 * (jj & 1) + hh, bh = jj >> 1;
-          *(u32x4*)(B + LY::CODES + m * LY::TSTR + (st * 2 + pp) * 2048 + bh * 1024 + (qa * 16 + spl) * 16) = pa[i];
-          if (su == 0) ((float*)(B + LY::DX))[m * 16 + spl] = pdx[i];
+          // region r = (2st + pp, bh) of tile m: [k-step st][part pp][byte half bh][lane]
+          int m, r, qa, spl;
+          fp4_item(it, m, r, qa, spl);
+          *(u32x4*)(B + LY::CODES + m * LY::TSTR + r * 1024 + (qa * 16 + spl) * 16) = pa[i];
+          if (sui[i] == 0) ((float*)(B + LY::DX))[m * 16 + spl] = pdx[i];
         } else if (!FP4 && it < PT * 16 * CPP) {   // uniform per wave
           const int pi = it >> 4, m = pi >> 4, spl = pi & 15;
           const int j = su >> 1, qa = 2 * (su & 1);
