@@ -27,15 +27,19 @@ TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20         # calibration copy for the FETCH_SIZE / WRITE_SIZE counters
 
 
+# sources the headline matvec kernel is compiled from
+_HEADLINE_SRC = ("ft_mmvq.hip", "ft_device.h", "ft_internal.h")
+
+
 def _src_hash():
-    """Hash of the kernel sources: traffic figures are void once the kernels change."""
+    """Hash of the headline kernel's sources: traffic figures are void once it changes."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_matvec_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in _HEADLINE_SRC:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "ft.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -61,6 +65,7 @@ def _args():
     ap.add_argument("--copies", type=int, default=0, help="weight copies per matrix (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=str, default="", help="comma list overriding the token counts")
+    ap.add_argument("--route", type=int, default=0, help="MoE route: 0 auto, 1 direct, 2 sorted tiles")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of `--workload counters` into "
                          "profiles/traffic.json and exit")
@@ -329,13 +334,14 @@ def bench_moe(args, np, torch, ft, synth):
             for i in range(G):
                 wgb, wub, wdb = banks[i % layers]
                 ft.moe_route(logits[i], topk, ids=ids[i], w=w[i])
-                ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, ids[i], w[i], out=y)
+                ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, ids[i], w[i], out=y, route=args.route)
 
         gs = _graph(torch, steps)
         sec = _time_graph(torch, gs, max(1, args.steps // G)) / G
         idh = ids.cpu().numpy()
         u = float(np.mean([len(np.unique(idh[i])) for i in range(G)]))
-        route = "sorted tiles" if (fmt, act) == ("MXFP4", "Q8_K") and t > 4 else "direct"
+        tiles_ok = (fmt, act) == ("MXFP4", "Q8_K")
+        route = "sorted tiles" if tiles_ok and (args.route == 2 or (args.route == 0 and t > 3)) else "direct"
         results.append({"tokens": t, "route": route, "tok_per_s": round(t / sec, 1), "layer_us": round(sec * 1e6, 2),
                         "unique_experts": round(u, 2),
                         "weight_GBps": round(u * per_expert / sec / 1e9, 1),

@@ -126,7 +126,7 @@ def test_moe_q4k_layer(t):
 @pytest.mark.parametrize("t", [1, 2, 3, 4])
 def test_moe_mxfp4_direct(t):
     log(f"moe mxfp4 t={t}")
-    _run_stages("mxfp4", t, route=0)
+    _run_stages("mxfp4", t, route=1)
 
 
 @pytest.mark.parametrize("t", [1, 3, 5, 9, 40])
