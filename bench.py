@@ -341,7 +341,7 @@ def bench_moe(args, np, torch, ft, synth):
         idh = ids.cpu().numpy()
         u = float(np.mean([len(np.unique(idh[i])) for i in range(G)]))
         tiles_ok = (fmt, act) == ("MXFP4", "Q8_K")
-        route = "sorted tiles" if tiles_ok and (args.route == 2 or (args.route == 0 and t > 3)) else "direct"
+        route = "sorted tiles" if tiles_ok and (args.route == 2 or (args.route == 0 and t > 8)) else "direct"
         results.append({"tokens": t, "route": route, "tok_per_s": round(t / sec, 1), "layer_us": round(sec * 1e6, 2),
                         "unique_experts": round(u, 2),
                         "weight_GBps": round(u * per_expert / sec / 1e9, 1),

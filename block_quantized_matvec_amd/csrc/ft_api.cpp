@@ -252,9 +252,10 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
   // sorted-tile route: token->expert sort + grouped MFMA GEMMs (MXFP4 x Q8_K)
   const bool tile_ok = moe_tile_pair(w, act);
   if (o.route == 2 && !tile_ok) return FT_ERR_UNSUPPORTED;
-  // default threshold: the MXFP4 tile route (FP4 MFMA) beats the direct route from
-  // 4 tokens on MI355X (measured: 190 vs 214 us per layer at t = 4)
-  const int64_t dmax = o.direct_max_t > 0 ? o.direct_max_t : 3;
+  // default threshold: up to 8 tokens (one launch chunk of the direct MXFP4 kernels)
+  // the direct route wins on MI355X (measured per layer: t = 8: 284 vs 290 us; t = 9:
+  // 317 vs 298 us for the sorted tiles)
+  const int64_t dmax = o.direct_max_t > 0 ? o.direct_max_t : 8;
   const bool tiles = o.route == 2 || (o.route == 0 && tile_ok && t > dmax);
   if ((o.tap_g && !aligned16(o.tap_g)) || (o.tap_u && !aligned16(o.tap_u)) || (o.tap_h && !aligned16(o.tap_h)) ||
       (o.tap_hq && !aligned16(o.tap_hq)) || (o.tap_down && !aligned16(o.tap_down)) ||

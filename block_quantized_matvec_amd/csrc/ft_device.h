@@ -487,6 +487,112 @@ __device__ __forceinline__ float xchg(float v) {
   return __int_as_float(r);
 }
 
+// Block quantizers over several elements per lane, bit-identical to q8_1_block /
+// q8_k_block (same amax, scale, codes and sums; max and integer sums do not
+// depend on the order of reduction).
+// Q8_1: 4 aligned lanes per 32-element block, lane l4 = 0..3 holds elements
+// 8*l4 .. 8*l4+7.  The 4 lanes call it together; ob: the 36-byte block.
+__device__ __forceinline__ void q8_1_part(const float (&v)[8], int l4, uint8_t* ob) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
+  a = fmaxf(a, xchg<1>(a));
+  a = fmaxf(a, xchg<2>(a));
+  uint32_t dh = f2h_bits(a / 127.0f);
+  const float d = h2f(dh);
+  uint32_t w[2] = {0u, 0u};
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = q8_code(v[j], d);
+    s += q;
+    w[j >> 2] |= ((uint32_t)(uint8_t)(int8_t)q) << (8 * (j & 3));
+  }
+  s += __float_as_int(xchg<1>(__int_as_float(s)));
+  s += __float_as_int(xchg<2>(__int_as_float(s)));
+  uint32_t* o = (uint32_t*)(ob + 4 + 8 * l4);
+  o[0] = w[0];
+  o[1] = w[1];
+  if (l4 == 0) {
+    if (d == 0.0f) dh = 0;
+    const uint32_t sh = f2h_bits(d * (float)s);
+    *(uint32_t*)ob = dh | (sh << 16);
+  }
+}
+
+// Q8_K: 16 aligned lanes (one DPP row) per 256-element block, lane l16 holds
+// elements 16*l16 .. 16*l16+15, i.e. exactly one 16-element bsum group.  Returns
+// the lane's 16 codes (w), their sum (s) and the block scale (d).
+__device__ __forceinline__ void q8_k_codes(const float (&v)[16], uint32_t (&w)[4], int& s, float& d) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
+  a = fmaxf(a, xchg<1>(a));
+  a = fmaxf(a, xchg<2>(a));
+  a = fmaxf(a, xchg<4>(a));   // row half-mirror: quad 0 <-> quad 1 of each 8
+  a = fmaxf(a, xchg<8>(a));   // row mirror: half 0 <-> half 1
+  d = a / 127.0f;
+  s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int q = q8_code(v[j], d);
+    s += q;
+    w[j >> 2] |= ((uint32_t)(uint8_t)(int8_t)q) << (8 * (j & 3));
+  }
+}
+// ... and stores the lane's part of the 292-byte block at ob
+__device__ __forceinline__ void q8_k_store(const uint32_t (&w)[4], int s, float d, int l16, uint8_t* ob) {
+  uint32_t* o = (uint32_t*)(ob + 4 + 16 * l16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = w[i];
+  *(int16_t*)(ob + 260 + 2 * l16) = (int16_t)s;
+  if (l16 == 0) *(float*)ob = d;
+}
+__device__ __forceinline__ void q8_k_part(const float (&v)[16], int l16, uint8_t* ob) {
+  uint32_t w[4];
+  int s;
+  float d;
+  q8_k_codes(v, w, s, d);
+  q8_k_store(w, s, d, l16, ob);
+}
+
+// ---------------------------------------------------------------------------
+// routed-MoE helpers (direct route)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int clamp_id(int e, int64_t n_expert) {
+  return e < 0 ? 0 : (e >= n_expert ? (int)n_expert - 1 : e);
+}
+
+// Which tokens of the chunk picked expert e = ids[slot]: bit i of mask, the slots
+// of token i naming e in bits 8i.. of smask.  Returns false if an earlier slot
+// already names e (that workgroup owns the expert).  Lane p reads pair p (one load
+// per lane, t_real * topk <= 64); every lane of the wave must call it.
+__device__ __forceinline__ bool expert_tokens(const int32_t* __restrict__ ids, int slot, int t_real, int topk,
+                                              int64_t n_expert, int& e, uint32_t& mask, uint64_t& smask) {
+  const int p = threadIdx.x & 63, npairs = t_real * topk;
+  const int ep = p < npairs ? clamp_id(ids[p], n_expert) : -1;
+  e = __builtin_amdgcn_readlane(ep, slot);
+  const uint64_t same = __ballot(p < npairs && ep == e);
+  if (same & ((1ull << slot) - 1)) return false;
+  mask = 0;
+  smask = 0;
+  for (int i = 0; i < t_real; ++i) {
+    const uint64_t b = (same >> (i * topk)) & ((1ull << topk) - 1);
+    smask |= b << (8 * i);
+    if (b) mask |= 1u << i;
+  }
+  return true;
+}
+
+// index of the j-th set bit of m
+__device__ __forceinline__ int nth_bit(uint32_t m, int j) {
+  for (int s = 0; s < j; ++s) m &= m - 1;
+  return __ffs(m) - 1;
+}
+
+
 // Reduce M values per lane over the lanes of an aligned group of L lanes
 // (L a power of two <= 64, M <= L).  Afterwards value index i's group total sits
 // in v[0] of lanes (i * L/M) .. (i * L/M + L/M - 1) of the group: each exchange

@@ -69,6 +69,10 @@ struct MoeArgs {
 };
 hipError_t ftk_launch_moe_gate_up(const MoeArgs& a, hipStream_t st);
 hipError_t ftk_launch_moe_down(const MoeArgs& a, hipStream_t st);
+// MXFP4 x Q8_K direct-route stages on the FP4 MFMA (hidden, inter multiples of 256)
+hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st);
+hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st);
+// y from the per-pair rows in dpair, slot order
 hipError_t ftk_launch_moe_combine(const MoeArgs& a, hipStream_t st);
 
 // grouped GEMM over expert-sorted pairs.  With W2 set (MXFP4 only) W and W2 are

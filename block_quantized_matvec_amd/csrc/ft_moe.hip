@@ -1,20 +1,25 @@
-// ft_moe.hip -- routed-MoE vector path: router, token->expert sort, and the
-// direct-route expert kernels (gate/up + SwiGLU, down, weighted combine).
+// ft_moe.hip -- routed-MoE vector path: router, token->expert sort, the slot-order
+// combine, and the direct-route dot4 expert kernels (gate/up + SwiGLU, down) used
+// for Q4_K x Q8_1 (MXFP4 x Q8_K has its own, on the FP4 MFMA: ft_moe_fp4.hip).
 //
-// ds4 PR #656 "Add ROCm MXFP4 routed expert kernels" (Summary): resident
-// MXFP4 x Q8_K routed gate/up and down kernels with SwiGLU between them,
-// coalesced weight reads with register unpack, and tiny batches (2-4 tokens)
-// sent through direct kernels instead of partly filled expert-sorted tiles.
-// FreeToken PR #136 (Summary): the routed MoE vector kernel with two-expert
-// routing.  MI355X design:
-//  * one workgroup per (distinct selected expert, tile of output rows); the
-//    expert's rows are streamed into LDS once with 16-byte global_load_lds and
-//    applied to every token that selected it (duplicates across tokens are read
-//    once; the first slot naming an expert owns it);
+// ds4 PR #656 "Add ROCm MXFP4 routed expert kernels" (Summary): routed gate/up and
+// down kernels with SwiGLU between them, coalesced weight reads with register
+// unpack, and tiny batches sent through direct kernels instead of partly filled
+// expert-sorted tiles.  FreeToken PR #136 (Summary): the routed MoE vector kernel.
+// MI355X design:
+//  * one workgroup per (distinct selected expert, share of its output rows); the
+//    share is streamed through LDS in tiles of whole rows with 16-byte loads (the
+//    next tile into VGPRs while the current one is computed) and applied to every
+//    token that selected the expert (duplicates across tokens are read once; the
+//    first slot naming an expert owns it);
+//  * the chunk's expert ids are read once, one pair per lane, and the ownership
+//    and token masks come from ballots;
+//  * each workgroup quantizes the activation rows it needs itself, with all loads
+//    of a batch in flight before any block is reduced;
 //  * activation codes of all tokens sit in VGPRs; a wave-uniform token mask skips
 //    tokens that did not pick the expert;
-//  * gate and up share the activations; SwiGLU is applied right after the
-//    64-lane reduction, before h leaves registers.
+//  * gate and up share the activations; SwiGLU is applied right after the 64-lane
+//    reduction, before h leaves registers.
 #include <stdlib.h>
 
 #include "ft_device.h"
@@ -219,43 +224,12 @@ sort_kernel(const int32_t* __restrict__ ids, int npairs, int n_expert, int chunk
 // ---------------------------------------------------------------------------
 // helpers shared by the expert kernels
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int clamp_id(int e, int64_t n_expert) {
-  return e < 0 ? 0 : (e >= n_expert ? (int)n_expert - 1 : e);
-}
-
-// Decide which tokens picked expert e (and at which slot); returns false if an
-// earlier slot already names e (that workgroup owns the expert).
-template <int T>
-__device__ __forceinline__ bool expert_tokens(const int32_t* __restrict__ ids, int slot, int t_real, int topk,
-                                              int64_t n_expert, int& e, uint32_t& mask, int (&pair)[T]) {
-  e = clamp_id(ids[slot], n_expert);
-  for (int s2 = 0; s2 < slot; ++s2)
-    if (clamp_id(ids[s2], n_expert) == e) return false;
-  mask = 0;
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    pair[i] = 0;
-    if (i < t_real) {
-      for (int k = 0; k < topk; ++k)
-        if (clamp_id(ids[i * topk + k], n_expert) == e) {
-          mask |= 1u << i;
-          pair[i] = i * topk + k;
-          break;
-        }
-    }
-  }
-  return true;
-}
-
 // ---------------------------------------------------------------------------
-// Direct-route expert kernels.  grid: x = workgroups per slot, y = the (token,
-// slot) pairs of this token chunk; the workgroup of the first slot naming an
-// expert owns it (later duplicates exit).  Each workgroup takes a contiguous share
-// of the expert's rows and walks it in tiles of whole rows: tile i+1 is fetched
-// into VGPRs with 16-byte loads while tile i is computed from LDS (as the matvec
-// does).  The activation rows the expert needs are quantized by the workgroup
-// itself into LDS first (x for gate/up; the expert's h rows for down), with the
-// same per-block arithmetic as ft_quantize_act.
+// Direct-route expert kernels.  Each workgroup streams whole weight rows through
+// LDS in tiles: tile i+1 is fetched into VGPRs with 16-byte loads while tile i is
+// computed from LDS (as the matvec does).  The activation rows a workgroup needs
+// are quantized by the workgroup itself into LDS first (x for gate/up, the
+// selected experts' h rows for down), with the arithmetic of ft_quantize_act.
 // ---------------------------------------------------------------------------
 template <int CPL>
 struct TileFetch {
@@ -282,26 +256,44 @@ struct TileFetch {
   }
 };
 
-// quantize `rows` fp32 rows of length k (row i at src + i*lds_src) into act
-// blocks at dst (row i at dst + i*rowb) with the whole workgroup
-template <int A>
-__device__ __forceinline__ void quantize_rows(const float* __restrict__ src, int64_t lds_src, int rows, int64_t k,
-                                              uint8_t* dst, int rowb, int tid) {
-  if constexpr (A == FT_Q8_1) {
-    const int nb = (int)(k / 32), l = tid & 31;
-    for (int gb = tid >> 5; gb < rows * nb; gb += MOE_THREADS / 32) {   // uniform per half-wave
-      const int r = gb / nb, b = gb % nb;
-      q8_1_block(src[r * lds_src + b * 32 + l], l, dst + r * rowb + b * 36);
-    }
-  } else {
-    const int nb = (int)(k / 256), lane = tid & 63;
-    for (int gb = tid >> 6; gb < rows * nb; gb += MOE_THREADS / 64) {   // uniform per wave
-      const int r = gb / nb, b = gb % nb;
-      const float* xp = src + r * lds_src + b * 256 + 4 * lane;
-      float v[4];
+// Quantize `rows` fp32 rows of k elements with the whole workgroup: src(r) is row
+// r's data (16-byte aligned), dst(r) its first activation block.  A thread takes 8
+// (Q8_1) or 16 (Q8_K) consecutive elements, so a block is 4 or 16 aligned lanes;
+// the loads of up to 32 elements per thread are all issued before any block is
+// reduced, so a workgroup pays one memory latency per 8192 elements.
+template <int A, typename S, typename D>
+__device__ __forceinline__ void quantize_rows(int rows, int k, S src, D dst, int tid) {
+  constexpr int EPT = A == FT_Q8_1 ? 8 : 16;
+  constexpr int BATCH = 32 / EPT;
+  const int per_row = k / EPT;
+  const int total = rows * per_row;
+  for (int base = 0; base < total; base += MOE_THREADS * BATCH) {
+    float v[BATCH][EPT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = xp[i];
-      q8_k_block(v, lane, dst + r * rowb + b * 292);
+    for (int b = 0; b < BATCH; ++b) {
+      const int idx = base + b * MOE_THREADS + tid;
+      if (idx < total) {
+        const int r = idx / per_row, c = (idx - r * per_row) * EPT;
+        const float4* p = (const float4*)(src(r) + c);
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q) {
+          const float4 f = p[q];
+          v[b][4 * q] = f.x;
+          v[b][4 * q + 1] = f.y;
+          v[b][4 * q + 2] = f.z;
+          v[b][4 * q + 3] = f.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int idx = base + b * MOE_THREADS + tid;
+      if (idx < total) {   // the same for all lanes of a block: k is a whole number of blocks
+        const int r = idx / per_row, c = (idx - r * per_row) * EPT;
+        uint8_t* ob = dst(r) + (c / Act<A>::BLK) * Act<A>::BB;
+        if constexpr (A == FT_Q8_1) q8_1_part(v[b], tid & 3, ob);
+        else q8_k_part(v[b], tid & 15, ob);
+      }
     }
   }
 }
@@ -320,9 +312,10 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ w
   extern __shared__ u32x4 smem4[];
   const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
 
-  int e, pair[T];
+  int e;
   uint32_t mask;
-  if (!expert_tokens<T>(ids, blockIdx.y, t_real, topk, n_expert, e, mask, pair)) return;
+  uint64_t smask;
+  if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
   const int64_t wr0 = (int64_t)blockIdx.x * rows_per_wg;
   if (wr0 >= inter) return;
   const int wrows = (int)min<int64_t>(rows_per_wg, inter - wr0);
@@ -340,7 +333,8 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ w
   uint32_t sg = fg.fetch(gbase, (int64_t)tile_rows(0) * row_bytes, tid);
   uint32_t su = fu.fetch(ubase, (int64_t)tile_rows(0) * row_bytes, tid);
 
-  quantize_rows<A>(x, hidden, t_real, hidden, xql, xrb, tid);
+  quantize_rows<A>(
+      t_real, (int)hidden, [&](int r) { return x + (int64_t)r * hidden; }, [&](int r) { return xql + r * xrb; }, tid);
   __syncthreads();
   ActUnit<F> act[P][T];
   int ub[P], uu[P];
@@ -399,11 +393,16 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ w
       if (leader && idx < T) {
         const int i = idx;
         if (r < nr && ((mask >> i) & 1)) {
-          const float g = v[0], u = other;
-          const int64_t o = (int64_t)pair[i] * inter + wr0 + (int64_t)tile * rows_per_tile + r;
-          h[o] = g / (1.0f + expf(-g)) * u;
-          if (gtap) gtap[o] = g;
-          if (utap) utap[o] = u;
+          const float g = v[0], u = other, hv = g / (1.0f + expf(-g)) * u;
+          const int64_t row = wr0 + (int64_t)tile * rows_per_tile + r;
+          for (int k = 0; k < topk; ++k) {   // every slot of token i that names e
+            if ((smask >> (8 * i + k)) & 1) {
+              const int64_t o = (int64_t)(i * topk + k) * inter + row;
+              h[o] = hv;
+              if (gtap) gtap[o] = g;
+              if (utap) utap[o] = u;
+            }
+          }
         }
       }
     }
@@ -416,9 +415,10 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ w
   }
 }
 
-// down projection: dpair[pair][r] = W_down[e][r] . hhat(pair) for this workgroup's
-// share of rows; hhat of the expert's pairs is quantized here (or read from
-// in_hq), and the first workgroup of the slot writes it to hq_tap.
+// Down projection: d[pair][r] = W_down[e][r] . hhat(pair) for this workgroup's
+// share of rows of its expert; hhat of the expert's tokens is quantized here (or
+// read from in_hq), and the first workgroup of the slot writes it to hq_tap.
+// Slots that repeat an expert within a token share the first slot's h and d.
 template <int F, int A, int T, int LR, int P, int CPL>
 __global__ void __launch_bounds__(MOE_THREADS)
 moe_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int row_bytes,
@@ -432,9 +432,10 @@ moe_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden
   extern __shared__ u32x4 smem4[];
   const int tid = threadIdx.x, grp = tid / LR, gl = tid % LR;
 
-  int e, pair[T];
+  int e;
   uint32_t mask;
-  if (!expert_tokens<T>(ids, blockIdx.y, t_real, topk, n_expert, e, mask, pair)) return;
+  uint64_t smask;
+  if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
   const int64_t wr0 = (int64_t)blockIdx.x * rows_per_wg;
   if (wr0 >= hidden) return;
   const int wrows = (int)min<int64_t>(rows_per_wg, hidden - wr0);
@@ -449,25 +450,27 @@ moe_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden
   auto tile_rows = [&](int tile) { return min(rows_per_tile, wrows - tile * rows_per_tile); };
   uint32_t sd = fd.fetch(dbase, (int64_t)tile_rows(0) * row_bytes, tid);
 
-  // hhat of this expert's pairs (token slot i -> LDS row i)
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    if ((mask >> i) & 1) {
-      uint8_t* dst = hql + i * hrb;
-      if (in_hq) {
-        const uint8_t* srcq = in_hq + (int64_t)pair[i] * hrb;
-        for (int b = tid; b < hrb; b += MOE_THREADS) dst[b] = srcq[b];
-      } else {
-        quantize_rows<A>(h + (int64_t)pair[i] * inter, inter, 1, inter, dst, hrb, tid);
-      }
+  // hhat of the expert's tokens (token i -> LDS row i), from the first slot of
+  // token i that names e
+  const int ntok = __popc(mask);
+  auto first_pair = [&](int i) { return i * topk + __ffs((unsigned)(smask >> (8 * i)) & 0xFFu) - 1; };
+  if (in_hq) {
+    for (int c = tid; c < ntok * (hrb >> 2); c += MOE_THREADS) {
+      const int j = c / (hrb >> 2), w = c - j * (hrb >> 2), i = nth_bit(mask, j);
+      ((uint32_t*)(hql + i * hrb))[w] = ((const uint32_t*)(in_hq + (int64_t)first_pair(i) * hrb))[w];
     }
+  } else {
+    quantize_rows<A>(
+        ntok, (int)inter, [&](int j) { return h + (int64_t)first_pair(nth_bit(mask, j)) * inter; },
+        [&](int j) { return hql + nth_bit(mask, j) * hrb; }, tid);
   }
   __syncthreads();
   if (hq_tap && blockIdx.x == 0) {
-#pragma unroll
     for (int i = 0; i < T; ++i)
-      if ((mask >> i) & 1)
-        for (int b = tid; b < hrb; b += MOE_THREADS) hq_tap[(int64_t)pair[i] * hrb + b] = hql[i * hrb + b];
+      for (int k = 0; k < topk; ++k)
+        if ((smask >> (8 * i + k)) & 1)
+          for (int c = tid; c < (hrb >> 2); c += MOE_THREADS)
+            ((uint32_t*)(hq_tap + (int64_t)(i * topk + k) * hrb))[c] = ((const uint32_t*)(hql + i * hrb))[c];
   }
 
   ActUnit<F> act[P][T];
@@ -513,11 +516,11 @@ moe_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden
         }
       }
       group_reduce_multi<M, LR>(v, gl);
-      const int idx = gl / (LR / M);
-      if ((gl % (LR / M)) == 0) {
-        const int i = idx;
-        if (r < nr && ((mask >> i) & 1))
-          dpair[(int64_t)pair[i] * hidden + wr0 + (int64_t)tile * rows_per_tile + r] = v[0];
+      const int i = gl / (LR / M);
+      if ((gl % (LR / M)) == 0 && r < nr && ((mask >> i) & 1)) {
+        const int64_t row = wr0 + (int64_t)tile * rows_per_tile + r;
+        for (int k = 0; k < topk; ++k)
+          if ((smask >> (8 * i + k)) & 1) dpair[(int64_t)(i * topk + k) * hidden + row] = v[0];
       }
     }
     if (tile + 1 < ntiles) {
@@ -599,8 +602,8 @@ static hipError_t launch_down_t(const MoeArgs& a, const MoePlan& pl, int row_byt
   hipLaunchKernelGGL((moe_down_kernel<F, A, T, LR, P, MOE_CPL>), grid, dim3(MOE_THREADS), lds, st,
                      (const uint8_t*)a.w_down, a.n_expert, a.hidden, row_bytes, units, pl.rows_per_wg,
                      pl.rows_per_tile, a.h + p0 * a.inter, a.in_hq ? (const uint8_t*)a.in_hq + p0 * hrb : nullptr,
-                     a.hq_tap ? (uint8_t*)a.hq_tap + p0 * hrb : nullptr, a.inter, tchunk, a.ids + p0, a.topk,
-                     a.dpair + p0 * a.hidden);
+                     a.hq_tap ? (uint8_t*)a.hq_tap + p0 * hrb : nullptr, a.inter, tchunk, a.ids + p0,
+                     a.topk, a.dpair + p0 * a.hidden);
   return hipGetLastError();
 }
 
@@ -626,26 +629,34 @@ static hipError_t down_lp(const MoeArgs& a, const MoePlan& pl, int rb, int units
   return hipErrorInvalidValue;
 }
 
+// tokens are taken in chunks of up to 4 (fewer when the stage's LDS would not fit
+// in 64 KiB)
 template <int F, int A>
 static hipError_t moe_stage(const MoeArgs& a, bool gate, hipStream_t st) {
   const int64_t k = gate ? a.hidden : a.inter;
   const int64_t rows = gate ? a.inter : a.hidden;
   const int row_bytes = (int)(k / Fmt<F>::BLK * Fmt<F>::BB);
   const int units = (int)units_in_row<F>(k);
-  for (int64_t c0 = 0; c0 < a.t; c0 += 4) {
-    const int tc = (int)(a.t - c0 < 4 ? a.t - c0 : 4);
+  const size_t arb = (size_t)(k / Act<A>::BLK * Act<A>::BB);   // quantized activation row
+  const size_t tile = (size_t)(MOE_CPL * MOE_THREADS + 1) * 16 * (gate ? 2 : 1);
+  int cs = 4;
+  while (cs > 1 && tile + (size_t)cs * arb > 65536) cs /= 2;
+  if (tile + (size_t)cs * arb > 65536) return hipErrorInvalidValue;
+  for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
+    const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
     const int tslot = tc <= 1 ? 1 : tc <= 2 ? 2 : 4;
     MoePlan pl;
     if (!moe_plan(units, row_bytes, rows, tc * a.topk, pl)) return hipErrorInvalidValue;
+    const MoeArgs& ac = a;
     hipError_t err = hipErrorInvalidValue;
     if (gate) {
-      if (tslot == 1) err = gate_up_lp<F, A, 1>(a, pl, row_bytes, units, (int)c0, tc, st);
-      else if (tslot == 2) err = gate_up_lp<F, A, 2>(a, pl, row_bytes, units, (int)c0, tc, st);
-      else err = gate_up_lp<F, A, 4>(a, pl, row_bytes, units, (int)c0, tc, st);
+      if (tslot == 1) err = gate_up_lp<F, A, 1>(ac, pl, row_bytes, units, (int)c0, tc, st);
+      else if (tslot == 2) err = gate_up_lp<F, A, 2>(ac, pl, row_bytes, units, (int)c0, tc, st);
+      else err = gate_up_lp<F, A, 4>(ac, pl, row_bytes, units, (int)c0, tc, st);
     } else {
-      if (tslot == 1) err = down_lp<F, A, 1>(a, pl, row_bytes, units, (int)c0, tc, st);
-      else if (tslot == 2) err = down_lp<F, A, 2>(a, pl, row_bytes, units, (int)c0, tc, st);
-      else err = down_lp<F, A, 4>(a, pl, row_bytes, units, (int)c0, tc, st);
+      if (tslot == 1) err = down_lp<F, A, 1>(ac, pl, row_bytes, units, (int)c0, tc, st);
+      else if (tslot == 2) err = down_lp<F, A, 2>(ac, pl, row_bytes, units, (int)c0, tc, st);
+      else err = down_lp<F, A, 4>(ac, pl, row_bytes, units, (int)c0, tc, st);
     }
     if (err != hipSuccess) return err;
   }
@@ -685,15 +696,16 @@ hipError_t ftk_launch_sort(const int32_t* ids, int64_t t, int topk, int64_t n_ex
   return hipGetLastError();
 }
 
+// MXFP4 x Q8_K runs on the FP4 matrix cores (ft_moe_fp4.hip)
 hipError_t ftk_launch_moe_gate_up(const MoeArgs& a, hipStream_t st) {
   if (a.w == FT_Q4_K && a.act == FT_Q8_1) return moe_stage<FT_Q4_K, FT_Q8_1>(a, true, st);
-  if (a.w == FT_MXFP4 && a.act == FT_Q8_K) return moe_stage<FT_MXFP4, FT_Q8_K>(a, true, st);
+  if (a.w == FT_MXFP4 && a.act == FT_Q8_K) return ftk_launch_moe_fp4_gate_up(a, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t ftk_launch_moe_down(const MoeArgs& a, hipStream_t st) {
   if (a.w == FT_Q4_K && a.act == FT_Q8_1) return moe_stage<FT_Q4_K, FT_Q8_1>(a, false, st);
-  if (a.w == FT_MXFP4 && a.act == FT_Q8_K) return moe_stage<FT_MXFP4, FT_Q8_K>(a, false, st);
+  if (a.w == FT_MXFP4 && a.act == FT_Q8_K) return ftk_launch_moe_fp4_down(a, st);
   return hipErrorInvalidValue;
 }
 

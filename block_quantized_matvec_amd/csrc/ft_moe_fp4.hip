@@ -1,0 +1,430 @@
+// ft_moe_fp4.hip -- direct-route MXFP4 expert kernels (gate/up + SwiGLU, down) on
+// the block-scaled FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4).
+//
+// ds4 PR #656 "Add ROCm MXFP4 routed expert kernels" (Summary): resident MXFP4 x
+// Q8_K routed gate/up and down kernels with SwiGLU between them, and small batches
+// sent through direct kernels rather than partly filled expert-sorted tiles.
+// MI355X design:
+//  * the tokens of a chunk (up to 8) are rows of the MFMA A operand and 16 weight
+//    rows of one expert its columns; an MXFP4 block's 16 code bytes are one lane's
+//    FP4 B operand as stored and its E8M0 byte that lane's B scale, so no E2M1
+//    decode and no per-block scaling runs on the VALU;
+//  * a Q8_K code x is not an FP8 value, so the activations enter as two exact
+//    E4M3 halves x = 16*hi + lo (hi = x >> 4 in [-8, 7], lo = x & 15), chained in
+//    one accumulator with A scales 2^0 and 2^4; per 256-element superblock the
+//    four MFMAs (two k-steps x lo, hi) start from zero and the result is scaled by
+//    the token's Q8_K scale;
+//  * a workgroup of 8 waves owns 16-row groups of one expert, each split over K in
+//    KQ parts (summed in a fixed order through LDS); odd parts walk K downwards so
+//    that the cache line two parts share is fetched once;
+//  * each lane fetches its own block per k-step straight from global memory (five
+//    dwords: E8M0 byte + 16 code bytes at a 1..4 byte offset), one superblock
+//    ahead;
+//  * the workgroup quantizes its activation rows to Q8_K itself (the arithmetic of
+//    ft_quantize_act) and keeps them in LDS as the FP8 halves in the operand's
+//    nibble order, with the Q8_K scale of every (token, superblock).
+// The workgroup of the first slot naming an expert owns it and applies it to every
+// token of the chunk that picked it.
+#include <math.h>
+
+#include "ft_device.h"
+#include "ft_internal.h"
+
+namespace ftk {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int MF_WAVES = 8;
+constexpr int MF_THREADS = 64 * MF_WAVES;
+constexpr int MF_MAXT = 8;      // tokens per launch (A rows in use)
+
+// Byte-wise table lookup of 4-bit indices (one per byte) in a 16-byte table t0..t3.
+__device__ __forceinline__ uint32_t lut16(uint32_t n, uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
+  const uint32_t i = n & 0x07070707u;
+  const uint32_t a = __builtin_amdgcn_perm(t1, t0, i);
+  const uint32_t b = __builtin_amdgcn_perm(t3, t2, i);
+  const uint32_t sel = ((n >> 1) & 0x04040404u) | 0x03020100u;   // byte k of a, or of b if index >= 8
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// Four int8 codes -> their E4M3 (OCP) halves: lo = x & 15 (0..15), hi = x >> 4
+// (two's-complement nibble: 0..7, then -8..-1).  1.0 is 0x38; every value is exact.
+__device__ __forceinline__ void fp8_halves(uint32_t c, uint32_t& lo, uint32_t& hi) {
+  lo = lut16(c & 0x0F0F0F0Fu, 0x44403800u, 0x4E4C4A48u, 0x53525150u, 0x57565554u);
+  hi = lut16((c >> 4) & 0x0F0F0F0Fu, 0x44403800u, 0x4E4C4A48u, 0xCACCCED0u, 0xB8C0C4C8u);
+}
+
+// LDS activation image of one token: the lo halves of its K codes, then the hi
+// halves (2K bytes), plus dx[superblock][16 tokens] fp32.  Within each 32-element
+// block the codes are in the FP4 operand's nibble order: an MXFP4 block stores
+// element e < 16 in the low nibble and e + 16 in the high nibble of byte e, and the
+// MFMA takes nibble n (byte n/2, low first) as k-position n, so position n holds
+// element n/2 + 16*(n & 1).
+// Lane l16 holds elements 16*l16 .. 16*l16+15 of superblock sb (block l16/2, half
+// h = l16&1) and writes positions 16h .. 16h+15 of that block: its own first (h=0)
+// or the partner lane's second (h=1) eight codes interleaved with the partner's
+// first or its own second eight.  Both lanes of a pair must call it.
+__device__ __forceinline__ void stage_codes(const uint32_t (&w)[4], uint8_t* arow, int64_t k, int sb, int l16) {
+  uint32_t pw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pw[j] = (uint32_t)__float_as_int(xchg<1>(__int_as_float((int)w[j])));
+  const bool h = l16 & 1;
+  const uint32_t a0 = h ? pw[2] : w[0], a1 = h ? pw[3] : w[1];   // elements 8h .. 8h+7
+  const uint32_t b0 = h ? w[2] : pw[0], b1 = h ? w[3] : pw[1];   // elements 16+8h .. 16+8h+7
+  const uint32_t c[4] = {__builtin_amdgcn_perm(b0, a0, 0x05010400u), __builtin_amdgcn_perm(b0, a0, 0x07030602u),
+                         __builtin_amdgcn_perm(b1, a1, 0x05010400u), __builtin_amdgcn_perm(b1, a1, 0x07030602u)};
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fp8_halves(c[j], lo[j], hi[j]);
+  *(u32x4*)(arow + 256 * sb + 16 * l16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  *(u32x4*)(arow + k + 256 * sb + 16 * l16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+}
+
+// One lane's MXFP4 block for k-step s: the 17 bytes at 68*s + 17*b of its row
+// (b = lane >> 4) lie in the five dwords from dword 17*s + 4*b, at byte offset b.
+struct Fp4Blk {
+  uint32_t d[5];
+};
+__device__ __forceinline__ void fp4_fetch(const uint32_t* __restrict__ rowd, int s, int b, Fp4Blk& f) {
+  const uint32_t* p = rowd + 17 * s + 4 * b;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) f.d[i] = p[i];
+}
+// -> B operand (16 code bytes) and E8M0 scale byte
+__device__ __forceinline__ v8i fp4_operand(const Fp4Blk& f, int b, int& e8) {
+  const uint32_t sh = 8u * (uint32_t)(b + 1);   // 8..32 bits
+  v8i o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = (int)(uint32_t)((((uint64_t)f.d[j + 1] << 32) | f.d[j]) >> sh);
+  o[4] = o[5] = o[6] = o[7] = 0;
+  e8 = (int)((f.d[0] >> (8 * b)) & 0xFFu);
+  return o;
+}
+
+// The first superblock's blocks of a wave's rows (issued before the activation
+// staging so that their latency overlaps it; unconditional, so that nothing
+// waits for them early: a wave with no superblocks reads a valid one, unused).
+template <int NM>
+__device__ __forceinline__ void fp4_first(const uint32_t* const (&rowd)[NM], int sbf, int nsb, Fp4Blk (&nx)[NM][2]) {
+  const int b = (threadIdx.x & 63) >> 4;
+  sbf = sbf < 0 ? 0 : (sbf < nsb ? sbf : nsb - 1);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    fp4_fetch(rowd[m], 2 * sbf, b, nx[m][0]);
+    fp4_fetch(rowd[m], 2 * sbf + 1, b, nx[m][1]);
+  }
+}
+
+// The dot products of one wave: 16 rows (rowd[m] for each of NM matrices) over the
+// superblocks [sb0, sb1), walked upwards (dir = 1) or downwards (dir = -1), against
+// the activation image `act` (t_in tokens, those of tmask staged).  nx: the first
+// superblock's blocks.  Result acc[m][r]: row (lane & 15) x token 4*(lane >> 4) + r.
+template <int NM>
+__device__ __forceinline__ void fp4_rows(const uint32_t* const (&rowd)[NM], int sb0, int sb1, int dir,
+                                         Fp4Blk (&nx)[NM][2], const uint8_t* act, int64_t k, int t_in, uint32_t tmask,
+                                         const float* dx, v4f (&acc)[NM]) {
+  const int lane = threadIdx.x & 63, b = lane >> 4, tok = lane & 15;
+  const bool arow = tok < t_in && ((tmask >> tok) & 1);
+  const uint8_t* ap = act + (int64_t)tok * 2 * k + 16 * b;
+  const v4f zf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = zf;
+  const int n = sb1 - sb0;
+  for (int it = 0; it < n; ++it) {
+    const int sb = dir > 0 ? sb0 + it : sb1 - 1 - it;
+    Fp4Blk cur[NM][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      cur[m][0] = nx[m][0];
+      cur[m][1] = nx[m][1];
+    }
+    if (it + 1 < n) {
+      const int sn = sb + dir;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        fp4_fetch(rowd[m], 2 * sn, b, nx[m][0]);
+        fp4_fetch(rowd[m], 2 * sn + 1, b, nx[m][1]);
+      }
+    }
+    v4f dd[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) dd[m] = zf;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      int e8[NM];
+      v8i bw[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) bw[m] = fp4_operand(cur[m][st], b, e8[m]);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+        if (arow) {
+          const uint8_t* q = ap + pp * k + 256 * sb + 128 * st;
+          a0 = *(const u32x4*)q;
+          a1 = *(const u32x4*)(q + 64);
+        }
+        const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+          dd[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw[m], dd[m], 0, 4, 0, pp ? 131 : 127, 0,
+                                                                    e8[m]);
+      }
+    }
+    const v4f dxv = *(const v4f*)(dx + sb * 16 + 4 * b);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][r] = fmaf(dxv[r], dd[m][r], acc[m][r]);
+  }
+}
+
+// Sum the KQ K-parts of each row group (fixed order) through LDS `red`
+// ([row group][K part][64 lanes][NM * 4] fp32, wave = KQ * row group + part);
+// returns true in the waves of part 0, whose acc then holds the totals.
+template <int NM, int KQ>
+__device__ __forceinline__ bool fp4_reduce(v4f (&acc)[NM], float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* mine = red + ((size_t)wave * 64 + lane) * (NM * 4);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) *(v4f*)(mine + 4 * m) = acc[m];
+  __syncthreads();
+  if (wave % KQ != 0) return false;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    v4f s = *(const v4f*)(mine + 4 * m);
+#pragma unroll
+    for (int q = 1; q < KQ; ++q) {
+      const v4f o = *(const v4f*)(mine + (size_t)q * 64 * (NM * 4) + 4 * m);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] += o[r];
+    }
+    acc[m] = s;
+  }
+  return true;
+}
+
+// gate/up + SwiGLU for 16 * 8 / KQ rows of the expert of slot blockIdx.y (KQ K parts
+// per 16-row group; odd parts walk their superblocks downwards, so that a cache line
+// shared by two neighbouring parts is read by both at about the same time)
+template <int KQ>
+__global__ void __launch_bounds__(MF_THREADS)
+moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t n_expert,
+                       int64_t inter, int64_t hidden, const float* __restrict__ x, int t_real,
+                       const int32_t* __restrict__ ids, int topk, float* __restrict__ h, float* __restrict__ gtap,
+                       float* __restrict__ utap) {
+  extern __shared__ u32x4 smem4[];
+  uint8_t* act = (uint8_t*)smem4;                           // [t_real][2 * hidden]
+  float* dx = (float*)(act + (size_t)t_real * 2 * hidden);  // [hidden / 256][16]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int e;
+  uint32_t mask;
+  uint64_t smask;
+  if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
+
+  constexpr int RG = MF_WAVES / KQ;
+  const int nsb = (int)(hidden / 256), rg = wave / KQ, kq = wave % KQ, dir = (kq & 1) ? -1 : 1;
+  const int64_t row = (int64_t)blockIdx.x * (16 * RG) + rg * 16 + (lane & 15);
+  const int64_t row_bytes = hidden / 32 * 17;
+  const uint32_t* const rowd[2] = {(const uint32_t*)(wg + ((int64_t)e * inter + row) * row_bytes),
+                                   (const uint32_t*)(wu + ((int64_t)e * inter + row) * row_bytes)};
+  const int sb0 = kq * nsb / KQ, sb1 = (kq + 1) * nsb / KQ;
+  Fp4Blk nx[2][2];
+  fp4_first<2>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
+
+  // x -> Q8_K codes -> FP8 halves in LDS (16 elements per thread, 16 lanes per block)
+  for (int i = tid; i < nsb * 16; i += MF_THREADS) dx[i] = 0.0f;
+  __syncthreads();
+  const int per_row = (int)(hidden / 16), total = t_real * per_row;
+  for (int idx0 = 0; idx0 < total; idx0 += MF_THREADS) {
+    const int idx = idx0 + tid;
+    if (idx < total) {   // the same for all 16 lanes of a block
+      const int r = idx / per_row, c = idx - r * per_row;
+      const float4* p = (const float4*)(x + (int64_t)r * hidden) + 4 * c;
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = p[q];
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+      uint32_t w[4];
+      int s;
+      float d;
+      q8_k_codes(v, w, s, d);
+      stage_codes(w, act + (int64_t)r * 2 * hidden, hidden, c >> 4, c & 15);
+      if ((c & 15) == 0) dx[(c >> 4) * 16 + r] = d;
+    }
+  }
+  __syncthreads();
+
+  v4f acc[2];
+  fp4_rows<2>(rowd, sb0, sb1, dir, nx, act, hidden, t_real, 0xFFu, dx, acc);
+  __syncthreads();   // the activation image is dead: the reduction reuses its LDS
+  if (!fp4_reduce<2, KQ>(acc, (float*)smem4)) return;
+
+  const int b = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * b + r;
+    if (i < t_real && ((mask >> i) & 1)) {
+      const float g = acc[0][r], u = acc[1][r], hv = g / (1.0f + expf(-g)) * u;
+      for (int k = 0; k < topk; ++k) {
+        if ((smask >> (8 * i + k)) & 1) {
+          const int64_t o = (int64_t)(i * topk + k) * inter + row;
+          h[o] = hv;
+          if (gtap) gtap[o] = g;
+          if (utap) utap[o] = u;
+        }
+      }
+    }
+  }
+}
+
+// down projection for 16 * 8 / KQ rows of the expert of slot blockIdx.y: d[pair][r] for
+// every slot naming it.  hhat of the expert's tokens is quantized here from the
+// first slot's h row (or taken from in_hq); the workgroup of row block 0 writes
+// the Q8_K blocks to hq_tap for every slot naming the expert.
+template <int KQ>
+__global__ void __launch_bounds__(MF_THREADS)
+moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int64_t inter,
+                    const float* __restrict__ h, const uint8_t* __restrict__ in_hq, uint8_t* __restrict__ hq_tap,
+                    int t_real, const int32_t* __restrict__ ids, int topk, float* __restrict__ dpair) {
+  extern __shared__ u32x4 smem4[];
+  uint8_t* act = (uint8_t*)smem4;                          // [t_real][2 * inter]
+  float* dx = (float*)(act + (size_t)t_real * 2 * inter);  // [inter / 256][16]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int e;
+  uint32_t mask;
+  uint64_t smask;
+  if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
+
+  constexpr int RG = MF_WAVES / KQ;
+  const int nsb = (int)(inter / 256), rg = wave / KQ, kq = wave % KQ, dir = (kq & 1) ? -1 : 1;
+  const int64_t row = (int64_t)blockIdx.x * (16 * RG) + rg * 16 + (lane & 15);
+  const int64_t row_bytes = inter / 32 * 17;
+  const uint32_t* const rowd[1] = {(const uint32_t*)(wd + ((int64_t)e * hidden + row) * row_bytes)};
+  const int sb0 = kq * nsb / KQ, sb1 = (kq + 1) * nsb / KQ;
+  Fp4Blk nx[1][2];
+  fp4_first<1>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
+  const int hrb = nsb * 292;
+  auto first_pair = [&](int i) { return i * topk + __ffs((unsigned)(smask >> (8 * i)) & 0xFFu) - 1; };
+  const bool tap = hq_tap && blockIdx.x == 0;
+
+  for (int i = tid; i < nsb * 16; i += MF_THREADS) dx[i] = 0.0f;
+  __syncthreads();
+  const int ntok = __popc(mask), per_row = (int)(inter / 16), total = ntok * per_row;
+  for (int idx0 = 0; idx0 < total; idx0 += MF_THREADS) {
+    const int idx = idx0 + tid;
+    if (idx < total) {
+      const int j = idx / per_row, c = idx - j * per_row, i = nth_bit(mask, j), sb = c >> 4, l16 = c & 15;
+      const int64_t src = first_pair(i);
+      uint32_t w[4];
+      int s;
+      float d;
+      if (in_hq) {
+        const uint8_t* blk = in_hq + src * hrb + (int64_t)sb * 292;   // 4-byte aligned
+        const uint32_t* q = (const uint32_t*)(blk + 4 + 16 * l16);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w[jj] = q[jj];
+        d = *(const float*)blk;
+        s = *(const int16_t*)(blk + 260 + 2 * l16);
+      } else {
+        const float4* p = (const float4*)(h + src * inter) + 4 * c;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = p[q];
+          v[4 * q] = f.x;
+          v[4 * q + 1] = f.y;
+          v[4 * q + 2] = f.z;
+          v[4 * q + 3] = f.w;
+        }
+        q8_k_codes(v, w, s, d);
+      }
+      stage_codes(w, act + (int64_t)i * 2 * inter, inter, sb, l16);
+      if (l16 == 0) dx[sb * 16 + i] = d;
+      if (tap) {
+        for (int k = 0; k < topk; ++k)
+          if ((smask >> (8 * i + k)) & 1) q8_k_store(w, s, d, l16, hq_tap + (int64_t)(i * topk + k) * hrb + sb * 292);
+      }
+    }
+  }
+  __syncthreads();
+
+  v4f acc[1];
+  fp4_rows<1>(rowd, sb0, sb1, dir, nx, act, inter, t_real, mask, dx, acc);
+  __syncthreads();
+  if (!fp4_reduce<1, KQ>(acc, (float*)smem4)) return;
+
+  const int b = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * b + r;
+    if (i < t_real && ((mask >> i) & 1)) {
+      for (int k = 0; k < topk; ++k)
+        if ((smask >> (8 * i + k)) & 1) dpair[(int64_t)(i * topk + k) * hidden + row] = acc[0][r];
+    }
+  }
+}
+
+// LDS bytes of one launch: the activation image and scales, or the K-quarter
+// partials, whichever is larger
+static size_t fp4_lds(int t, int64_t k, int nm) {
+  const size_t img = (size_t)t * 2 * k + (size_t)(k / 256) * 16 * 4;
+  const size_t red = (size_t)MF_WAVES * 64 * nm * 4 * 4;
+  return img > red ? img : red;
+}
+
+}  // namespace ftk
+
+using namespace ftk;
+
+// Direct-route stages for MXFP4 x Q8_K.  Shapes: hidden and inter multiples of
+// 256 (so every workgroup's rows exist); tokens in chunks of up to 8 that fit
+// 64 KiB of LDS.  gate/up: 4 K parts x 2 row groups; down (half the K): 2 K parts x
+// 4 row groups.
+constexpr int MF_KQ_GU = 4, MF_KQ_DN = 2;
+static int fp4_chunk(int64_t k, int nm) {
+  int cs = MF_MAXT;
+  while (cs > 1 && fp4_lds(cs, k, nm) > 65536) cs /= 2;
+  return fp4_lds(cs, k, nm) > 65536 ? 0 : cs;
+}
+
+hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
+  const int cs = fp4_chunk(a.hidden, 2);
+  if (cs < 1 || a.hidden % 256 || a.inter % 256) return hipErrorInvalidValue;
+  for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
+    const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
+    const dim3 grid((unsigned)(a.inter / (16 * MF_WAVES / MF_KQ_GU)), (unsigned)(tc * a.topk));
+    const size_t p0 = (size_t)c0 * a.topk;
+    hipLaunchKernelGGL(moe_fp4_gate_up_kernel<MF_KQ_GU>, grid, dim3(MF_THREADS), fp4_lds(tc, a.hidden, 2), st,
+                       (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, a.hidden,
+                       a.x + (size_t)c0 * a.hidden, tc, a.ids + p0, a.topk, a.h + p0 * a.inter,
+                       a.g_tap ? a.g_tap + p0 * a.inter : nullptr, a.u_tap ? a.u_tap + p0 * a.inter : nullptr);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st) {
+  const int cs = fp4_chunk(a.inter, 1);
+  if (cs < 1 || a.hidden % 256 || a.inter % 256) return hipErrorInvalidValue;
+  const int64_t hrb = a.inter / 256 * 292;
+  for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
+    const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
+    const dim3 grid((unsigned)(a.hidden / (16 * MF_WAVES / MF_KQ_DN)), (unsigned)(tc * a.topk));
+    const size_t p0 = (size_t)c0 * a.topk;
+    hipLaunchKernelGGL(moe_fp4_down_kernel<MF_KQ_DN>, grid, dim3(MF_THREADS), fp4_lds(tc, a.inter, 1), st,
+                       (const uint8_t*)a.w_down, a.n_expert, a.hidden, a.inter, a.h + p0 * a.inter,
+                       a.in_hq ? (const uint8_t*)a.in_hq + p0 * hrb : nullptr,
+                       a.hq_tap ? (uint8_t*)a.hq_tap + p0 * hrb : nullptr, tc, a.ids + p0, a.topk,
+                       a.dpair + p0 * a.hidden);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}

@@ -140,7 +140,7 @@ ft_status ft_moe_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert,
 typedef struct {
   int route;          /* 0 auto, 1 force the direct route, 2 force sorted tiles
                          (tiles: (MXFP4, Q8_K) only, else FT_ERR_UNSUPPORTED) */
-  int direct_max_t;   /* auto route: direct for t <= direct_max_t (0 = default 3),
+  int direct_max_t;   /* auto route: direct for t <= direct_max_t (0 = default 8),
                          sorted tiles above it where supported */
   float* tap_g;       /* nullable [t*topk][inter] fp32: gate projections */
   float* tap_u;       /* nullable [t*topk][inter] fp32: up projections */

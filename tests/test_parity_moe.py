@@ -67,12 +67,16 @@ def _bank(name):
     return _banks[name]
 
 
-def _run_stages(name, t, route, seed=0, dup=False):
+def _run_stages(name, t, route, seed=0, dup=False, rep=False):
     c = CASES[name]
     wg, wu, wd, dwg, dwu, dwd = _bank(name)
     g = synth.rng(303, t, seed)
     x = synth.activations(t, c["hidden"], g)
     ids = synth.expert_ids(t, c["E"], c["topk"], g)
+    if rep:
+        # slot 1 repeats slot 0's expert in every token: both pairs get the same
+        # h and d, each with its own weight in the combine
+        ids[:, 1] = ids[:, 0]
     if dup and t > 1:
         # every token picks expert ids[0, 0] at slot 0 (still distinct within a token)
         e0 = ids[0, 0]
@@ -117,13 +121,45 @@ def test_moe_shared_experts(name):
     _run_stages(name, 4, route=1, dup=True)
 
 
+@pytest.mark.parametrize("name,t,route", [("q4k_small", 3, 1), ("mxfp4_small", 2, 1), ("mxfp4_small", 5, 2),
+                                          ("q4k", 1, 1), ("mxfp4", 2, 1)])
+def test_moe_repeated_expert_in_token(name, t, route):
+    log(f"moe {name} repeated expert t={t} route={route}")
+    _run_stages(name, t, route=route, rep=True)
+
+
+@pytest.mark.parametrize("name,t,route", [("q4k", 1, 1), ("q4k", 4, 1), ("mxfp4", 3, 1), ("mxfp4", 5, 2),
+                                          ("mxfp4_small", 6, 2)])
+def test_moe_down_from_given_hq(name, t, route):
+    """The down stage and the combine alone: the quantized h rows come from the
+    oracle (in_hq), so the check does not depend on the GPU's gate/up."""
+    c = CASES[name]
+    wg, wu, wd, dwg, dwu, dwd = _bank(name)
+    g = synth.rng(306, t, route)
+    H, I, E, K = c["hidden"], c["inter"], c["E"], c["topk"]
+    x = synth.activations(t, H, g)
+    ids = synth.expert_ids(t, E, K, g)
+    ew = synth.expert_weights(t, K, g)
+    _, _, rh = oracle.moe_gate_up(c["w"], wg, wu, E, H, I, c["a"], oracle.quantize(c["a"], x), ids)
+    hq = oracle.quantize(c["a"], rh.astype(np.float32))
+    taps = {"hq": torch.empty(t * K, ft.row_bytes(c["a"], I), dtype=torch.uint8, device="cuda"),
+            "down": torch.empty(t * K, H, device="cuda")}
+    log(f"moe {name} down from given hq t={t} route={route}")
+    y = host(ft.moe_q_vec(c["w"], dwg, dwu, dwd, E, H, I, c["a"], dev(x), dev(ids), dev(ew), route=route, taps=taps,
+                          in_hq=dev(hq)))
+    assert np.array_equal(host(taps["hq"]), hq), "hq tap differs from the given blocks"
+    rd = oracle.moe_down(c["w"], wd, E, H, I, c["a"], hq, ids)
+    check_fp32(host(taps["down"]), rd, "down")
+    check_fp32(y, oracle.moe_combine(rd, ew), "combine")
+
+
 @pytest.mark.parametrize("t", [1, 2, 3, 4])
 def test_moe_q4k_layer(t):
     log(f"moe q4k layer t={t}")
     _run_stages("q4k", t, route=0)
 
 
-@pytest.mark.parametrize("t", [1, 2, 3, 4])
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 6, 8, 11])
 def test_moe_mxfp4_direct(t):
     log(f"moe mxfp4 t={t}")
     _run_stages("mxfp4", t, route=1)
@@ -140,10 +176,10 @@ def test_moe_mxfp4_small_tiles_shared_experts():
     _run_stages("mxfp4_small", 6, route=2, dup=True)
 
 
-@pytest.mark.parametrize("t,route", [(1, 2), (4, 2), (5, 0), (9, 0)])
+@pytest.mark.parametrize("t,route", [(1, 2), (4, 2), (5, 0), (9, 0), (12, 0)])
 def test_moe_mxfp4_tiles(t, route):
     """Full-size MXFP4 bank (hidden 4096, 256 experts of 2048): route 0 takes the
-    tiles above 4 tokens."""
+    direct route up to 8 tokens and the tiles above."""
     log(f"moe mxfp4 tiles t={t} route={route}")
     _run_stages("mxfp4", t, route=route)
 
