@@ -32,6 +32,9 @@ struct MmvqPlan {
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out);
 int ftk_mmvq_plan_fmt(int units_per_row, int tslot, int row_bytes, int64_t n, bool aligned_kquant, MmvqPlan* out);
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
+// int8-MFMA matvec for 2..8 tokens (K % 256 == 0; Q4_0, Q8_0, Q4_K x Q8_1)
+bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t);
+hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st);
 
 hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
                                hipStream_t st);

@@ -444,8 +444,21 @@ int ftk_num_cus() {
   return cached;
 }
 
+// Several tokens go to the int8 MFMA kernels (ft_mmvq_mfma.hip) when K is a whole
+// number of 256-element chunks from 4 tokens on (measured: 2 tokens run faster on
+// the dot4 kernels, 4 about even, 8 faster on MFMA); FT_MMVQ_MFMA_MIN_T moves the
+// threshold (tuning sweeps).
+static int mfma_min_t() {
+  static const int v = [] {
+    const char* e = getenv("FT_MMVQ_MFMA_MIN_T");
+    return e && atoi(e) > 0 ? atoi(e) : 4;
+  }();
+  return v;
+}
+
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;
+  if (a.t >= mfma_min_t() && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t)) return ftk_launch_mmvq_mfma(a, k, st);
   if (a.act == FT_Q8_1) {
     switch (a.w) {
       case FT_Q4_0: return launch_fa<FT_Q4_0, FT_Q8_1>(a, k, st);

@@ -1,0 +1,237 @@
+// ft_mmvq_mfma.hip -- Q-matvec for 2..8 tokens on the int8 matrix cores
+// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0 and Q4_K weights against Q8_1 activations.
+//
+// ggml-cuda "mul_mat_vec_q" (the pages' MMVQ path, ds4 PR #656 Summary): a block's
+// integer dot product of weight and activation codes, then the fp32 scale
+// combine.  MI355X design for more than one token:
+//  * the tokens are rows of the MFMA A operand (up to 16; 2..8 here) and 16 weight
+//    rows its columns, so one instruction takes a 32-element block of 16 rows
+//    against every token: no activation codes are held in VGPRs per token and the
+//    per-token cost is the scale combine only (the dot4 kernels keep every
+//    token's codes in VGPRs and spill from 4 tokens on);
+//  * a workgroup owns 16 rows split over K in KP parts, one wave each; a wave
+//    streams 256-element chunks of its 16 rows and of the activation rows into
+//    its own LDS slice with 16-byte loads (two chunks ahead in VGPRs) and reads
+//    its operands from there; no barrier until the parts are summed, in a fixed
+//    order, through LDS;
+//  * per block: D = sum over the block of weight code x activation code (int32,
+//    exact); y += D * (d_w * d_x) (Q8_0, and Q4_0 whose codes enter as n - 8);
+//    Q4_K: y += d_x * (d * sc_j * D - dmin * m_j * S) with S the activation code
+//    sum of sub-block j, from a second MFMA against an all-ones operand.
+#include "ft_device.h"
+#include "ft_internal.h"
+
+namespace ftk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int MV_ACB = 288;   // 256 elements of one token's Q8_1 row (8 blocks of 36 bytes)
+constexpr int MV_MAXT = 8;
+
+// bytes of one row's 256-element chunk
+template <int F> struct MvGeo;
+template <> struct MvGeo<FT_Q4_0> { static constexpr int CB = 144; };
+template <> struct MvGeo<FT_Q8_0> { static constexpr int CB = 272; };
+template <> struct MvGeo<FT_Q4_K> { static constexpr int CB = 144; };
+
+template <int F> struct MvRegs {
+  static constexpr int NW = (16 * MvGeo<F>::CB / 16 + 63) / 64;   // 16-byte weight pieces per lane
+  static constexpr int NA = (MV_MAXT * MV_ACB / 16 + 63) / 64;    // activation pieces per lane
+  u32x4 w[NW];
+  u32x4 a[NA];
+};
+
+// 8 bytes at a 2- or 4-byte aligned LDS offset
+__device__ __forceinline__ uint64_t lds_u64(const uint8_t* base, uint32_t off) {
+  const uint32_t* d = (const uint32_t*)(base + (off & ~3u));
+  const uint32_t s = off & 3u;
+  const uint32_t d0 = d[0], d1 = d[1];
+  if (s == 0) return (uint64_t)d0 | ((uint64_t)d1 << 32);
+  const uint32_t d2 = d[2];
+  return (uint64_t)__builtin_amdgcn_alignbyte(d1, d0, s) | ((uint64_t)__builtin_amdgcn_alignbyte(d2, d1, s) << 32);
+}
+__device__ __forceinline__ float lds_h2f(const uint8_t* base, uint32_t off) {
+  return h2f(*(const uint16_t*)(base + off));
+}
+
+template <int F, int KP>
+__global__ void __launch_bounds__(64 * KP)
+mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t row_bytes,
+                 const uint8_t* __restrict__ xq, int64_t xrb, int t, float* __restrict__ y, int64_t ldy) {
+  constexpr int CB = MvGeo<F>::CB, NWP = 16 * CB / 16, SLICE = 16 * CB + MV_MAXT * MV_ACB;
+  using R = MvRegs<F>;
+  extern __shared__ u32x4 smem4[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint8_t* wl = (uint8_t*)smem4 + wave * SLICE;   // this wave's 16 rows x CB
+  uint8_t* al = wl + 16 * CB;                     // t activation rows x 288
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int nch = (int)(k / 256), c0 = wave * nch / KP, c1 = (wave + 1) * nch / KP;
+  const int nap = 18 * t;   // activation pieces per chunk
+
+  // Every lane issues every load (pieces past the end, rows past n and chunks past
+  // the part re-read valid bytes that are never committed or used), so that the
+  // loads in flight are the same on every path and the waits stay exact.
+  auto fetch = [&](int c, R& r) {
+    c = c < nch ? c : nch - 1;
+#pragma unroll
+    for (int i = 0; i < R::NW; ++i) {
+      int p = lane + 64 * i;
+      p = p < NWP ? p : NWP - 1;
+      const int row = p / (CB / 16), off = (p - row * (CB / 16)) * 16;
+      const int64_t gr = row0 + row < n ? row0 + row : n - 1;
+      r.w[i] = *(const u32x4*)(W + gr * row_bytes + (int64_t)c * CB + off);
+    }
+#pragma unroll
+    for (int i = 0; i < R::NA; ++i) {
+      int p = lane + 64 * i;
+      p = p < nap ? p : nap - 1;
+      const int tok = p / 18, off = (p - tok * 18) * 16;
+      r.a[i] = *(const u32x4*)(xq + (int64_t)tok * xrb + (int64_t)c * MV_ACB + off);
+    }
+  };
+  auto commit = [&](const R& r) {
+#pragma unroll
+    for (int i = 0; i < R::NW; ++i) {
+      const int p = lane + 64 * i;
+      if (p < NWP) *(u32x4*)(wl + 16 * p) = r.w[i];
+    }
+#pragma unroll
+    for (int i = 0; i < R::NA; ++i) {
+      const int p = lane + 64 * i;
+      if (p < nap) *(u32x4*)(al + 16 * p) = r.a[i];
+    }
+  };
+
+  // Token i sits in A row 4*(i % 4) + i / 4, so that result row 4*kq + r (lane
+  // group kq) is token kq + 4*r: with t tokens only r < ceil(t/4) carries results
+  // and every lane group has its share (the scale combine runs ceil(t/4) times per
+  // lane, not 4).
+  const int col = lane & 15, kq = lane >> 4;
+  const int atok = (col >> 2) + 4 * (col & 3);   // the token of A row col
+  const bool arow = atok < t;
+  const int nr = (t + 3) >> 2;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const v4i zi = {0, 0, 0, 0};
+
+  auto compute = [&]() {
+    if constexpr (F == FT_Q4_K) {
+      const u32x4 hd = *(const u32x4*)(wl + col * CB);
+      const float d = h2f(hd.x & 0xFFFFu), dmin = h2f(hd.x >> 16);
+      uint32_t sc_lo, sc_hi, m_lo, m_hi;
+      kq_unpack_scales(hd.y, hd.z, hd.w, sc_lo, sc_hi, m_lo, m_hi);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sh = 8u * (uint32_t)(j & 3);
+        const float dsc = d * (float)(((j < 4 ? sc_lo : sc_hi) >> sh) & 0xFFu);
+        const float dmn = dmin * (float)(((j < 4 ? m_lo : m_hi) >> sh) & 0xFFu);
+        const uint64_t q = *(const uint64_t*)(wl + col * CB + 16 + 32 * (j >> 1) + 8 * kq);
+        const uint64_t b = (j & 1) ? (q >> 4) & 0x0F0F0F0F0F0F0F0Full : q & 0x0F0F0F0F0F0F0F0Full;
+        const uint64_t a = arow ? lds_u64(al, (uint32_t)(atok * MV_ACB + 36 * j + 4 + 8 * kq)) : 0ull;
+        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, zi, 0, 0, 0);
+        const v4i S = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)0x0101010101010101ll, zi, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = kq + 4 * r;
+          if (r < nr && tok < t) {
+            const float dx = lds_h2f(al, (uint32_t)(tok * MV_ACB + 36 * j));
+            acc[r] = fmaf(dx, fmaf(dsc, (float)D[r], -dmn * (float)S[r]), acc[r]);
+          }
+        }
+      }
+    } else {
+      constexpr int BB = F == FT_Q8_0 ? 34 : 18;
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const uint32_t wb = (uint32_t)(col * CB + BB * blk);
+        const float dw = lds_h2f(wl, wb);
+        uint64_t b;
+        if constexpr (F == FT_Q8_0) {
+          b = lds_u64(wl, wb + 2 + 8 * kq);
+        } else {
+          // elements 8kq..8kq+7: low nibbles of bytes 0..7 (kq 0) or 8..15 (kq 1),
+          // high nibbles of the same (kq 2, 3); as int8 n - 8
+          const uint64_t q = lds_u64(wl, wb + 2 + 8 * (kq & 1));
+          const uint64_t nib = (q >> (4 * (kq >> 1))) & 0x0F0F0F0F0F0F0F0Full;
+          const uint32_t lo = ((uint32_t)nib + 0x78787878u) ^ 0x80808080u;
+          const uint32_t hi = ((uint32_t)(nib >> 32) + 0x78787878u) ^ 0x80808080u;
+          b = (uint64_t)lo | ((uint64_t)hi << 32);
+        }
+        const uint64_t a = arow ? lds_u64(al, (uint32_t)(atok * MV_ACB + 36 * blk + 4 + 8 * kq)) : 0ull;
+        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, zi, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = kq + 4 * r;
+          if (r < nr && tok < t) {
+            const float dx = lds_h2f(al, (uint32_t)(tok * MV_ACB + 36 * blk));
+            acc[r] = fmaf((float)D[r], dw * dx, acc[r]);
+          }
+        }
+      }
+    }
+  };
+
+  // two register buffers: chunk c is committed to the slice while c + 1 and c + 2
+  // are in flight
+  R ra, rb;
+  fetch(c0, ra);
+  fetch(c0 + 1, rb);
+  for (int c = c0; c < c1; c += 2) {
+    commit(ra);
+    fetch(c + 2, ra);
+    compute();
+    commit(rb);   // past the part's last chunk: committed, never computed
+    fetch(c + 3, rb);
+    if (c + 1 < c1) compute();
+  }
+
+  // the KP parts, in order, through LDS (the slices are free now)
+  __syncthreads();
+  float* red = (float*)smem4;
+  *(u32x4*)(red + (wave * 64 + lane) * 4) =
+      u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t row = row0 + col;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = kq + 4 * r;
+    if (tok < t && row < n) {
+      float s = red[lane * 4 + r];
+      for (int q = 1; q < KP; ++q) s += red[(q * 64 + lane) * 4 + r];
+      y[(int64_t)tok * ldy + row] = s;
+    }
+  }
+}
+
+template <int F>
+static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
+  constexpr int SLICE = 16 * MvGeo<F>::CB + MV_MAXT * MV_ACB;
+  const unsigned grid = (unsigned)((a.n + 15) / 16);
+  // about eight waves per CU: 4 K parts when there are many rows, else 8
+  if ((int64_t)grid * 4 >= (int64_t)ftk_num_cus() * 8) {
+    hipLaunchKernelGGL((mmvq_mfma_kernel<F, 4>), dim3(grid), dim3(256), (size_t)4 * SLICE, st, (const uint8_t*)a.W,
+                       a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq, (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
+  } else {
+    hipLaunchKernelGGL((mmvq_mfma_kernel<F, 8>), dim3(grid), dim3(512), (size_t)8 * SLICE, st, (const uint8_t*)a.W,
+                       a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq, (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ftk
+
+// 2..8 tokens, K a multiple of 256, (Q4_0 | Q8_0 | Q4_K) x Q8_1
+bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t) {
+  return act == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K) && k % 256 == 0 && k > 0 && t >= 2 &&
+         t <= ftk::MV_MAXT;
+}
+
+hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st) {
+  using namespace ftk;
+  switch (a.w) {
+    case FT_Q4_0: return launch_mfma_f<FT_Q4_0>(a, k, st);
+    case FT_Q8_0: return launch_mfma_f<FT_Q8_0>(a, k, st);
+    case FT_Q4_K: return launch_mfma_f<FT_Q4_K>(a, k, st);
+    default: return hipErrorInvalidValue;
+  }
+}

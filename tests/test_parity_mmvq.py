@@ -58,6 +58,43 @@ def test_mmvq_small(w, a, n, k, t):
     check_fp32(y, oracle.matvec(w, W, n, k, a, xq, t), f"{w} n={n} k={k} t={t}")
 
 
+@pytest.mark.parametrize("w", ["Q4_0", "Q8_0"])
+@pytest.mark.parametrize("n,k", [(77, 800), (300, 1056)])
+@pytest.mark.parametrize("t", [2, 4, 8])
+def test_mmvq_k_not_whole_chunks(w, n, k, t):
+    """K that is not a multiple of 256: several tokens take the dot4 kernels."""
+    log(f"mmvq {w} n={n} k={k} t={t}")
+    g = synth.rng(203, n, k, t)
+    W = synth.weights(w, n, k, g)
+    xq = oracle.quantize("Q8_1", synth.activations(t, k, g))
+    y = host(ft.mul_mat_vec_q(w, dev(W), n, k, "Q8_1", dev(xq), t))
+    check_fp32(y, oracle.matvec(w, W, n, k, "Q8_1", xq, t), f"{w} n={n} k={k} t={t}")
+
+
+@pytest.mark.parametrize("w,a", MMVQ)
+@pytest.mark.parametrize("t", [1, 2, 8])
+def test_mmvq_extreme_codes(w, a, t):
+    """Every weight byte 0xFF (codes at their extremes, largest scales) against
+    activation codes alternating -128 / +127: the integer block sums are at their
+    largest magnitudes."""
+    n, k = 50, 1024
+    be, bb = synth.BLOCK[w]
+    W = np.full((n, k // be * bb), 0xFF, np.uint8)
+    if w in ("Q4_0", "Q8_0"):
+        W.reshape(n, k // be, bb)[:, :, 0:2] = np.frombuffer(np.float16(0.0625).tobytes(), np.uint8)
+    else:
+        W.reshape(n, k // be, bb)[:, :, 0:4] = np.frombuffer(np.array([0.0625, 0.03125], np.float16).tobytes(),
+                                                             np.uint8)
+    abe, abb = synth.BLOCK[a]
+    xq = np.zeros((t, k // abe, abb), np.uint8)
+    xq[:, :, 0:4] = np.frombuffer(np.array([0.5, 0.0], np.float16).tobytes(), np.uint8)
+    xq[:, :, 4:4 + abe] = np.where(np.arange(abe) % 2 == 0, 0x80, 0x7F).astype(np.uint8)
+    xq[:, 1::3, 4:4 + abe] = 0x81
+    xq = xq.reshape(t, -1)
+    y = host(ft.mul_mat_vec_q(w, dev(W), n, k, a, dev(xq), t))
+    check_fp32(y, oracle.matvec(w, W, n, k, a, xq, t), f"{w} extreme t={t}")
+
+
 @pytest.mark.parametrize("w,a", MMVQ)
 def test_mmvq_ldy_and_row_tail(w, a):
     n, k, t = 1000, 1024, 3
