@@ -18,6 +18,8 @@
 //    exact); y += D * (d_w * d_x) (Q8_0, and Q4_0 whose codes enter as n - 8);
 //    Q4_K: y += d_x * (d * sc_j * D - dmin * m_j * S) with S the activation code
 //    sum of sub-block j, from a second MFMA against an all-ones operand.
+#include <stdlib.h>
+
 #include "ft_device.h"
 #include "ft_internal.h"
 
@@ -69,10 +71,13 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   const int nap = 18 * t;   // activation pieces per chunk
 
   // Every lane issues every load (pieces past the end, rows past n and chunks past
-  // the part re-read valid bytes that are never committed or used), so that the
-  // loads in flight are the same on every path and the waits stay exact.
+  // the part re-read valid bytes of the part that are never committed or used), so
+  // that the loads in flight are the same on every path and the waits stay exact.
+  // Re-reads stay inside the part: a neighbouring part's chunk read early would be
+  // fetched from HBM twice.
+  const int clast = c1 > c0 ? c1 - 1 : c0;
   auto fetch = [&](int c, R& r) {
-    c = c < nch ? c : nch - 1;
+    c = c < clast ? c : clast;
 #pragma unroll
     for (int i = 0; i < R::NW; ++i) {
       int p = lane + 64 * i;
@@ -203,19 +208,28 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   }
 }
 
+template <int F, int KP>
+static hipError_t launch_mfma_kp(const MmvqArgs& a, int64_t k, hipStream_t st) {
+  constexpr int SLICE = 16 * MvGeo<F>::CB + MV_MAXT * MV_ACB;
+  hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP>), dim3((unsigned)((a.n + 15) / 16)), dim3(64 * KP), (size_t)KP * SLICE,
+                     st, (const uint8_t*)a.W, a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq,
+                     (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+// K parts per 16 rows: about eight waves per CU (4 parts when there are many
+// rows, else 8); FT_MMVQ_MFMA_KP = 2, 4 or 8 forces it (tuning sweeps)
 template <int F>
 static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
-  constexpr int SLICE = 16 * MvGeo<F>::CB + MV_MAXT * MV_ACB;
-  const unsigned grid = (unsigned)((a.n + 15) / 16);
-  // about eight waves per CU: 4 K parts when there are many rows, else 8
-  if ((int64_t)grid * 4 >= (int64_t)ftk_num_cus() * 8) {
-    hipLaunchKernelGGL((mmvq_mfma_kernel<F, 4>), dim3(grid), dim3(256), (size_t)4 * SLICE, st, (const uint8_t*)a.W,
-                       a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq, (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
-  } else {
-    hipLaunchKernelGGL((mmvq_mfma_kernel<F, 8>), dim3(grid), dim3(512), (size_t)8 * SLICE, st, (const uint8_t*)a.W,
-                       a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq, (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
-  }
-  return hipGetLastError();
+  static const int force = [] {
+    const char* e = getenv("FT_MMVQ_MFMA_KP");
+    return e ? atoi(e) : 0;
+  }();
+  const int64_t groups = (a.n + 15) / 16;
+  const int kp = force == 2 || force == 4 || force == 8 ? force : (groups * 4 >= (int64_t)ftk_num_cus() * 8 ? 4 : 8);
+  if (kp == 2) return launch_mfma_kp<F, 2>(a, k, st);
+  if (kp == 4) return launch_mfma_kp<F, 4>(a, k, st);
+  return launch_mfma_kp<F, 8>(a, k, st);
 }
 
 }  // namespace ftk
