@@ -26,6 +26,7 @@
 // The workgroup of the first slot naming an expert owns it and applies it to every
 // token of the chunk that picked it.
 #include <math.h>
+#include <stdlib.h>
 
 #include "ft_device.h"
 #include "ft_internal.h"
@@ -384,27 +385,43 @@ using namespace ftk;
 
 // Direct-route stages for MXFP4 x Q8_K.  Shapes: hidden and inter multiples of
 // 256 (so every workgroup's rows exist); tokens in chunks of up to 8 that fit
-// 64 KiB of LDS.  gate/up: 4 K parts x 2 row groups; down (half the K): 2 K parts x
-// 4 row groups.
-constexpr int MF_KQ_GU = 4, MF_KQ_DN = 2;
+// 64 KiB of LDS.  down: 2 K parts x 4 row groups.
+constexpr int MF_KQ_DN = 2;
 static int fp4_chunk(int64_t k, int nm) {
   int cs = MF_MAXT;
   while (cs > 1 && fp4_lds(cs, k, nm) > 65536) cs /= 2;
   return fp4_lds(cs, k, nm) > 65536 ? 0 : cs;
 }
 
+template <int KQ>
+static hipError_t fp4_gate_up_kq(const MoeArgs& a, int c0, int tc, hipStream_t st) {
+  const dim3 grid((unsigned)(a.inter / (16 * MF_WAVES / KQ)), (unsigned)(tc * a.topk));
+  const size_t p0 = (size_t)c0 * a.topk;
+  hipLaunchKernelGGL(moe_fp4_gate_up_kernel<KQ>, grid, dim3(MF_THREADS), fp4_lds(tc, a.hidden, 2), st,
+                     (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, a.hidden,
+                     a.x + (size_t)c0 * a.hidden, tc, a.ids + p0, a.topk, a.h + p0 * a.inter,
+                     a.g_tap ? a.g_tap + p0 * a.inter : nullptr, a.u_tap ? a.u_tap + p0 * a.inter : nullptr);
+  return hipGetLastError();
+}
+
+// gate/up K parts: 2 (each row's K in two halves: one cache line shared per row)
+// when that still gives two workgroups per CU, else 4 (more workgroups, three
+// shared lines per row; measured at 1 token: 46.4 vs 47.6 us per layer, at 2-8
+// tokens 2 parts win by 5-10%).  FT_MOE_FP4_KQ = 2, 4 or 8 forces it (sweeps).
 hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
+  static const int force = [] {
+    const char* e = getenv("FT_MOE_FP4_KQ");
+    return e ? atoi(e) : 0;
+  }();
   const int cs = fp4_chunk(a.hidden, 2);
   if (cs < 1 || a.hidden % 256 || a.inter % 256) return hipErrorInvalidValue;
   for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
     const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
-    const dim3 grid((unsigned)(a.inter / (16 * MF_WAVES / MF_KQ_GU)), (unsigned)(tc * a.topk));
-    const size_t p0 = (size_t)c0 * a.topk;
-    hipLaunchKernelGGL(moe_fp4_gate_up_kernel<MF_KQ_GU>, grid, dim3(MF_THREADS), fp4_lds(tc, a.hidden, 2), st,
-                       (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, a.hidden,
-                       a.x + (size_t)c0 * a.hidden, tc, a.ids + p0, a.topk, a.h + p0 * a.inter,
-                       a.g_tap ? a.g_tap + p0 * a.inter : nullptr, a.u_tap ? a.u_tap + p0 * a.inter : nullptr);
-    const hipError_t err = hipGetLastError();
+    const int64_t wgs2 = a.inter / (16 * MF_WAVES / 2) * tc * a.topk;
+    const int kq = force == 2 || force == 4 || force == 8 ? force : (wgs2 >= 2 * (int64_t)ftk_num_cus() ? 2 : 4);
+    const hipError_t err = kq == 2   ? fp4_gate_up_kq<2>(a, (int)c0, tc, st)
+                           : kq == 8 ? fp4_gate_up_kq<8>(a, (int)c0, tc, st)
+                                     : fp4_gate_up_kq<4>(a, (int)c0, tc, st);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
