@@ -445,13 +445,14 @@ int ftk_num_cus() {
 }
 
 // Several tokens go to the int8 MFMA kernels (ft_mmvq_mfma.hip) when K is a whole
-// number of 256-element chunks from 4 tokens on (measured: 2 tokens run faster on
-// the dot4 kernels, 4 about even, 8 faster on MFMA); FT_MMVQ_MFMA_MIN_T moves the
+// number of 256-element chunks from 3 tokens on (measured: 2 tokens run faster on
+// the dot4 kernels, which keep 4 token slots from 3 tokens on; 4 and 8 tokens are
+// faster on MFMA); FT_MMVQ_MFMA_MIN_T moves the
 // threshold (tuning sweeps).
 static int mfma_min_t() {
   static const int v = [] {
     const char* e = getenv("FT_MMVQ_MFMA_MIN_T");
-    return e && atoi(e) > 0 ? atoi(e) : 4;
+    return e && atoi(e) > 0 ? atoi(e) : 3;
   }();
   return v;
 }

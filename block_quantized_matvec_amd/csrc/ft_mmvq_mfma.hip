@@ -11,9 +11,9 @@
 //    token's codes in VGPRs and spill from 4 tokens on);
 //  * a workgroup owns 16 rows split over K in KP parts, one wave each; a wave
 //    streams 256-element chunks of its 16 rows and of the activation rows into
-//    its own LDS slice with 16-byte loads (two chunks ahead in VGPRs) and reads
-//    its operands from there; no barrier until the parts are summed, in a fixed
-//    order, through LDS;
+//    its own LDS slice with 16-byte loads (the next chunk in VGPRs while the
+//    current one is computed) and reads its operands from there; no barrier
+//    until the parts are summed, in a fixed order, through LDS;
 //  * per block: D = sum over the block of weight code x activation code (int32,
 //    exact); y += D * (d_w * d_x) (Q8_0, and Q4_0 whose codes enter as n - 8);
 //    Q4_K: y += d_x * (d * sc_j * D - dmin * m_j * S) with S the activation code
@@ -27,18 +27,18 @@ namespace ftk {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int MV_ACB = 288;   // 256 elements of one token's Q8_1 row (8 blocks of 36 bytes)
 constexpr int MV_MAXT = 8;
 
-// bytes of one row's 256-element chunk
-template <int F> struct MvGeo;
-template <> struct MvGeo<FT_Q4_0> { static constexpr int CB = 144; };
-template <> struct MvGeo<FT_Q8_0> { static constexpr int CB = 272; };
-template <> struct MvGeo<FT_Q4_K> { static constexpr int CB = 144; };
+// bytes of one row's CE-element chunk (CE = 256 or 512)
+template <int F, int CE> struct MvGeo;
+template <int CE> struct MvGeo<FT_Q4_0, CE> { static constexpr int CB = 18 * CE / 32; };
+template <int CE> struct MvGeo<FT_Q8_0, CE> { static constexpr int CB = 34 * CE / 32; };
+template <int CE> struct MvGeo<FT_Q4_K, CE> { static constexpr int CB = 144 * CE / 256; };
 
-template <int F> struct MvRegs {
-  static constexpr int NW = (16 * MvGeo<F>::CB / 16 + 63) / 64;   // 16-byte weight pieces per lane
-  static constexpr int NA = (MV_MAXT * MV_ACB / 16 + 63) / 64;    // activation pieces per lane
+template <int F, int CE> struct MvRegs {
+  static constexpr int ACB = 36 * CE / 32;                             // one token's Q8_1 chunk
+  static constexpr int NW = (16 * MvGeo<F, CE>::CB / 16 + 63) / 64;   // 16-byte weight pieces per lane
+  static constexpr int NA = (MV_MAXT * ACB / 16 + 63) / 64;           // activation pieces per lane
   u32x4 w[NW];
   u32x4 a[NA];
 };
@@ -56,19 +56,20 @@ __device__ __forceinline__ float lds_h2f(const uint8_t* base, uint32_t off) {
   return h2f(*(const uint16_t*)(base + off));
 }
 
-template <int F, int KP>
+template <int F, int KP, int CE, int NB>
 __global__ void __launch_bounds__(64 * KP)
 mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t row_bytes,
                  const uint8_t* __restrict__ xq, int64_t xrb, int t, float* __restrict__ y, int64_t ldy) {
-  constexpr int CB = MvGeo<F>::CB, NWP = 16 * CB / 16, SLICE = 16 * CB + MV_MAXT * MV_ACB;
-  using R = MvRegs<F>;
+  using R = MvRegs<F, CE>;
+  constexpr int CB = MvGeo<F, CE>::CB, NWP = 16 * CB / 16, MV_ACB = R::ACB, SLICE = 16 * CB + MV_MAXT * MV_ACB;
+  constexpr int APT = MV_ACB / 16;   // activation pieces per token
   extern __shared__ u32x4 smem4[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint8_t* wl = (uint8_t*)smem4 + wave * SLICE;   // this wave's 16 rows x CB
-  uint8_t* al = wl + 16 * CB;                     // t activation rows x 288
+  uint8_t* al = wl + 16 * CB;                     // t activation rows x MV_ACB
   const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int nch = (int)(k / 256), c0 = wave * nch / KP, c1 = (wave + 1) * nch / KP;
-  const int nap = 18 * t;   // activation pieces per chunk
+  const int nch = (int)(k / CE), c0 = wave * nch / KP, c1 = (wave + 1) * nch / KP;
+  const int nap = APT * t;   // activation pieces per chunk
 
   // Every lane issues every load (pieces past the end, rows past n and chunks past
   // the part re-read valid bytes of the part that are never committed or used), so
@@ -90,7 +91,7 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
     for (int i = 0; i < R::NA; ++i) {
       int p = lane + 64 * i;
       p = p < nap ? p : nap - 1;
-      const int tok = p / 18, off = (p - tok * 18) * 16;
+      const int tok = p / APT, off = (p - tok * APT) * 16;
       r.a[i] = *(const u32x4*)(xq + (int64_t)tok * xrb + (int64_t)c * MV_ACB + off);
     }
   };
@@ -120,7 +121,9 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
 
   auto compute = [&]() {
     if constexpr (F == FT_Q4_K) {
-      const u32x4 hd = *(const u32x4*)(wl + col * CB);
+#pragma unroll
+     for (int sbk = 0; sbk < CE / 256; ++sbk) {
+      const u32x4 hd = *(const u32x4*)(wl + col * CB + 144 * sbk);
       const float d = h2f(hd.x & 0xFFFFu), dmin = h2f(hd.x >> 16);
       uint32_t sc_lo, sc_hi, m_lo, m_hi;
       kq_unpack_scales(hd.y, hd.z, hd.w, sc_lo, sc_hi, m_lo, m_hi);
@@ -129,24 +132,25 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
         const uint32_t sh = 8u * (uint32_t)(j & 3);
         const float dsc = d * (float)(((j < 4 ? sc_lo : sc_hi) >> sh) & 0xFFu);
         const float dmn = dmin * (float)(((j < 4 ? m_lo : m_hi) >> sh) & 0xFFu);
-        const uint64_t q = *(const uint64_t*)(wl + col * CB + 16 + 32 * (j >> 1) + 8 * kq);
+        const uint64_t q = *(const uint64_t*)(wl + col * CB + 144 * sbk + 16 + 32 * (j >> 1) + 8 * kq);
         const uint64_t b = (j & 1) ? (q >> 4) & 0x0F0F0F0F0F0F0F0Full : q & 0x0F0F0F0F0F0F0F0Full;
-        const uint64_t a = arow ? lds_u64(al, (uint32_t)(atok * MV_ACB + 36 * j + 4 + 8 * kq)) : 0ull;
+        const uint64_t a = arow ? lds_u64(al, (uint32_t)(atok * MV_ACB + 288 * sbk + 36 * j + 4 + 8 * kq)) : 0ull;
         const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, zi, 0, 0, 0);
         const v4i S = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)0x0101010101010101ll, zi, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tok = kq + 4 * r;
           if (r < nr && tok < t) {
-            const float dx = lds_h2f(al, (uint32_t)(tok * MV_ACB + 36 * j));
+            const float dx = lds_h2f(al, (uint32_t)(tok * MV_ACB + 288 * sbk + 36 * j));
             acc[r] = fmaf(dx, fmaf(dsc, (float)D[r], -dmn * (float)S[r]), acc[r]);
           }
         }
       }
+     }
     } else {
       constexpr int BB = F == FT_Q8_0 ? 34 : 18;
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
+      for (int blk = 0; blk < CE / 32; ++blk) {
         const uint32_t wb = (uint32_t)(col * CB + BB * blk);
         const float dw = lds_h2f(wl, wb);
         uint64_t b;
@@ -175,18 +179,28 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
     }
   };
 
-  // two register buffers: chunk c is committed to the slice while c + 1 and c + 2
-  // are in flight
-  R ra, rb;
-  fetch(c0, ra);
-  fetch(c0 + 1, rb);
-  for (int c = c0; c < c1; c += 2) {
-    commit(ra);
-    fetch(c + 2, ra);
-    compute();
-    commit(rb);   // past the part's last chunk: committed, never computed
-    fetch(c + 3, rb);
-    if (c + 1 < c1) compute();
+  // NB register buffers: chunk c is committed to the slice while the next NB are in
+  // flight
+  if constexpr (NB == 2) {
+    R ra, rb;
+    fetch(c0, ra);
+    fetch(c0 + 1, rb);
+    for (int c = c0; c < c1; c += 2) {
+      commit(ra);
+      fetch(c + 2, ra);
+      compute();
+      commit(rb);   // past the part's last chunk: committed, never computed
+      fetch(c + 3, rb);
+      if (c + 1 < c1) compute();
+    }
+  } else {
+    R ra;
+    fetch(c0, ra);
+    for (int c = c0; c < c1; ++c) {
+      commit(ra);
+      fetch(c + 1, ra);
+      compute();
+    }
   }
 
   // the KP parts, in order, through LDS (the slices are free now)
@@ -208,28 +222,41 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   }
 }
 
-template <int F, int KP>
+template <int F, int KP, int CE, int NB>
 static hipError_t launch_mfma_kp(const MmvqArgs& a, int64_t k, hipStream_t st) {
-  constexpr int SLICE = 16 * MvGeo<F>::CB + MV_MAXT * MV_ACB;
-  hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP>), dim3((unsigned)((a.n + 15) / 16)), dim3(64 * KP), (size_t)KP * SLICE,
-                     st, (const uint8_t*)a.W, a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq,
+  constexpr int SLICE = 16 * MvGeo<F, CE>::CB + MV_MAXT * MvRegs<F, CE>::ACB;
+  hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP, CE, NB>), dim3((unsigned)((a.n + 15) / 16)), dim3(64 * KP),
+                     (size_t)KP * SLICE, st, (const uint8_t*)a.W, a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq,
                      (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
   return hipGetLastError();
 }
 
+template <int F, int KP>
+static hipError_t launch_mfma_ce(const MmvqArgs& a, int64_t k, int ce, int nb, hipStream_t st) {
+  if (ce == 512) return nb == 2 ? launch_mfma_kp<F, KP, 512, 2>(a, k, st) : launch_mfma_kp<F, KP, 512, 1>(a, k, st);
+  return nb == 2 ? launch_mfma_kp<F, KP, 256, 2>(a, k, st) : launch_mfma_kp<F, KP, 256, 1>(a, k, st);
+}
+
 // K parts per 16 rows: about eight waves per CU (4 parts when there are many
-// rows, else 8); FT_MMVQ_MFMA_KP = 2, 4 or 8 forces it (tuning sweeps)
+// rows, else 8); chunks of 256 elements and one register buffer (measured: 512-
+// element chunks or a second buffer cost more in occupancy than they gain in
+// contiguity).  FT_MMVQ_MFMA_KP = 2, 4 or 8, FT_MMVQ_MFMA_CE = 256 or 512 and
+// FT_MMVQ_MFMA_NB = 1 or 2 force a choice (tuning sweeps).
 template <int F>
 static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
-  static const int force = [] {
-    const char* e = getenv("FT_MMVQ_MFMA_KP");
-    return e ? atoi(e) : 0;
-  }();
+  static const int force_kp = [] { const char* e = getenv("FT_MMVQ_MFMA_KP"); return e ? atoi(e) : 0; }();
+  static const int force_ce = [] { const char* e = getenv("FT_MMVQ_MFMA_CE"); return e ? atoi(e) : 0; }();
+  static const int force_nb = [] { const char* e = getenv("FT_MMVQ_MFMA_NB"); return e ? atoi(e) : 0; }();
   const int64_t groups = (a.n + 15) / 16;
-  const int kp = force == 2 || force == 4 || force == 8 ? force : (groups * 4 >= (int64_t)ftk_num_cus() * 8 ? 4 : 8);
-  if (kp == 2) return launch_mfma_kp<F, 2>(a, k, st);
-  if (kp == 4) return launch_mfma_kp<F, 4>(a, k, st);
-  return launch_mfma_kp<F, 8>(a, k, st);
+  const int kp = force_kp == 2 || force_kp == 4 || force_kp == 8
+                     ? force_kp
+                     : (groups * 4 >= (int64_t)ftk_num_cus() * 8 ? 4 : 8);
+  int ce = force_ce == 256 || force_ce == 512 ? force_ce : 256;
+  if (k % ce) ce = 256;
+  const int nb = force_nb == 1 || force_nb == 2 ? force_nb : 1;
+  if (kp == 2) return launch_mfma_ce<F, 2>(a, k, ce, nb, st);
+  if (kp == 4) return launch_mfma_ce<F, 4>(a, k, ce, nb, st);
+  return launch_mfma_ce<F, 8>(a, k, ce, nb, st);
 }
 
 }  // namespace ftk
