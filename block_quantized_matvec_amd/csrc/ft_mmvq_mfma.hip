@@ -28,8 +28,9 @@ namespace ftk {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int MV_MAXT = 8;
+constexpr int MV_CE = 256;   // elements of a row per chunk
 
-// bytes of one row's CE-element chunk (CE = 256 or 512)
+// bytes of one row's CE-element chunk
 template <int F, int CE> struct MvGeo;
 template <int CE> struct MvGeo<FT_Q4_0, CE> { static constexpr int CB = 18 * CE / 32; };
 template <int CE> struct MvGeo<FT_Q8_0, CE> { static constexpr int CB = 34 * CE / 32; };
@@ -56,10 +57,11 @@ __device__ __forceinline__ float lds_h2f(const uint8_t* base, uint32_t off) {
   return h2f(*(const uint16_t*)(base + off));
 }
 
-template <int F, int KP, int CE, int NB>
+template <int F, int KP>
 __global__ void __launch_bounds__(64 * KP)
 mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t row_bytes,
                  const uint8_t* __restrict__ xq, int64_t xrb, int t, float* __restrict__ y, int64_t ldy) {
+  constexpr int CE = MV_CE;
   using R = MvRegs<F, CE>;
   constexpr int CB = MvGeo<F, CE>::CB, NWP = 16 * CB / 16, MV_ACB = R::ACB, SLICE = 16 * CB + MV_MAXT * MV_ACB;
   constexpr int APT = MV_ACB / 16;   // activation pieces per token
@@ -179,28 +181,13 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
     }
   };
 
-  // NB register buffers: chunk c is committed to the slice while the next NB are in
-  // flight
-  if constexpr (NB == 2) {
-    R ra, rb;
-    fetch(c0, ra);
-    fetch(c0 + 1, rb);
-    for (int c = c0; c < c1; c += 2) {
-      commit(ra);
-      fetch(c + 2, ra);
-      compute();
-      commit(rb);   // past the part's last chunk: committed, never computed
-      fetch(c + 3, rb);
-      if (c + 1 < c1) compute();
-    }
-  } else {
-    R ra;
-    fetch(c0, ra);
-    for (int c = c0; c < c1; ++c) {
-      commit(ra);
-      fetch(c + 1, ra);
-      compute();
-    }
+  // one register buffer: chunk c + 1 is in flight while chunk c is computed
+  R ra;
+  fetch(c0, ra);
+  for (int c = c0; c < c1; ++c) {
+    commit(ra);
+    fetch(c + 1, ra);
+    compute();
   }
 
   // the KP parts, in order, through LDS (the slices are free now)
@@ -222,41 +209,29 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   }
 }
 
-template <int F, int KP, int CE, int NB>
+template <int F, int KP>
 static hipError_t launch_mfma_kp(const MmvqArgs& a, int64_t k, hipStream_t st) {
-  constexpr int SLICE = 16 * MvGeo<F, CE>::CB + MV_MAXT * MvRegs<F, CE>::ACB;
-  hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP, CE, NB>), dim3((unsigned)((a.n + 15) / 16)), dim3(64 * KP),
-                     (size_t)KP * SLICE, st, (const uint8_t*)a.W, a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq,
+  constexpr int SLICE = 16 * MvGeo<F, MV_CE>::CB + MV_MAXT * MvRegs<F, MV_CE>::ACB;
+  hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP>), dim3((unsigned)((a.n + 15) / 16)), dim3(64 * KP), (size_t)KP * SLICE,
+                     st, (const uint8_t*)a.W, a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq,
                      (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
   return hipGetLastError();
 }
 
-template <int F, int KP>
-static hipError_t launch_mfma_ce(const MmvqArgs& a, int64_t k, int ce, int nb, hipStream_t st) {
-  if (ce == 512) return nb == 2 ? launch_mfma_kp<F, KP, 512, 2>(a, k, st) : launch_mfma_kp<F, KP, 512, 1>(a, k, st);
-  return nb == 2 ? launch_mfma_kp<F, KP, 256, 2>(a, k, st) : launch_mfma_kp<F, KP, 256, 1>(a, k, st);
-}
-
 // K parts per 16 rows: about eight waves per CU (4 parts when there are many
-// rows, else 8); chunks of 256 elements and one register buffer (measured: 512-
-// element chunks or a second buffer cost more in occupancy than they gain in
-// contiguity).  FT_MMVQ_MFMA_KP = 2, 4 or 8, FT_MMVQ_MFMA_CE = 256 or 512 and
-// FT_MMVQ_MFMA_NB = 1 or 2 force a choice (tuning sweeps).
+// rows, else 8).  Measured: 512-element chunks or a second register buffer cost
+// more in occupancy than they gain in contiguity.  FT_MMVQ_MFMA_KP = 2, 4 or 8
+// forces the parts (tuning sweeps).
 template <int F>
 static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
   static const int force_kp = [] { const char* e = getenv("FT_MMVQ_MFMA_KP"); return e ? atoi(e) : 0; }();
-  static const int force_ce = [] { const char* e = getenv("FT_MMVQ_MFMA_CE"); return e ? atoi(e) : 0; }();
-  static const int force_nb = [] { const char* e = getenv("FT_MMVQ_MFMA_NB"); return e ? atoi(e) : 0; }();
   const int64_t groups = (a.n + 15) / 16;
   const int kp = force_kp == 2 || force_kp == 4 || force_kp == 8
                      ? force_kp
                      : (groups * 4 >= (int64_t)ftk_num_cus() * 8 ? 4 : 8);
-  int ce = force_ce == 256 || force_ce == 512 ? force_ce : 256;
-  if (k % ce) ce = 256;
-  const int nb = force_nb == 1 || force_nb == 2 ? force_nb : 1;
-  if (kp == 2) return launch_mfma_ce<F, 2>(a, k, ce, nb, st);
-  if (kp == 4) return launch_mfma_ce<F, 4>(a, k, ce, nb, st);
-  return launch_mfma_ce<F, 8>(a, k, ce, nb, st);
+  if (kp == 2) return launch_mfma_kp<F, 2>(a, k, st);
+  if (kp == 4) return launch_mfma_kp<F, 4>(a, k, st);
+  return launch_mfma_kp<F, 8>(a, k, st);
 }
 
 }  // namespace ftk
