@@ -353,30 +353,55 @@ __device__ __forceinline__ constexpr int seg_first(int s) {
   return j0;
 }
 
-// Load the activation codes of unit (block b, unit ui) of one token row.
-// xrow: that token's activation blocks (dword aligned).
+// Load the activation codes of unit (block b, unit ui) of one token row, in two
+// steps: load_act_raw issues the loads only (codes into x, the raw scale bits of
+// each segment parked in bsum), finish_act_unit derives the rest once they have
+// arrived (so that other loads can be issued between the two), and zeroes the
+// unit when !valid.  xrow: that token's activation blocks (dword aligned).
 template <int F, int A>
-__device__ __forceinline__ void load_act_unit(const uint8_t* __restrict__ xrow, int b, int ui, ActUnit<F>& a) {
+__device__ __forceinline__ void load_act_raw(const uint8_t* __restrict__ xrow, int b, int ui, ActUnit<F>& a) {
   constexpr int S = Fmt<F>::S, NW = Fmt<F>::NW;
-#pragma unroll
-  for (int s = 0; s < S; ++s) a.bsum[s] = 0;
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
     const int e = b * Fmt<F>::BLK + Fmt<F>::act_elem(ui, j);
     const int ab = e / Act<A>::BLK, pos = e % Act<A>::BLK;
     a.x[j] = *(const uint32_t*)(xrow + (size_t)ab * Act<A>::BB + 4 + pos);
-    a.bsum[Fmt<F>::seg_of(j)] = dot4(a.x[j], 0x01010101u, a.bsum[Fmt<F>::seg_of(j)]);
   }
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int e = b * Fmt<F>::BLK + Fmt<F>::act_elem(ui, seg_first<F>(s));
     const uint8_t* ab = xrow + (size_t)(e / Act<A>::BLK) * Act<A>::BB;
-    float dx;
-    if (A == FT_Q8_1) dx = h2f(*(const uint16_t*)ab);
-    else dx = *(const float*)ab;
-    a.dxb[s] = dx * (float)a.bsum[s];
-    a.dx[s] = (Fmt<F>::XF1 && s == 1) ? dx * 0.0625f : dx;
+    if (A == FT_Q8_1) a.bsum[s] = (int)*(const uint16_t*)ab;
+    else a.bsum[s] = *(const int*)ab;
   }
+}
+
+template <int F, int A>
+__device__ __forceinline__ void finish_act_unit(ActUnit<F>& a, bool valid) {
+  constexpr int S = Fmt<F>::S, NW = Fmt<F>::NW;
+  float dx[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const float d = A == FT_Q8_1 ? h2f((uint32_t)a.bsum[s]) : __int_as_float(a.bsum[s]);
+    dx[s] = valid ? d : 0.0f;
+    a.bsum[s] = 0;
+  }
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    a.x[j] = valid ? a.x[j] : 0u;
+    a.bsum[Fmt<F>::seg_of(j)] = dot4(a.x[j], 0x01010101u, a.bsum[Fmt<F>::seg_of(j)]);
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    a.dxb[s] = dx[s] * (float)a.bsum[s];
+    a.dx[s] = (Fmt<F>::XF1 && s == 1) ? dx[s] * 0.0625f : dx[s];
+  }
+}
+
+template <int F, int A>
+__device__ __forceinline__ void load_act_unit(const uint8_t* __restrict__ xrow, int b, int ui, ActUnit<F>& a) {
+  load_act_raw<F, A>(xrow, b, ui, a);
+  finish_act_unit<F, A>(a, true);
 }
 
 // true integer dot of segment s from the raw dot D of the unpacked codes
@@ -625,6 +650,39 @@ __device__ __forceinline__ void group_reduce_multi(float (&v)[M], int lane) {
   if constexpr (L >= 8) reduce_level<M, 4>(v, m, lane);
   if constexpr (L >= 4) reduce_level<M, 2>(v, m, lane);
   if constexpr (L >= 2) reduce_level<M, 1>(v, m, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS loads (global_load_lds_dwordx4) and the waits that go with them.
+// One wave-wide call moves 16 bytes per active lane from src (per lane) to
+// lds_base + 16 * lane (lds_base uniform over the wave); no VGPRs hold the data.
+// The load counts in the wave's vmcnt like any global load and its LDS write is
+// done when the count says so.  __syncthreads() would drain every such load
+// (its fence covers LDS writes), so a ring of DMA stages waits with
+// wait_vm<N>() for its own stage and meets at lds_barrier(), whose fence covers
+// only the wave's LDS instructions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 2 /* nt */);
+}
+
+// wait until at most N global loads / stores of this wave are outstanding
+// (gfx9 s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at max)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// workgroup barrier after this wave's LDS reads and writes (lgkmcnt(0)); global
+// loads in flight, DMA or not, stay in flight
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace ftk

@@ -23,9 +23,11 @@ struct MmvqArgs {
 
 struct MmvqPlan {
   int direct;         // 1: LDS-free variant (aligned K-quants), rows_per_wg = rows per wave
+  int wave;           // 1: per-wave LDS ring, rows_per_wg = rows per wave
   int tslot;          // token slots of the kernel (1, 2, 4, 8)
   int lr, p;          // lanes per row, units per lane
   int cpl;            // 16-byte chunks per lane per tile (LDS variant)
+  int stages;         // tiles in the LDS ring (LDS variant; cpl * stages <= 16)
   int rb;             // rows per register batch (direct variant)
   int rows_per_tile, rows_per_wg, grid;
 };

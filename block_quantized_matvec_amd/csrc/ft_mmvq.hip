@@ -4,12 +4,12 @@
 // matvec with quantized activations) and the non-grouped keep-quant op of
 // vllm.cpp PR #523 (What changed).  Design for MI355X:
 //  * Each workgroup (4 waves) owns a contiguous, equal share of the rows and walks
-//    it in tiles of whole rows.  A tile's bytes are contiguous in HBM and are
-//    fetched with fully coalesced 16-byte loads (lane i of the workgroup reads
-//    bytes 16i..16i+15 of each 4 KiB slice), into VGPRs for tile t+1 while tile t
-//    is computed from LDS; then one ds_write_b128 per slice publishes it.  Any
-//    block size or alignment works because lanes read their units back from LDS
-//    at byte granularity.
+//    it in tiles of whole rows.  A tile's bytes are contiguous in HBM; lane i of
+//    the workgroup moves bytes 16i..16i+15 of each 4 KiB slice straight into LDS
+//    (global_load_lds_dwordx4, no VGPRs), into a 64 KiB ring of tile stages, so up
+//    to 64 KiB per workgroup is in flight and a share of up to that size is
+//    requested at kernel start.  Any block size or alignment works because lanes
+//    read their units back from LDS at byte granularity.
 //  * Each lane owns fixed 32-weight units of a row and keeps the matching
 //    activation codes and scales in VGPRs for the whole kernel, so LDS carries
 //    only weight bytes.  Nibble / 6-bit / high-bit unpack happens in registers;
@@ -26,9 +26,24 @@ namespace ftk {
 
 constexpr int MMVQ_THREADS = 256;
 
+// LDS ring per workgroup: S stages of one tile (CPL 16-byte chunks per thread),
+// at most MMVQ_RING_CHUNKS chunks per thread (64 KiB).
+constexpr int MMVQ_RING_CHUNKS = 16;
+constexpr size_t mmvq_lds_bytes(int cpl, int s) {
+  return (size_t)cpl * s * 256 * 16 + 16 + 2 * (256 / 64) * 64 * sizeof(float);
+}
+
+template <int CPL, int S>
+__device__ __forceinline__ void wait_tiles(int k) {   // k later tiles may stay in flight
+  if constexpr (S > 3) if (k >= 3) { wait_vm<3 * CPL>(); return; }
+  if constexpr (S > 2) if (k >= 2) { wait_vm<2 * CPL>(); return; }
+  if constexpr (S > 1) if (k >= 1) { wait_vm<CPL>(); return; }
+  wait_vm<0>();
+}
+
 // LR: lanes per row (64, 128 or 256); P: units per lane; T: token slots;
-// CPL: 16-byte chunks per lane per tile (tile <= CPL * 4 KiB).
-template <int F, int A, int T, int LR, int P, int CPL>
+// CPL: 16-byte chunks per lane per tile (tile <= CPL * 4 KiB); S: ring stages.
+template <int F, int A, int T, int LR, int P, int CPL, int S>
 __global__ void __launch_bounds__(MMVQ_THREADS)
 mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_per_row, int rows_per_wg,
             int rows_per_tile, const uint8_t* __restrict__ xq, int xrow_bytes, int t_real,
@@ -38,9 +53,11 @@ mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_p
   constexpr int RA = T >= 2 ? 1 : 2;          // rows per group per reduction step
   constexpr int M = RA * T;                   // values reduced per step
   constexpr int WPR = LR / 64;                // waves per row
+  constexpr int TB = CPL * MMVQ_THREADS * 16; // bytes per stage
+  static_assert(S >= 2 && S * CPL <= MMVQ_RING_CHUNKS, "");
   extern __shared__ u32x4 smem4[];
-  const uint32_t* smem = (const uint32_t*)smem4;
-  float* red = (float*)(smem4 + CPL * MMVQ_THREADS + 1);
+  uint8_t* ring = (uint8_t*)smem4;
+  float* red = (float*)(ring + S * TB + 16);   // 16 bytes of slack for reads past a row
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -51,27 +68,32 @@ mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_p
   const int wrows = (int)min<int64_t>(rows_per_wg, n - wr0);
   const int ntiles = (wrows + rows_per_tile - 1) / rows_per_tile;
 
-  u32x4 pre[CPL];
-  auto fetch = [&](int tile) {
-    const int64_t r0 = wr0 + (int64_t)tile * rows_per_tile;
+  // tile -> ring stage tile % S, chunk c at byte 16c of the stage.  Every wave
+  // issues exactly CPL loads per tile (chunks past the tile re-read its last
+  // chunk into unused bytes), so the vmcnt arithmetic of wait_tiles holds.  The
+  // prologue fills all S stages; a stage past the last tile (never read) takes
+  // one 16-byte chunk.
+  auto issue = [&](int tile) {
+    const bool real = tile < ntiles;
+    const int64_t r0 = wr0 + (int64_t)(real ? tile : ntiles - 1) * rows_per_tile;
     const int nr = min(rows_per_tile, (int)(wr0 + wrows - r0));
     const int64_t start = r0 * row_bytes, a0 = start & ~(int64_t)15;
-    const int nch = (int)((start + (int64_t)nr * row_bytes - a0 + 15) >> 4);
-    const u32x4* src = (const u32x4*)(W + a0);
+    const int nch = real ? (int)((start + (int64_t)nr * row_bytes - a0 + 15) >> 4) : 1;
+    const uint8_t* src = W + a0;
+    uint8_t* dst = ring + (tile % S) * TB + 1024 * wave;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const int c = i * MMVQ_THREADS + tid;
-      if (c < nch) pre[i] = __builtin_nontemporal_load(src + c);
+      const int c = min(i * MMVQ_THREADS + tid, nch - 1);
+      lds_dma16(src + 16 * (int64_t)c, dst + 4096 * i);
     }
   };
-  auto commit = [&]() {
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) smem4[i * MMVQ_THREADS + tid] = pre[i];
-  };
+  issue(0);
+  asm volatile("" ::: "memory");   // keep the activation loads between the two
 
-  fetch(0);
-
-  // activations of this lane's units (VGPR-resident for the whole kernel)
+  // activations of this lane's units (VGPR-resident for the whole kernel): loaded
+  // unconditionally (idle lanes and token slots read a real unit and are zeroed
+  // afterwards) between the first tile and the rest of the ring, so that waiting
+  // for them does not wait for the ring
   ActUnit<F> act[P][T];
   uint32_t ub[P];
   int uu[P];
@@ -80,25 +102,38 @@ mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_p
   for (int p = 0; p < P; ++p) {
     const int u0 = gl + p * LR;
     uv[p] = u0 < units_per_row;
-    const int u = uv[p] ? u0 : 0;   // idle lanes read a real unit, against zero activations
+    const int u = uv[p] ? u0 : 0;
     ub[p] = (uint32_t)(u / FT::UPB) * FT::BB;
     uu[p] = u % FT::UPB;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      if (uv[p] && t < t_real) load_act_unit<F, A>(xq + (size_t)t * xrow_bytes, u / FT::UPB, uu[p], act[p][t]);
-      else zero_act_unit<F>(act[p][t]);
-    }
+    for (int t = 0; t < T; ++t)
+      load_act_raw<F, A>(xq + (size_t)(t < t_real ? t : 0) * xrow_bytes, u / FT::UPB, uu[p], act[p][t]);
   }
-  commit();
-  __syncthreads();
+  asm volatile("" ::: "memory");
+  int issued = S - 1;   // last tile in flight
+#pragma unroll
+  for (int i = 1; i < S; ++i) issue(i);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<(S - 1) * CPL>();   // the activations (and the first tile) have arrived
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int t = 0; t < T; ++t) finish_act_unit<F, A>(act[p][t], uv[p] && t < t_real);
 
-  const Reader<const uint32_t*> rd{smem};
+  const Reader<const uint32_t*> rd{(const uint32_t*)ring};
   int parity = 0;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    if (tile + 1 < ntiles) fetch(tile + 1);
+  int tile = 0;
+  do {   // ntiles >= 1
+    wait_tiles<CPL, S>(issued - tile);
+    lds_barrier();   // the whole tile has landed; every wave is done with the previous one
+    if (tile >= 1 && tile + S - 1 < ntiles) {
+      issue(tile + S - 1);   // into the previous tile's stage
+      issued = tile + S - 1;
+    }
     const int64_t r0 = wr0 + (int64_t)tile * rows_per_tile;
     const int nr = min(rows_per_tile, (int)(wr0 + wrows - r0));
-    const uint32_t shift = (uint32_t)((r0 * row_bytes) & 15);
+    const uint32_t shift = (uint32_t)((tile % S) * TB) + (uint32_t)((r0 * row_bytes) & 15);
 
     for (int rb = 0; rb < nr; rb += G * RA) {
       float v[M];
@@ -131,7 +166,7 @@ mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_p
       } else {
         float* rp = red + parity * (MMVQ_THREADS / 64) * M;
         if (leader) rp[wave * M + idx] = v[0];
-        __syncthreads();
+        lds_barrier();
         if (gl < M) {
           const int ra = gl / T, t = gl % T;
           const int r = rb + ra * G + grp;
@@ -143,10 +178,126 @@ mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_p
         parity ^= 1;
       }
     }
-    if (tile + 1 < ntiles) {
-      __syncthreads();   // every wave is done reading the tile
-      commit();
-      __syncthreads();
+  } while (++tile < ntiles);
+}
+
+// ---------------------------------------------------------------------------
+// Per-wave ring: every wave owns a contiguous share of the rows and streams it
+// through its own LDS ring of S stages, one 64-unit segment of a row per stage
+// (lane l takes unit l of the segment), waiting only on its own vmcnt: no
+// workgroup barriers, so a wave computes a segment as soon as its bytes have
+// landed and the work left after the last byte arrives is one segment.
+// ---------------------------------------------------------------------------
+template <int F> struct SegGeo {
+  static constexpr int BYTES = 64 / Fmt<F>::UPB * Fmt<F>::BB;   // bytes of 64 units
+  static constexpr int CPW = (BYTES + 15 + 1023) / 1024;         // 16-byte chunks per lane per stage
+};
+template <int F, int S>
+constexpr size_t mmvq_wave_lds_bytes() {
+  return (size_t)(MMVQ_THREADS / 64) * (S * SegGeo<F>::CPW * 1024 + 16);
+}
+
+template <int F, int A, int T, int P, int S>
+__global__ void __launch_bounds__(MMVQ_THREADS)
+mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_per_row, int rows_per_wave,
+                 const uint8_t* __restrict__ xq, int xrow_bytes, int t_real, float* __restrict__ y, int64_t ldy) {
+  using FT = Fmt<F>;
+  constexpr int SEG = SegGeo<F>::BYTES;
+  constexpr int CPW = SegGeo<F>::CPW;
+  constexpr int SB = CPW * 1024;              // bytes per stage
+  constexpr int RA = T >= 2 ? 1 : 2;          // rows per reduction step
+  constexpr int M = RA * T;                   // values reduced per step
+  extern __shared__ u32x4 smem4[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint8_t* ring = (uint8_t*)smem4 + wave * (S * SB + 16);   // 16 bytes of slack past each ring
+
+  const int64_t r0 = ((int64_t)blockIdx.x * (MMVQ_THREADS / 64) + wave) * rows_per_wave;
+  if (r0 >= n) return;   // whole wave; there are no workgroup barriers
+  const int nrows = (int)min<int64_t>(rows_per_wave, n - r0);
+  const int nseg = (units_per_row + 63) >> 6;   // segments per row, <= P
+  const int ntiles = nrows * nseg;
+
+  // tile j = segment (j % nseg) of row (j / nseg), in ring stage j % S.  Every
+  // tile is CPW loads per lane (chunks past the segment re-read its last chunk
+  // into unused bytes; tiles past the share read one chunk), so the vmcnt
+  // arithmetic of wait_tiles holds.
+  int issued = 0, is_row = 0, is_seg = 0;
+  auto issue_next = [&]() {
+    const bool real = issued < ntiles;
+    const int64_t start = (r0 + (real ? is_row : 0)) * (int64_t)row_bytes + (int64_t)is_seg * SEG;
+    const int len = min(SEG, row_bytes - is_seg * SEG);
+    const int64_t a0 = start & ~(int64_t)15;
+    const int nch = real ? (int)((start + len - a0 + 15) >> 4) : 1;
+    uint8_t* dst = ring + (issued % S) * SB;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int c = min(lane + 64 * i, nch - 1);
+      lds_dma16(W + a0 + 16 * (int64_t)c, dst + 1024 * i);
+    }
+    ++issued;
+    if (++is_seg == nseg) { is_seg = 0; ++is_row; }
+  };
+  issue_next();
+  asm volatile("" ::: "memory");   // keep the activation loads between the first tile and the rest
+
+  // activations of this lane's units (VGPR-resident for the whole kernel);
+  // idle lanes read the segment's first unit against zero activations
+  ActUnit<F> act[P][T];
+  const uint32_t ub = (uint32_t)(lane / FT::UPB) * FT::BB;   // unit offset in a full segment
+  const int uu = lane % FT::UPB;
+  bool uv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int u0 = 64 * p + lane;
+    uv[p] = u0 < units_per_row;
+    const int u = uv[p] ? u0 : 0;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      load_act_raw<F, A>(xq + (size_t)(t < t_real ? t : 0) * xrow_bytes, u / FT::UPB, u % FT::UPB, act[p][t]);
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 1; i < S; ++i) issue_next();
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<(S - 1) * CPW>();   // the activations (and the first tile) have arrived
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int t = 0; t < T; ++t) finish_act_unit<F, A>(act[p][t], uv[p] && t < t_real);
+
+  const Reader<const uint32_t*> rd{(const uint32_t*)ring};
+  int cur = 0;   // tiles consumed
+  for (int rp = 0; rp < nrows; rp += RA) {
+    float v[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] = 0.0f;
+#pragma unroll
+    for (int ra = 0; ra < RA; ++ra) {
+      if (rp + ra < nrows) {
+        const int64_t rowb = (r0 + rp + ra) * (int64_t)row_bytes;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          if (p < nseg) {
+            wait_tiles<CPW, S>(issued - 1 - cur);
+            const uint32_t so = (uint32_t)((cur % S) * SB) + (uint32_t)((rowb + (int64_t)p * SEG) & 15);
+            Unit<F> un;
+            unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, so + (uv[p] ? ub : 0u), uv[p] ? uu : 0, un);
+#pragma unroll
+            for (int t = 0; t < T; ++t) v[ra * T + t] = unit_combine<F>(un, act[p][t], v[ra * T + t]);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the stage is read
+            issue_next();   // refill the stage just read
+            ++cur;
+          }
+        }
+      }
+    }
+    group_reduce_multi<M, 64>(v, lane);
+    const int idx = lane / (64 / M);
+    if ((lane % (64 / M)) == 0) {
+      const int ra = idx / T, t = idx % T;
+      if (rp + ra < nrows && t < t_real) y[(int64_t)t * ldy + r0 + rp + ra] = v[0];
     }
   }
 }
@@ -275,13 +426,41 @@ mmvq_direct_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int 
 
 static int num_cus() { return ftk_num_cus(); }
 
-template <int F, int A, int T, int LR, int P, int CPL>
+template <int F, int A, int T, int LR, int P, int CPL, int S>
 static hipError_t launch_mmvq_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
-  const size_t lds = (size_t)CPL * MMVQ_THREADS * 16 + 16 + 2 * (MMVQ_THREADS / 64) * 64 * sizeof(float);
-  hipLaunchKernelGGL((mmvq_kernel<F, A, T, LR, P, CPL>), dim3((unsigned)pl.grid), dim3(MMVQ_THREADS), lds, st,
+  constexpr size_t lds = mmvq_lds_bytes(CPL, S);
+  static const bool attr = hipFuncSetAttribute((const void*)mmvq_kernel<F, A, T, LR, P, CPL, S>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
+  if (!attr) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mmvq_kernel<F, A, T, LR, P, CPL, S>), dim3((unsigned)pl.grid), dim3(MMVQ_THREADS), lds, st,
                      (const uint8_t*)a.W, a.n, a.row_bytes, a.units_per_row, pl.rows_per_wg, pl.rows_per_tile,
                      (const uint8_t*)a.xq, a.xrow_bytes, a.t, a.y, a.ldy);
   return hipGetLastError();
+}
+
+template <int F, int A, int T, int P, int S>
+static hipError_t launch_wave_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
+  constexpr size_t lds = mmvq_wave_lds_bytes<F, S>();
+  static const bool attr = hipFuncSetAttribute((const void*)mmvq_wave_kernel<F, A, T, P, S>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
+  if (!attr) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mmvq_wave_kernel<F, A, T, P, S>), dim3((unsigned)pl.grid), dim3(MMVQ_THREADS), lds, st,
+                     (const uint8_t*)a.W, a.n, a.row_bytes, a.units_per_row, pl.rows_per_wg,
+                     (const uint8_t*)a.xq, a.xrow_bytes, a.t, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+template <int F, int A, int T>
+static hipError_t dispatch_wave(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
+#define FT_WV(PV) \
+  if constexpr (PV * T <= 16) {                                              \
+    if (pl.p == PV && pl.stages == 2) return launch_wave_t<F, A, T, PV, 2>(a, pl, st); \
+    if (pl.p == PV && pl.stages == 3) return launch_wave_t<F, A, T, PV, 3>(a, pl, st); \
+    if (pl.p == PV && pl.stages == 4) return launch_wave_t<F, A, T, PV, 4>(a, pl, st); \
+  }
+  FT_WV(1) FT_WV(2) FT_WV(4) FT_WV(8)
+#undef FT_WV
+  return hipErrorInvalidValue;
 }
 
 template <int F, int A, int T, int P, int RB>
@@ -304,11 +483,11 @@ static hipError_t dispatch_direct(const MmvqArgs& a, const MmvqPlan& pl, hipStre
   return hipErrorInvalidValue;
 }
 
-template <int F, int A, int T, int CPL>
+template <int F, int A, int T, int CPL, int S>
 static hipError_t dispatch_lp(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
 #define FT_LP(LRV, PV)                                                             \
   if constexpr (PV * T <= 16)                                                     \
-    if (pl.lr == LRV && pl.p == PV) return launch_mmvq_t<F, A, T, LRV, PV, CPL>(a, pl, st);
+    if (pl.lr == LRV && pl.p == PV) return launch_mmvq_t<F, A, T, LRV, PV, CPL, S>(a, pl, st);
   FT_LP(64, 1) FT_LP(64, 2) FT_LP(64, 4) FT_LP(64, 8)
   FT_LP(128, 1) FT_LP(128, 2) FT_LP(128, 4) FT_LP(128, 8)
   FT_LP(256, 1) FT_LP(256, 2) FT_LP(256, 4) FT_LP(256, 8)
@@ -318,9 +497,11 @@ static hipError_t dispatch_lp(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t
 
 template <int F, int A, int T>
 static hipError_t dispatch_c(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
+  if (pl.wave) return dispatch_wave<F, A, T>(a, pl, st);
   if (pl.direct) return dispatch_direct<F, A, T>(a, pl, st);
-  if (pl.cpl == 4) return dispatch_lp<F, A, T, 4>(a, pl, st);
-  if (pl.cpl == 8) return dispatch_lp<F, A, T, 8>(a, pl, st);
+  if (pl.cpl == 4 && pl.stages == 2) return dispatch_lp<F, A, T, 4, 2>(a, pl, st);
+  if (pl.cpl == 4 && pl.stages == 4) return dispatch_lp<F, A, T, 4, 4>(a, pl, st);
+  if (pl.cpl == 8 && pl.stages == 2) return dispatch_lp<F, A, T, 8, 2>(a, pl, st);
   return hipErrorInvalidValue;
 }
 
@@ -341,7 +522,8 @@ static hipError_t dispatch_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t 
 // fewest idle lanes, at most 16 unit-token activation sets per lane; a tile is
 // as many whole rows as fit in CPL * 4 KiB and must give every row group a row;
 // the grid is a few workgroups per CU, each owning an equal share of rows.
-// FT_MMVQ_PLAN="lr,p,cpl,wgs_per_cu" forces a plan (tuning sweeps).
+// FT_MMVQ_PLAN="lr,p,cpl,wgs_per_cu,mode,rb,stages" forces a plan (tuning sweeps;
+// 0 = choose).
 static int mmvq_plan_direct(int units_per_row, int tslot, int64_t n, int force_p, int force_rb, int force_wpc,
                             MmvqPlan* out) {
   // units per lane: enough 64-lane passes to cover the row
@@ -367,6 +549,37 @@ static int mmvq_plan_direct(int units_per_row, int tslot, int64_t n, int force_p
   return 1;
 }
 
+// Per-wave ring: units per lane cover the row in 64-unit segments; every wave
+// owns an equal share of the rows.  Measured on the 14336 x 4096 and 4096 x 14336
+// Q4_K / Q8_0 matrices at 1 and 2 tokens (grid of 1..4 workgroups per CU x 2..4
+// stages): rows of one or two segments run best with 2 workgroups per CU and 2
+// stages, longer rows (more activation registers per lane) with 1 workgroup per
+// CU and 4 stages; more waves or deeper rings only add requests in flight.
+static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n, int force_p, int force_wpc,
+                          int force_st, MmvqPlan* out) {
+  int P = 1;
+  while (P * 64 < units_per_row) P *= 2;
+  if (force_p) P = force_p;
+  if (P > 8 || P * 64 < units_per_row || P * tslot > 16) return 0;
+  const int stages = force_st ? force_st : (P >= 4 ? 4 : 2);
+  if (stages < 2 || stages > 4) return 0;
+  int wpc = force_wpc ? force_wpc : (P >= 4 ? 1 : 2);
+  wpc = wpc < 1 ? 1 : (wpc > 10 ? 10 : wpc);
+  const int64_t waves = (int64_t)ftk::num_cus() * wpc * 4;
+  int64_t rpw = (n + waves - 1) / waves;
+  if (rpw < 1) rpw = 1;
+  MmvqPlan pl{};
+  pl.wave = 1;
+  pl.stages = stages;
+  pl.tslot = tslot;
+  pl.p = P;
+  pl.rows_per_wg = (int)rpw;   // rows per wave
+  const int64_t nwaves = (n + rpw - 1) / rpw;
+  pl.grid = (int)((nwaves + 3) / 4);
+  *out = pl;
+  return 1;
+}
+
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out) {
   return ftk_mmvq_plan_fmt(units_per_row, tslot, row_bytes, n, false, out);
 }
@@ -374,10 +587,14 @@ int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPl
 int ftk_mmvq_plan_fmt(int units_per_row, int tslot, int row_bytes, int64_t n, bool aligned_kquant, MmvqPlan* out) {
   MmvqPlan best{};
   double best_cost = 1e30;
-  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0, force_mode = 0, force_rb = 0;
+  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0, force_mode = 0, force_rb = 0, force_st = 0;
   if (const char* e = getenv("FT_MMVQ_PLAN"))
-    sscanf(e, "%d,%d,%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs, &force_mode, &force_rb);
-  // mode 0 and 1: LDS tiles; 2: the direct variant (aligned K-quants only)
+    sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs, &force_mode, &force_rb,
+           &force_st);
+  // mode 0 and 3: per-wave rings; 1: workgroup LDS tiles; 2: the direct variant
+  // (aligned K-quants only)
+  if (force_mode == 0 || force_mode == 3)
+    if (mmvq_plan_wave(units_per_row, tslot, row_bytes, n, force_p, force_wgs, force_st, out)) return 1;
   if (aligned_kquant && force_mode == 2)
     if (mmvq_plan_direct(units_per_row, tslot, n, force_p, force_rb, force_wgs, out)) return 1;
   for (int cpl = 4; cpl <= 8; cpl += 4) {
@@ -409,6 +626,7 @@ int ftk_mmvq_plan_fmt(int units_per_row, int tslot, int row_bytes, int64_t n, bo
   }
   if (!best.lr) return 0;
   best.tslot = tslot;
+  best.stages = best.cpl == 8 ? 2 : (force_st == 2 ? 2 : 4);
   const int wgs_per_cu = force_wgs ? force_wgs : 2;
   const int64_t slots = (int64_t)ftk::num_cus() * wgs_per_cu;
   const int64_t tiles = (n + best.rows_per_tile - 1) / best.rows_per_tile;
