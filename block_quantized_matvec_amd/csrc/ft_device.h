@@ -441,8 +441,8 @@ __device__ __forceinline__ float unit_combine(const Unit<F>& u, const ActUnit<F>
 }
 
 // ---------------------------------------------------------------------------
-// activation quantizers, one block per call (shared by the standalone quantize
-// kernels and the fused prologues of the MoE kernels, so both are bit-identical).
+// activation quantizers (shared by the standalone quantize kernels and the fused
+// prologues of the MoE kernels, so both are bit-identical).
 // amax, d = amax/127 (fp16 for Q8_1, fp32 for Q8_K), q = clamp(round half away
 // from zero of x/d against the stored d, +-127), IEEE correctly rounded division.
 // ---------------------------------------------------------------------------
@@ -450,48 +450,6 @@ __device__ __forceinline__ int q8_code(float v, float d) {
   if (d == 0.0f) return 0;
   const float rq = roundf(v / d);
   return rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
-}
-
-// Q8_1: a half-wave per 32-element block, lane l (0..31) holds element l; every
-// lane of the wave must call it.  ob: the 36-byte block.
-__device__ __forceinline__ void q8_1_block(float v, int l, uint8_t* ob) {
-  float a = fabsf(v);
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 32));
-  uint32_t dh = f2h_bits(a / 127.0f);
-  const float d = h2f(dh);
-  const int q = q8_code(v, d);
-  int s = q;
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) s += __shfl_xor(s, m, 32);
-  ob[4 + l] = (uint8_t)(int8_t)q;
-  if (l == 0) {
-    if (d == 0.0f) dh = 0;
-    const uint32_t sh = f2h_bits(d * (float)s);
-    *(uint32_t*)ob = dh | (sh << 16);
-  }
-}
-
-// Q8_K: a wave per 256-element block, lane holds elements 4*lane .. 4*lane+3;
-// every lane of the wave must call it.  ob: the 292-byte block.
-__device__ __forceinline__ void q8_k_block(const float (&v)[4], int lane, uint8_t* ob) {
-  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
-  const float d = a / 127.0f;
-  uint32_t packed = 0;
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = q8_code(v[i], d);
-    s += q;
-    packed |= ((uint32_t)(uint8_t)(int8_t)q) << (8 * i);
-  }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);  // 16-element group: lanes 4g .. 4g+3
-  *(uint32_t*)(ob + 4 + 4 * lane) = packed;
-  if ((lane & 3) == 0) *(int16_t*)(ob + 260 + 2 * (lane >> 2)) = (int16_t)s;
-  if (lane == 0) *(float*)ob = d;
 }
 
 // ---------------------------------------------------------------------------
@@ -512,9 +470,9 @@ __device__ __forceinline__ float xchg(float v) {
   return __int_as_float(r);
 }
 
-// Block quantizers over several elements per lane, bit-identical to q8_1_block /
-// q8_k_block (same amax, scale, codes and sums; max and integer sums do not
-// depend on the order of reduction).
+// Block quantizers over several elements per lane; the lanes of one block combine
+// their amax (and Q8_1's code sum) with DPP moves.  Max and integer sums do not
+// depend on the order of reduction, so any lane split gives the same block.
 // Q8_1: 4 aligned lanes per 32-element block, lane l4 = 0..3 holds elements
 // 8*l4 .. 8*l4+7.  The 4 lanes call it together; ob: the 36-byte block.
 __device__ __forceinline__ void q8_1_part(const float (&v)[8], int l4, uint8_t* ob) {
@@ -622,8 +580,36 @@ __device__ __forceinline__ int nth_bit(uint32_t m, int j) {
 // (L a power of two <= 64, M <= L).  Afterwards value index i's group total sits
 // in v[0] of lanes (i * L/M) .. (i * L/M + L/M - 1) of the group: each exchange
 // step keeps the half of the values selected by the lane bit it pairs across.
+// v_permlane{32,16}_swap(x, y) hands the lane whose bit S is clear (x_self,
+// x_partner) and the lane whose bit S is set (y_partner, y_self), so with x the
+// value the lower lane keeps and y the one the upper lane keeps, first + second
+// is own + partner in every lane (no select; the sum is the same either order).
+template <int S>
+__device__ __forceinline__ float swap_sum(float x, float y) {
+  static_assert(S == 16 || S == 32, "");
+  uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
+  if constexpr (S == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 template <int M, int S>
 __device__ __forceinline__ void reduce_level(float (&v)[M], int& m, int lane) {
+  if constexpr (S == 16 || S == 32) {
+    if (m > 1) {
+#pragma unroll
+      for (int i = 0; i < M / 2; ++i)
+        if (i < m / 2) v[i] = swap_sum<S>(v[i], v[i + m / 2]);
+      m >>= 1;
+    } else {
+      v[0] = swap_sum<S>(v[0], v[0]);
+    }
+    return;
+  }
   if (m > 1) {
     const bool upper = (lane & S) != 0;
 #pragma unroll

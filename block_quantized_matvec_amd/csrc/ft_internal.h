@@ -24,6 +24,7 @@ struct MmvqArgs {
 struct MmvqPlan {
   int direct;         // 1: LDS-free variant (aligned K-quants), rows_per_wg = rows per wave
   int wave;           // 1: per-wave LDS ring, rows_per_wg = rows per wave
+  int64_t row_stride; // per-wave ring: 1 = contiguous shares, else rows interleaved over the waves
   int tslot;          // token slots of the kernel (1, 2, 4, 8)
   int lr, p;          // lanes per row, units per lane
   int cpl;            // 16-byte chunks per lane per tile (LDS variant)

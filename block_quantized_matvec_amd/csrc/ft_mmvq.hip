@@ -200,7 +200,8 @@ constexpr size_t mmvq_wave_lds_bytes() {
 template <int F, int A, int T, int P, int S>
 __global__ void __launch_bounds__(MMVQ_THREADS)
 mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_per_row, int rows_per_wave,
-                 const uint8_t* __restrict__ xq, int xrow_bytes, int t_real, float* __restrict__ y, int64_t ldy) {
+                 int64_t row_stride, const uint8_t* __restrict__ xq, int xrow_bytes, int t_real,
+                 float* __restrict__ y, int64_t ldy) {
   using FT = Fmt<F>;
   constexpr int SEG = SegGeo<F>::BYTES;
   constexpr int CPW = SegGeo<F>::CPW;
@@ -211,9 +212,13 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint8_t* ring = (uint8_t*)smem4 + wave * (S * SB + 16);   // 16 bytes of slack past each ring
 
-  const int64_t r0 = ((int64_t)blockIdx.x * (MMVQ_THREADS / 64) + wave) * rows_per_wave;
+  // the wave's rows: r0 + i * row_stride, i < nrows (a contiguous share when
+  // row_stride is 1, every row_stride-th row from the wave's index otherwise)
+  const int64_t gw = (int64_t)blockIdx.x * (MMVQ_THREADS / 64) + wave;
+  const int64_t r0 = row_stride == 1 ? gw * rows_per_wave : gw;
   if (r0 >= n) return;   // whole wave; there are no workgroup barriers
-  const int nrows = (int)min<int64_t>(rows_per_wave, n - r0);
+  const int nrows = row_stride == 1 ? (int)min<int64_t>(rows_per_wave, n - r0)
+                                    : (int)((n - r0 + row_stride - 1) / row_stride);
   const int nseg = (units_per_row + 63) >> 6;   // segments per row, <= P
   const int ntiles = nrows * nseg;
 
@@ -224,7 +229,7 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
   int issued = 0, is_row = 0, is_seg = 0;
   auto issue_next = [&]() {
     const bool real = issued < ntiles;
-    const int64_t start = (r0 + (real ? is_row : 0)) * (int64_t)row_bytes + (int64_t)is_seg * SEG;
+    const int64_t start = (r0 + (real ? is_row : 0) * row_stride) * (int64_t)row_bytes + (int64_t)is_seg * SEG;
     const int len = min(SEG, row_bytes - is_seg * SEG);
     const int64_t a0 = start & ~(int64_t)15;
     const int nch = real ? (int)((start + len - a0 + 15) >> 4) : 1;
@@ -275,7 +280,7 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
 #pragma unroll
     for (int ra = 0; ra < RA; ++ra) {
       if (rp + ra < nrows) {
-        const int64_t rowb = (r0 + rp + ra) * (int64_t)row_bytes;
+        const int64_t rowb = (r0 + (rp + ra) * row_stride) * (int64_t)row_bytes;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           if (p < nseg) {
@@ -297,7 +302,7 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
     const int idx = lane / (64 / M);
     if ((lane % (64 / M)) == 0) {
       const int ra = idx / T, t = idx % T;
-      if (rp + ra < nrows && t < t_real) y[(int64_t)t * ldy + r0 + rp + ra] = v[0];
+      if (rp + ra < nrows && t < t_real) y[(int64_t)t * ldy + r0 + (rp + ra) * row_stride] = v[0];
     }
   }
 }
@@ -445,7 +450,7 @@ static hipError_t launch_wave_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
   if (!attr) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((mmvq_wave_kernel<F, A, T, P, S>), dim3((unsigned)pl.grid), dim3(MMVQ_THREADS), lds, st,
-                     (const uint8_t*)a.W, a.n, a.row_bytes, a.units_per_row, pl.rows_per_wg,
+                     (const uint8_t*)a.W, a.n, a.row_bytes, a.units_per_row, pl.rows_per_wg, pl.row_stride,
                      (const uint8_t*)a.xq, a.xrow_bytes, a.t, a.y, a.ldy);
   return hipGetLastError();
 }
@@ -549,21 +554,27 @@ static int mmvq_plan_direct(int units_per_row, int tslot, int64_t n, int force_p
   return 1;
 }
 
-// Per-wave ring: units per lane cover the row in 64-unit segments; every wave
-// owns an equal share of the rows.  Measured on the 14336 x 4096 and 4096 x 14336
-// Q4_K / Q8_0 matrices at 1 and 2 tokens (grid of 1..4 workgroups per CU x 2..4
-// stages): rows of one or two segments run best with 2 workgroups per CU and 2
-// stages, longer rows (more activation registers per lane) with 1 workgroup per
-// CU and 4 stages; more waves or deeper rings only add requests in flight.
+// Per-wave ring: units per lane cover the row in 64-unit segments.  Measured on
+// the 14336 x 4096 and 4096 x 14336 Q4_K / Q8_0 matrices at 1 and 2 tokens (grid
+// of 1..4 workgroups per CU x 2..4 stages, contiguous or interleaved rows): rows
+// of one or two segments run best with 3 workgroups per CU, 2 stages and the rows
+// interleaved over all waves (the waves' requests then stay inside one band of
+// the matrix) once every wave gets at least 4 rows, else with 2 workgroups per CU
+// and contiguous shares; longer rows (more activation registers per lane) with 1
+// workgroup per CU, 4 stages and a contiguous share per wave.  More waves or
+// deeper rings only add requests in flight.
 static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n, int force_p, int force_wpc,
-                          int force_st, MmvqPlan* out) {
+                          int force_st, int force_il, MmvqPlan* out) {
   int P = 1;
   while (P * 64 < units_per_row) P *= 2;
   if (force_p) P = force_p;
   if (P > 8 || P * 64 < units_per_row || P * tslot > 16) return 0;
   const int stages = force_st ? force_st : (P >= 4 ? 4 : 2);
   if (stages < 2 || stages > 4) return 0;
-  int wpc = force_wpc ? force_wpc : (P >= 4 ? 1 : 2);
+  // interleave when every wave of 3 workgroups per CU gets at least 4 rows
+  const bool big = n >= (int64_t)ftk::num_cus() * 3 * 4 * 4;
+  int wpc = force_wpc ? force_wpc : (P >= 4 ? 1 : (big ? 3 : 2));
+  const int il = force_il ? force_il - 1 : (P <= 2 && big);   // FT_MMVQ_PLAN field 8: 1 contiguous, 2 interleaved
   wpc = wpc < 1 ? 1 : (wpc > 10 ? 10 : wpc);
   const int64_t waves = (int64_t)ftk::num_cus() * wpc * 4;
   int64_t rpw = (n + waves - 1) / waves;
@@ -574,7 +585,12 @@ static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n
   pl.tslot = tslot;
   pl.p = P;
   pl.rows_per_wg = (int)rpw;   // rows per wave
-  const int64_t nwaves = (n + rpw - 1) / rpw;
+  int64_t nwaves = (n + rpw - 1) / rpw;
+  pl.row_stride = 1;
+  if (il) {   // interleaved rows over all waves
+    nwaves = waves < n ? waves : n;
+    pl.row_stride = nwaves;
+  }
   pl.grid = (int)((nwaves + 3) / 4);
   *out = pl;
   return 1;
@@ -587,14 +603,15 @@ int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPl
 int ftk_mmvq_plan_fmt(int units_per_row, int tslot, int row_bytes, int64_t n, bool aligned_kquant, MmvqPlan* out) {
   MmvqPlan best{};
   double best_cost = 1e30;
-  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0, force_mode = 0, force_rb = 0, force_st = 0;
+  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0, force_mode = 0, force_rb = 0, force_st = 0,
+      force_il = 0;
   if (const char* e = getenv("FT_MMVQ_PLAN"))
-    sscanf(e, "%d,%d,%d,%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs, &force_mode, &force_rb,
-           &force_st);
+    sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs, &force_mode, &force_rb,
+           &force_st, &force_il);
   // mode 0 and 3: per-wave rings; 1: workgroup LDS tiles; 2: the direct variant
   // (aligned K-quants only)
   if (force_mode == 0 || force_mode == 3)
-    if (mmvq_plan_wave(units_per_row, tslot, row_bytes, n, force_p, force_wgs, force_st, out)) return 1;
+    if (mmvq_plan_wave(units_per_row, tslot, row_bytes, n, force_p, force_wgs, force_st, force_il, out)) return 1;
   if (aligned_kquant && force_mode == 2)
     if (mmvq_plan_direct(units_per_row, tslot, n, force_p, force_rb, force_wgs, out)) return 1;
   for (int cpl = 4; cpl <= 8; cpl += 4) {

@@ -15,33 +15,57 @@
 namespace ftk {
 
 // ---------------------------------------------------------------------------
-// Q8_1: one 32-element block per half-wave, one element per lane
+// Q8_1: four lanes per 32-element block, eight consecutive elements per lane;
+// the block's amax and code sum combine over its four lanes with DPP moves (no
+// LDS round trips on the path).  VEC: x and ldx keep every block 16-byte
+// aligned, so a lane reads its elements with two 16-byte loads.
 // ---------------------------------------------------------------------------
+template <bool VEC>
 __global__ void __launch_bounds__(256)
 quant_q8_1_kernel(const float* __restrict__ x, int64_t total_blocks, int64_t nb, int64_t ldx,
                   uint8_t* __restrict__ xq) {
-  const int64_t gb = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int l = threadIdx.x & 31;
-  if (gb >= total_blocks) return;  // uniform over the half-wave
+  const int64_t gb = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int l4 = threadIdx.x & 3;
+  if (gb >= total_blocks) return;  // uniform over the block's four lanes
   const int64_t r = gb / nb, b = gb % nb;
-  q8_1_block(x[r * ldx + b * 32 + l], l, xq + gb * 36);
+  const float* xp = x + r * ldx + b * 32 + 8 * l4;
+  float v[8];
+  if constexpr (VEC) {
+    const float4 a = ((const float4*)xp)[0], c = ((const float4*)xp)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = xp[j];
+  }
+  q8_1_part(v, l4, xq + gb * 36);
 }
 
 // ---------------------------------------------------------------------------
-// Q8_K: one 256-element block per wave, four consecutive elements per lane
+// Q8_K: sixteen lanes per 256-element block, sixteen consecutive elements per
+// lane (one 16-element code sum each); amax over the sixteen lanes by DPP.
 // ---------------------------------------------------------------------------
+template <bool VEC>
 __global__ void __launch_bounds__(256)
 quant_q8_k_kernel(const float* __restrict__ x, int64_t total_blocks, int64_t nb, int64_t ldx,
                   uint8_t* __restrict__ xq) {
-  const int64_t gb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (gb >= total_blocks) return;  // uniform over the wave
+  const int64_t gb = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gb >= total_blocks) return;  // uniform over the block's sixteen lanes
   const int64_t r = gb / nb, b = gb % nb;
-  const float* xp = x + r * ldx + b * 256 + 4 * lane;
-  float v[4];
+  const float* xp = x + r * ldx + b * 256 + 16 * l16;
+  float v[16];
+  if constexpr (VEC) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = xp[i];
-  q8_k_block(v, lane, xq + gb * 292);
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = ((const float4*)xp)[i];
+      v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = xp[j];
+  }
+  q8_k_part(v, l16, xq + gb * 292);
 }
 
 // ---------------------------------------------------------------------------
@@ -201,16 +225,19 @@ using namespace ftk;
 
 hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
                                hipStream_t st) {
+  const bool vec = ((uintptr_t)x & 15) == 0 && (ldx & 3) == 0;
   if (act == FT_Q8_1) {
     const int64_t total = rows * (k / 32);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_q8_1_kernel, dim3((unsigned)((total + 7) / 8)), dim3(256), 0, st, x, total,
-                       k / 32, ldx, (uint8_t*)xq);
+    const dim3 grid((unsigned)((total + 63) / 64));
+    if (vec) hipLaunchKernelGGL(quant_q8_1_kernel<true>, grid, dim3(256), 0, st, x, total, k / 32, ldx, (uint8_t*)xq);
+    else hipLaunchKernelGGL(quant_q8_1_kernel<false>, grid, dim3(256), 0, st, x, total, k / 32, ldx, (uint8_t*)xq);
   } else {
     const int64_t total = rows * (k / 256);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_q8_k_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, st, x, total,
-                       k / 256, ldx, (uint8_t*)xq);
+    const dim3 grid((unsigned)((total + 15) / 16));
+    if (vec) hipLaunchKernelGGL(quant_q8_k_kernel<true>, grid, dim3(256), 0, st, x, total, k / 256, ldx, (uint8_t*)xq);
+    else hipLaunchKernelGGL(quant_q8_k_kernel<false>, grid, dim3(256), 0, st, x, total, k / 256, ldx, (uint8_t*)xq);
   }
   return hipGetLastError();
 }

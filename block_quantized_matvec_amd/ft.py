@@ -130,11 +130,16 @@ def version() -> str:
 
 
 def quantize_act(act: str, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    _dev(x, "x")
+    """x: (rows, k) fp32 on the device; rows may be strided (row stride -> ldx)."""
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
     rows, k = x.shape
+    if x.stride(1) != 1 or (rows > 1 and x.stride(0) < k):
+        raise ValueError("x must have unit element stride and rows at least k apart")
+    ldx = x.stride(0) if rows > 1 else k
     if out is None:
         out = torch.empty((rows, row_bytes(act, k)), dtype=torch.uint8, device=x.device)
-    _check(lib().ft_quantize_act(TYPES[act], _ptr(x), rows, k, k, _ptr(out), _stream(stream)), "ft_quantize_act")
+    _check(lib().ft_quantize_act(TYPES[act], _ptr(x), rows, k, ldx, _ptr(out), _stream(stream)), "ft_quantize_act")
     return out
 
 

@@ -26,6 +26,21 @@ def test_quantize_bit_exact(act, rows, k):
 
 
 @pytest.mark.parametrize("act", ["Q8_1", "Q8_K"])
+@pytest.mark.parametrize("pad", [1, 3, 4])
+def test_quantize_strided_rows(act, pad):
+    """rows k + pad floats apart (ldx = k + pad): a row stride that is not a
+    multiple of 4 floats takes the scalar-load path of the quantizers"""
+    rows, k = 6, 2048
+    log(f"quantize {act} strided pad={pad}")
+    x = synth.activations(rows, k, synth.rng(102, pad))
+    big = np.zeros((rows, k + pad), dtype=np.float32)
+    big[:, :k] = x
+    xd = dev(big)[:, :k]
+    got = host(ft.quantize_act(act, xd))
+    assert np.array_equal(got, oracle.quantize(act, x))
+
+
+@pytest.mark.parametrize("act", ["Q8_1", "Q8_K"])
 def test_quantize_edge_values(act):
     be = synth.BLOCK[act][0]
     g = synth.rng(101)
