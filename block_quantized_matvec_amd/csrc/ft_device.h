@@ -662,6 +662,16 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
+// a ring of S stages of CPL loads each: wait until the oldest stage has landed
+// while k (<= S - 1) later stages stay in flight
+template <int CPL, int S>
+__device__ __forceinline__ void wait_tiles(int k) {
+  if constexpr (S > 3) if (k >= 3) { wait_vm<3 * CPL>(); return; }
+  if constexpr (S > 2) if (k >= 2) { wait_vm<2 * CPL>(); return; }
+  if constexpr (S > 1) if (k >= 1) { wait_vm<CPL>(); return; }
+  wait_vm<0>();
+}
+
 // workgroup barrier after this wave's LDS reads and writes (lgkmcnt(0)); global
 // loads in flight, DMA or not, stay in flight
 __device__ __forceinline__ void lds_barrier() {

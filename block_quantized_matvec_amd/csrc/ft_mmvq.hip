@@ -33,14 +33,6 @@ constexpr size_t mmvq_lds_bytes(int cpl, int s) {
   return (size_t)cpl * s * 256 * 16 + 16 + 2 * (256 / 64) * 64 * sizeof(float);
 }
 
-template <int CPL, int S>
-__device__ __forceinline__ void wait_tiles(int k) {   // k later tiles may stay in flight
-  if constexpr (S > 3) if (k >= 3) { wait_vm<3 * CPL>(); return; }
-  if constexpr (S > 2) if (k >= 2) { wait_vm<2 * CPL>(); return; }
-  if constexpr (S > 1) if (k >= 1) { wait_vm<CPL>(); return; }
-  wait_vm<0>();
-}
-
 // LR: lanes per row (64, 128 or 256); P: units per lane; T: token slots;
 // CPL: 16-byte chunks per lane per tile (tile <= CPL * 4 KiB); S: ring stages.
 template <int F, int A, int T, int LR, int P, int CPL, int S>
