@@ -71,6 +71,23 @@ def test_mmvq_k_not_whole_chunks(w, n, k, t):
     check_fp32(y, oracle.matvec(w, W, n, k, "Q8_1", xq, t), f"{w} n={n} k={k} t={t}")
 
 
+@pytest.mark.parametrize("w,n,k,t", [
+    ("Q8_0", 96, 16640, 1), ("Q8_0", 96, 16640, 2), ("Q4_0", 130, 16640, 1),   # > 512 units per row
+    ("Q4_0", 200, 4128, 5), ("Q8_0", 70, 4128, 6),                              # 4 segments x 8 token slots
+    ("Q4_K", 40, 32768, 2),                                                     # the largest K: 8 segments
+])
+def test_mmvq_long_rows(w, n, k, t):
+    """Rows or token counts beyond what the per-wave ring holds in registers take the
+    workgroup-tile kernel (Q4_K rows stop at 512 units at the largest K, 32768, and
+    still take the per-wave ring)."""
+    log(f"mmvq long rows {w} n={n} k={k} t={t}")
+    g = synth.rng(205, n, k, t)
+    W = synth.weights(w, n, k, g)
+    xq = oracle.quantize("Q8_1", synth.activations(t, k, g))
+    y = host(ft.mul_mat_vec_q(w, dev(W), n, k, "Q8_1", dev(xq), t))
+    check_fp32(y, oracle.matvec(w, W, n, k, "Q8_1", xq, t), f"{w} n={n} k={k} t={t}")
+
+
 @pytest.mark.parametrize("w,a", MMVQ)
 @pytest.mark.parametrize("t", [1, 2, 8])
 def test_mmvq_extreme_codes(w, a, t):
