@@ -61,7 +61,8 @@ def _args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_decode",
-                    choices=["dense_decode", "q4_0_matvec", "moe_q4k", "moe_mxfp4", "grouped_kq", "counters"])
+                    choices=["dense_decode", "q4_0_matvec", "moe_q4k", "moe_mxfp4", "grouped_kq", "counters",
+                             "ceilings"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies per matrix (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=str, default="", help="comma list overriding the token counts")
@@ -90,7 +91,8 @@ def main():
         sys.exit(1)
     ft.lib()
     fn = {"dense_decode": bench_dense, "q4_0_matvec": bench_q4_0, "moe_q4k": bench_moe,
-          "moe_mxfp4": bench_moe, "grouped_kq": bench_grouped, "counters": run_counters}[args.workload]
+          "moe_mxfp4": bench_moe, "grouped_kq": bench_grouped, "counters": run_counters,
+          "ceilings": lambda a, n, t, f, s: measure_ceilings(t, f)}[args.workload]
     out = fn(args, np, torch, ft, synth)
     print(json.dumps(out), flush=True)
 
@@ -117,6 +119,53 @@ def _graph(torch, fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def measure_ceilings(torch, ft):
+    """Ceilings measured on this part with the library's microkernels, best of 5 timed
+    calls each: a streaming read of 4 GiB (GB/s), the int8 MFMA issue rate of the
+    16x16x32 instruction the kernels use and of gfx950's 16x16x64 one, and the VALU
+    dot4 rate (TOP/s), on 8 workgroups of 256 threads per CU."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        b = float("inf")
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            b = min(b, e0.elapsed_time(e1) / 1e3)
+        return b
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    read = nbytes / best(lambda: ft.debug_ceiling("stream_read", buf, out=out)) / 1e9
+    del buf
+    waves = cus * 8 * 4
+    im, idot = 4096, 16384
+    mfma = waves * im * 8 * 16384 / best(lambda: ft.debug_ceiling("mfma_i8", iters=im, out=out)) / 1e12
+    dot4 = waves * 64 * idot * 8 * 8 / best(lambda: ft.debug_ceiling("dot4", iters=idot, out=out)) / 1e12
+    mfma64 = waves * im * 8 * 32768 / best(lambda: ft.debug_ceiling("mfma_i8_k64", iters=im, out=out)) / 1e12
+    return {"stream_read_GBps": round(read, 1), "mfma_i8_TOPS": round(mfma, 1),
+            "mfma_i8_k64_TOPS": round(mfma64, 1), "dot4_TOPS": round(dot4, 1), "stream_read_bytes": nbytes}
+
+
+def _add_ceilings(out, torch, ft, tops=None):
+    """Attach the measured ceilings and the roofline's fraction of the measured one
+    (stream read for an HBM-bound line; tops: also the int8 MFMA fraction)."""
+    ceil = measure_ceilings(torch, ft)
+    out["ceilings"] = ceil
+    rf = out["roofline"]
+    rf["measured_peak"] = ceil["stream_read_GBps"]
+    rf["frac_of_measured"] = round(rf["achieved"] / ceil["stream_read_GBps"], 4)
+    if tops is not None:
+        rf["mfma_frac_of_measured"] = round(tops / ceil["mfma_i8_TOPS"], 4)
+    return out
 
 
 def _time_graph(torch, g, reps):
@@ -239,6 +288,7 @@ def bench_dense(args, np, torch, ft, synth):
                      "kernel_us": round(h_us, 3), "alg_bytes_per_launch": h_alg},
         "cases": per_case,
     }
+    _add_ceilings(out, torch, ft)
     if not args.no_cpu_baseline:
         import oracle
         xqs = {key: oracle.quantize("Q8_1", v) for key, v in xs.items()}
@@ -295,6 +345,7 @@ def bench_q4_0(args, np, torch, ft, synth):
                      "dequant_us": round(dus, 3),
                      "dequant_GBps": round((W.nbytes + 4 * n * k) / dus / 1e3, 1)},
     }
+    _add_ceilings(out, torch, ft)
     if not args.no_cpu_baseline:
         import oracle
         xqn = oracle.quantize("Q8_1", x.cpu().numpy())
@@ -363,7 +414,7 @@ def bench_moe(args, np, torch, ft, synth):
                      "frac": head["hbm_frac"], "traffic": None},
         "per_tokens": results,
     }
-    return out
+    return _add_ceilings(out, torch, ft)
 
 
 # ---------------------------------------------------------------------------
@@ -409,7 +460,7 @@ def bench_grouped(args, np, torch, ft, synth):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["hbm_frac"], "traffic": None},
         "cases": results,
     }
-    return out
+    return _add_ceilings(out, torch, ft, tops=head["int8_TOPS"])
 
 
 # ---------------------------------------------------------------------------

@@ -401,6 +401,17 @@ ft_status ft_debug_block_dots(ft_type w, const void* W, int64_t n, int64_t k, ft
   return hip_status(ftk_launch_block_dots(w, W, n, k, act, xq, t, partials, hs(stream)));
 }
 
+ft_status ft_debug_ceiling(int which, const void* buf, int64_t bytes, int64_t iters, void* out,
+                           ft_stream_t stream) {
+  if (which < 0 || which > 3 || !out || iters < 0) return FT_ERR_INVALID_ARG;
+  if (which == 0) {
+    if (!buf || bytes < 0 || bytes % 16) return FT_ERR_INVALID_ARG;
+    if (!aligned16(buf)) return FT_ERR_ALIGNMENT;
+    if (bytes == 0) return FT_OK;
+  }
+  return hip_status(ftk_launch_probe(which, buf, bytes, iters, (uint32_t*)out, hs(stream)));
+}
+
 ft_status ft_scratch_reserve(ft_stream_t stream, size_t bytes) {
   void* p = nullptr;
   return pool_get(hs(stream), bytes, &p);

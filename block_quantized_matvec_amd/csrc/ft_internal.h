@@ -39,6 +39,8 @@ hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t);
 hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st);
 
+// measurement microkernels (ft_probe.hip): 0 streaming read, 1 int8 MFMA, 2 dot4
+hipError_t ftk_launch_probe(int which, const void* buf, int64_t bytes, int64_t iters, uint32_t* out, hipStream_t st);
 hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
                                hipStream_t st);
 // Q8_K rows [rows][k/256] -> FP8 halves for the FP4 MFMA, 512 bytes per superblock

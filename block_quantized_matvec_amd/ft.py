@@ -61,6 +61,8 @@ EXPORTS = {
     "ft_debug_block_dots": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_void_p]),
+    "ft_debug_ceiling": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
     "ft_scratch_reserve": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t]),
     "ft_moe_scratch_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
@@ -230,6 +232,23 @@ def debug_block_dots(w: str, W: torch.Tensor, n: int, k: int, act: str, xq: torc
     _check(lib().ft_debug_block_dots(TYPES[w], _ptr(W), n, k, TYPES[act], _ptr(xq), t, _ptr(out),
                                      _stream(stream)), "ft_debug_block_dots")
     return out
+
+
+def debug_ceiling(which: str, buf: torch.Tensor | None = None, iters: int = 0, out: torch.Tensor | None = None,
+                  stream=None) -> None:
+    """Enqueue one measurement microkernel: "stream_read" over buf, "mfma_i8"
+    (K = 32), "mfma_i8_k64" or "dot4" for iters rounds.  out: a device int32 scalar
+    (allocated if None)."""
+    code = {"stream_read": 0, "mfma_i8": 1, "dot4": 2, "mfma_i8_k64": 3}[which]
+    dev = buf.device if buf is not None else torch.device("cuda")
+    if out is None:
+        out = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = 0
+    if buf is not None:
+        _dev(buf, "buf")
+        nbytes = buf.numel() * buf.element_size()
+    _check(lib().ft_debug_ceiling(code, _ptr(buf) if buf is not None else None, nbytes, iters, _ptr(out),
+                                  _stream(stream)), "ft_debug_ceiling")
 
 
 def scratch_reserve(nbytes: int, stream=None) -> None:

@@ -190,6 +190,18 @@ ft_status ft_debug_block_dots(ft_type w, const void* W, int64_t n, int64_t k,
                               ft_type act, const void* xq, int64_t t,
                               int32_t* partials, ft_stream_t stream);
 
+/* Measurement microkernels (not part of the method): the ceilings the hot path is
+   held against, measured on the part next to its published peaks.
+   which = 0: streaming read of `bytes` bytes at `buf` (device, 16-byte aligned,
+   bytes a multiple of 16) with 16-byte loads; which = 1: `iters` rounds of eight
+   independent int8 MFMA chains (v_mfma_i32_16x16x32_i8, 16384 ops each) per wave;
+   which = 2: `iters` rounds of eight independent v_dot4_i32_i8 chains per lane
+   (8 ops per lane each); which = 3: as 1 with v_mfma_i32_16x16x64_i8 (32768 ops
+   each).  1-3 run 8 workgroups of 256 threads per CU and ignore buf/bytes.  out: one device uint32 that receives nothing in practice (it keeps
+   the work live).  The caller times the call. */
+ft_status ft_debug_ceiling(int which, const void* buf, int64_t bytes, int64_t iters, void* out,
+                           ft_stream_t stream);
+
 /* Grow the stream's scratch pool to at least `bytes` [P3 review: grow-only
    per-stream pool].  Call before capturing a graph.  The pool is never shrunk;
    retired buffers are released by ft_shutdown(). */

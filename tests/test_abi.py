@@ -106,6 +106,12 @@ def test_shape_and_pointer_checks():
     # topk out of range for the MoE path
     assert L.ft_moe_q_vec(T["Q4_K"], fake, fake, fake, 4, 256, 256, T["Q8_1"], fake, 1, fake, fake, 9,
                           fake, None, None) == ST["FT_ERR_SHAPE"]
+    # measurement microkernels: unknown kind, NULL output, misaligned or ragged read
+    assert L.ft_debug_ceiling(4, None, 0, 1, fake, None) == ST["FT_ERR_INVALID_ARG"]
+    assert L.ft_debug_ceiling(1, None, 0, 1, None, None) == ST["FT_ERR_INVALID_ARG"]
+    assert L.ft_debug_ceiling(0, odd, 64, 0, fake, None) == ST["FT_ERR_ALIGNMENT"]
+    assert L.ft_debug_ceiling(0, fake, 40, 0, fake, None) == ST["FT_ERR_INVALID_ARG"]
+    assert L.ft_debug_ceiling(0, fake, 0, 0, fake, None) == 0   # empty read: no launch
 
 
 def test_moe_route_options_refused_on_host():
