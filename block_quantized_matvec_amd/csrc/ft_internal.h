@@ -22,18 +22,15 @@ struct MmvqArgs {
 };
 
 struct MmvqPlan {
-  int direct;         // 1: LDS-free variant (aligned K-quants), rows_per_wg = rows per wave
   int wave;           // 1: per-wave LDS ring, rows_per_wg = rows per wave
   int64_t row_stride; // per-wave ring: 1 = contiguous shares, else rows interleaved over the waves
   int tslot;          // token slots of the kernel (1, 2, 4, 8)
   int lr, p;          // lanes per row, units per lane
   int cpl;            // 16-byte chunks per lane per tile (LDS variant)
   int stages;         // tiles in the LDS ring (LDS variant; cpl * stages <= 16)
-  int rb;             // rows per register batch (direct variant)
   int rows_per_tile, rows_per_wg, grid;
 };
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out);
-int ftk_mmvq_plan_fmt(int units_per_row, int tslot, int row_bytes, int64_t n, bool aligned_kquant, MmvqPlan* out);
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
 // int8-MFMA matvec for 2..8 tokens (K % 256 == 0; Q4_0, Q8_0, Q4_K x Q8_1)
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t);

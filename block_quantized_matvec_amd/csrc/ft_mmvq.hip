@@ -299,126 +299,6 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
   }
 }
 
-// ---------------------------------------------------------------------------
-// Direct variant for the 16-byte-aligned K-quant formats (Q4_K, Q5_K): no LDS and
-// no barriers.  Every wave owns a contiguous range of rows; lane l takes units
-// l, l+64, ... of each row and loads their bytes straight into VGPRs with 16-byte
-// loads (the header once per lane, then the unit's 32 nibble bytes; a wave's loads
-// of one row cover its bytes contiguously).  Two register batches of RB rows
-// alternate: the next batch is in flight while the current one is computed.
-// ---------------------------------------------------------------------------
-template <int F> struct Raw;
-template <> struct Raw<FT_Q4_K> { u32x4 h, q0, q1; };
-template <> struct Raw<FT_Q5_K> { u32x4 h, q0, q1, e0, e1; };
-
-template <int F>
-__device__ __forceinline__ void raw_load(const uint8_t* __restrict__ row, uint32_t boff, int c, Raw<F>& r) {
-  const u32x4* b = (const u32x4*)(row + boff);
-  r.h = __builtin_nontemporal_load(b);
-  if constexpr (F == FT_Q4_K) {
-    r.q0 = __builtin_nontemporal_load(b + 1 + 2 * c);
-    r.q1 = __builtin_nontemporal_load(b + 2 + 2 * c);
-  } else {
-    r.e0 = __builtin_nontemporal_load(b + 1);
-    r.e1 = __builtin_nontemporal_load(b + 2);
-    r.q0 = __builtin_nontemporal_load(b + 3 + 2 * c);
-    r.q1 = __builtin_nontemporal_load(b + 4 + 2 * c);
-  }
-}
-
-template <int F>
-__device__ __forceinline__ void raw_unit(const Raw<F>& r, int c, Unit<F>& u) {
-  const uint32_t h[4] = {r.h.x, r.h.y, r.h.z, r.h.w};
-  const uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
-  uint32_t qh[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if constexpr (F == FT_Q5_K) {
-    qh[0] = r.e0.x; qh[1] = r.e0.y; qh[2] = r.e0.z; qh[3] = r.e0.w;
-    qh[4] = r.e1.x; qh[5] = r.e1.y; qh[6] = r.e1.z; qh[7] = r.e1.w;
-  }
-  kq_unit<F>(h, q, qh, c, u);
-}
-
-template <int F, int A, int T, int P, int RB>
-__global__ void __launch_bounds__(MMVQ_THREADS)
-mmvq_direct_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_per_row,
-                   int rows_per_wave, const uint8_t* __restrict__ xq, int xrow_bytes, int t_real,
-                   float* __restrict__ y, int64_t ldy) {
-  using FT = Fmt<F>;
-  constexpr int M = RB * T;
-  static_assert(M <= 64, "");
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * (MMVQ_THREADS / 64) + (threadIdx.x >> 6);
-  const int64_t r0 = gw * rows_per_wave;
-  if (r0 >= n) return;   // whole wave; there are no workgroup barriers
-  const int64_t r1 = min<int64_t>(r0 + rows_per_wave, n);
-
-  uint32_t boff[P];
-  int cc[P];
-  bool uv[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int u0 = lane + 64 * p;
-    uv[p] = u0 < units_per_row;
-    const int u = uv[p] ? u0 : 0;
-    boff[p] = (uint32_t)(u / FT::UPB) * FT::BB;
-    cc[p] = u % FT::UPB;
-  }
-  Raw<F> ra[RB][P], rb[RB][P];
-  // rows past the range re-read the last row (always valid) and are not stored
-  auto load = [&](Raw<F> (&dst)[RB][P], int64_t rs) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int64_t row = min<int64_t>(rs + i, r1 - 1);
-      const uint8_t* rp = W + row * row_bytes;
-#pragma unroll
-      for (int p = 0; p < P; ++p) raw_load<F>(rp, boff[p], cc[p], dst[i][p]);
-    }
-  };
-  load(ra, r0);
-
-  ActUnit<F> act[P][T];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int u = uv[p] ? lane + 64 * p : 0;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      if (uv[p] && t < t_real) load_act_unit<F, A>(xq + (size_t)t * xrow_bytes, u / FT::UPB, u % FT::UPB, act[p][t]);
-      else zero_act_unit<F>(act[p][t]);
-    }
-  }
-
-  auto compute = [&](Raw<F> (&src)[RB][P], int64_t rs) {
-    float v[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) v[i] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        Unit<F> un;
-        raw_unit<F>(src[i][p], cc[p], un);
-#pragma unroll
-        for (int t = 0; t < T; ++t) v[i * T + t] = unit_combine<F>(un, act[p][t], v[i * T + t]);
-      }
-    }
-    group_reduce_multi<M, 64>(v, lane);
-    const int idx = lane / (64 / M);
-    if ((lane % (64 / M)) == 0) {
-      const int i = idx / T, t = idx % T;
-      const int64_t row = rs + i;
-      if (row < r1 && t < t_real) y[(int64_t)t * ldy + row] = v[0];
-    }
-  };
-
-  for (int64_t rs = r0; rs < r1; rs += 2 * RB) {
-    load(rb, rs + RB);
-    compute(ra, rs);
-    if (rs + RB >= r1) break;
-    load(ra, rs + 2 * RB);
-    compute(rb, rs + RB);
-  }
-}
-
 // host side -------------------------------------------------------------------
 
 static int num_cus() { return ftk_num_cus(); }
@@ -460,26 +340,6 @@ static hipError_t dispatch_wave(const MmvqArgs& a, const MmvqPlan& pl, hipStream
   return hipErrorInvalidValue;
 }
 
-template <int F, int A, int T, int P, int RB>
-static hipError_t launch_direct_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_direct_kernel<F, A, T, P, RB>), dim3((unsigned)pl.grid), dim3(MMVQ_THREADS), 0, st,
-                     (const uint8_t*)a.W, a.n, a.row_bytes, a.units_per_row, pl.rows_per_wg,
-                     (const uint8_t*)a.xq, a.xrow_bytes, a.t, a.y, a.ldy);
-  return hipGetLastError();
-}
-
-template <int F, int A, int T>
-static hipError_t dispatch_direct(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
-  if constexpr (F == FT_Q4_K || F == FT_Q5_K) {
-#define FT_DR(PV, RBV)                                                                  \
-    if constexpr (PV * T * RBV <= 16)                                                   \
-      if (pl.p == PV && pl.rb == RBV) return launch_direct_t<F, A, T, PV, RBV>(a, pl, st);
-    FT_DR(1, 1) FT_DR(1, 2) FT_DR(1, 4) FT_DR(2, 1) FT_DR(2, 2) FT_DR(4, 1) FT_DR(4, 2) FT_DR(8, 1)
-#undef FT_DR
-  }
-  return hipErrorInvalidValue;
-}
-
 template <int F, int A, int T, int CPL, int S>
 static hipError_t dispatch_lp(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
 #define FT_LP(LRV, PV)                                                             \
@@ -495,7 +355,6 @@ static hipError_t dispatch_lp(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t
 template <int F, int A, int T>
 static hipError_t dispatch_c(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t st) {
   if (pl.wave) return dispatch_wave<F, A, T>(a, pl, st);
-  if (pl.direct) return dispatch_direct<F, A, T>(a, pl, st);
   if (pl.cpl == 4 && pl.stages == 2) return dispatch_lp<F, A, T, 4, 2>(a, pl, st);
   if (pl.cpl == 4 && pl.stages == 4) return dispatch_lp<F, A, T, 4, 4>(a, pl, st);
   if (pl.cpl == 8 && pl.stages == 2) return dispatch_lp<F, A, T, 8, 2>(a, pl, st);
@@ -519,33 +378,9 @@ static hipError_t dispatch_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t 
 // fewest idle lanes, at most 16 unit-token activation sets per lane; a tile is
 // as many whole rows as fit in CPL * 4 KiB and must give every row group a row;
 // the grid is a few workgroups per CU, each owning an equal share of rows.
-// FT_MMVQ_PLAN="lr,p,cpl,wgs_per_cu,mode,rb,stages" forces a plan (tuning sweeps;
-// 0 = choose).
-static int mmvq_plan_direct(int units_per_row, int tslot, int64_t n, int force_p, int force_rb, int force_wpc,
-                            MmvqPlan* out) {
-  // units per lane: enough 64-lane passes to cover the row
-  int P = 1;
-  while (P * 64 < units_per_row) P *= 2;
-  if (force_p) P = force_p;
-  if (P > 8 || P * 64 < units_per_row) return 0;
-  int rb = force_rb ? force_rb : (P * tslot <= 2 ? 2 : 1);
-  if (P * tslot * rb > 16) return 0;
-  const int waves_per_cu = force_wpc ? force_wpc : 8;
-  const int64_t waves = (int64_t)ftk::num_cus() * waves_per_cu;
-  int64_t rpw = (n + waves - 1) / waves;
-  if (rpw < 1) rpw = 1;
-  MmvqPlan pl{};
-  pl.direct = 1;
-  pl.tslot = tslot;
-  pl.p = P;
-  pl.rb = rb;
-  pl.rows_per_wg = (int)rpw;   // rows per wave in the direct variant
-  const int64_t nwaves = (n + rpw - 1) / rpw;
-  pl.grid = (int)((nwaves + 3) / 4);
-  *out = pl;
-  return 1;
-}
-
+// FT_MMVQ_PLAN="lr,p,cpl,wgs_per_cu,mode,-,stages,rows" forces a plan (tuning
+// sweeps; 0 = choose; mode 1 = workgroup tiles, 3 = per-wave rings; rows 1 =
+// contiguous shares, 2 = interleaved).
 // Per-wave ring: units per lane cover the row in 64-unit segments.  Measured on
 // the 14336 x 4096 and 4096 x 14336 Q4_K / Q8_0 matrices at 1 and 2 tokens (grid
 // of 1..4 workgroups per CU x 2..4 stages, contiguous or interleaved rows): rows
@@ -589,23 +424,16 @@ static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n
 }
 
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out) {
-  return ftk_mmvq_plan_fmt(units_per_row, tslot, row_bytes, n, false, out);
-}
-
-int ftk_mmvq_plan_fmt(int units_per_row, int tslot, int row_bytes, int64_t n, bool aligned_kquant, MmvqPlan* out) {
   MmvqPlan best{};
   double best_cost = 1e30;
-  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0, force_mode = 0, force_rb = 0, force_st = 0,
+  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0, force_mode = 0, unused = 0, force_st = 0,
       force_il = 0;
   if (const char* e = getenv("FT_MMVQ_PLAN"))
-    sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs, &force_mode, &force_rb,
+    sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs, &force_mode, &unused,
            &force_st, &force_il);
-  // mode 0 and 3: per-wave rings; 1: workgroup LDS tiles; 2: the direct variant
-  // (aligned K-quants only)
+  // mode 0 and 3: per-wave rings; 1: workgroup LDS tiles
   if (force_mode == 0 || force_mode == 3)
     if (mmvq_plan_wave(units_per_row, tslot, row_bytes, n, force_p, force_wgs, force_st, force_il, out)) return 1;
-  if (aligned_kquant && force_mode == 2)
-    if (mmvq_plan_direct(units_per_row, tslot, n, force_p, force_rb, force_wgs, out)) return 1;
   for (int cpl = 4; cpl <= 8; cpl += 4) {
     if (force_cpl && cpl != force_cpl) continue;
     const int rt = (cpl * 4096 - 15) / row_bytes;
@@ -652,7 +480,7 @@ static hipError_t launch_fa(MmvqArgs a, int64_t k, hipStream_t st) {
   const int tslot = a.t <= 1 ? 1 : a.t <= 2 ? 2 : a.t <= 4 ? 4 : 8;
   a.units_per_row = (int)units_in_row<F>(k);
   MmvqPlan pl;
-  if (!ftk_mmvq_plan_fmt(a.units_per_row, tslot, a.row_bytes, a.n, F == FT_Q4_K || F == FT_Q5_K, &pl))
+  if (!ftk_mmvq_plan(a.units_per_row, tslot, a.row_bytes, a.n, &pl))
     return hipErrorInvalidValue;
   return dispatch_t<F, A>(a, pl, st);
 }
