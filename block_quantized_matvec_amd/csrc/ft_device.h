@@ -135,6 +135,11 @@ __device__ __forceinline__ float e8m0_half(uint32_t e) {
   uint32_t bits = e >= 2 ? (e - 1) << 23 : (0x00400000u >> (1 - e));
   return __uint_as_float(bits);
 }
+// Index of the calling wave in its workgroup, as a wave-uniform (SGPR) value.  The
+// compiler cannot tell that threadIdx.x / 64 is the same in every lane; anything
+// derived from it (row shares, loop bounds, load addresses) would otherwise be
+// per-lane VALU work under exec-masked branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }

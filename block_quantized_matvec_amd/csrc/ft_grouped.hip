@@ -218,7 +218,7 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
   const int p0 = offsets[e], p1 = offsets[e + 1];
   if (p0 >= p1) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int q = lane >> 4, rl = lane & 15;
   const int64_t wrow0 = tile * (OROWS * GM_WAVES) + (int64_t)wave * OROWS;   // first output row of this wave
   const uint8_t* wexp = W + (int64_t)e * n * row_bytes;

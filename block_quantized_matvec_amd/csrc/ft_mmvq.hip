@@ -201,7 +201,7 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
   constexpr int RA = T >= 2 ? 1 : 2;          // rows per reduction step
   constexpr int M = RA * T;                   // values reduced per step
   extern __shared__ u32x4 smem4[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   uint8_t* ring = (uint8_t*)smem4 + wave * (S * SB + 16);   // 16 bytes of slack past each ring
 
   // the wave's rows: r0 + i * row_stride, i < nrows (a contiguous share when
@@ -216,23 +216,33 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
 
   // tile j = segment (j % nseg) of row (j / nseg), in ring stage j % S.  Every
   // tile is CPW loads per lane (chunks past the segment re-read its last chunk
-  // into unused bytes; tiles past the share read one chunk), so the vmcnt
-  // arithmetic of wait_tiles holds.
-  int issued = 0, is_row = 0, is_seg = 0;
+  // into unused bytes; tiles past the share re-read the first chunk of the share),
+  // so the vmcnt arithmetic of wait_tiles holds.  The bookkeeping is wave-uniform
+  // (scalar): running byte offsets, no multiplies per tile.
+  const int64_t row_step = row_stride * (int64_t)row_bytes;
+  const int64_t first_a0 = (r0 * (int64_t)row_bytes) & ~(int64_t)15;
+  const int last_len = row_bytes - (nseg - 1) * SEG;   // bytes of a row's last segment
+  int64_t is_base = r0 * (int64_t)row_bytes;            // row of the next tile to issue
+  int issued = 0, is_seg = 0, is_stage = 0;
+  int c_nch = -1;          // chunk count the lane offsets below were made for
+  uint32_t c_off[CPW];     // byte offset of this lane's chunk i: 16 * min(lane + 64 i, nch - 1)
   auto issue_next = [&]() {
     const bool real = issued < ntiles;
-    const int64_t start = (r0 + (real ? is_row : 0) * row_stride) * (int64_t)row_bytes + (int64_t)is_seg * SEG;
-    const int len = min(SEG, row_bytes - is_seg * SEG);
-    const int64_t a0 = start & ~(int64_t)15;
-    const int nch = real ? (int)((start + len - a0 + 15) >> 4) : 1;
-    uint8_t* dst = ring + (issued % S) * SB;
+    const int64_t start = is_base + is_seg * SEG;
+    const int64_t a0 = real ? start & ~(int64_t)15 : first_a0;
+    const int nch = real ? ((int)(start & 15) + (is_seg == nseg - 1 ? last_len : SEG) + 15) >> 4 : 1;
+    if (nch != c_nch) {    // uniform; rows of 16-byte multiples keep one count
+      c_nch = nch;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int c = min(lane + 64 * i, nch - 1);
-      lds_dma16(W + a0 + 16 * (int64_t)c, dst + 1024 * i);
+      for (int i = 0; i < CPW; ++i) c_off[i] = 16u * (uint32_t)min(lane + 64 * i, nch - 1);
     }
+    uint8_t* dst = ring + is_stage * SB;
+    const uint8_t* src = W + a0;   // uniform base, 32-bit lane offsets
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) lds_dma16(src + c_off[i], dst + 1024 * i);
     ++issued;
-    if (++is_seg == nseg) { is_seg = 0; ++is_row; }
+    is_stage = is_stage + 1 == S ? 0 : is_stage + 1;
+    if (++is_seg == nseg) { is_seg = 0; is_base += row_step; }
   };
   issue_next();
   asm volatile("" ::: "memory");   // keep the activation loads between the first tile and the rest
@@ -264,7 +274,8 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
     for (int t = 0; t < T; ++t) finish_act_unit<F, A>(act[p][t], uv[p] && t < t_real);
 
   const Reader<const uint32_t*> rd{(const uint32_t*)ring};
-  int cur = 0;   // tiles consumed
+  int cur = 0, cs_stage = 0;                             // tiles consumed, stage of the next one
+  uint32_t cs_off = (uint32_t)(r0 * (int64_t)row_bytes);   // low bits of the consumed row's offset
   for (int rp = 0; rp < nrows; rp += RA) {
     float v[M];
 #pragma unroll
@@ -272,12 +283,11 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
 #pragma unroll
     for (int ra = 0; ra < RA; ++ra) {
       if (rp + ra < nrows) {
-        const int64_t rowb = (r0 + (rp + ra) * row_stride) * (int64_t)row_bytes;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           if (p < nseg) {
             wait_tiles<CPW, S>(issued - 1 - cur);
-            const uint32_t so = (uint32_t)((cur % S) * SB) + (uint32_t)((rowb + (int64_t)p * SEG) & 15);
+            const uint32_t so = (uint32_t)(cs_stage * SB) + ((cs_off + (uint32_t)(p * SEG)) & 15u);
             Unit<F> un;
             unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, so + (uv[p] ? ub : 0u), uv[p] ? uu : 0, un);
 #pragma unroll
@@ -286,8 +296,10 @@ mmvq_wave_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int un
             __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the stage is read
             issue_next();   // refill the stage just read
             ++cur;
+            cs_stage = cs_stage + 1 == S ? 0 : cs_stage + 1;
           }
         }
+        cs_off += (uint32_t)row_step;
       }
     }
     group_reduce_multi<M, 64>(v, lane);
@@ -500,10 +512,12 @@ int ftk_num_cus() {
 }
 
 // Several tokens go to the int8 MFMA kernels (ft_mmvq_mfma.hip) when K is a whole
-// number of 256-element chunks from 3 tokens on (measured: 2 tokens run faster on
-// the dot4 kernels, which keep 4 token slots from 3 tokens on; 4 and 8 tokens are
-// faster on MFMA); FT_MMVQ_MFMA_MIN_T moves the
-// threshold (tuning sweeps).
+// number of 256-element chunks from 3 tokens on, except 3-4 tokens on rows of at
+// most 128 units, which the per-wave dot4 ring (4 token slots) runs faster.
+// Measured (14336 x 4096 / 4096 x 14336): 2 tokens are faster on dot4 everywhere;
+// 4 tokens on dot4 vs MFMA: Q8_0 13.6 vs 17.3 us and Q4_K 11.3 vs 11.7 us at K =
+// 4096, but Q4_K 16.2 vs 13.1 us at K = 14336; 8 tokens are faster on MFMA.
+// FT_MMVQ_MFMA_MIN_T moves the token threshold (tuning sweeps).
 static int mfma_min_t() {
   static const int v = [] {
     const char* e = getenv("FT_MMVQ_MFMA_MIN_T");
@@ -512,9 +526,20 @@ static int mfma_min_t() {
   return v;
 }
 
+static int64_t units_of(int w, int64_t k) {
+  switch (w) {
+    case FT_Q4_0: return ftk::units_in_row<FT_Q4_0>(k);
+    case FT_Q8_0: return ftk::units_in_row<FT_Q8_0>(k);
+    case FT_Q4_K: return ftk::units_in_row<FT_Q4_K>(k);
+    default: return 0;
+  }
+}
+
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;
-  if (a.t >= mfma_min_t() && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t)) return ftk_launch_mmvq_mfma(a, k, st);
+  const bool dot4_short = a.t <= 4 && units_of(a.w, k) <= 128;
+  if (a.t >= mfma_min_t() && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t) && !dot4_short)
+    return ftk_launch_mmvq_mfma(a, k, st);
   if (a.act == FT_Q8_1) {
     switch (a.w) {
       case FT_Q4_0: return launch_fa<FT_Q4_0, FT_Q8_1>(a, k, st);

@@ -55,7 +55,7 @@ route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk
   __shared__ uint32_t s_key[4][8];
   __shared__ int s_idx[4][8];
   __shared__ float s_ex[4][8];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
   if (tok >= t) return;
   const float* l = logits + tok * n_expert;
@@ -144,7 +144,7 @@ __device__ __forceinline__ int clamp_e(int e, int n_expert) {
 // Returns the total in every thread.  Needs wsum[SORT_THREADS / 64 + 1] in LDS.
 template <typename G, typename P>
 __device__ __forceinline__ int block_exclusive_scan(int n, int* wsum, G get, P put) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   constexpr int NW = SORT_THREADS / 64;
   const int per = (n + SORT_THREADS - 1) / SORT_THREADS;
   const int i0 = tid * per;

@@ -185,7 +185,7 @@ __device__ __forceinline__ void fp4_rows(const uint32_t* const (&rowd)[NM], int 
 // returns true in the waves of part 0, whose acc then holds the totals.
 template <int NM, int KQ>
 __device__ __forceinline__ bool fp4_reduce(v4f (&acc)[NM], float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   float* mine = red + ((size_t)wave * 64 + lane) * (NM * 4);
 #pragma unroll
   for (int m = 0; m < NM; ++m) *(v4f*)(mine + 4 * m) = acc[m];
@@ -217,7 +217,7 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   extern __shared__ u32x4 smem4[];
   uint8_t* act = (uint8_t*)smem4;                           // [t_real][2 * hidden]
   float* dx = (float*)(act + (size_t)t_real * 2 * hidden);  // [hidden / 256][16]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   int e;
   uint32_t mask;
   uint64_t smask;
@@ -296,7 +296,7 @@ moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hi
   extern __shared__ u32x4 smem4[];
   uint8_t* act = (uint8_t*)smem4;                          // [t_real][2 * inter]
   float* dx = (float*)(act + (size_t)t_real * 2 * inter);  // [inter / 256][16]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   int e;
   uint32_t mask;
   uint64_t smask;
