@@ -394,26 +394,43 @@ static hipError_t dispatch_t(const MmvqArgs& a, const MmvqPlan& pl, hipStream_t 
 // sweeps; 0 = choose; mode 1 = workgroup tiles, 3 = per-wave rings; rows 1 =
 // contiguous shares, 2 = interleaved).
 // Per-wave ring: units per lane cover the row in 64-unit segments.  Measured on
-// the 14336 x 4096 and 4096 x 14336 Q4_K / Q8_0 matrices at 1 and 2 tokens (grid
-// of 1..4 workgroups per CU x 2..4 stages, contiguous or interleaved rows): rows
-// of one or two segments run best with 3 workgroups per CU, 2 stages and the rows
-// interleaved over all waves (the waves' requests then stay inside one band of
-// the matrix) once every wave gets at least 4 rows, else with 2 workgroups per CU
-// and contiguous shares; longer rows (more activation registers per lane) with 1
-// workgroup per CU, 4 stages and a contiguous share per wave.  More waves or
-// deeper rings only add requests in flight.
+// the 14336 x 4096 and 4096 x 14336 Q4_K / Q8_0 matrices at 1, 2 and 4 tokens
+// (grid of 1..4 workgroups per CU x 2..4 stages, contiguous or interleaved rows):
+// rows of one or two segments run best with the rows interleaved over all waves
+// (the waves' requests then stay inside one band of the matrix) once every wave
+// gets at least 4 rows, with 3 workgroups per CU and 2 stages for 1 token (Q4_K
+// 7.25 us), 2 and 3 for 2 tokens (8.84 -> 8.59 us) and 2 and 2 for 4 token slots
+// (11.43 -> 10.80 us: more activation registers per lane), else with 2
+// workgroups per CU and contiguous shares.  Rows of 8 segments (Q8_0, K = 14336)
+// take 1 workgroup per CU, 4 stages, interleaved (12.01 -> 11.64 us); 4 segments
+// (Q4_K, K = 14336) 1 workgroup per CU, 4 stages, contiguous, except 1 token: 2
+// workgroups per CU, 2 stages (9.17 -> 8.84 us).  More waves or deeper rings
+// beyond these only add requests in flight.
 static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n, int force_p, int force_wpc,
                           int force_st, int force_il, MmvqPlan* out) {
   int P = 1;
   while (P * 64 < units_per_row) P *= 2;
   if (force_p) P = force_p;
   if (P > 8 || P * 64 < units_per_row || P * tslot > 16) return 0;
-  const int stages = force_st ? force_st : (P >= 4 ? 4 : 2);
+  int wpc, stages, il;
+  if (P >= 8) {
+    wpc = 1; stages = 4; il = 1;
+  } else if (P >= 4) {
+    const bool one = tslot == 1;
+    wpc = one ? 2 : 1; stages = one ? 2 : 4; il = 0;
+  } else {
+    wpc = tslot == 1 ? 3 : 2; stages = tslot == 2 ? 3 : 2; il = 1;
+  }
+  // interleave only when every wave gets at least 4 rows; short-row matrices
+  // that small take 2 workgroups per CU, 2 stages, contiguous shares
+  if (n < (int64_t)ftk::num_cus() * wpc * 4 * 4) {
+    il = 0;
+    if (P <= 2) { wpc = 2; stages = 2; }
+  }
+  if (force_st) stages = force_st;
   if (stages < 2 || stages > 4) return 0;
-  // interleave when every wave of 3 workgroups per CU gets at least 4 rows
-  const bool big = n >= (int64_t)ftk::num_cus() * 3 * 4 * 4;
-  int wpc = force_wpc ? force_wpc : (P >= 4 ? 1 : (big ? 3 : 2));
-  const int il = force_il ? force_il - 1 : (P <= 2 && big);   // FT_MMVQ_PLAN field 8: 1 contiguous, 2 interleaved
+  if (force_wpc) wpc = force_wpc;
+  if (force_il) il = force_il - 1;   // FT_MMVQ_PLAN field 8: 1 contiguous, 2 interleaved
   wpc = wpc < 1 ? 1 : (wpc > 10 ? 10 : wpc);
   const int64_t waves = (int64_t)ftk::num_cus() * wpc * 4;
   int64_t rpw = (n + waves - 1) / waves;
