@@ -57,7 +57,7 @@ __device__ __forceinline__ float lds_h2f(const uint8_t* base, uint32_t off) {
   return h2f(*(const uint16_t*)(base + off));
 }
 
-template <int F, int KP>
+template <int F, int KP, int NR>
 __global__ void __launch_bounds__(64 * KP)
 mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t row_bytes,
                  const uint8_t* __restrict__ xq, int64_t xrb, int t, float* __restrict__ y, int64_t ldy) {
@@ -114,10 +114,21 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   // group kq) is token kq + 4*r: with t tokens only r < ceil(t/4) carries results
   // and every lane group has its share (the scale combine runs ceil(t/4) times per
   // lane, not 4).
+  // NR = ceil(t / 4) result rows per lane carry tokens (a template argument, so
+  // the per-block combine has no branches); slot r of a lane holds token kq + 4r,
+  // and a slot past t reads token 0's scale and adds it times zero.  Every LDS
+  // read is unconditional, so the compiler can batch them ahead of the MFMAs.
   const int col = lane & 15, kq = lane >> 4;
   const int atok = (col >> 2) + 4 * (col & 3);   // the token of A row col
   const bool arow = atok < t;
-  const int nr = (t + 3) >> 2;
+  const uint32_t arow_off = (uint32_t)((arow ? atok : 0) * MV_ACB);
+  bool sv[NR];
+  uint32_t s_off[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    sv[r] = kq + 4 * r < t;
+    s_off[r] = (uint32_t)((sv[r] ? kq + 4 * r : 0) * MV_ACB);
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const v4i zi = {0, 0, 0, 0};
 
@@ -136,16 +147,15 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
         const float dmn = dmin * (float)(((j < 4 ? m_lo : m_hi) >> sh) & 0xFFu);
         const uint64_t q = *(const uint64_t*)(wl + col * CB + 144 * sbk + 16 + 32 * (j >> 1) + 8 * kq);
         const uint64_t b = (j & 1) ? (q >> 4) & 0x0F0F0F0F0F0F0F0Full : q & 0x0F0F0F0F0F0F0F0Full;
-        const uint64_t a = arow ? lds_u64(al, (uint32_t)(atok * MV_ACB + 288 * sbk + 36 * j + 4 + 8 * kq)) : 0ull;
+        const uint64_t ar = lds_u64(al, arow_off + (uint32_t)(288 * sbk + 36 * j + 4 + 8 * kq));
+        const uint64_t a = arow ? ar : 0ull;
         const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, zi, 0, 0, 0);
         const v4i S = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)0x0101010101010101ll, zi, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = kq + 4 * r;
-          if (r < nr && tok < t) {
-            const float dx = lds_h2f(al, (uint32_t)(tok * MV_ACB + 288 * sbk + 36 * j));
-            acc[r] = fmaf(dx, fmaf(dsc, (float)D[r], -dmn * (float)S[r]), acc[r]);
-          }
+        for (int r = 0; r < NR; ++r) {
+          const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(288 * sbk + 36 * j));
+          const float dx = sv[r] ? dxr : 0.0f;
+          acc[r] = fmaf(dx, fmaf(dsc, (float)D[r], -dmn * (float)S[r]), acc[r]);
         }
       }
      }
@@ -167,15 +177,14 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
           const uint32_t hi = ((uint32_t)(nib >> 32) + 0x78787878u) ^ 0x80808080u;
           b = (uint64_t)lo | ((uint64_t)hi << 32);
         }
-        const uint64_t a = arow ? lds_u64(al, (uint32_t)(atok * MV_ACB + 36 * blk + 4 + 8 * kq)) : 0ull;
+        const uint64_t ar = lds_u64(al, arow_off + (uint32_t)(36 * blk + 4 + 8 * kq));
+        const uint64_t a = arow ? ar : 0ull;
         const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, zi, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = kq + 4 * r;
-          if (r < nr && tok < t) {
-            const float dx = lds_h2f(al, (uint32_t)(tok * MV_ACB + 36 * blk));
-            acc[r] = fmaf((float)D[r], dw * dx, acc[r]);
-          }
+        for (int r = 0; r < NR; ++r) {
+          const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(36 * blk));
+          const float dx = sv[r] ? dxr : 0.0f;
+          acc[r] = fmaf((float)D[r], dw * dx, acc[r]);
         }
       }
     }
@@ -187,6 +196,9 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   for (int c = c0; c < c1; ++c) {
     commit(ra);
     fetch(c + 1, ra);
+    // keep the loads ahead of the compute: the scheduler would otherwise sink
+    // them to their use in the next commit (shorter live ranges, no overlap)
+    __builtin_amdgcn_sched_barrier(0);
     compute();
   }
 
@@ -212,9 +224,13 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
 template <int F, int KP>
 static hipError_t launch_mfma_kp(const MmvqArgs& a, int64_t k, hipStream_t st) {
   constexpr int SLICE = 16 * MvGeo<F, MV_CE>::CB + MV_MAXT * MvRegs<F, MV_CE>::ACB;
-  hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP>), dim3((unsigned)((a.n + 15) / 16)), dim3(64 * KP), (size_t)KP * SLICE,
-                     st, (const uint8_t*)a.W, a.n, k, (int64_t)a.row_bytes, (const uint8_t*)a.xq,
-                     (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
+  const dim3 grid((unsigned)((a.n + 15) / 16)), block(64 * KP);
+  if (a.t <= 4)
+    hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP, 1>), grid, block, (size_t)KP * SLICE, st, (const uint8_t*)a.W, a.n,
+                       k, (int64_t)a.row_bytes, (const uint8_t*)a.xq, (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
+  else
+    hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP, 2>), grid, block, (size_t)KP * SLICE, st, (const uint8_t*)a.W, a.n,
+                       k, (int64_t)a.row_bytes, (const uint8_t*)a.xq, (int64_t)a.xrow_bytes, a.t, a.y, a.ldy);
   return hipGetLastError();
 }
 
