@@ -529,16 +529,18 @@ int ftk_num_cus() {
 }
 
 // Several tokens go to the int8 MFMA kernels (ft_mmvq_mfma.hip) when K is a whole
-// number of 256-element chunks from 3 tokens on, except 3-4 tokens on rows of at
-// most 128 units, which the per-wave dot4 ring (4 token slots) runs faster.
+// number of 256-element chunks from 3 tokens on, except 3-4 tokens of Q8_0 on rows
+// of at most 128 units, which the per-wave dot4 ring (4 token slots) runs faster.
 // Measured (14336 x 4096 / 4096 x 14336): 2 tokens are faster on dot4 everywhere;
-// 4 tokens on dot4 vs MFMA: Q8_0 13.6 vs 17.3 us and Q4_K 11.3 vs 11.7 us at K =
-// 4096, but Q4_K 16.2 vs 13.1 us at K = 14336; 8 tokens are faster on MFMA.
-// FT_MMVQ_MFMA_MIN_T moves the token threshold (tuning sweeps).
-static int mfma_min_t() {
+// 4 tokens on dot4 vs MFMA at K = 4096: Q8_0 13.1 vs 15.2 us, Q4_K 10.8 vs 10.4 us,
+// Q4_0 12.1 vs 11.5 us; at K = 14336 Q4_K 16.2 vs 9.8 us; 8 tokens are faster on
+// MFMA.
+// FT_MMVQ_MFMA_MIN_T = m sends every t >= m to MFMA and the rest to dot4 (tuning
+// sweeps).
+static int mfma_min_t() {   // 0: the automatic choice
   static const int v = [] {
     const char* e = getenv("FT_MMVQ_MFMA_MIN_T");
-    return e && atoi(e) > 0 ? atoi(e) : 3;
+    return e && atoi(e) > 0 ? atoi(e) : 0;
   }();
   return v;
 }
@@ -554,9 +556,10 @@ static int64_t units_of(int w, int64_t k) {
 
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;
-  const bool dot4_short = a.t <= 4 && units_of(a.w, k) <= 128;
-  if (a.t >= mfma_min_t() && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t) && !dot4_short)
-    return ftk_launch_mmvq_mfma(a, k, st);
+  const int mt = mfma_min_t();
+  const bool short_dot4 = a.t <= 4 && a.w == FT_Q8_0 && units_of(a.w, k) <= 128;
+  const bool mfma = mt ? a.t >= mt : a.t >= 3 && !short_dot4;
+  if (mfma && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t)) return ftk_launch_mmvq_mfma(a, k, st);
   if (a.act == FT_Q8_1) {
     switch (a.w) {
       case FT_Q4_0: return launch_fa<FT_Q4_0, FT_Q8_1>(a, k, st);
