@@ -529,12 +529,13 @@ int ftk_num_cus() {
 }
 
 // Several tokens go to the int8 MFMA kernels (ft_mmvq_mfma.hip) when K is a whole
-// number of 256-element chunks from 3 tokens on, except 3-4 tokens of Q8_0 on rows
-// of at most 128 units, which the per-wave dot4 ring (4 token slots) runs faster.
-// Measured (14336 x 4096 / 4096 x 14336): 2 tokens are faster on dot4 everywhere;
-// 4 tokens on dot4 vs MFMA at K = 4096: Q8_0 13.1 vs 15.2 us, Q4_K 10.8 vs 10.4 us,
-// Q4_0 12.1 vs 11.5 us; at K = 14336 Q4_K 16.2 vs 9.8 us; 8 tokens are faster on
-// MFMA.
+// number of 256-element chunks: Q4_0 / Q4_K from 3 tokens on, and at 2 tokens on
+// rows of more than 128 units; Q8_0 from 5 tokens on, and at 3-4 tokens on rows of
+// more than 128 units.  The rest stay on the per-wave dot4 ring.  Measured
+// (dot4 vs MFMA, us): 2 tokens, 14336 x 4096: Q8_0 12.0 / 14.9, Q4_K 8.7 / 10.4,
+// Q4_0 9.4 / 10.4; 4096 x 14336: Q8_0 13.2 / 13.7, Q4_K 11.3 / 9.7, Q4_0 12.7 /
+// 10.1.  4 tokens, 14336 x 4096: Q8_0 13.1 / 15.2, Q4_K 10.8 / 10.4, Q4_0 12.1 /
+// 11.5; 4096 x 14336: Q4_K 16.2 / 9.8.  8 tokens are faster on MFMA throughout.
 // FT_MMVQ_MFMA_MIN_T = m sends every t >= m to MFMA and the rest to dot4 (tuning
 // sweeps).
 static int mfma_min_t() {   // 0: the automatic choice
@@ -557,8 +558,9 @@ static int64_t units_of(int w, int64_t k) {
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;
   const int mt = mfma_min_t();
-  const bool short_dot4 = a.t <= 4 && a.w == FT_Q8_0 && units_of(a.w, k) <= 128;
-  const bool mfma = mt ? a.t >= mt : a.t >= 3 && !short_dot4;
+  const bool lng = units_of(a.w, k) > 128;
+  const bool mfma = mt ? a.t >= mt
+                       : (a.w == FT_Q8_0 ? a.t >= 5 || (a.t >= 3 && lng) : a.t >= 3 || (a.t == 2 && lng));
   if (mfma && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t)) return ftk_launch_mmvq_mfma(a, k, st);
   if (a.act == FT_Q8_1) {
     switch (a.w) {
