@@ -182,6 +182,25 @@ def _time_graph(torch, g, reps):
     return e0.elapsed_time(e1) / 1e3 / reps
 
 
+def _time_graph_median(torch, g, reps=7):
+    """Median over `reps` replays of graph g of one replay's time (s), each replay
+    between its own two events on the launch stream (a host-side stall in one
+    replay, e.g. a profiler flushing its buffers, does not enter the figure)."""
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
 def _cpu_baseline(fn, sample_desc, unit, work, min_seconds=10.0):
     """Time the oracle (as it stands) on the host cores: repeat fn until about
     min_seconds of CPU work, report work per second."""
@@ -246,7 +265,8 @@ def bench_dense(args, np, torch, ft, synth):
     steps_done = reps * copies
 
     # per-case kernel duration: a graph of R back-to-back launches of that case's
-    # matvec over the rotating copies, timed with two events on the same stream
+    # matvec over the rotating copies; the median of 7 replays, each timed with two
+    # events on the launch stream
     R = 8 * copies
     wbytes = {c: mats[c[:3]].nbytes for c in cases}
     abytes = {c: c[3] * ft.row_bytes("Q8_1", c[2]) + 4 * c[3] * c[1] for c in cases}
@@ -255,7 +275,7 @@ def bench_dense(args, np, torch, ft, synth):
         fmt, n, k, t = c
         gk = _graph(torch, lambda: [ft.mul_mat_vec_q(fmt, dev[(fmt, n, k)][i % copies], n, k, "Q8_1",
                                                      xq[(k, t)], t, out=ys[c]) for i in range(R)])
-        us = _time_graph(torch, gk, 3) / R * 1e6
+        us = _time_graph_median(torch, gk) / R * 1e6
         kus[c] = us
         alg = wbytes[c] + abytes[c]
         per_case.append({"case": f"{fmt} {n}x{k} t={t}", "kernel_us": round(us, 2),
@@ -328,9 +348,9 @@ def bench_q4_0(args, np, torch, ft, synth):
     sec = _time_graph(torch, gs, max(1, args.steps // R)) / R
     gm = _graph(torch, lambda: [ft.mul_mat_vec_q("Q4_0", dWs[j % copies], n, k, "Q8_1", xq, 1, out=y)
                                 for j in range(R)])
-    us = _time_graph(torch, gm, 3) / R * 1e6
+    us = _time_graph_median(torch, gm) / R * 1e6
     gd = _graph(torch, lambda: [ft.dequant("Q4_0", dWs[j % copies], n, k, out=deq) for j in range(R)])
-    dus = _time_graph(torch, gd, 3) / R * 1e6
+    dus = _time_graph_median(torch, gd) / R * 1e6
     alg = W.nbytes + ft.row_bytes("Q8_1", k) + 4 * n
     out = {
         "metric": "Q-matvec effective weight GB/s", "value": round(W.nbytes / sec / 1e9, 2), "unit": "GB/s",
