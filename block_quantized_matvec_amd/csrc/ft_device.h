@@ -657,6 +657,14 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 2 /* nt */);
 }
 
+// Geometry of a per-wave LDS-DMA ring stage: 64 units of weight blocks (one
+// segment of a row, or several whole rows of at most 64 units together), read
+// as CPW 16-byte chunks per lane from the 16-byte boundary at or below its start.
+template <int F> struct SegGeo {
+  static constexpr int BYTES = 64 / Fmt<F>::UPB * Fmt<F>::BB;   // bytes of 64 units
+  static constexpr int CPW = (BYTES + 15 + 1023) / 1024;         // 16-byte chunks per lane per stage
+};
+
 // wait until at most N global loads / stores of this wave are outstanding
 // (gfx9 s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at max)
 template <int N>

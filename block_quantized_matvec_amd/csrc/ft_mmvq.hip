@@ -180,10 +180,6 @@ mmvq_kernel(const uint8_t* __restrict__ W, int64_t n, int row_bytes, int units_p
 // workgroup barriers, so a wave computes a segment as soon as its bytes have
 // landed and the work left after the last byte arrives is one segment.
 // ---------------------------------------------------------------------------
-template <int F> struct SegGeo {
-  static constexpr int BYTES = 64 / Fmt<F>::UPB * Fmt<F>::BB;   // bytes of 64 units
-  static constexpr int CPW = (BYTES + 15 + 1023) / 1024;         // 16-byte chunks per lane per stage
-};
 template <int F, int S>
 constexpr size_t mmvq_wave_lds_bytes() {
   return (size_t)(MMVQ_THREADS / 64) * (S * SegGeo<F>::CPW * 1024 + 16);

@@ -22,6 +22,8 @@
 //    reduction, before h leaves registers.
 #include <stdlib.h>
 
+#include <string.h>
+
 #include "ft_device.h"
 #include "ft_internal.h"
 
@@ -661,6 +663,361 @@ static hipError_t down_lp(const MoeArgs& a, const MoePlan& pl, int rb, int units
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Direct-route expert kernels on per-wave LDS-DMA rings (rows of at most 64
+// units).  As in the dense 1-2 token matvec, every wave streams its own rows
+// through an S-stage ring with global_load_lds_dwordx4 and waits only on its own
+// vmcnt; the one workgroup barrier follows the activation quantize prologue.  A
+// stage holds a group of G = 64 / LR consecutive rows of one matrix (LR lanes per
+// row: lane = (row in group, unit)), so that short rows still fill the wave; the
+// gate/up kernel streams a group's gate rows and then its up rows, and the SwiGLU
+// pair meets in one reduction.  Groups are dealt to the slot's waves in turn
+// (group_stride > 1) or in contiguous shares.  Every tile is CPW loads per lane
+// (chunks past the group re-read its last chunk; tiles past the share re-read the
+// share's first chunk), so the vmcnt arithmetic of wait_tiles holds.
+// ---------------------------------------------------------------------------
+struct RingShare {
+  int64_t g0;   // first group of the wave
+  int ng;       // groups of the wave
+};
+__device__ __forceinline__ RingShare ring_share(int64_t ngroups, int groups_per_wave, int64_t group_stride,
+                                                int wave) {
+  const int64_t gw = (int64_t)blockIdx.x * (MOE_THREADS / 64) + wave;
+  RingShare r;
+  r.g0 = group_stride == 1 ? gw * groups_per_wave : gw;
+  r.ng = r.g0 >= ngroups ? 0
+         : group_stride == 1 ? (int)min<int64_t>(groups_per_wave, ngroups - r.g0)
+                             : (int)((ngroups - r.g0 + group_stride - 1) / group_stride);
+  return r;
+}
+
+// NM matrices of one expert (gate and up, or down) streamed group by group: tile j
+// is group j / NM of the share in matrix j % NM.
+template <int F, int NM, int S>
+struct ExpertRing {
+  static constexpr int CPW = SegGeo<F>::CPW;
+  static constexpr int SB = CPW * 1024;
+  const uint8_t* mat[NM];   // the expert's matrices
+  uint8_t* ring;
+  int64_t rows, row_bytes, gbytes, gstep;   // end row of the expert in the bank, bytes per row / group / step
+  int64_t first_a0;
+  int ntiles, issued = 0, is_mat = 0, is_stage = 0, c_nch = -1, lane;
+  int64_t is_off, is_row;                   // the next tile's group: byte offset and first row
+  uint32_t c_off[CPW];
+  __device__ __forceinline__ void issue_next() {
+    const bool real = issued < ntiles;
+    const int64_t a0 = real ? is_off & ~(int64_t)15 : first_a0;
+    const int64_t nb = min<int64_t>(gbytes, (rows - is_row) * row_bytes);
+    const int nch = real ? (int)(((is_off & 15) + nb + 15) >> 4) : 1;
+    if (nch != c_nch) {   // uniform; whole groups of 16-byte rows keep one count
+      c_nch = nch;
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) c_off[i] = 16u * (uint32_t)min(lane + 64 * i, nch - 1);
+    }
+    const uint8_t* src = mat[NM == 1 ? 0 : is_mat] + a0;
+    uint8_t* dst = ring + is_stage * SB;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) lds_dma16(src + c_off[i], dst + 1024 * i);
+    ++issued;
+    is_stage = is_stage + 1 == S ? 0 : is_stage + 1;
+    if (++is_mat == NM) {
+      is_mat = 0;
+      is_off += gstep;
+      is_row += gstep / row_bytes;
+    }
+  }
+};
+
+// gate/up + SwiGLU on the ring: h[pair][r] = silu(g) * u
+template <int F, int A, int T, int LR, int S>
+__global__ void __launch_bounds__(MOE_THREADS)
+moe_ring_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t n_expert,
+                        int64_t inter, int row_bytes, int units_per_row, int groups_per_wave, int64_t group_stride,
+                        const float* __restrict__ x, int64_t hidden, int t_real, const int32_t* __restrict__ ids,
+                        int topk, float* __restrict__ h, float* __restrict__ gtap, float* __restrict__ utap) {
+  using FT = Fmt<F>;
+  using RG = ExpertRing<F, 2, S>;
+  constexpr int G = 64 / LR;   // rows per group
+  constexpr int M = 2 * T;     // g values then u values of one row per lane group
+  static_assert(M <= LR, "");
+  extern __shared__ u32x4 smem4[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int xrb = (int)(hidden / Act<A>::BLK * Act<A>::BB);
+  uint8_t* xql = (uint8_t*)smem4;
+  uint8_t* ring = xql + ((T * xrb + 15) & ~15) + wave * (S * RG::SB + 16);
+
+  int e;
+  uint32_t mask;
+  uint64_t smask;
+  if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
+  const int64_t ngroups = (inter + G - 1) / G;
+  const RingShare sh = ring_share(ngroups, groups_per_wave, group_stride, wave);
+  // offsets from the 16-byte aligned bank bases, so that a0 is an aligned address
+  const int64_t ebase = (int64_t)e * inter * row_bytes;
+  RG rg;
+  rg.mat[0] = wg;
+  rg.mat[1] = wu;
+  rg.ring = ring;
+  rg.rows = (int64_t)(e + 1) * inter;
+  rg.row_bytes = row_bytes;
+  rg.gbytes = (int64_t)G * row_bytes;
+  rg.gstep = group_stride * rg.gbytes;
+  rg.is_off = ebase + sh.g0 * rg.gbytes;
+  rg.is_row = (int64_t)e * inter + sh.g0 * G;
+  rg.first_a0 = rg.is_off & ~(int64_t)15;
+  rg.ntiles = 2 * sh.ng;
+  rg.lane = lane;
+  if (sh.ng > 0) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) rg.issue_next();
+  }
+  quantize_rows<A>(
+      t_real, (int)hidden, [&](int r) { return x + (int64_t)r * hidden; }, [&](int r) { return xql + r * xrb; }, tid);
+  lds_barrier();
+  if (sh.ng == 0) return;   // whole wave, after the only barrier
+
+  const int gl = lane % LR, rig = lane / LR;   // unit, row in the group
+  const bool uv = gl < units_per_row;
+  const int u = uv ? gl : 0;
+  ActUnit<F> act[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    if (uv && ((mask >> i) & 1)) load_act_unit<F, A>(xql + i * xrb, u / FT::UPB, u % FT::UPB, act[i]);
+    else zero_act_unit<F>(act[i]);
+  }
+  const uint32_t lane_off = (uint32_t)(rig * row_bytes + (u / FT::UPB) * FT::BB);
+
+  const Reader<const uint32_t*> rd{(const uint32_t*)ring};
+  int cur = 0, cs_stage = 0;
+  int64_t cs_off = ebase + sh.g0 * rg.gbytes, cs_row = sh.g0 * G;
+  for (int gi = 0; gi < sh.ng; ++gi) {
+    float v[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      wait_tiles<RG::CPW, S>(rg.issued - 1 - cur);
+      const uint32_t so = (uint32_t)(cs_stage * RG::SB) + (uint32_t)(cs_off & 15) + lane_off;
+      Unit<F> un;
+      unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, so, u % FT::UPB, un);
+#pragma unroll
+      for (int i = 0; i < T; ++i) v[m * T + i] = unit_combine<F>(un, act[i], v[m * T + i]);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the stage is read
+      rg.issue_next();
+      ++cur;
+      cs_stage = cs_stage + 1 == S ? 0 : cs_stage + 1;
+    }
+    group_reduce_multi<M, LR>(v, gl);
+    const int idx = gl / (LR / M);
+    const bool leader = (gl % (LR / M)) == 0;
+    const float other = __shfl_xor(v[0], LR / 2, 64);   // the u value of the same token
+    const int64_t row = cs_row + rig;
+    if (leader && idx < T && row < inter && ((mask >> idx) & 1)) {
+      const float g = v[0], uu = other, hv = g / (1.0f + expf(-g)) * uu;
+      for (int k = 0; k < topk; ++k) {   // every slot of token idx that names e
+        if ((smask >> (8 * idx + k)) & 1) {
+          const int64_t o = (int64_t)(idx * topk + k) * inter + row;
+          h[o] = hv;
+          if (gtap) gtap[o] = g;
+          if (utap) utap[o] = uu;
+        }
+      }
+    }
+    cs_off += rg.gstep;
+    cs_row += group_stride * G;
+  }
+}
+
+// down projection on the ring: d[pair][r] = W_down[e][r] . hhat(pair); hhat of the
+// expert's tokens is quantized here (or read from in_hq), and the first workgroup
+// of the slot writes it to hq_tap
+template <int F, int A, int T, int LR, int S>
+__global__ void __launch_bounds__(MOE_THREADS)
+moe_ring_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int row_bytes,
+                     int units_per_row, int groups_per_wave, int64_t group_stride, const float* __restrict__ h,
+                     const uint8_t* __restrict__ in_hq, uint8_t* __restrict__ hq_tap, int64_t inter, int t_real,
+                     const int32_t* __restrict__ ids, int topk, float* __restrict__ dpair) {
+  using FT = Fmt<F>;
+  using RG = ExpertRing<F, 1, S>;
+  constexpr int G = 64 / LR;
+  constexpr int M = T;
+  static_assert(M <= LR, "");
+  extern __shared__ u32x4 smem4[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int hrb = (int)(inter / Act<A>::BLK * Act<A>::BB);
+  uint8_t* hql = (uint8_t*)smem4;
+  uint8_t* ring = hql + ((T * hrb + 15) & ~15) + wave * (S * RG::SB + 16);
+
+  int e;
+  uint32_t mask;
+  uint64_t smask;
+  if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
+  const int64_t ngroups = (hidden + G - 1) / G;
+  const RingShare sh = ring_share(ngroups, groups_per_wave, group_stride, wave);
+  const int64_t ebase = (int64_t)e * hidden * row_bytes;   // from the aligned bank base
+  RG rg;
+  rg.mat[0] = wd;
+  rg.ring = ring;
+  rg.rows = (int64_t)(e + 1) * hidden;
+  rg.row_bytes = row_bytes;
+  rg.gbytes = (int64_t)G * row_bytes;
+  rg.gstep = group_stride * rg.gbytes;
+  rg.is_off = ebase + sh.g0 * rg.gbytes;
+  rg.is_row = (int64_t)e * hidden + sh.g0 * G;
+  rg.first_a0 = rg.is_off & ~(int64_t)15;
+  rg.ntiles = sh.ng;
+  rg.lane = lane;
+  if (sh.ng > 0) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) rg.issue_next();
+  }
+  // hhat of the expert's tokens (token i -> LDS row i), from the first slot of
+  // token i that names e
+  const int ntok = __popc(mask);
+  auto first_pair = [&](int i) { return i * topk + __ffs((unsigned)(smask >> (8 * i)) & 0xFFu) - 1; };
+  if (in_hq) {
+    for (int c = tid; c < ntok * (hrb >> 2); c += MOE_THREADS) {
+      const int j = c / (hrb >> 2), w = c - j * (hrb >> 2), i = nth_bit(mask, j);
+      ((uint32_t*)(hql + i * hrb))[w] = ((const uint32_t*)(in_hq + (int64_t)first_pair(i) * hrb))[w];
+    }
+  } else {
+    quantize_rows<A>(
+        ntok, (int)inter, [&](int j) { return h + (int64_t)first_pair(nth_bit(mask, j)) * inter; },
+        [&](int j) { return hql + nth_bit(mask, j) * hrb; }, tid);
+  }
+  lds_barrier();
+  if (hq_tap && blockIdx.x == 0) {
+    for (int i = 0; i < T; ++i)
+      for (int k = 0; k < topk; ++k)
+        if ((smask >> (8 * i + k)) & 1)
+          for (int c = tid; c < (hrb >> 2); c += MOE_THREADS)
+            ((uint32_t*)(hq_tap + (int64_t)(i * topk + k) * hrb))[c] = ((const uint32_t*)(hql + i * hrb))[c];
+  }
+  if (sh.ng == 0) return;   // whole wave, after the only barrier
+
+  const int gl = lane % LR, rig = lane / LR;
+  const bool uv = gl < units_per_row;
+  const int u = uv ? gl : 0;
+  ActUnit<F> act[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    if (uv && ((mask >> i) & 1)) load_act_unit<F, A>(hql + i * hrb, u / FT::UPB, u % FT::UPB, act[i]);
+    else zero_act_unit<F>(act[i]);
+  }
+  const uint32_t lane_off = (uint32_t)(rig * row_bytes + (u / FT::UPB) * FT::BB);
+
+  const Reader<const uint32_t*> rd{(const uint32_t*)ring};
+  int cur = 0, cs_stage = 0;
+  int64_t cs_off = ebase + sh.g0 * rg.gbytes, cs_row = sh.g0 * G;
+  for (int gi = 0; gi < sh.ng; ++gi) {
+    float v[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] = 0.0f;
+    wait_tiles<RG::CPW, S>(rg.issued - 1 - cur);
+    const uint32_t so = (uint32_t)(cs_stage * RG::SB) + (uint32_t)(cs_off & 15) + lane_off;
+    Unit<F> un;
+    unpack_unit<F, (F == FT_Q4_K || F == FT_Q5_K)>(rd, so, u % FT::UPB, un);
+#pragma unroll
+    for (int i = 0; i < T; ++i) v[i] = unit_combine<F>(un, act[i], v[i]);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the stage is read
+    rg.issue_next();
+    ++cur;
+    cs_stage = cs_stage + 1 == S ? 0 : cs_stage + 1;
+    group_reduce_multi<M, LR>(v, gl);
+    const int idx = gl / (LR / M);
+    const int64_t row = cs_row + rig;
+    if ((gl % (LR / M)) == 0 && idx < T && row < hidden && ((mask >> idx) & 1)) {
+      for (int k = 0; k < topk; ++k)
+        if ((smask >> (8 * idx + k)) & 1) dpair[(int64_t)(idx * topk + k) * hidden + row] = v[0];
+    }
+    cs_off += rg.gstep;
+    cs_row += group_stride * G;
+  }
+}
+
+// Ring plan for rows of at most 64 units: LR lanes per row (16, 32 or 64), about
+// wpc workgroups per CU over all the launch's slots, S ring stages, row groups dealt
+// to the slot's waves in contiguous shares or in turn.  Measured on the Q4_K layer
+// (2048 hidden, 768 intermediate, 128 experts, top-8; layer us, old workgroup-tile
+// kernels -> rings): 1 token 22.1 -> 22.1, 2 tokens 30.5 -> 29.5 (2 workgroups per
+// CU, 2 stages, contiguous), 3 tokens 46.7 -> 40.5 and 4 tokens 48.2 -> 47.9 (3 per
+// CU, 2 stages, interleaved); 3 stages were slower throughout.  The direct kernels
+// are bound by latency (expert ids, then the first weight bytes), not by the
+// stream.  FT_MOE_RING = "wpc,stages,rows" overrides (tuning sweeps; 0 = choose;
+// rows 1 = contiguous, 2 = interleaved), "off" keeps the workgroup-tile kernels.
+struct RingPlan { int lr, stages, groups_per_wave, wgs; int64_t group_stride; };
+
+static bool moe_ring_plan(int units, int64_t rows, int slots, int tslot, RingPlan& pl) {
+  static const char* env = getenv("FT_MOE_RING");
+  if (units > 64 || (env && strcmp(env, "off") == 0)) return false;
+  int wpc = 0, st = 0, il = 0;
+  if (env) sscanf(env, "%d,%d,%d", &wpc, &st, &il);
+  if (wpc <= 0) wpc = tslot >= 4 ? 3 : 2;
+  if (st < 2 || st > 4) st = 2;
+  il = il == 0 ? (tslot >= 4 ? 1 : 0) : il - 1;
+  pl.lr = 16;
+  while (pl.lr < units) pl.lr *= 2;
+  pl.stages = st;
+  const int64_t ngroups = (rows + 64 / pl.lr - 1) / (64 / pl.lr);
+  const int64_t per_slot = ((int64_t)wpc * ftk_num_cus() + slots - 1) / slots;   // workgroups
+  int64_t waves = per_slot * (MOE_THREADS / 64);
+  if (waves > ngroups) waves = ngroups;
+  if (il) {
+    pl.group_stride = waves;
+    pl.groups_per_wave = 0;
+  } else {
+    pl.group_stride = 1;
+    pl.groups_per_wave = (int)((ngroups + waves - 1) / waves);
+    waves = (ngroups + pl.groups_per_wave - 1) / pl.groups_per_wave;
+  }
+  pl.wgs = (int)((waves + MOE_THREADS / 64 - 1) / (MOE_THREADS / 64));
+  return true;
+}
+
+template <int F, int A, int T, int LR, int S>
+static hipError_t launch_ring(const MoeArgs& a, bool gate, const RingPlan& pl, int row_bytes, int units, int c0,
+                              int tc, hipStream_t st) {
+  const int64_t k = gate ? a.hidden : a.inter;
+  const size_t arb = (size_t)(k / Act<A>::BLK * Act<A>::BB);
+  const size_t lds = ((T * arb + 15) & ~(size_t)15) + (size_t)(MOE_THREADS / 64) * (S * SegGeo<F>::CPW * 1024 + 16);
+  const dim3 grid((unsigned)pl.wgs, (unsigned)(tc * a.topk));
+  const size_t p0 = (size_t)c0 * a.topk;
+  // more than 64 KiB of LDS needs the opt-in (rows of 64 units, 4 stages, 4 tokens)
+  static const bool attr_g = hipFuncSetAttribute((const void*)moe_ring_gate_up_kernel<F, A, T, LR, S>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+  static const bool attr_d = hipFuncSetAttribute((const void*)moe_ring_down_kernel<F, A, T, LR, S>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+  if (lds > 65536 && !(gate ? attr_g : attr_d)) return hipErrorInvalidConfiguration;
+  if (gate) {
+    hipLaunchKernelGGL((moe_ring_gate_up_kernel<F, A, T, LR, S>), grid, dim3(MOE_THREADS), lds, st,
+                       (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, row_bytes, units,
+                       pl.groups_per_wave, pl.group_stride, a.x + (size_t)c0 * a.hidden, a.hidden, tc,
+                       a.ids + p0, a.topk, a.h + p0 * a.inter, a.g_tap ? a.g_tap + p0 * a.inter : nullptr,
+                       a.u_tap ? a.u_tap + p0 * a.inter : nullptr);
+  } else {
+    const size_t hrb = arb;
+    hipLaunchKernelGGL((moe_ring_down_kernel<F, A, T, LR, S>), grid, dim3(MOE_THREADS), lds, st,
+                       (const uint8_t*)a.w_down, a.n_expert, a.hidden, row_bytes, units, pl.groups_per_wave,
+                       pl.group_stride, a.h + p0 * a.inter, a.in_hq ? (const uint8_t*)a.in_hq + p0 * hrb : nullptr,
+                       a.hq_tap ? (uint8_t*)a.hq_tap + p0 * hrb : nullptr, a.inter, tc, a.ids + p0, a.topk,
+                       a.dpair + p0 * a.hidden);
+  }
+  return hipGetLastError();
+}
+
+template <int F, int A, int T>
+static hipError_t ring_lp(const MoeArgs& a, bool gate, const RingPlan& pl, int rb, int units, int c0, int tc,
+                          hipStream_t st) {
+#define FT_RG(LRV, SV) \
+  if (pl.lr == LRV && pl.stages == SV) return launch_ring<F, A, T, LRV, SV>(a, gate, pl, rb, units, c0, tc, st);
+  FT_RG(16, 2) FT_RG(16, 3) FT_RG(16, 4) FT_RG(32, 2) FT_RG(32, 3) FT_RG(32, 4)
+  FT_RG(64, 2) FT_RG(64, 3) FT_RG(64, 4)
+#undef FT_RG
+  return hipErrorInvalidValue;
+}
+
 // tokens are taken in chunks of up to 4 (fewer when the stage's LDS would not fit
 // in 64 KiB)
 template <int F, int A>
@@ -677,6 +1034,15 @@ static hipError_t moe_stage(const MoeArgs& a, bool gate, hipStream_t st) {
   for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
     const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
     const int tslot = tc <= 1 ? 1 : tc <= 2 ? 2 : 4;
+    RingPlan rp;
+    if (moe_ring_plan(units, rows, tc * a.topk, tslot, rp)) {
+      hipError_t err;
+      if (tslot == 1) err = ring_lp<F, A, 1>(a, gate, rp, row_bytes, units, (int)c0, tc, st);
+      else if (tslot == 2) err = ring_lp<F, A, 2>(a, gate, rp, row_bytes, units, (int)c0, tc, st);
+      else err = ring_lp<F, A, 4>(a, gate, rp, row_bytes, units, (int)c0, tc, st);
+      if (err != hipSuccess) return err;
+      continue;
+    }
     MoePlan pl;
     if (!moe_plan(units, row_bytes, rows, tc * a.topk, pl)) return hipErrorInvalidValue;
     const MoeArgs& ac = a;

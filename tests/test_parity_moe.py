@@ -50,6 +50,8 @@ CASES = {
     "q4k": dict(w="Q4_K", a="Q8_1", hidden=2048, inter=768, E=128, topk=8),
     "mxfp4": dict(w="MXFP4", a="Q8_K", hidden=4096, inter=2048, E=256, topk=8),
     "q4k_small": dict(w="Q4_K", a="Q8_1", hidden=512, inter=256, E=6, topk=2),
+    # rows of 68 units: both stages take the workgroup-tile kernels, not the rings
+    "q4k_wide": dict(w="Q4_K", a="Q8_1", hidden=4352, inter=4352, E=3, topk=2),
     "mxfp4_small": dict(w="MXFP4", a="Q8_K", hidden=512, inter=512, E=5, topk=3),
 }
 
@@ -151,6 +153,12 @@ def test_moe_down_from_given_hq(name, t, route):
     rd = oracle.moe_down(c["w"], wd, E, H, I, c["a"], hq, ids)
     check_fp32(host(taps["down"]), rd, "down")
     check_fp32(y, oracle.moe_combine(rd, ew), "combine")
+
+
+@pytest.mark.parametrize("t", [1, 3])
+def test_moe_q4k_wide_rows(t):
+    log(f"moe q4k_wide t={t}")
+    _run_stages("q4k_wide", t, route=1)
 
 
 @pytest.mark.parametrize("t", [1, 2, 3, 4])
