@@ -28,7 +28,7 @@ COPY_BYTES = 256 << 20         # calibration copy for the FETCH_SIZE / WRITE_SIZ
 
 
 # sources the headline matvec kernel is compiled from
-_HEADLINE_SRC = ("ft_mmvq.hip", "ft_device.h", "ft_internal.h")
+_HEADLINE_SRC = ("ft_mmvq.hip", "ft_mmvq_kernels.h", "ft_device.h", "ft_internal.h")
 
 
 def _src_hash():

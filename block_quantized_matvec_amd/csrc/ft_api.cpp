@@ -106,9 +106,7 @@ SortScratch sort_layout(int64_t n_expert, int64_t t, int topk, size_t xf8_bytes 
 }
 size_t xf8_bytes_of(int w, int64_t rows, int64_t k) { return w == FT_MXFP4 ? (size_t)rows * (k / 256) * 512 : 0; }
 
-bool mmvq_pair(int w, int a) {
-  return a == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K);
-}
+bool mmvq_pair(int w, int a) { return a == FT_Q8_1 && is_weight(w); }
 bool moe_pair(int w, int a) { return (w == FT_Q4_K && a == FT_Q8_1) || (w == FT_MXFP4 && a == FT_Q8_K); }
 bool moe_tile_pair(int w, int a) { return w == FT_MXFP4 && a == FT_Q8_K; }
 // the tile route splits x, then h, into FP8 halves in one buffer

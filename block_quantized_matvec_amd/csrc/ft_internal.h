@@ -31,6 +31,8 @@ struct MmvqPlan {
   int rows_per_tile, rows_per_wg, grid;
 };
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out);
+// dot4 matvec of Q5_K / Q6_K / MXFP4 x Q8_1 (ft_mmvq_kq.hip)
+hipError_t ftk_launch_mmvq_kq(const MmvqArgs& a, int64_t k, hipStream_t st);
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
 // int8-MFMA matvec for 2..8 tokens (K % 256 == 0; Q4_0, Q8_0, Q4_K x Q8_1)
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t);

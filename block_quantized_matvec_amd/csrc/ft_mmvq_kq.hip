@@ -1,0 +1,18 @@
+// ft_mmvq_kq.hip -- the dot4 quantized matvec for Q5_K, Q6_K and MXFP4 weights
+// against Q8_1 activations (kernels in ft_mmvq_kernels.h; a translation unit of
+// its own so that it compiles in parallel with ft_mmvq.hip).  Same unit core as
+// the expert kernels: Q5_K's fifth bits, Q6_K's 2-bit pairs and 16-element scale
+// groups, MXFP4's E2M1 codes doubled to integers with the E8M0 exponent in the
+// scale.
+#include "ft_mmvq_kernels.h"
+
+hipError_t ftk_launch_mmvq_kq(const MmvqArgs& a, int64_t k, hipStream_t st) {
+  using namespace ftk;
+  if (a.act != FT_Q8_1) return hipErrorInvalidValue;
+  switch (a.w) {
+    case FT_Q5_K: return launch_fa<FT_Q5_K, FT_Q8_1>(a, k, st);
+    case FT_Q6_K: return launch_fa<FT_Q6_K, FT_Q8_1>(a, k, st);
+    case FT_MXFP4: return launch_fa<FT_MXFP4, FT_Q8_1>(a, k, st);
+    default: return hipErrorInvalidValue;
+  }
+}

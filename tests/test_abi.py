@@ -46,7 +46,7 @@ def test_block_sizes():
 
 
 def test_capability_table():
-    expect_mmvq = {("Q4_0", "Q8_1"), ("Q8_0", "Q8_1"), ("Q4_K", "Q8_1")}
+    expect_mmvq = {(w, "Q8_1") for w in ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4")}
     expect_moe = {("Q4_K", "Q8_1"), ("MXFP4", "Q8_K")}
     expect_grp = {("Q4_K", "Q8_K"), ("Q5_K", "Q8_K"), ("Q6_K", "Q8_K"), ("MXFP4", "Q8_K")}
     for w in W:
