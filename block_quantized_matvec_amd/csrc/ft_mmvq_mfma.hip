@@ -1,5 +1,7 @@
 // ft_mmvq_mfma.hip -- Q-matvec for 2..8 tokens on the int8 matrix cores
-// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0 and Q4_K weights against Q8_1 activations.
+// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0, Q4_K, Q5_K and MXFP4 weights against Q8_1
+// activations (Q5_K adds the fifth bits to Q4_K's nibbles; MXFP4 enters as twice
+// its E2M1 values with 2^(e-128) as the block scale, in 512-element chunks).
 //
 // ggml-cuda "mul_mat_vec_q" (the pages' MMVQ path, ds4 PR #656 Summary): a block's
 // integer dot product of weight and activation codes, then the fp32 scale
@@ -28,13 +30,16 @@ namespace ftk {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int MV_MAXT = 8;
-constexpr int MV_CE = 256;   // elements of a row per chunk
+constexpr int MV_CE = 256;   // elements of a row per chunk (512 for MXFP4)
 
-// bytes of one row's CE-element chunk
-template <int F, int CE> struct MvGeo;
-template <int CE> struct MvGeo<FT_Q4_0, CE> { static constexpr int CB = 18 * CE / 32; };
-template <int CE> struct MvGeo<FT_Q8_0, CE> { static constexpr int CB = 34 * CE / 32; };
-template <int CE> struct MvGeo<FT_Q4_K, CE> { static constexpr int CB = 144 * CE / 256; };
+// elements CE of a row's chunk and its bytes CB (a whole number of 16-byte pieces:
+// MXFP4's 17-byte blocks need 512-element chunks for that)
+template <int F, int CE_ = MV_CE> struct MvGeo;
+template <int CE_> struct MvGeo<FT_Q4_0, CE_> { static constexpr int CE = 256, CB = 18 * CE / 32; };
+template <int CE_> struct MvGeo<FT_Q8_0, CE_> { static constexpr int CE = 256, CB = 34 * CE / 32; };
+template <int CE_> struct MvGeo<FT_Q4_K, CE_> { static constexpr int CE = 256, CB = 144 * CE / 256; };
+template <int CE_> struct MvGeo<FT_Q5_K, CE_> { static constexpr int CE = 256, CB = 176 * CE / 256; };
+template <int CE_> struct MvGeo<FT_MXFP4, CE_> { static constexpr int CE = 512, CB = 17 * CE / 32; };
 
 template <int F, int CE> struct MvRegs {
   static constexpr int ACB = 36 * CE / 32;                             // one token's Q8_1 chunk
@@ -61,7 +66,7 @@ template <int F, int KP, int NR>
 __global__ void __launch_bounds__(64 * KP)
 mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t row_bytes,
                  const uint8_t* __restrict__ xq, int64_t xrb, int t, float* __restrict__ y, int64_t ldy) {
-  constexpr int CE = MV_CE;
+  constexpr int CE = MvGeo<F>::CE;
   using R = MvRegs<F, CE>;
   constexpr int CB = MvGeo<F, CE>::CB, NWP = 16 * CB / 16, MV_ACB = R::ACB, SLICE = 16 * CB + MV_MAXT * MV_ACB;
   constexpr int APT = MV_ACB / 16;   // activation pieces per token
@@ -133,10 +138,14 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   const v4i zi = {0, 0, 0, 0};
 
   auto compute = [&]() {
-    if constexpr (F == FT_Q4_K) {
+    if constexpr (F == FT_Q4_K || F == FT_Q5_K) {
+      constexpr int SBB = F == FT_Q5_K ? 176 : 144, QS = F == FT_Q5_K ? 48 : 16;   // superblock, qs offset
 #pragma unroll
      for (int sbk = 0; sbk < CE / 256; ++sbk) {
-      const u32x4 hd = *(const u32x4*)(wl + col * CB + 144 * sbk);
+      const u32x4 hd = *(const u32x4*)(wl + col * CB + SBB * sbk);
+      // Q5_K: fifth bits of elements 8kq..8kq+7 of every sub-block (bit j of qh[l])
+      uint64_t qh = 0;
+      if constexpr (F == FT_Q5_K) qh = *(const uint64_t*)(wl + col * CB + SBB * sbk + 16 + 8 * kq);
       const float d = h2f(hd.x & 0xFFFFu), dmin = h2f(hd.x >> 16);
       uint32_t sc_lo, sc_hi, m_lo, m_hi;
       kq_unpack_scales(hd.y, hd.z, hd.w, sc_lo, sc_hi, m_lo, m_hi);
@@ -145,8 +154,9 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
         const uint32_t sh = 8u * (uint32_t)(j & 3);
         const float dsc = d * (float)(((j < 4 ? sc_lo : sc_hi) >> sh) & 0xFFu);
         const float dmn = dmin * (float)(((j < 4 ? m_lo : m_hi) >> sh) & 0xFFu);
-        const uint64_t q = *(const uint64_t*)(wl + col * CB + 144 * sbk + 16 + 32 * (j >> 1) + 8 * kq);
-        const uint64_t b = (j & 1) ? (q >> 4) & 0x0F0F0F0F0F0F0F0Full : q & 0x0F0F0F0F0F0F0F0Full;
+        const uint64_t q = *(const uint64_t*)(wl + col * CB + SBB * sbk + QS + 32 * (j >> 1) + 8 * kq);
+        uint64_t b = (j & 1) ? (q >> 4) & 0x0F0F0F0F0F0F0F0Full : q & 0x0F0F0F0F0F0F0F0Full;
+        if constexpr (F == FT_Q5_K) b |= ((qh >> j) & 0x0101010101010101ull) << 4;
         const uint64_t ar = lds_u64(al, arow_off + (uint32_t)(288 * sbk + 36 * j + 4 + 8 * kq));
         const uint64_t a = arow ? ar : 0ull;
         const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, zi, 0, 0, 0);
@@ -160,14 +170,22 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
       }
      }
     } else {
-      constexpr int BB = F == FT_Q8_0 ? 34 : 18;
+      constexpr int BB = F == FT_Q8_0 ? 34 : F == FT_MXFP4 ? 17 : 18;
+      constexpr int HB = F == FT_MXFP4 ? 1 : 2;   // header bytes (scale) before the codes
 #pragma unroll
       for (int blk = 0; blk < CE / 32; ++blk) {
         const uint32_t wb = (uint32_t)(col * CB + BB * blk);
-        const float dw = lds_h2f(wl, wb);
+        float dw;
+        if constexpr (F == FT_MXFP4) dw = e8m0_half(wl[wb]);   // codes enter doubled: 2^(e-128)
+        else dw = lds_h2f(wl, wb);
         uint64_t b;
         if constexpr (F == FT_Q8_0) {
           b = lds_u64(wl, wb + 2 + 8 * kq);
+        } else if constexpr (F == FT_MXFP4) {
+          // elements 8kq..8kq+7 as Q4_0's nibbles, each E2M1 code as twice its value
+          const uint64_t q = lds_u64(wl, wb + HB + 8 * (kq & 1));
+          const uint64_t nib = (q >> (4 * (kq >> 1))) & 0x0F0F0F0F0F0F0F0Full;
+          b = (uint64_t)e2m1x2_bytes((uint32_t)nib) | ((uint64_t)e2m1x2_bytes((uint32_t)(nib >> 32)) << 32);
         } else {
           // elements 8kq..8kq+7: low nibbles of bytes 0..7 (kq 0) or 8..15 (kq 1),
           // high nibbles of the same (kq 2, 3); as int8 n - 8
@@ -223,7 +241,7 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
 
 template <int F, int KP>
 static hipError_t launch_mfma_kp(const MmvqArgs& a, int64_t k, hipStream_t st) {
-  constexpr int SLICE = 16 * MvGeo<F, MV_CE>::CB + MV_MAXT * MvRegs<F, MV_CE>::ACB;
+  constexpr int SLICE = 16 * MvGeo<F>::CB + MV_MAXT * MvRegs<F, MvGeo<F>::CE>::ACB;
   const dim3 grid((unsigned)((a.n + 15) / 16)), block(64 * KP);
   if (a.t <= 4)
     hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP, 1>), grid, block, (size_t)KP * SLICE, st, (const uint8_t*)a.W, a.n,
@@ -246,7 +264,7 @@ static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
   const int64_t groups = (a.n + 15) / 16;
   const bool many = groups * 4 >= (int64_t)ftk_num_cus() * 8;
   const int kp = force_kp == 2 || force_kp == 4 || force_kp == 8 ? force_kp
-                 : many && MvGeo<F, MV_CE>::CB >= 256       ? 2
+                 : many && MvGeo<F>::CB >= 256 && F == FT_Q8_0 ? 2
                                                             : 8;
   if (kp == 2) return launch_mfma_kp<F, 2>(a, k, st);
   if (kp == 4) return launch_mfma_kp<F, 4>(a, k, st);
@@ -255,10 +273,12 @@ static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
 
 }  // namespace ftk
 
-// 2..8 tokens, K a multiple of 256, (Q4_0 | Q8_0 | Q4_K) x Q8_1
+// 2..8 tokens, K a whole number of chunks, (Q4_0 | Q8_0 | Q4_K | Q5_K | MXFP4) x Q8_1
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t) {
-  return act == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K) && k % 256 == 0 && k > 0 && t >= 2 &&
-         t <= ftk::MV_MAXT;
+  using namespace ftk;
+  const int ce = w == FT_MXFP4 ? MvGeo<FT_MXFP4>::CE : MV_CE;
+  return act == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K || w == FT_Q5_K || w == FT_MXFP4) &&
+         k % ce == 0 && k > 0 && t >= 2 && t <= MV_MAXT;
 }
 
 hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st) {
@@ -267,6 +287,8 @@ hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st) {
     case FT_Q4_0: return launch_mfma_f<FT_Q4_0>(a, k, st);
     case FT_Q8_0: return launch_mfma_f<FT_Q8_0>(a, k, st);
     case FT_Q4_K: return launch_mfma_f<FT_Q4_K>(a, k, st);
+    case FT_Q5_K: return launch_mfma_f<FT_Q5_K>(a, k, st);
+    case FT_MXFP4: return launch_mfma_f<FT_MXFP4>(a, k, st);
     default: return hipErrorInvalidValue;
   }
 }
