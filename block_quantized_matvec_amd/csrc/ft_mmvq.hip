@@ -135,15 +135,15 @@ int ftk_num_cus() {
 }
 
 // Several tokens go to the int8 MFMA kernels (ft_mmvq_mfma.hip) when K is a whole
-// number of chunks: Q4_0 / Q4_K / MXFP4 from 3 tokens on, and at 2 tokens on rows
-// of more than 128 units; Q8_0 / Q5_K from 5 tokens on, and at 3-4 tokens on rows of
-// more than 128 units; Q6_K stays on dot4 (its 210-byte blocks are not whole
-// 16-byte pieces per chunk).  The rest stay on the per-wave dot4 ring.  Measured
+// number of chunks: Q4_0 / Q4_K / Q6_K / MXFP4 from 3 tokens on, and at 2 tokens on
+// rows of more than 128 units; Q8_0 / Q5_K from 5 tokens on, and at 3-4 tokens on
+// rows of more than 128 units.  The rest stay on the per-wave dot4 ring.  Measured
 // (dot4 vs MFMA, us): 2 tokens, 14336 x 4096: Q8_0 12.0 / 14.9, Q4_K 8.7 / 10.4,
 // Q4_0 9.4 / 10.4; 4096 x 14336: Q8_0 13.2 / 13.7, Q4_K 11.3 / 9.7, Q4_0 12.7 /
 // 10.1.  4 tokens, 14336 x 4096: Q8_0 13.1 / 15.2, Q4_K 10.8 / 10.4, Q4_0 12.1 /
 // 11.5, Q5_K 12.2 / 13.8, MXFP4 13.8 / 14.0; 4096 x 14336: Q4_K 16.2 / 9.8.  8 tokens
-// are faster on MFMA throughout (Q5_K 25.6 / 16.6, MXFP4 24.5 / 16.5).
+// are faster on MFMA throughout (Q5_K 25.6 / 16.6, Q6_K 59.5 / 20.7, MXFP4 24.5 /
+// 16.5); Q6_K 4096 x 14336 at 2 tokens 21.7 / 18.0.
 // FT_MMVQ_MFMA_MIN_T = m sends every t >= m to MFMA and the rest to dot4 (tuning
 // sweeps).
 static int mfma_min_t() {   // 0: the automatic choice

@@ -1,7 +1,8 @@
 // ft_mmvq_mfma.hip -- Q-matvec for 2..8 tokens on the int8 matrix cores
-// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0, Q4_K, Q5_K and MXFP4 weights against Q8_1
-// activations (Q5_K adds the fifth bits to Q4_K's nibbles; MXFP4 enters as twice
-// its E2M1 values with 2^(e-128) as the block scale, in 512-element chunks).
+// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0, Q4_K, Q5_K, Q6_K and MXFP4 weights against
+// Q8_1 activations (Q5_K adds the fifth bits to Q4_K's nibbles; Q6_K enters as q6 -
+// 32 with one MFMA per 16-element scale group; MXFP4 as twice its E2M1 values with
+// 2^(e-128) as the block scale, in 512-element chunks).
 //
 // ggml-cuda "mul_mat_vec_q" (the pages' MMVQ path, ds4 PR #656 Summary): a block's
 // integer dot product of weight and activation codes, then the fp32 scale
@@ -32,18 +33,28 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int MV_MAXT = 8;
 constexpr int MV_CE = 256;   // elements of a row per chunk (512 for MXFP4)
 
-// elements CE of a row's chunk and its bytes CB (a whole number of 16-byte pieces:
-// MXFP4's 17-byte blocks need 512-element chunks for that)
+// elements CE of a row's chunk and its bytes CB; a row's chunk goes to an LDS slot of
+// NPR 16-byte pieces.  Chunks of whole pieces (CB % 16 == 0; MXFP4's 17-byte blocks
+// need 512-element chunks for that) sit at the slot's start; Q6_K's 210-byte chunks
+// are copied from the 16-byte boundary below them, one piece more, and read at
+// their byte offset in the slot.
+template <int F_, int CB_> struct MvSlot {
+  static constexpr int CB = CB_;
+  static constexpr bool UNAL = CB % 16 != 0;
+  static constexpr int NPR = UNAL ? (CB + 30) / 16 : CB / 16;
+  static constexpr int SLOT = 16 * NPR;
+};
 template <int F, int CE_ = MV_CE> struct MvGeo;
-template <int CE_> struct MvGeo<FT_Q4_0, CE_> { static constexpr int CE = 256, CB = 18 * CE / 32; };
-template <int CE_> struct MvGeo<FT_Q8_0, CE_> { static constexpr int CE = 256, CB = 34 * CE / 32; };
-template <int CE_> struct MvGeo<FT_Q4_K, CE_> { static constexpr int CE = 256, CB = 144 * CE / 256; };
-template <int CE_> struct MvGeo<FT_Q5_K, CE_> { static constexpr int CE = 256, CB = 176 * CE / 256; };
-template <int CE_> struct MvGeo<FT_MXFP4, CE_> { static constexpr int CE = 512, CB = 17 * CE / 32; };
+template <int CE_> struct MvGeo<FT_Q4_0, CE_> : MvSlot<FT_Q4_0, 18 * 256 / 32> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q8_0, CE_> : MvSlot<FT_Q8_0, 34 * 256 / 32> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q4_K, CE_> : MvSlot<FT_Q4_K, 144> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q5_K, CE_> : MvSlot<FT_Q5_K, 176> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q6_K, CE_> : MvSlot<FT_Q6_K, 210> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_MXFP4, CE_> : MvSlot<FT_MXFP4, 17 * 512 / 32> { static constexpr int CE = 512; };
 
 template <int F, int CE> struct MvRegs {
-  static constexpr int ACB = 36 * CE / 32;                             // one token's Q8_1 chunk
-  static constexpr int NW = (16 * MvGeo<F, CE>::CB / 16 + 63) / 64;   // 16-byte weight pieces per lane
+  static constexpr int ACB = 36 * CE / 32;                              // one token's Q8_1 chunk
+  static constexpr int NW = (16 * MvGeo<F>::NPR + 63) / 64;            // 16-byte weight pieces per lane
   static constexpr int NA = (MV_MAXT * ACB / 16 + 63) / 64;           // activation pieces per lane
   u32x4 w[NW];
   u32x4 a[NA];
@@ -68,12 +79,14 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
                  const uint8_t* __restrict__ xq, int64_t xrb, int t, float* __restrict__ y, int64_t ldy) {
   constexpr int CE = MvGeo<F>::CE;
   using R = MvRegs<F, CE>;
-  constexpr int CB = MvGeo<F, CE>::CB, NWP = 16 * CB / 16, MV_ACB = R::ACB, SLICE = 16 * CB + MV_MAXT * MV_ACB;
+  using GE = MvGeo<F>;
+  constexpr int CB = GE::CB, NPR = GE::NPR, SLOT = GE::SLOT, NWP = 16 * NPR, MV_ACB = R::ACB;
+  constexpr int SLICE = 16 * SLOT + MV_MAXT * MV_ACB;
   constexpr int APT = MV_ACB / 16;   // activation pieces per token
   extern __shared__ u32x4 smem4[];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  uint8_t* wl = (uint8_t*)smem4 + wave * SLICE;   // this wave's 16 rows x CB
-  uint8_t* al = wl + 16 * CB;                     // t activation rows x MV_ACB
+  uint8_t* wl = (uint8_t*)smem4 + wave * SLICE;   // this wave's 16 row slots
+  uint8_t* al = wl + 16 * SLOT;                   // t activation rows x MV_ACB
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int nch = (int)(k / CE), c0 = wave * nch / KP, c1 = (wave + 1) * nch / KP;
   const int nap = APT * t;   // activation pieces per chunk
@@ -90,9 +103,16 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
     for (int i = 0; i < R::NW; ++i) {
       int p = lane + 64 * i;
       p = p < NWP ? p : NWP - 1;
-      const int row = p / (CB / 16), off = (p - row * (CB / 16)) * 16;
+      const int row = p / NPR;
+      int pc = p - row * NPR;
       const int64_t gr = row0 + row < n ? row0 + row : n - 1;
-      r.w[i] = *(const u32x4*)(W + gr * row_bytes + (int64_t)c * CB + off);
+      int64_t b = gr * row_bytes + (int64_t)c * CB;
+      if constexpr (GE::UNAL) {   // from the 16-byte boundary; pieces past the chunk re-read its last one
+        const int npc = ((int)(b & 15) + CB + 15) >> 4;
+        pc = pc < npc ? pc : npc - 1;
+        b &= ~(int64_t)15;
+      }
+      r.w[i] = *(const u32x4*)(W + b + 16 * pc);
     }
 #pragma unroll
     for (int i = 0; i < R::NA; ++i) {
@@ -137,7 +157,9 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const v4i zi = {0, 0, 0, 0};
 
-  auto compute = [&]() {
+  // byte offset of this lane's row chunk in its slot (Q6_K)
+  const int64_t col_row = row0 + (lane & 15) < n ? row0 + (lane & 15) : n - 1;
+  auto compute = [&](int c) {
     if constexpr (F == FT_Q4_K || F == FT_Q5_K) {
       constexpr int SBB = F == FT_Q5_K ? 176 : 144, QS = F == FT_Q5_K ? 48 : 16;   // superblock, qs offset
 #pragma unroll
@@ -169,6 +191,37 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
         }
       }
      }
+    } else if constexpr (F == FT_Q6_K) {
+      // Q6_K: ql[128] @0, qh[64] @128, int8 scales[16] @192, fp16 d @208; the
+      // 32-element block j = 4g + r holds elements 128g + 32r + l, l = 0..31, whose
+      // halves l < 16 and l >= 16 have their own scale (2j, 2j + 1): two MFMAs per
+      // block, each with the other half's lanes (kq >= 2 or kq < 2) zeroed.  Codes
+      // enter as q6 - 32 (int8).
+      const uint32_t base = (uint32_t)(col * SLOT) + (uint32_t)((col_row * row_bytes + (int64_t)c * CB) & 15);
+      const float d = lds_h2f(wl, base + 208);
+      const uint64_t sc_a = lds_u64(wl, base + 192), sc_b = lds_u64(wl, base + 200);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int g = j >> 2, rr = j & 3;
+        const uint64_t q = lds_u64(wl, base + (uint32_t)(64 * g + 32 * (rr & 1) + 8 * kq));
+        const uint64_t h = lds_u64(wl, base + (uint32_t)(128 + 32 * g + 8 * kq));
+        uint64_t x = ((q >> (4 * (rr >> 1))) & 0x0F0F0F0F0F0F0F0Full) | (((h >> (2 * rr)) & 0x0303030303030303ull) << 4);
+        // x - 32 in every byte (x <= 63): no borrow crosses a byte once bit 7 is set
+        x = ((x | 0x8080808080808080ull) - 0x2020202020202020ull) ^ 0x8080808080808080ull;
+        const uint64_t blo = kq < 2 ? x : 0ull, bhi = kq < 2 ? 0ull : x;
+        const uint64_t scw = j < 4 ? sc_a : sc_b;
+        const float sl = (float)(int8_t)(uint8_t)(scw >> (16 * (j & 3))), sh = (float)(int8_t)(uint8_t)(scw >> (16 * (j & 3) + 8));
+        const uint64_t ar = lds_u64(al, arow_off + (uint32_t)(36 * j + 4 + 8 * kq));
+        const uint64_t a = arow ? ar : 0ull;
+        const v4i Dl = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)blo, zi, 0, 0, 0);
+        const v4i Dh = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)bhi, zi, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(36 * j));
+          const float dx = sv[r] ? dxr : 0.0f;
+          acc[r] = fmaf(dx, d * fmaf(sl, (float)Dl[r], sh * (float)Dh[r]), acc[r]);
+        }
+      }
     } else {
       constexpr int BB = F == FT_Q8_0 ? 34 : F == FT_MXFP4 ? 17 : 18;
       constexpr int HB = F == FT_MXFP4 ? 1 : 2;   // header bytes (scale) before the codes
@@ -217,7 +270,7 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
     // keep the loads ahead of the compute: the scheduler would otherwise sink
     // them to their use in the next commit (shorter live ranges, no overlap)
     __builtin_amdgcn_sched_barrier(0);
-    compute();
+    compute(c);
   }
 
   // the KP parts, in order, through LDS (the slices are free now)
@@ -241,7 +294,7 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
 
 template <int F, int KP>
 static hipError_t launch_mfma_kp(const MmvqArgs& a, int64_t k, hipStream_t st) {
-  constexpr int SLICE = 16 * MvGeo<F>::CB + MV_MAXT * MvRegs<F, MvGeo<F>::CE>::ACB;
+  constexpr int SLICE = 16 * MvGeo<F>::SLOT + MV_MAXT * MvRegs<F, MvGeo<F>::CE>::ACB;
   const dim3 grid((unsigned)((a.n + 15) / 16)), block(64 * KP);
   if (a.t <= 4)
     hipLaunchKernelGGL((mmvq_mfma_kernel<F, KP, 1>), grid, block, (size_t)KP * SLICE, st, (const uint8_t*)a.W, a.n,
@@ -273,11 +326,15 @@ static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
 
 }  // namespace ftk
 
-// 2..8 tokens, K a whole number of chunks, (Q4_0 | Q8_0 | Q4_K | Q5_K | MXFP4) x Q8_1
+// 2..8 tokens, K a whole number of chunks, (Q4_0 | Q8_0 | Q4_K | Q5_K | Q6_K | MXFP4) x Q8_1
+static bool is_mmvq_mfma_format(int w) {
+  return w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4;
+}
+
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t) {
   using namespace ftk;
   const int ce = w == FT_MXFP4 ? MvGeo<FT_MXFP4>::CE : MV_CE;
-  return act == FT_Q8_1 && (w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K || w == FT_Q5_K || w == FT_MXFP4) &&
+  return act == FT_Q8_1 && is_mmvq_mfma_format(w) &&
          k % ce == 0 && k > 0 && t >= 2 && t <= MV_MAXT;
 }
 
@@ -288,6 +345,7 @@ hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st) {
     case FT_Q8_0: return launch_mfma_f<FT_Q8_0>(a, k, st);
     case FT_Q4_K: return launch_mfma_f<FT_Q4_K>(a, k, st);
     case FT_Q5_K: return launch_mfma_f<FT_Q5_K>(a, k, st);
+    case FT_Q6_K: return launch_mfma_f<FT_Q6_K>(a, k, st);
     case FT_MXFP4: return launch_mfma_f<FT_MXFP4>(a, k, st);
     default: return hipErrorInvalidValue;
   }
