@@ -23,8 +23,9 @@ import numpy as np
 BLOCK = {  # name: (elements, bytes)
     "Q4_0": (32, 18), "Q8_0": (32, 34), "Q4_K": (256, 144), "Q5_K": (256, 176),
     "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292),
+    "Q2_K": (256, 84), "Q3_K": (256, 110),
 }
-WEIGHT_FORMATS = ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4")
+WEIGHT_FORMATS = ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K")
 ACT_FORMATS = ("Q8_1", "Q8_K")
 
 
@@ -60,6 +61,11 @@ def weights(fmt: str, rows: int, k: int, g: np.random.Generator) -> np.ndarray:
         b[:, 208:210] = _fp16_scales(g, nb)  # d (scales[16] at 192 stay uniform int8)
     elif fmt == "MXFP4":
         b[:, 0] = g.integers(118, 127, size=nb, dtype=np.uint8)
+    elif fmt == "Q2_K":
+        b[:, 80:82] = _fp16_scales(g, nb)    # d
+        b[:, 82:84] = _fp16_scales(g, nb)    # dmin
+    elif fmt == "Q3_K":
+        b[:, 108:110] = _fp16_scales(g, nb)  # d
     else:
         raise ValueError(f"not a weight format: {fmt}")
     return b.reshape(rows, row_bytes(fmt, k))

@@ -22,7 +22,7 @@
 int or_block_elems(int fmt) {
   switch (fmt) {
     case OR_Q4_0: case OR_Q8_0: case OR_MXFP4: case OR_Q8_1: return 32;
-    case OR_Q4_K: case OR_Q5_K: case OR_Q6_K: case OR_Q8_K: return 256;
+    case OR_Q4_K: case OR_Q5_K: case OR_Q6_K: case OR_Q8_K: case OR_Q2_K: case OR_Q3_K: return 256;
     default: return 0;
   }
 }
@@ -37,11 +37,13 @@ int or_block_bytes(int fmt) {
     case OR_MXFP4: return 17;   /* E8M0 exponent byte, 16 bytes of E2M1 codes */
     case OR_Q8_1: return 36;    /* fp16 d, fp16 s, 32 int8 */
     case OR_Q8_K: return 292;   /* fp32 d, 256 int8, 16 int16 group sums */
+    case OR_Q2_K: return 84;    /* 16 scale/min bytes, 64 bytes of 2-bit codes, fp16 d, fp16 dmin */
+    case OR_Q3_K: return 110;   /* 32 high-bit bytes, 64 bytes of 2-bit codes, 12 scale bytes, fp16 d */
     default: return 0;
   }
 }
 
-int or_sub_elems(int wfmt) { return wfmt == OR_Q6_K ? 16 : 32; }
+int or_sub_elems(int wfmt) { return wfmt == OR_Q6_K || wfmt == OR_Q2_K || wfmt == OR_Q3_K ? 16 : 32; }
 
 int or_threads(void) {
 #ifdef _OPENMP
@@ -196,6 +198,33 @@ static int code_mxfp4(const uint8_t* b, int e) {
   return e2m1_doubled(c);
 }
 
+/* Q2_K and Q3_K share one code order: element e = 128g + 32r + l (g<2, r<4, l<32)
+   takes bits 2r..2r+1 of byte 32g + l of the 64 code bytes; its sub-block is e/16.
+   Q2_K: scales[16] @0 (low nibble scale, high nibble min), codes @16, d @80,
+   dmin @82;  w = (d * sc_j) * q - dmin * m_j with q in 0..3. */
+static int code_q2_k(const uint8_t* b, int e) {
+  int g = e / 128, r = (e / 32) & 3, l = e & 31;
+  return (b[16 + 32 * g + l] >> (2 * r)) & 3;
+}
+
+/* Q3_K: hmask[32] @0, codes @32, scales[12] @96, d @108.  The third bit of element
+   e is bit (4g + r) of hmask[l]; q = low two bits + 4 * third bit - 4, in -4..3. */
+static int code_q3_k(const uint8_t* b, int e) {
+  int g = e / 128, r = (e / 32) & 3, l = e & 31;
+  int lo = (b[32 + 32 * g + l] >> (2 * r)) & 3;
+  int hi = (b[l] >> (4 * g + r)) & 1;
+  return lo + 4 * hi - 4;
+}
+
+/* Q3_K signed 6-bit scale of sub-block j (0..15), stored plus 32: the low four bits
+   are the low nibble of byte j for j<8 and the high nibble of byte j-8 for j>=8; the
+   top two bits are bits 2(j/4)..2(j/4)+1 of byte 8 + j%4. */
+static int q3k_scale(const uint8_t* sc12, int j) {
+  int lo = j < 8 ? (sc12[j] & 15) : (sc12[j - 8] >> 4);
+  int hi = (sc12[8 + (j & 3)] >> (2 * (j >> 2))) & 3;
+  return (lo | (hi << 4)) - 32;
+}
+
 /* integer code of weight element e */
 static int wcode(int fmt, const uint8_t* b, int e) {
   switch (fmt) {
@@ -205,6 +234,8 @@ static int wcode(int fmt, const uint8_t* b, int e) {
     case OR_Q5_K: return code_q5_k(b, e);
     case OR_Q6_K: return code_q6_k(b, e);
     case OR_MXFP4: return code_mxfp4(b, e);
+    case OR_Q2_K: return code_q2_k(b, e);
+    case OR_Q3_K: return code_q3_k(b, e);
     default: return 0;
   }
 }
@@ -228,6 +259,11 @@ static void wscale(int fmt, const uint8_t* b, int e, double* scale, double* mn) 
     }
     case OR_Q6_K: *scale = f16d(b + 208) * (double)(int8_t)b[192 + e / 16]; break;
     case OR_MXFP4: *scale = e8m0_half(b[0]); break;
+    case OR_Q2_K:
+      *scale = f16d(b + 80) * (b[e / 16] & 15);
+      *mn = f16d(b + 82) * (b[e / 16] >> 4);
+      break;
+    case OR_Q3_K: *scale = f16d(b + 108) * q3k_scale(b + 96, e / 16); break;
     default: *scale = 0.0;
   }
 }
@@ -254,7 +290,7 @@ double or_elem(int fmt, const uint8_t* b, int e) {
   return scale * wcode(fmt, b, e) - mn;
 }
 
-static int is_weight(int f) { return f >= OR_Q4_0 && f <= OR_MXFP4; }
+static int is_weight(int f) { return (f >= OR_Q4_0 && f <= OR_MXFP4) || f == OR_Q2_K || f == OR_Q3_K; }
 static int is_act(int f) { return f == OR_Q8_1 || f == OR_Q8_K; }
 
 void or_dequant_f32(int fmt, const uint8_t* blocks, int64_t rows, int64_t k, float* out) {

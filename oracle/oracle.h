@@ -35,12 +35,12 @@ extern "C" {
 /* oracle format codes */
 enum {
   OR_Q4_0 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_Q5_K = 3, OR_Q6_K = 4, OR_MXFP4 = 5,
-  OR_Q8_1 = 6, OR_Q8_K = 7
+  OR_Q8_1 = 6, OR_Q8_K = 7, OR_Q2_K = 8, OR_Q3_K = 9
 };
 
 int    or_block_elems(int fmt);            /* 32 or 256, 0 for unknown */
 int    or_block_bytes(int fmt);            /* bytes per block, 0 for unknown */
-int    or_sub_elems(int wfmt);             /* elements per integer partial: 16 for Q6_K, else 32 */
+int    or_sub_elems(int wfmt);             /* elements per integer partial: 16 for Q2_K, Q3_K, Q6_K, else 32 */
 int    or_threads(void);                   /* OpenMP threads the oracle will use */
 
 /* IEEE binary16 <-> binary32, written by hand (round to nearest even). */

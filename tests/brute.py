@@ -18,7 +18,8 @@ E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
                         -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
 
 BLOCK = {"Q4_0": (32, 18), "Q8_0": (32, 34), "Q4_K": (256, 144), "Q5_K": (256, 176),
-         "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292)}
+         "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292),
+         "Q2_K": (256, 84), "Q3_K": (256, 110)}
 
 
 def _blocks(fmt, data):
@@ -87,6 +88,26 @@ def unpack(fmt, data):
         sc = b[:, 192:208].view(np.int8).astype(np.float64)          # [nb, 16]
         scale = np.repeat(_f16(b[:, 208:210])[:, None] * sc, 16, 1)
         off = np.zeros_like(scale)
+    elif fmt in ("Q2_K", "Q3_K"):
+        # 64 code bytes as [g][l]; the element order is (g, r, l) with the 2-bit
+        # field r of each byte
+        qb = b[:, 16:80] if fmt == "Q2_K" else b[:, 32:96]
+        qb = qb.astype(np.int64).reshape(nb, 2, 1, 32)
+        code = ((qb >> (2 * np.arange(4)[None, None, :, None])) & 3).reshape(nb, 256)
+        if fmt == "Q2_K":
+            s = b[:, 0:16].astype(np.int64)
+            scale = np.repeat(_f16(b[:, 80:82])[:, None] * (s & 15), 16, 1)
+            off = np.repeat(_f16(b[:, 82:84])[:, None] * (s >> 4), 16, 1)
+        else:
+            hm = b[:, 0:32].astype(np.int64)                               # [nb, l]
+            third = (hm[:, None, :] >> np.arange(8)[None, :, None]) & 1    # [nb, 4g + r, l]
+            code = code + 4 * third.reshape(nb, 256) - 4
+            s = b[:, 96:108].astype(np.int64)
+            low = np.concatenate([s[:, 0:8] & 15, s[:, 0:8] >> 4], 1)      # scales 0..15
+            top = np.concatenate([(s[:, 8:12] >> (2 * q)) & 3 for q in range(4)], 1)
+            sc = (low | (top << 4)) - 32
+            scale = np.repeat(_f16(b[:, 108:110])[:, None] * sc, 16, 1)
+            off = np.zeros_like(scale)
     elif fmt == "MXFP4":
         c = _nibbles_q4_0_order(b[:, 1:17])
         code = (2 * E2M1_VALUES[c]).astype(np.int64)                 # doubled: integers

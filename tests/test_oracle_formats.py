@@ -37,7 +37,8 @@ def test_every_bit_flip_matches_brute(fmt):
     base = synth.weights(fmt, 1, be, synth.rng(2, WF.index(fmt)))[0].copy()
     # keep the fp16 / E8M0 scale fields fixed at sane values; flip every other bit
     scale_bytes = {"Q4_0": {0, 1}, "Q8_0": {0, 1}, "Q4_K": {0, 1, 2, 3}, "Q5_K": {0, 1, 2, 3},
-                   "Q6_K": {208, 209}, "MXFP4": {0}}[fmt]
+                   "Q6_K": {208, 209}, "MXFP4": {0}, "Q2_K": {80, 81, 82, 83},
+                   "Q3_K": {108, 109}}[fmt]
     for byte in range(bb):
         if byte in scale_bytes:
             continue
@@ -122,6 +123,68 @@ def test_q6_k_closed_form():
                           sc.view(np.uint8), _f16bytes(d)])
     w = oracle.dequant("Q6_K", blk, 1, 256)[0]
     assert np.array_equal(w, np.repeat(d * sc.astype(np.float64) * 31.0, 16).astype(np.float32))
+
+
+# Q2_K / Q3_K: the 2-bit field r of code byte 32g + l holds element 128g + 32r + l;
+# 16-element sub-blocks, so element e uses scale e // 16.
+def _elem_r(e):
+    return (e // 32) % 4
+
+
+def test_q2_k_closed_form():
+    d, dmin = 2.0 ** -4, 2.0 ** -6
+    scales = np.array([j | ((15 - j) << 4) for j in range(16)], np.uint8)  # sc_j = j, m_j = 15 - j
+    codes = np.full(64, 0b11100100, np.uint8)                               # field r holds r
+    blk = np.concatenate([scales, codes, _f16bytes(d), _f16bytes(dmin)])
+    w = oracle.dequant("Q2_K", blk, 1, 256)[0]
+    e = np.arange(256)
+    expect = d * (e // 16) * _elem_r(e) - dmin * (15 - e // 16)
+    assert np.array_equal(w, expect.astype(np.float32))
+
+
+@pytest.mark.parametrize("g,r,l", [(0, 0, 0), (1, 1, 5), (0, 3, 31), (1, 2, 16)])
+def test_q2_k_code_position(g, r, l):
+    codes = np.zeros(64, np.uint8)
+    codes[32 * g + l] = 2 << (2 * r)
+    blk = np.concatenate([np.full(16, 1, np.uint8), codes, _f16bytes(1.0), _f16bytes(0.0)])
+    w = oracle.dequant("Q2_K", blk, 1, 256)[0]
+    assert list(np.nonzero(w)[0]) == [128 * g + 32 * r + l] and w[128 * g + 32 * r + l] == 2.0
+
+
+def _pack_q3k_scales(u):
+    """Sixteen 6-bit stored scales (value + 32) -> the 12 packed bytes: low four bits
+    in the low nibbles of bytes 0-7 (scales 0-7) and their high nibbles (8-15), the top
+    two bits of scale j in bits 2(j // 4) of byte 8 + j % 4."""
+    b = np.zeros(12, np.uint8)
+    for j in range(16):
+        b[j % 8] |= (u[j] & 15) << (4 * (j // 8))
+        b[8 + j % 4] |= (u[j] >> 4) << (2 * (j // 4))
+    return b
+
+
+@pytest.mark.parametrize("third", [0x00, 0xFF])
+def test_q3_k_closed_form(third):
+    u = np.array([(5 * j + 3) % 64 for j in range(16)])
+    d = 2.0 ** -5
+    blk = np.concatenate([np.full(32, third, np.uint8), np.full(64, 0b11100100, np.uint8),
+                          _pack_q3k_scales(u), _f16bytes(d)])
+    w = oracle.dequant("Q3_K", blk, 1, 256)[0]
+    e = np.arange(256)
+    q = _elem_r(e) - (0 if third else 4)      # third bit clear subtracts 4
+    expect = d * (u[e // 16] - 32) * q
+    assert np.array_equal(w, expect.astype(np.float32))
+
+
+@pytest.mark.parametrize("g,r,l", [(0, 0, 0), (1, 2, 7), (0, 3, 31), (1, 3, 20)])
+def test_q3_k_third_bit_position(g, r, l):
+    hm = np.zeros(32, np.uint8)
+    hm[l] = 1 << (4 * g + r)
+    blk = np.concatenate([hm, np.zeros(64, np.uint8), _pack_q3k_scales(np.full(16, 33)),
+                          _f16bytes(1.0)])
+    w = oracle.dequant("Q3_K", blk, 1, 256)[0]
+    # every code is 0 - 4 except the one whose third bit is set
+    e = 128 * g + 32 * r + l
+    assert w[e] == 0.0 and np.all(np.delete(w, e) == -4.0)
 
 
 @pytest.mark.parametrize("e8", [0, 1, 2, 118, 126, 127, 128, 254])
