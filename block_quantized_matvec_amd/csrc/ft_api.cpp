@@ -19,10 +19,11 @@
 
 namespace {
 
-constexpr int kElems[8] = {32, 32, 256, 256, 256, 32, 32, 256};
-constexpr int kBytes[8] = {18, 34, 144, 176, 210, 17, 36, 292};
+constexpr int kTypes = 10;
+constexpr int kElems[kTypes] = {32, 32, 256, 256, 256, 32, 32, 256, 256, 256};
+constexpr int kBytes[kTypes] = {18, 34, 144, 176, 210, 17, 36, 292, 84, 110};
 
-bool is_weight(int t) { return t >= FT_Q4_0 && t <= FT_MXFP4; }
+bool is_weight(int t) { return (t >= FT_Q4_0 && t <= FT_MXFP4) || t == FT_Q2_K || t == FT_Q3_K; }
 bool is_act(int t) { return t == FT_Q8_1 || t == FT_Q8_K; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int64_t row_bytes_of(int type, int64_t k) { return k / kElems[type] * kBytes[type]; }
@@ -122,8 +123,8 @@ bool grouped_pair(int w, int a) {
 
 extern "C" {
 
-int ft_block_elems(ft_type t) { return ((int)t >= 0 && (int)t < 8) ? kElems[t] : 0; }
-size_t ft_block_bytes(ft_type t) { return ((int)t >= 0 && (int)t < 8) ? (size_t)kBytes[t] : 0; }
+int ft_block_elems(ft_type t) { return ((int)t >= 0 && (int)t < kTypes) ? kElems[t] : 0; }
+size_t ft_block_bytes(ft_type t) { return ((int)t >= 0 && (int)t < kTypes) ? (size_t)kBytes[t] : 0; }
 
 const char* ft_version(void) { return "ft 0.1 (gfx950)"; }
 

@@ -105,6 +105,32 @@ template <> struct Fmt<FT_Q6_K> {
   __device__ static constexpr int seg_of(int j) { return j >> 1; }
 };
 
+// Q2_K: scales[16] @0 (low nibble scale, high nibble min of 16-element sub-block
+// j), qs[64] @16, fp16 d @80, dmin @82.  Element e = 128g + 32r + l is bits
+// 2r..2r+1 of qs[32g + l]; w = d*sc_j*q - dmin*m_j with j = e/16.  Unit ui = 4g + r
+// covers that (g, r): dwords 0-3 are sub-block 2ui, dwords 4-7 sub-block 2ui+1.
+template <> struct Fmt<FT_Q2_K> {
+  static constexpr int BLK = 256, BB = 84, UPB = 8, NW = 8, S = 2, SUB = 16;
+  static constexpr bool XF1 = false;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int CODE_OFF = 0;
+  __device__ static int act_elem(int ui, int j) { return 32 * ui + 4 * j; }
+  __device__ static constexpr int seg_of(int j) { return j >> 2; }
+};
+// Q3_K: hmask[32] @0, qs[64] @32, scales[12] @96, fp16 d @108.  Codes as Q2_K plus
+// a third bit, bit 4g + r of hmask[l]; the unit carries q + 4 (0..7) and the -4
+// offset enters through wmin = 4 * wscale.  Signed 6-bit scale of sub-block j,
+// stored plus 32: low four bits in the low (j < 8) or high (j >= 8) nibble of
+// scales[j % 8], top two bits at bit 2(j/4) of scales[8 + j % 4].
+template <> struct Fmt<FT_Q3_K> {
+  static constexpr int BLK = 256, BB = 110, UPB = 8, NW = 8, S = 2, SUB = 16;
+  static constexpr bool XF1 = false;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int CODE_OFF = 4;
+  __device__ static int act_elem(int ui, int j) { return 32 * ui + 4 * j; }
+  __device__ static constexpr int seg_of(int j) { return j >> 2; }
+};
+
 template <int A> struct Act;
 template <> struct Act<FT_Q8_1> { static constexpr int BLK = 32, BB = 36; };
 template <> struct Act<FT_Q8_K> { static constexpr int BLK = 256, BB = 292; };
@@ -314,6 +340,37 @@ __device__ __forceinline__ void unpack_unit(const R& rd, uint32_t bo, int ui, Un
       if constexpr (F == FT_Q5_K) rd.template dwords<8>(bo + 16, qh);
     }
     kq_unit<F>(h, q, qh, ui, u);
+  } else if constexpr (F == FT_Q2_K || F == FT_Q3_K) {
+    const int g = ui >> 2, r = ui & 3;
+    uint32_t q[8];
+    rd.template dwords<8>(bo + (F == FT_Q2_K ? 16 : 32) + 32 * g, q);
+    if constexpr (F == FT_Q2_K) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) u.w[m] = (q[m] >> (2 * r)) & 0x03030303u;
+      const uint32_t sc = rd.u16(bo + 2 * ui);   // scale|min bytes of sub-blocks 2ui, 2ui+1
+      const uint32_t dd = rd.u32(bo + 80);
+      const float d = h2f(dd & 0xFFFF), dmin = h2f(dd >> 16);
+      u.ws[0] = d * (float)(sc & 15);
+      u.wm[0] = dmin * (float)((sc >> 4) & 15);
+      u.ws[1] = d * (float)((sc >> 8) & 15);
+      u.wm[1] = dmin * (float)(sc >> 12);
+    } else {
+      uint32_t hm[8];
+      rd.template dwords<8>(bo, hm);
+      const int hb = 4 * g + r;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        u.w[m] = ((q[m] >> (2 * r)) & 0x03030303u) | (((hm[m] >> hb) & 0x01010101u) << 2);
+      const float d = h2f(rd.u16(bo + 108));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int j = 2 * ui + s;
+        const uint32_t lo = (rd.u8(bo + 96 + (j & 7)) >> (j < 8 ? 0 : 4)) & 15;
+        const uint32_t hi = (rd.u8(bo + 104 + (j & 3)) >> (2 * (j >> 2))) & 3;
+        u.ws[s] = d * (float)((int)(lo | (hi << 4)) - 32);
+        u.wm[s] = 4.0f * u.ws[s];
+      }
+    }
   } else {  // Q6_K
     const int g = ui >> 2, l0 = 8 * (ui & 3);
     uint32_t qa[2], qb[2], qh[2];

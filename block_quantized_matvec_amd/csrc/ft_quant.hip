@@ -146,6 +146,22 @@ __device__ __forceinline__ float elem_value(const Reader<const uint32_t*>& rd, u
     const float a = (d * (float)sc) * (float)n;   // exact
     const float b = dmin * (float)m;              // exact
     return a - b;                                 // one rounding
+  } else if constexpr (F == FT_Q2_K) {
+    const int g = e >> 7, r = (e >> 5) & 3, l = e & 31;
+    const int q = (int)((rd.u8(bo + 16 + 32 * g + l) >> (2 * r)) & 3);
+    const uint32_t sm = rd.u8(bo + (e >> 4));
+    const uint32_t dd = rd.u32(bo + 80);
+    const float a = (h2f(dd & 0xFFFF) * (float)(sm & 15)) * (float)q;   // exact
+    const float b = h2f(dd >> 16) * (float)(sm >> 4);                     // exact
+    return a - b;                                                         // one rounding
+  } else if constexpr (F == FT_Q3_K) {
+    const int g = e >> 7, r = (e >> 5) & 3, l = e & 31, j = e >> 4;
+    const int lo2 = (int)((rd.u8(bo + 32 + 32 * g + l) >> (2 * r)) & 3);
+    const int third = (int)((rd.u8(bo + l) >> (4 * g + r)) & 1);
+    const uint32_t lo = (rd.u8(bo + 96 + (j & 7)) >> (j < 8 ? 0 : 4)) & 15;
+    const uint32_t hi = (rd.u8(bo + 104 + (j & 3)) >> (2 * (j >> 2))) & 3;
+    const float sc = (float)((int)(lo | (hi << 4)) - 32);
+    return (h2f(rd.u16(bo + 108)) * sc) * (float)(lo2 + 4 * third - 4);
   } else {  // Q6_K
     const int g = e >> 7, r = (e >> 5) & 3, l = e & 31;
     const uint32_t lq = rd.u8(bo + 64 * g + 32 * (r & 1) + l);
@@ -267,6 +283,8 @@ hipError_t ftk_launch_dequant(int w, const void* blocks, int64_t rows, int64_t k
     case FT_Q5_K: return launch_dequant_t<FT_Q5_K>(blocks, rows, k, out, st);
     case FT_Q6_K: return launch_dequant_t<FT_Q6_K>(blocks, rows, k, out, st);
     case FT_MXFP4: return launch_dequant_t<FT_MXFP4>(blocks, rows, k, out, st);
+    case FT_Q2_K: return launch_dequant_t<FT_Q2_K>(blocks, rows, k, out, st);
+    case FT_Q3_K: return launch_dequant_t<FT_Q3_K>(blocks, rows, k, out, st);
   }
   return hipErrorInvalidValue;
 }
@@ -289,6 +307,7 @@ hipError_t ftk_launch_block_dots(int w, const void* W, int64_t n, int64_t k, int
                           : launch_dots_t<F, FT_Q8_K>(W, n, k, xq, t, partials, st);
   switch (w) {
     FT_D(FT_Q4_0) FT_D(FT_Q8_0) FT_D(FT_Q4_K) FT_D(FT_Q5_K) FT_D(FT_Q6_K) FT_D(FT_MXFP4)
+    FT_D(FT_Q2_K) FT_D(FT_Q3_K)
   }
 #undef FT_D
   return hipErrorInvalidValue;

@@ -15,7 +15,8 @@ import torch  # loaded first so libft.so binds to the same HIP runtime as torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libft.so")
 
-TYPES = {"Q4_0": 0, "Q8_0": 1, "Q4_K": 2, "Q5_K": 3, "Q6_K": 4, "MXFP4": 5, "Q8_1": 6, "Q8_K": 7}
+TYPES = {"Q4_0": 0, "Q8_0": 1, "Q4_K": 2, "Q5_K": 3, "Q6_K": 4, "MXFP4": 5, "Q8_1": 6, "Q8_K": 7,
+         "Q2_K": 8, "Q3_K": 9}
 OPS = {"quantize": 0, "dequant": 1, "mmvq": 2, "moe_vec": 3, "grouped": 4, "block_dots": 5}
 STATUS = {0: "FT_OK", 1: "FT_ERR_INVALID_ARG", 2: "FT_ERR_UNSUPPORTED", 3: "FT_ERR_SHAPE",
           4: "FT_ERR_ALIGNMENT", 5: "FT_ERR_NO_SCRATCH", 6: "FT_ERR_HIP"}
@@ -227,7 +228,7 @@ def debug_block_dots(w: str, W: torch.Tensor, n: int, k: int, act: str, xq: torc
                      stream=None) -> torch.Tensor:
     _dev(W, "W")
     _dev(xq, "xq")
-    sub = 16 if w == "Q6_K" else 32
+    sub = 16 if w in ("Q6_K", "Q2_K", "Q3_K") else 32
     out = torch.empty((t, n, k // sub), dtype=torch.int32, device=W.device)
     _check(lib().ft_debug_block_dots(TYPES[w], _ptr(W), n, k, TYPES[act], _ptr(xq), t, _ptr(out),
                                      _stream(stream)), "ft_debug_block_dots")

@@ -62,7 +62,11 @@ typedef enum {
                    fp16 d; w = d*sc*(q6-32) per 16-element sub-block         210 B */
   FT_MXFP4 = 5, /* 32: E8M0 exponent e, 16 B E2M1 codes; w = E2M1*2^(e-127)   17 B */
   FT_Q8_1 = 6,  /* activation, 32: fp16 d, fp16 s = d*sum(q), 32 int8         36 B */
-  FT_Q8_K = 7   /* activation, 256: fp32 d, 256 int8, 16 int16 group sums   292 B */
+  FT_Q8_K = 7,  /* activation, 256: fp32 d, 256 int8, 16 int16 group sums   292 B */
+  FT_Q2_K = 8,  /* 256: 16 B of 4-bit scale|min pairs, 64 B of 2-bit codes, fp16 d,
+                   fp16 dmin; w = d*sc*q - dmin*m per 16 elements              84 B */
+  FT_Q3_K = 9   /* 256: 32 B third bits, 64 B of 2-bit codes, 12 B of 6-bit
+                   scales (+32), fp16 d; w = d*(sc-32)*(q-4) per 16 elements 110 B */
 } ft_type;
 
 typedef enum {
@@ -119,8 +123,9 @@ ft_status ft_dequant(ft_type w, const void* blocks, int64_t rows, int64_t k, flo
    integer dots per block followed by an fp32 scale combine.  Any t >= 0 (t = 0 is a
    no-op); batches beyond 8 tokens are processed 8 at a time.  Supported (w, act):
    every weight type x FT_Q8_1.  From 2-5 tokens on (the threshold depends on the
-   format and on k) every format runs on the int8 matrix cores when k is a multiple
-   of 256 (512 for MXFP4); the result is the same integer dots either way. */
+   format and on k) every format but Q2_K and Q3_K runs on the int8 matrix cores when
+   k is a multiple of 256 (512 for MXFP4); the result is the same integer dots
+   either way. */
 ft_status ft_mul_mat_vec_q(ft_type w, const void* W, int64_t n, int64_t k,
                            ft_type act, const void* xq, int64_t t,
                            float* y, int64_t ldy, ft_stream_t stream);
@@ -184,10 +189,11 @@ ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t 
                             float* y, ft_stream_t stream);
 
 /* Integer partials of the block dots (debug tap; [P3 What changed: bit-identical
-   integer core]).  partials: [t][n][k/sub] int32, sub = 16 for Q6_K and 32 otherwise:
-   the sum over each sub-block of the weight's integer code (n-8 for Q4_0, q for Q8_0,
-   the 4/5-bit n for Q4_K/Q5_K, q6-32 for Q6_K, twice the E2M1 value for MXFP4) times
-   the activation's int8 code.  Computed by the same unpack and dot core as the
+   integer core]).  partials: [t][n][k/sub] int32, sub = 16 for Q2_K, Q3_K and Q6_K
+   and 32 otherwise: the sum over each sub-block of the weight's integer code (n-8 for
+   Q4_0, q for Q8_0, the 4/5-bit n for Q4_K/Q5_K, q6-32 for Q6_K, twice the E2M1 value
+   for MXFP4, the 2-bit q for Q2_K, the 3-bit q-4 for Q3_K) times the activation's
+   int8 code.  Computed by the same unpack and dot core as the
    matvec kernels. */
 ft_status ft_debug_block_dots(ft_type w, const void* W, int64_t n, int64_t k,
                               ft_type act, const void* xq, int64_t t,

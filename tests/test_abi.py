@@ -17,7 +17,7 @@ from block_quantized_matvec_amd import ft
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-W = ["Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4"]
+W = ["Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K"]
 A = ["Q8_1", "Q8_K"]
 ST = {v: k for k, v in ft.STATUS.items()}
 
@@ -39,14 +39,15 @@ def test_every_declared_symbol_is_exported():
 
 def test_block_sizes():
     sizes = {"Q4_0": (32, 18), "Q8_0": (32, 34), "Q4_K": (256, 144), "Q5_K": (256, 176),
-             "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292)}
+             "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292),
+             "Q2_K": (256, 84), "Q3_K": (256, 110)}
     for t, (e, b) in sizes.items():
         assert ft.block_elems(t) == e and ft.block_bytes(t) == b
     assert ft.lib().ft_block_elems(99) == 0 and ft.lib().ft_block_bytes(-1) == 0
 
 
 def test_capability_table():
-    expect_mmvq = {(w, "Q8_1") for w in ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4")}
+    expect_mmvq = {(w, "Q8_1") for w in W}
     expect_moe = {("Q4_K", "Q8_1"), ("MXFP4", "Q8_K")}
     expect_grp = {("Q4_K", "Q8_K"), ("Q5_K", "Q8_K"), ("Q6_K", "Q8_K"), ("MXFP4", "Q8_K")}
     for w in W:
