@@ -10,7 +10,8 @@ whole path (activation quantize + quantized matvec) over all 16 cases.  Weights
 are resident in HBM before timing; every case rotates over enough distinct
 weight copies that no launch can be served from the 256 MB last-level cache.
 
-Other workloads (--workload): q4_0_matvec, moe_q4k, moe_mxfp4, grouped_kq.
+Other workloads (--workload): q4_0_matvec, moe_q4k, moe_mxfp4, grouped_kq, and
+formats (every weight format x Q8_1 at W 14336x4096, 1/2/4/8 tokens; no CPU leg).
 """
 from __future__ import annotations
 
@@ -62,7 +63,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_decode",
                     choices=["dense_decode", "q4_0_matvec", "moe_q4k", "moe_mxfp4", "grouped_kq", "counters",
-                             "ceilings"])
+                             "ceilings", "formats"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies per matrix (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=str, default="", help="comma list overriding the token counts")
@@ -90,7 +91,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     ft.lib()
-    fn = {"dense_decode": bench_dense, "q4_0_matvec": bench_q4_0, "moe_q4k": bench_moe,
+    fn = {"dense_decode": bench_dense, "formats": bench_dense, "q4_0_matvec": bench_q4_0, "moe_q4k": bench_moe,
           "moe_mxfp4": bench_moe, "grouped_kq": bench_grouped, "counters": run_counters,
           "ceilings": lambda a, n, t, f, s: measure_ceilings(t, f)}[args.workload]
     out = fn(args, np, torch, ft, synth)
@@ -221,7 +222,8 @@ def _cpu_baseline(fn, sample_desc, unit, work, min_seconds=10.0):
 # dense decode matvec (the headline workload)
 # ---------------------------------------------------------------------------
 def bench_dense(args, np, torch, ft, synth):
-    cfg = synth.DENSE_DECODE
+    fmts_only = args.workload == "formats"
+    cfg = synth.DECODE_FORMATS if fmts_only else synth.DENSE_DECODE
     tokens = [int(x) for x in args.tokens.split(",")] if args.tokens else list(cfg["tokens"])
     g = synth.rng(7, 1)
     mats = {}
@@ -229,15 +231,17 @@ def bench_dense(args, np, torch, ft, synth):
         for (n, k) in cfg["shapes"]:
             W = synth.weights(fmt, n, k, g)
             mats[(fmt, n, k)] = W
-    # each matrix is used once per token count per step and every use takes the
-    # next copy: with 8 copies, >= 1.5 GB of other weights stream between two
-    # uses of one copy (the last-level cache is 256 MB)
+    # every use of a matrix takes its next copy; a matrix has at least 8 copies and
+    # enough that >= 600 MB of its other copies stream between two uses of one copy
+    # (the last-level cache is 256 MB), also in the per-case graphs below, which
+    # launch one case only
     total = sum(W.nbytes for W in mats.values())
-    copies = args.copies or 8
+    ncp = {key: args.copies or max(8, -(-600_000_000 // W.nbytes) + 1) for key, W in mats.items()}
+    copies = max(ncp.values())
     dev = {key: [torch.from_numpy(W).cuda()] for key, W in mats.items()}
     for key in dev:
         base = dev[key][0]
-        dev[key] += [base.clone() for _ in range(copies - 1)]
+        dev[key] += [base.clone() for _ in range(ncp[key] - 1)]
     xs = {(k, t): synth.activations(t, k, g) for (_, _, k) in mats for t in tokens}
     dxs = {key: torch.from_numpy(v).cuda() for key, v in xs.items()}
     xq = {(k, t): torch.empty((t, ft.row_bytes("Q8_1", k)), dtype=torch.uint8, device="cuda")
@@ -249,7 +253,8 @@ def bench_dense(args, np, torch, ft, synth):
         """one pass of the path over every case, weight copy j"""
         for (fmt, n, k, t) in cases:
             ft.quantize_act("Q8_1", dxs[(k, t)], out=xq[(k, t)])
-            ft.mul_mat_vec_q(fmt, dev[(fmt, n, k)][j], n, k, "Q8_1", xq[(k, t)], t, out=ys[(fmt, n, k, t)])
+            cp = dev[(fmt, n, k)]
+            ft.mul_mat_vec_q(fmt, cp[j % len(cp)], n, k, "Q8_1", xq[(k, t)], t, out=ys[(fmt, n, k, t)])
 
     # one graph holds `copies` consecutive steps (step j reads weight copy j)
     g_steps = _graph(torch, lambda: [step(j) for j in range(copies)])
@@ -267,13 +272,14 @@ def bench_dense(args, np, torch, ft, synth):
     # per-case kernel duration: a graph of R back-to-back launches of that case's
     # matvec over the rotating copies; the median of 7 replays, each timed with two
     # events on the launch stream
-    R = 8 * copies
     wbytes = {c: mats[c[:3]].nbytes for c in cases}
     abytes = {c: c[3] * ft.row_bytes("Q8_1", c[2]) + 4 * c[3] * c[1] for c in cases}
     per_case, kus = [], {}
     for c in cases:
         fmt, n, k, t = c
-        gk = _graph(torch, lambda: [ft.mul_mat_vec_q(fmt, dev[(fmt, n, k)][i % copies], n, k, "Q8_1",
+        cp = dev[(fmt, n, k)]
+        R = 8 * len(cp)
+        gk = _graph(torch, lambda: [ft.mul_mat_vec_q(fmt, cp[i % len(cp)], n, k, "Q8_1",
                                                      xq[(k, t)], t, out=ys[c]) for i in range(R)])
         us = _time_graph_median(torch, gk) / R * 1e6
         kus[c] = us
@@ -297,10 +303,13 @@ def bench_dense(args, np, torch, ft, synth):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8 dot4 -> i32, f32 scale combine",
         "data": "synthetic (seeded GGUF blocks, N(0,1) activations)",
-        "config": {"workload": "dense decode matvec: Q8_0 and Q4_K, W 14336x4096 and 4096x14336, "
-                               f"batch {'/'.join(map(str, tokens))}, Q8_1 activations; step = quantize + "
+        "config": {"workload": (f"decode matvec, every weight format ({'/'.join(cfg['formats'])}), "
+                                "W 14336x4096" if fmts_only else
+                                "dense decode matvec: Q8_0 and Q4_K, W 14336x4096 and 4096x14336")
+                               + f", batch {'/'.join(map(str, tokens))}, Q8_1 activations; step = quantize + "
                                "matvec for all cases, replayed as a HIP graph",
-                   "cases": len(cases), "weight_copies_per_matrix": copies,
+                   "cases": len(cases),
+                   "weight_copies_per_matrix": {f"{f} {n}x{k}": c for (f, n, k), c in ncp.items()},
                    "weight_bytes_per_step": total_w},
         "roofline": {"bound": "hbm", "kernel": f"mmvq {hc[0]} {hc[1]}x{hc[2]} t={hc[3]}",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -309,7 +318,7 @@ def bench_dense(args, np, torch, ft, synth):
         "cases": per_case,
     }
     _add_ceilings(out, torch, ft)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fmts_only:
         import oracle
         xqs = {key: oracle.quantize("Q8_1", v) for key, v in xs.items()}
 

@@ -1,8 +1,9 @@
 // ft_mmvq_mfma.hip -- Q-matvec for 2..8 tokens on the int8 matrix cores
-// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0, Q4_K, Q5_K, Q6_K and MXFP4 weights against
-// Q8_1 activations (Q5_K adds the fifth bits to Q4_K's nibbles; Q6_K enters as q6 -
-// 32 with one MFMA per 16-element scale group; MXFP4 as twice its E2M1 values with
-// 2^(e-128) as the block scale, in 512-element chunks).
+// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0, Q4_K, Q5_K, Q6_K, MXFP4, Q2_K and Q3_K
+// weights against Q8_1 activations (Q5_K adds the fifth bits to Q4_K's nibbles;
+// Q6_K enters as q6 - 32 with one MFMA per 16-element scale group, and so do Q2_K's
+// 2-bit codes and Q3_K's q - 4; MXFP4 as twice its E2M1 values with 2^(e-128) as
+// the block scale, in 512-element chunks).
 //
 // ggml-cuda "mul_mat_vec_q" (the pages' MMVQ path, ds4 PR #656 Summary): a block's
 // integer dot product of weight and activation codes, then the fp32 scale
@@ -35,9 +36,9 @@ constexpr int MV_CE = 256;   // elements of a row per chunk (512 for MXFP4)
 
 // elements CE of a row's chunk and its bytes CB; a row's chunk goes to an LDS slot of
 // NPR 16-byte pieces.  Chunks of whole pieces (CB % 16 == 0; MXFP4's 17-byte blocks
-// need 512-element chunks for that) sit at the slot's start; Q6_K's 210-byte chunks
-// are copied from the 16-byte boundary below them, one piece more, and read at
-// their byte offset in the slot.
+// need 512-element chunks for that) sit at the slot's start; Q6_K's 210-, Q3_K's
+// 110- and Q2_K's 84-byte chunks are copied from the 16-byte boundary below them,
+// one piece more, and read at their byte offset in the slot.
 template <int F_, int CB_> struct MvSlot {
   static constexpr int CB = CB_;
   static constexpr bool UNAL = CB % 16 != 0;
@@ -51,6 +52,8 @@ template <int CE_> struct MvGeo<FT_Q4_K, CE_> : MvSlot<FT_Q4_K, 144> { static co
 template <int CE_> struct MvGeo<FT_Q5_K, CE_> : MvSlot<FT_Q5_K, 176> { static constexpr int CE = 256; };
 template <int CE_> struct MvGeo<FT_Q6_K, CE_> : MvSlot<FT_Q6_K, 210> { static constexpr int CE = 256; };
 template <int CE_> struct MvGeo<FT_MXFP4, CE_> : MvSlot<FT_MXFP4, 17 * 512 / 32> { static constexpr int CE = 512; };
+template <int CE_> struct MvGeo<FT_Q2_K, CE_> : MvSlot<FT_Q2_K, 84> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q3_K, CE_> : MvSlot<FT_Q3_K, 110> { static constexpr int CE = 256; };
 
 template <int F, int CE> struct MvRegs {
   static constexpr int ACB = 36 * CE / 32;                              // one token's Q8_1 chunk
@@ -222,6 +225,79 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
           acc[r] = fmaf(dx, d * fmaf(sl, (float)Dl[r], sh * (float)Dh[r]), acc[r]);
         }
       }
+    } else if constexpr (F == FT_Q2_K || F == FT_Q3_K) {
+      // Q2_K: scale|min bytes[16] @0, qs[64] @16, d @80, dmin @82.  Q3_K: hmask[32]
+      // @0, qs[64] @32, 6-bit scales[12] @96, d @108.  The 32-element block
+      // j = 4g + r holds elements 128g + 32r + l: bits 2r..2r+1 of qs[32g + l]
+      // (Q3_K: bit 4g + r of hmask[l] is the third bit; codes enter as q - 4).
+      // Its halves l < 16 and l >= 16 are sub-blocks 2j and 2j + 1 with their own
+      // scales: two MFMAs per block with the other half's lanes zeroed, and for
+      // Q2_K's mins two more against all-ones halves (the activation code sums).
+      const uint32_t base = (uint32_t)(col * SLOT) + (uint32_t)((col_row * row_bytes + (int64_t)c * CB) & 15);
+      constexpr uint32_t QS = F == FT_Q2_K ? 16 : 32;
+      constexpr uint64_t ONES = 0x0101010101010101ull;
+      const uint64_t olo = kq < 2 ? ONES : 0ull, ohi = kq < 2 ? 0ull : ONES;
+      float d, dmin = 0.0f;
+      uint64_t sc_a = 0, sc_b = 0, hm = 0;
+      uint32_t s3[4] = {0u, 0u, 0u, 0u};
+      if constexpr (F == FT_Q2_K) {
+        d = lds_h2f(wl, base + 80);
+        dmin = lds_h2f(wl, base + 82);
+        sc_a = lds_u64(wl, base);
+        sc_b = lds_u64(wl, base + 8);
+      } else {
+        d = lds_h2f(wl, base + 108);
+        const uint64_t s01 = lds_u64(wl, base + 96);
+        const uint32_t s0 = (uint32_t)s01, s1 = (uint32_t)(s01 >> 32);
+        const uint32_t s2 = (uint32_t)lds_u64(wl, base + 104);
+        // byte p of s3[q] = stored scale 4q + p: low nibbles of bytes 0-7 are scales
+        // 0-7, their high nibbles 8-15; byte 8 + p holds the top bits of scales p,
+        // 4 + p, 8 + p, 12 + p in bit pairs 0, 2, 4, 6
+        s3[0] = (s0 & 0x0F0F0F0Fu) | ((s2 & 0x03030303u) << 4);
+        s3[1] = (s1 & 0x0F0F0F0Fu) | (((s2 >> 2) & 0x03030303u) << 4);
+        s3[2] = ((s0 >> 4) & 0x0F0F0F0Fu) | (((s2 >> 4) & 0x03030303u) << 4);
+        s3[3] = ((s1 >> 4) & 0x0F0F0F0Fu) | (((s2 >> 6) & 0x03030303u) << 4);
+        hm = lds_u64(wl, base + 8 * kq);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int g = j >> 2, rr = j & 3;
+        const uint64_t q = lds_u64(wl, base + QS + (uint32_t)(32 * g + 8 * kq));
+        uint64_t x = (q >> (2 * rr)) & 0x0303030303030303ull;
+        if constexpr (F == FT_Q3_K) {
+          x |= ((hm >> (4 * g + rr)) & ONES) << 2;
+          // x - 4 in every byte (x <= 7): no borrow crosses a byte once bit 7 is set
+          x = ((x | 0x8080808080808080ull) - 0x0404040404040404ull) ^ 0x8080808080808080ull;
+        }
+        const uint64_t blo = kq < 2 ? x : 0ull, bhi = kq < 2 ? 0ull : x;
+        const uint64_t ar = lds_u64(al, arow_off + (uint32_t)(36 * j + 4 + 8 * kq));
+        const uint64_t a = arow ? ar : 0ull;
+        const v4i Dl = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)blo, zi, 0, 0, 0);
+        const v4i Dh = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)bhi, zi, 0, 0, 0);
+        if constexpr (F == FT_Q2_K) {
+          const v4i Sl = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)olo, zi, 0, 0, 0);
+          const v4i Sh = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)ohi, zi, 0, 0, 0);
+          const uint32_t sm = (uint32_t)((j < 4 ? sc_a : sc_b) >> (16 * (j & 3)));   // bytes 2j, 2j + 1
+          const float dl = d * (float)(sm & 15), ml = dmin * (float)((sm >> 4) & 15);
+          const float dh = d * (float)((sm >> 8) & 15), mh = dmin * (float)((sm >> 12) & 15);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(36 * j));
+            const float dx = sv[r] ? dxr : 0.0f;
+            const float w = fmaf(dl, (float)Dl[r], fmaf(dh, (float)Dh[r], -fmaf(ml, (float)Sl[r], mh * (float)Sh[r])));
+            acc[r] = fmaf(dx, w, acc[r]);
+          }
+        } else {
+          const uint32_t sp = s3[j >> 1] >> (16 * (j & 1));   // scales 2j, 2j + 1
+          const float sl = (float)((int)(sp & 0xFFu) - 32), sh = (float)((int)((sp >> 8) & 0xFFu) - 32);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(36 * j));
+            const float dx = sv[r] ? dxr : 0.0f;
+            acc[r] = fmaf(dx, d * fmaf(sl, (float)Dl[r], sh * (float)Dh[r]), acc[r]);
+          }
+        }
+      }
     } else {
       constexpr int BB = F == FT_Q8_0 ? 34 : F == FT_MXFP4 ? 17 : 18;
       constexpr int HB = F == FT_MXFP4 ? 1 : 2;   // header bytes (scale) before the codes
@@ -326,9 +402,10 @@ static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
 
 }  // namespace ftk
 
-// 2..8 tokens, K a whole number of chunks, (Q4_0 | Q8_0 | Q4_K | Q5_K | Q6_K | MXFP4) x Q8_1
+// 2..8 tokens, K a whole number of chunks, every weight format x Q8_1
 static bool is_mmvq_mfma_format(int w) {
-  return w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4;
+  return w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4 ||
+         w == FT_Q2_K || w == FT_Q3_K;
 }
 
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t) {
@@ -347,6 +424,8 @@ hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st) {
     case FT_Q5_K: return launch_mfma_f<FT_Q5_K>(a, k, st);
     case FT_Q6_K: return launch_mfma_f<FT_Q6_K>(a, k, st);
     case FT_MXFP4: return launch_mfma_f<FT_MXFP4>(a, k, st);
+    case FT_Q2_K: return launch_mfma_f<FT_Q2_K>(a, k, st);
+    case FT_Q3_K: return launch_mfma_f<FT_Q3_K>(a, k, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,6 +12,8 @@ value distributions, so these are stated choices):
   * Q8_0 codes are clip(rint(N(0, 40)), -127, 127).
   * Q6_K int8 scales are uniform over [-128, 127].
   * MXFP4 E8M0 exponents are uniform over 118..126.
+  * Q2_K d and dmin and Q3_K d are fp16 scales as above; their scale, code and
+    third-bit bytes are uniform random bytes.
   * activations and router logits are fp32 N(0, 1).
 Weight block layouts (byte offsets of the scale fields) follow the public GGUF
 block formats.
@@ -88,6 +90,8 @@ def logits(t: int, n_expert: int, g: np.random.Generator) -> np.ndarray:
 Q4_0_MATVEC = dict(fmt="Q4_0", act="Q8_1", n=2048, k=2048, t=1)
 DENSE_DECODE = dict(formats=("Q8_0", "Q4_K"), act="Q8_1",
                     shapes=((14336, 4096), (4096, 14336)), tokens=(1, 2, 4, 8))
+# every weight format against Q8_1 at the first dense-decode shape
+DECODE_FORMATS = dict(formats=WEIGHT_FORMATS, act="Q8_1", shapes=((14336, 4096),), tokens=(1, 2, 4, 8))
 MOE_Q4K = dict(fmt="Q4_K", act="Q8_1", hidden=2048, inter=768, n_expert=128, topk=8,
                tokens=(1, 2, 3, 4))
 GROUPED_KQ = dict(formats=("Q5_K", "Q6_K"), act="Q8_K", tokens=512, hidden=4096,
