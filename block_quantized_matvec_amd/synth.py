@@ -12,7 +12,7 @@ value distributions, so these are stated choices):
   * Q8_0 codes are clip(rint(N(0, 40)), -127, 127).
   * Q6_K int8 scales are uniform over [-128, 127].
   * MXFP4 E8M0 exponents are uniform over 118..126.
-  * Q2_K d and dmin and Q3_K d are fp16 scales as above; their scale, code and
+  * Q4_1 / Q5_1 d and m, Q5_0 d, Q2_K d and dmin and Q3_K d are fp16 scales as above; their scale, code and
     third-bit bytes are uniform random bytes.
   * activations and router logits are fp32 N(0, 1).
 Weight block layouts (byte offsets of the scale fields) follow the public GGUF
@@ -25,9 +25,9 @@ import numpy as np
 BLOCK = {  # name: (elements, bytes)
     "Q4_0": (32, 18), "Q8_0": (32, 34), "Q4_K": (256, 144), "Q5_K": (256, 176),
     "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292),
-    "Q2_K": (256, 84), "Q3_K": (256, 110),
+    "Q2_K": (256, 84), "Q3_K": (256, 110), "Q4_1": (32, 20), "Q5_0": (32, 22), "Q5_1": (32, 24),
 }
-WEIGHT_FORMATS = ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K")
+WEIGHT_FORMATS = ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K", "Q4_1", "Q5_0", "Q5_1")
 ACT_FORMATS = ("Q8_1", "Q8_K")
 
 
@@ -50,8 +50,11 @@ def weights(fmt: str, rows: int, k: int, g: np.random.Generator) -> np.ndarray:
     be, bb = BLOCK[fmt]
     nb = rows * (k // be)
     b = g.integers(0, 256, size=(nb, bb), dtype=np.uint8)
-    if fmt in ("Q4_0",):
+    if fmt in ("Q4_0", "Q5_0"):
         b[:, 0:2] = _fp16_scales(g, nb)
+    elif fmt in ("Q4_1", "Q5_1"):
+        b[:, 0:2] = _fp16_scales(g, nb)      # d
+        b[:, 2:4] = _fp16_scales(g, nb)      # m
     elif fmt == "Q8_0":
         b[:, 0:2] = _fp16_scales(g, nb)
         q = np.clip(np.rint(g.normal(0.0, 40.0, size=(nb, 32))), -127, 127).astype(np.int8)

@@ -21,7 +21,8 @@
 
 int or_block_elems(int fmt) {
   switch (fmt) {
-    case OR_Q4_0: case OR_Q8_0: case OR_MXFP4: case OR_Q8_1: return 32;
+    case OR_Q4_0: case OR_Q8_0: case OR_MXFP4: case OR_Q8_1: case OR_Q4_1: case OR_Q5_0: case OR_Q5_1:
+      return 32;
     case OR_Q4_K: case OR_Q5_K: case OR_Q6_K: case OR_Q8_K: case OR_Q2_K: case OR_Q3_K: return 256;
     default: return 0;
   }
@@ -38,7 +39,10 @@ int or_block_bytes(int fmt) {
     case OR_Q8_1: return 36;    /* fp16 d, fp16 s, 32 int8 */
     case OR_Q8_K: return 292;   /* fp32 d, 256 int8, 16 int16 group sums */
     case OR_Q2_K: return 84;    /* 16 scale/min bytes, 64 bytes of 2-bit codes, fp16 d, fp16 dmin */
-    case OR_Q3_K: return 110;   /* 32 high-bit bytes, 64 bytes of 2-bit codes, 12 scale bytes, fp16 d */
+    case OR_Q3_K: return 110;
+    case OR_Q4_1: return 20;    /* fp16 d, fp16 m, 16 bytes of nibbles */
+    case OR_Q5_0: return 22;    /* fp16 d, 4 bytes of fifth bits, 16 bytes of nibbles */
+    case OR_Q5_1: return 24;    /* fp16 d, fp16 m, 4 bytes of fifth bits, 16 bytes of nibbles */   /* 32 high-bit bytes, 64 bytes of 2-bit codes, 12 scale bytes, fp16 d */
     default: return 0;
   }
 }
@@ -225,6 +229,23 @@ static int q3k_scale(const uint8_t* sc12, int j) {
   return (lo | (hi << 4)) - 32;
 }
 
+/* Q4_1: d @0, m @2, nibbles @4 in Q4_0's order; w = d * n + m. */
+static int code_q4_1(const uint8_t* b, int e) {
+  const uint8_t* qs = b + 4;
+  return e < 16 ? (qs[e] & 15) : (qs[e - 16] >> 4);
+}
+
+/* Q5_0 / Q5_1: nibbles in Q4_0's order plus a fifth bit, bit e of the little-endian
+   32-bit qh.  Q5_0: d @0, qh @2, nibbles @6, w = d * (q - 16).  Q5_1: d @0, m @2,
+   qh @4, nibbles @8, w = d * q + m. */
+static int code_q5(const uint8_t* b, int e, int qh_off) {
+  const uint8_t* qh = b + qh_off;
+  const uint8_t* qs = b + qh_off + 4;
+  int n = e < 16 ? (qs[e] & 15) : (qs[e - 16] >> 4);
+  int fifth = (qh[e / 8] >> (e % 8)) & 1;
+  return n + 16 * fifth;
+}
+
 /* integer code of weight element e */
 static int wcode(int fmt, const uint8_t* b, int e) {
   switch (fmt) {
@@ -236,6 +257,9 @@ static int wcode(int fmt, const uint8_t* b, int e) {
     case OR_MXFP4: return code_mxfp4(b, e);
     case OR_Q2_K: return code_q2_k(b, e);
     case OR_Q3_K: return code_q3_k(b, e);
+    case OR_Q4_1: return code_q4_1(b, e);
+    case OR_Q5_0: return code_q5(b, e, 2) - 16;
+    case OR_Q5_1: return code_q5(b, e, 4);
     default: return 0;
   }
 }
@@ -264,6 +288,12 @@ static void wscale(int fmt, const uint8_t* b, int e, double* scale, double* mn) 
       *mn = f16d(b + 82) * (b[e / 16] >> 4);
       break;
     case OR_Q3_K: *scale = f16d(b + 108) * q3k_scale(b + 96, e / 16); break;
+    case OR_Q5_0: *scale = f16d(b); break;
+    case OR_Q4_1:
+    case OR_Q5_1:   /* the offset m is added: w = scale * code - (-m) */
+      *scale = f16d(b);
+      *mn = -f16d(b + 2);
+      break;
     default: *scale = 0.0;
   }
 }
@@ -290,7 +320,7 @@ double or_elem(int fmt, const uint8_t* b, int e) {
   return scale * wcode(fmt, b, e) - mn;
 }
 
-static int is_weight(int f) { return (f >= OR_Q4_0 && f <= OR_MXFP4) || f == OR_Q2_K || f == OR_Q3_K; }
+static int is_weight(int f) { return (f >= OR_Q4_0 && f <= OR_MXFP4) || (f >= OR_Q2_K && f <= OR_Q5_1); }
 static int is_act(int f) { return f == OR_Q8_1 || f == OR_Q8_K; }
 
 void or_dequant_f32(int fmt, const uint8_t* blocks, int64_t rows, int64_t k, float* out) {

@@ -35,7 +35,7 @@ extern "C" {
 /* oracle format codes */
 enum {
   OR_Q4_0 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_Q5_K = 3, OR_Q6_K = 4, OR_MXFP4 = 5,
-  OR_Q8_1 = 6, OR_Q8_K = 7, OR_Q2_K = 8, OR_Q3_K = 9
+  OR_Q8_1 = 6, OR_Q8_K = 7, OR_Q2_K = 8, OR_Q3_K = 9, OR_Q4_1 = 10, OR_Q5_0 = 11, OR_Q5_1 = 12
 };
 
 int    or_block_elems(int fmt);            /* 32 or 256, 0 for unknown */

@@ -19,7 +19,7 @@ E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
 
 BLOCK = {"Q4_0": (32, 18), "Q8_0": (32, 34), "Q4_K": (256, 144), "Q5_K": (256, 176),
          "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292),
-         "Q2_K": (256, 84), "Q3_K": (256, 110)}
+         "Q2_K": (256, 84), "Q3_K": (256, 110), "Q4_1": (32, 20), "Q5_0": (32, 22), "Q5_1": (32, 24)}
 
 
 def _blocks(fmt, data):
@@ -88,6 +88,16 @@ def unpack(fmt, data):
         sc = b[:, 192:208].view(np.int8).astype(np.float64)          # [nb, 16]
         scale = np.repeat(_f16(b[:, 208:210])[:, None] * sc, 16, 1)
         off = np.zeros_like(scale)
+    elif fmt in ("Q4_1", "Q5_0", "Q5_1"):
+        qo = {"Q4_1": 4, "Q5_0": 6, "Q5_1": 8}[fmt]                   # first nibble byte
+        code = _nibbles_q4_0_order(b[:, qo:qo + 16])
+        if fmt != "Q4_1":
+            qh = np.unpackbits(b[:, qo - 4:qo], axis=1, bitorder="little").astype(np.int64)  # bit e of qh
+            code = code + 16 * qh
+        if fmt == "Q5_0":
+            code = code - 16
+        scale = np.repeat(_f16(b[:, 0:2])[:, None], 32, 1)
+        off = np.zeros_like(scale) if fmt == "Q5_0" else -np.repeat(_f16(b[:, 2:4])[:, None], 32, 1)
     elif fmt in ("Q2_K", "Q3_K"):
         # 64 code bytes as [g][l]; the element order is (g, r, l) with the 2-bit
         # field r of each byte

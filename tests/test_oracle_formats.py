@@ -38,7 +38,8 @@ def test_every_bit_flip_matches_brute(fmt):
     # keep the fp16 / E8M0 scale fields fixed at sane values; flip every other bit
     scale_bytes = {"Q4_0": {0, 1}, "Q8_0": {0, 1}, "Q4_K": {0, 1, 2, 3}, "Q5_K": {0, 1, 2, 3},
                    "Q6_K": {208, 209}, "MXFP4": {0}, "Q2_K": {80, 81, 82, 83},
-                   "Q3_K": {108, 109}}[fmt]
+                   "Q3_K": {108, 109}, "Q4_1": {0, 1, 2, 3}, "Q5_0": {0, 1},
+                   "Q5_1": {0, 1, 2, 3}}[fmt]
     for byte in range(bb):
         if byte in scale_bytes:
             continue
@@ -123,6 +124,30 @@ def test_q6_k_closed_form():
                           sc.view(np.uint8), _f16bytes(d)])
     w = oracle.dequant("Q6_K", blk, 1, 256)[0]
     assert np.array_equal(w, np.repeat(d * sc.astype(np.float64) * 31.0, 16).astype(np.float32))
+
+
+def test_q4_1_closed_form():
+    # d = 0.25, m = -1.5; nibble bytes 0x5A: low nibbles (elements 0..15) 10,
+    # high nibbles (16..31) 5
+    blk = np.concatenate([_f16bytes(0.25), _f16bytes(-1.5), np.full(16, 0x5A, np.uint8)])
+    w = oracle.dequant("Q4_1", blk, 1, 32)[0]
+    assert np.all(w[:16] == 0.25 * 10 - 1.5) and np.all(w[16:] == 0.25 * 5 - 1.5)
+
+
+@pytest.mark.parametrize("fmt", ["Q5_0", "Q5_1"])
+@pytest.mark.parametrize("e", [0, 7, 8, 15, 16, 23, 31])
+def test_q5_fifth_bit_position(fmt, e):
+    # all nibbles 3; only bit e of the little-endian 32-bit qh set: element e gets 16 + 3
+    qh = np.zeros(4, np.uint8)
+    qh[e // 8] = 1 << (e % 8)
+    hdr = [_f16bytes(0.5)] + ([_f16bytes(2.0)] if fmt == "Q5_1" else [])
+    blk = np.concatenate(hdr + [qh, np.full(16, 0x33, np.uint8)])
+    w = oracle.dequant(fmt, blk, 1, 32)[0]
+    off = -16 if fmt == "Q5_0" else 0
+    add = 2.0 if fmt == "Q5_1" else 0.0
+    expect = np.full(32, 0.5 * (3 + off) + add)
+    expect[e] = 0.5 * (19 + off) + add
+    assert np.array_equal(w, expect.astype(np.float32))
 
 
 # Q2_K / Q3_K: the 2-bit field r of code byte 32g + l holds element 128g + 32r + l;
