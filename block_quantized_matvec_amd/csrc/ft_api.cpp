@@ -19,11 +19,11 @@
 
 namespace {
 
-constexpr int kTypes = 10;
-constexpr int kElems[kTypes] = {32, 32, 256, 256, 256, 32, 32, 256, 256, 256};
-constexpr int kBytes[kTypes] = {18, 34, 144, 176, 210, 17, 36, 292, 84, 110};
+constexpr int kTypes = 13;
+constexpr int kElems[kTypes] = {32, 32, 256, 256, 256, 32, 32, 256, 256, 256, 32, 32, 32};
+constexpr int kBytes[kTypes] = {18, 34, 144, 176, 210, 17, 36, 292, 84, 110, 20, 22, 24};
 
-bool is_weight(int t) { return (t >= FT_Q4_0 && t <= FT_MXFP4) || t == FT_Q2_K || t == FT_Q3_K; }
+bool is_weight(int t) { return (t >= FT_Q4_0 && t <= FT_MXFP4) || (t >= FT_Q2_K && t <= FT_Q5_1); }
 bool is_act(int t) { return t == FT_Q8_1 || t == FT_Q8_K; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int64_t row_bytes_of(int type, int64_t k) { return k / kElems[type] * kBytes[type]; }

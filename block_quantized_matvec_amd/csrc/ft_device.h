@@ -131,6 +131,21 @@ template <> struct Fmt<FT_Q3_K> {
   __device__ static constexpr int seg_of(int j) { return j >> 2; }
 };
 
+// Q4_1: fp16 d @0, fp16 m @2, qs[16] @4 (nibble order as Q4_0); w = d*n + m, the
+// offset entering as wmin = -m.  Q5_0: d @0, qh @2 (32 bits, bit e the fifth bit of
+// element e), qs[16] @6; w = d*(q-16), the -16 as wmin = 16d.  Q5_1: d @0, m @2,
+// qh @4, qs[16] @8; w = d*q + m.  One unit, one segment, as Q4_0.
+template <int F> struct FmtLegacy {
+  static constexpr int BLK = 32, UPB = 1, NW = 8, S = 1, SUB = 32;
+  static constexpr bool XF1 = false;
+  static constexpr bool HAS_MIN = true;
+  __device__ static int act_elem(int, int j) { return 4 * j; }
+  __device__ static constexpr int seg_of(int) { return 0; }
+};
+template <> struct Fmt<FT_Q4_1> : FmtLegacy<FT_Q4_1> { static constexpr int BB = 20, CODE_OFF = 0; };
+template <> struct Fmt<FT_Q5_0> : FmtLegacy<FT_Q5_0> { static constexpr int BB = 22, CODE_OFF = 16; };
+template <> struct Fmt<FT_Q5_1> : FmtLegacy<FT_Q5_1> { static constexpr int BB = 24, CODE_OFF = 0; };
+
 template <int A> struct Act;
 template <> struct Act<FT_Q8_1> { static constexpr int BLK = 32, BB = 36; };
 template <> struct Act<FT_Q8_K> { static constexpr int BLK = 256, BB = 292; };
@@ -264,6 +279,12 @@ __device__ __forceinline__ void kq_header(uint32_t h_ddm, uint32_t h0, uint32_t 
   wm[1] = dmin * (float)((m >> 8) & 0xFF);
 }
 
+// bits 0..3 of h to bit 0 of bytes 0..3 (the fifth bits of four consecutive elements)
+__device__ __forceinline__ uint32_t spread4(uint32_t h) {
+  h &= 15u;
+  return (h | (h << 7) | (h << 14) | (h << 21)) & 0x01010101u;
+}
+
 // E2M1 codes (one per byte, 0..15) -> twice their value as int8, via byte permutes:
 // magnitudes 0,1,2,3,4,6,8,12 for codes 0..7; codes 8..15 are the negatives.
 __device__ __forceinline__ uint32_t e2m1x2_bytes(uint32_t c) {
@@ -340,6 +361,24 @@ __device__ __forceinline__ void unpack_unit(const R& rd, uint32_t bo, int ui, Un
       if constexpr (F == FT_Q5_K) rd.template dwords<8>(bo + 16, qh);
     }
     kq_unit<F>(h, q, qh, ui, u);
+  } else if constexpr (F == FT_Q4_1 || F == FT_Q5_0 || F == FT_Q5_1) {
+    constexpr uint32_t QO = F == FT_Q4_1 ? 4 : F == FT_Q5_0 ? 6 : 8;   // first nibble byte
+    uint32_t q[4];
+    rd.template dwords<4>(bo + QO, q);
+    const float d = h2f(rd.u16(bo));
+    uint32_t qh = 0;
+    if constexpr (F != FT_Q4_1) qh = rd.u32(bo + QO - 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      u.w[m] = q[m] & 0x0F0F0F0Fu;
+      u.w[4 + m] = (q[m] >> 4) & 0x0F0F0F0Fu;
+      if constexpr (F != FT_Q4_1) {
+        u.w[m] |= spread4(qh >> (4 * m)) << 4;
+        u.w[4 + m] |= spread4(qh >> (16 + 4 * m)) << 4;
+      }
+    }
+    u.ws[0] = d;
+    u.wm[0] = F == FT_Q5_0 ? 16.0f * d : -h2f(rd.u16(bo + 2));
   } else if constexpr (F == FT_Q2_K || F == FT_Q3_K) {
     const int g = ui >> 2, r = ui & 3;
     uint32_t q[8];

@@ -167,6 +167,9 @@ static int64_t units_of(int w, int64_t k) {
     case FT_MXFP4: return ftk::units_in_row<FT_MXFP4>(k);
     case FT_Q2_K: return ftk::units_in_row<FT_Q2_K>(k);
     case FT_Q3_K: return ftk::units_in_row<FT_Q3_K>(k);
+    case FT_Q4_1: return ftk::units_in_row<FT_Q4_1>(k);
+    case FT_Q5_0: return ftk::units_in_row<FT_Q5_0>(k);
+    case FT_Q5_1: return ftk::units_in_row<FT_Q5_1>(k);
     default: return 0;
   }
 }
@@ -189,5 +192,5 @@ hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
       default: break;
     }
   }
-  return ftk_launch_mmvq_kq(a, k, st);   // Q5_K, Q6_K, MXFP4, Q2_K, Q3_K (ft_mmvq_kq.hip)
+  return ftk_launch_mmvq_kq(a, k, st);   // the other formats (ft_mmvq_kq.hip)
 }

@@ -146,6 +146,14 @@ __device__ __forceinline__ float elem_value(const Reader<const uint32_t*>& rd, u
     const float a = (d * (float)sc) * (float)n;   // exact
     const float b = dmin * (float)m;              // exact
     return a - b;                                 // one rounding
+  } else if constexpr (F == FT_Q4_1 || F == FT_Q5_0 || F == FT_Q5_1) {
+    constexpr uint32_t QO = F == FT_Q4_1 ? 4 : F == FT_Q5_0 ? 6 : 8;
+    const uint32_t v = rd.u8(bo + QO + (e & 15));
+    int q = e < 16 ? (int)(v & 15) : (int)(v >> 4);
+    if (F != FT_Q4_1) q += 16 * (int)((rd.u8(bo + QO - 4 + (e >> 3)) >> (e & 7)) & 1);
+    const float d = h2f(rd.u16(bo));
+    if (F == FT_Q5_0) return d * (float)(q - 16);       // exact
+    return fmaf(d, (float)q, h2f(rd.u16(bo + 2)));      // d*q exact; one rounding
   } else if constexpr (F == FT_Q2_K) {
     const int g = e >> 7, r = (e >> 5) & 3, l = e & 31;
     const int q = (int)((rd.u8(bo + 16 + 32 * g + l) >> (2 * r)) & 3);
@@ -285,6 +293,9 @@ hipError_t ftk_launch_dequant(int w, const void* blocks, int64_t rows, int64_t k
     case FT_MXFP4: return launch_dequant_t<FT_MXFP4>(blocks, rows, k, out, st);
     case FT_Q2_K: return launch_dequant_t<FT_Q2_K>(blocks, rows, k, out, st);
     case FT_Q3_K: return launch_dequant_t<FT_Q3_K>(blocks, rows, k, out, st);
+    case FT_Q4_1: return launch_dequant_t<FT_Q4_1>(blocks, rows, k, out, st);
+    case FT_Q5_0: return launch_dequant_t<FT_Q5_0>(blocks, rows, k, out, st);
+    case FT_Q5_1: return launch_dequant_t<FT_Q5_1>(blocks, rows, k, out, st);
   }
   return hipErrorInvalidValue;
 }
@@ -307,7 +318,7 @@ hipError_t ftk_launch_block_dots(int w, const void* W, int64_t n, int64_t k, int
                           : launch_dots_t<F, FT_Q8_K>(W, n, k, xq, t, partials, st);
   switch (w) {
     FT_D(FT_Q4_0) FT_D(FT_Q8_0) FT_D(FT_Q4_K) FT_D(FT_Q5_K) FT_D(FT_Q6_K) FT_D(FT_MXFP4)
-    FT_D(FT_Q2_K) FT_D(FT_Q3_K)
+    FT_D(FT_Q2_K) FT_D(FT_Q3_K) FT_D(FT_Q4_1) FT_D(FT_Q5_0) FT_D(FT_Q5_1)
   }
 #undef FT_D
   return hipErrorInvalidValue;

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libft.so")
 
 TYPES = {"Q4_0": 0, "Q8_0": 1, "Q4_K": 2, "Q5_K": 3, "Q6_K": 4, "MXFP4": 5, "Q8_1": 6, "Q8_K": 7,
-         "Q2_K": 8, "Q3_K": 9}
+         "Q2_K": 8, "Q3_K": 9, "Q4_1": 10, "Q5_0": 11, "Q5_1": 12}
 OPS = {"quantize": 0, "dequant": 1, "mmvq": 2, "moe_vec": 3, "grouped": 4, "block_dots": 5}
 STATUS = {0: "FT_OK", 1: "FT_ERR_INVALID_ARG", 2: "FT_ERR_UNSUPPORTED", 3: "FT_ERR_SHAPE",
           4: "FT_ERR_ALIGNMENT", 5: "FT_ERR_NO_SCRATCH", 6: "FT_ERR_HIP"}

@@ -65,8 +65,12 @@ typedef enum {
   FT_Q8_K = 7,  /* activation, 256: fp32 d, 256 int8, 16 int16 group sums   292 B */
   FT_Q2_K = 8,  /* 256: 16 B of 4-bit scale|min pairs, 64 B of 2-bit codes, fp16 d,
                    fp16 dmin; w = d*sc*q - dmin*m per 16 elements              84 B */
-  FT_Q3_K = 9   /* 256: 32 B third bits, 64 B of 2-bit codes, 12 B of 6-bit
+  FT_Q3_K = 9,  /* 256: 32 B third bits, 64 B of 2-bit codes, 12 B of 6-bit
                    scales (+32), fp16 d; w = d*(sc-32)*(q-4) per 16 elements 110 B */
+  FT_Q4_1 = 10, /* 32: fp16 d, fp16 m, 16 B nibbles; w = d*n + m              20 B */
+  FT_Q5_0 = 11, /* 32: fp16 d, 4 B fifth bits, 16 B nibbles; w = d*(q-16)     22 B */
+  FT_Q5_1 = 12  /* 32: fp16 d, fp16 m, 4 B fifth bits, 16 B nibbles; w = d*q + m
+                                                                            24 B */
 } ft_type;
 
 typedef enum {
@@ -113,7 +117,8 @@ ft_status ft_quantize_act(ft_type act, const float* x, int64_t rows, int64_t k, 
 /* Dequantization [P1 Summary: Q4_0 dequantization; P2: packed K-quants].
    blocks: [rows][k/blk] of weight type w.  out: [rows][k] fp32 -- each value is
    the exact weight rounded once to fp32 (exact for every format but the Q4_K /
-   Q5_K difference d*sc*n - dmin*m, which rounds once). */
+   Q5_K / Q2_K difference d*sc*n - dmin*m and the Q4_1 / Q5_1 sum d*q + m, which
+   round once). */
 ft_status ft_dequant(ft_type w, const void* blocks, int64_t rows, int64_t k, float* out,
                      ft_stream_t stream);
 

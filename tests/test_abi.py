@@ -17,7 +17,7 @@ from block_quantized_matvec_amd import ft
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-W = ["Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K"]
+W = ["Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K", "Q4_1", "Q5_0", "Q5_1"]
 A = ["Q8_1", "Q8_K"]
 ST = {v: k for k, v in ft.STATUS.items()}
 
@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 def test_block_sizes():
     sizes = {"Q4_0": (32, 18), "Q8_0": (32, 34), "Q4_K": (256, 144), "Q5_K": (256, 176),
              "Q6_K": (256, 210), "MXFP4": (32, 17), "Q8_1": (32, 36), "Q8_K": (256, 292),
-             "Q2_K": (256, 84), "Q3_K": (256, 110)}
+             "Q2_K": (256, 84), "Q3_K": (256, 110), "Q4_1": (32, 20), "Q5_0": (32, 22), "Q5_1": (32, 24)}
     for t, (e, b) in sizes.items():
         assert ft.block_elems(t) == e and ft.block_bytes(t) == b
     assert ft.lib().ft_block_elems(99) == 0 and ft.lib().ft_block_bytes(-1) == 0

@@ -12,7 +12,8 @@ pytestmark = pytest.mark.gpu
 
 PAIRS = [(w, a) for w in synth.WEIGHT_FORMATS for a in synth.ACT_FORMATS]
 MMVQ = [("Q4_0", "Q8_1"), ("Q8_0", "Q8_1"), ("Q4_K", "Q8_1"), ("Q5_K", "Q8_1"), ("Q6_K", "Q8_1"),
-        ("MXFP4", "Q8_1"), ("Q2_K", "Q8_1"), ("Q3_K", "Q8_1")]
+        ("MXFP4", "Q8_1"), ("Q2_K", "Q8_1"), ("Q3_K", "Q8_1"), ("Q4_1", "Q8_1"), ("Q5_0", "Q8_1"),
+        ("Q5_1", "Q8_1")]
 
 
 @pytest.fixture(autouse=True)
@@ -102,7 +103,8 @@ def test_mmvq_extreme_codes(w, a, t):
     # finite scales where the format keeps them (GGUF layouts): d at 0 (Q4_0, Q8_0),
     # d and dmin at 0 (Q4_K, Q5_K), d at 208 after the int8 sub-block scales (Q6_K),
     # the E8M0 exponent in byte 0 (MXFP4, 127: unit scale), d and dmin at 80 after
-    # the scale bytes and codes (Q2_K), d at 108 (Q3_K)
+    # the scale bytes and codes (Q2_K), d at 108 (Q3_K), d (and m) at 0 (Q5_0, Q4_1,
+    # Q5_1)
     if w in ("Q4_0", "Q8_0"):
         blocks[:, :, 0:2] = np.frombuffer(np.float16(0.0625).tobytes(), np.uint8)
     elif w in ("Q4_K", "Q5_K"):
@@ -113,6 +115,10 @@ def test_mmvq_extreme_codes(w, a, t):
         blocks[:, :, 80:84] = np.frombuffer(np.array([0.0625, 0.03125], np.float16).tobytes(), np.uint8)
     elif w == "Q3_K":
         blocks[:, :, 108:110] = np.frombuffer(np.float16(0.0625).tobytes(), np.uint8)
+    elif w == "Q5_0":
+        blocks[:, :, 0:2] = np.frombuffer(np.float16(0.0625).tobytes(), np.uint8)
+    elif w in ("Q4_1", "Q5_1"):
+        blocks[:, :, 0:4] = np.frombuffer(np.array([0.0625, -0.5], np.float16).tobytes(), np.uint8)
     else:
         blocks[:, :, 0] = 127
     abe, abb = synth.BLOCK[a]
