@@ -146,7 +146,9 @@ int ftk_num_cus() {
 // 16.5); Q6_K 4096 x 14336 at 2 tokens 21.7 / 18.0.  Q2_K / Q3_K from 5 tokens on
 // (14336 x 4096, 4 tokens 12.7 / 14.7 and 15.3 / 22.4, 8 tokens 27.9 / 21.5 and
 // 30.4 / 23.5: their few bytes per chunk leave the MFMA kernel bound by its
-// per-block unpack and combine).
+// per-block unpack and combine), and so do Q4_1 / Q5_0 / Q5_1 (4 tokens 12.4 / 13.4,
+// 13.1 / 14.8, 13.5 / 21.1; 8 tokens 24.6 / 15.4, 26.7 / 16.3, 27.0 / 22.9 before
+// Q5_1's slot pad).
 // FT_MMVQ_MFMA_MIN_T = m sends every t >= m to MFMA and the rest to dot4 (tuning
 // sweeps).
 static int mfma_min_t() {   // 0: the automatic choice
@@ -178,9 +180,9 @@ hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;
   const int mt = mfma_min_t();
   const bool lng = units_of(a.w, k) > 128;
-  const bool lowbit = a.w == FT_Q2_K || a.w == FT_Q3_K;
+  const bool late = a.w == FT_Q2_K || a.w == FT_Q3_K || a.w == FT_Q4_1 || a.w == FT_Q5_0 || a.w == FT_Q5_1;
   const bool mfma = mt ? a.t >= mt
-                       : lowbit ? a.t >= 5
+                       : late ? a.t >= 5
                        : (a.w == FT_Q8_0 || a.w == FT_Q5_K ? a.t >= 5 || (a.t >= 3 && lng)
                                                              : a.t >= 3 || (a.t == 2 && lng));
   if (mfma && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t)) return ftk_launch_mmvq_mfma(a, k, st);

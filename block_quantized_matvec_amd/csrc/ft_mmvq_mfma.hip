@@ -1,9 +1,10 @@
 // ft_mmvq_mfma.hip -- Q-matvec for 2..8 tokens on the int8 matrix cores
-// (v_mfma_i32_16x16x32_i8): Q4_0, Q8_0, Q4_K, Q5_K, Q6_K, MXFP4, Q2_K and Q3_K
-// weights against Q8_1 activations (Q5_K adds the fifth bits to Q4_K's nibbles;
+// (v_mfma_i32_16x16x32_i8): every weight format (Q4_0, Q8_0, Q4_K, Q5_K, Q6_K,
+// MXFP4, Q2_K, Q3_K, Q4_1, Q5_0, Q5_1) against Q8_1 activations (Q5_K adds the fifth bits to Q4_K's nibbles;
 // Q6_K enters as q6 - 32 with one MFMA per 16-element scale group, and so do Q2_K's
 // 2-bit codes and Q3_K's q - 4; MXFP4 as twice its E2M1 values with 2^(e-128) as
-// the block scale, in 512-element chunks).
+// the block scale, in 512-element chunks; Q4_1 / Q5_0 / Q5_1 as Q4_0 with their
+// fifth bits and the offset m from a second MFMA against an all-ones operand).
 //
 // ggml-cuda "mul_mat_vec_q" (the pages' MMVQ path, ds4 PR #656 Summary): a block's
 // integer dot product of weight and activation codes, then the fp32 scale
@@ -39,10 +40,13 @@ constexpr int MV_CE = 256;   // elements of a row per chunk (512 for MXFP4)
 // need 512-element chunks for that) sit at the slot's start; Q6_K's 210-, Q3_K's
 // 110- and Q2_K's 84-byte chunks are copied from the 16-byte boundary below them,
 // one piece more, and read at their byte offset in the slot.
-template <int F_, int CB_> struct MvSlot {
+// PAD adds a piece to a whole-piece slot whose stride would put the 16 rows' reads
+// of one offset on a few LDS banks (192-byte slots: 4-way conflicts); the pad piece
+// re-reads the chunk's last one.
+template <int F_, int CB_, int PAD_ = 0> struct MvSlot {
   static constexpr int CB = CB_;
   static constexpr bool UNAL = CB % 16 != 0;
-  static constexpr int NPR = UNAL ? (CB + 30) / 16 : CB / 16;
+  static constexpr int NPR = UNAL ? (CB + 30) / 16 : CB / 16 + PAD_;
   static constexpr int SLOT = 16 * NPR;
 };
 template <int F, int CE_ = MV_CE> struct MvGeo;
@@ -53,6 +57,9 @@ template <int CE_> struct MvGeo<FT_Q5_K, CE_> : MvSlot<FT_Q5_K, 176> { static co
 template <int CE_> struct MvGeo<FT_Q6_K, CE_> : MvSlot<FT_Q6_K, 210> { static constexpr int CE = 256; };
 template <int CE_> struct MvGeo<FT_MXFP4, CE_> : MvSlot<FT_MXFP4, 17 * 512 / 32> { static constexpr int CE = 512; };
 template <int CE_> struct MvGeo<FT_Q2_K, CE_> : MvSlot<FT_Q2_K, 84> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q4_1, CE_> : MvSlot<FT_Q4_1, 20 * 256 / 32> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q5_0, CE_> : MvSlot<FT_Q5_0, 22 * 256 / 32> { static constexpr int CE = 256; };
+template <int CE_> struct MvGeo<FT_Q5_1, CE_> : MvSlot<FT_Q5_1, 24 * 256 / 32, 1> { static constexpr int CE = 256; };
 template <int CE_> struct MvGeo<FT_Q3_K, CE_> : MvSlot<FT_Q3_K, 110> { static constexpr int CE = 256; };
 
 template <int F, int CE> struct MvRegs {
@@ -110,6 +117,7 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
       int pc = p - row * NPR;
       const int64_t gr = row0 + row < n ? row0 + row : n - 1;
       int64_t b = gr * row_bytes + (int64_t)c * CB;
+      if constexpr (!GE::UNAL && GE::SLOT > CB) pc = pc < CB / 16 ? pc : CB / 16 - 1;   // the pad piece
       if constexpr (GE::UNAL) {   // from the 16-byte boundary; pieces past the chunk re-read its last one
         const int npc = ((int)(b & 15) + CB + 15) >> 4;
         pc = pc < npc ? pc : npc - 1;
@@ -299,11 +307,14 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
         }
       }
     } else {
-      constexpr int BB = F == FT_Q8_0 ? 34 : F == FT_MXFP4 ? 17 : 18;
-      constexpr int HB = F == FT_MXFP4 ? 1 : 2;   // header bytes (scale) before the codes
+      constexpr int BB = F == FT_Q8_0 ? 34 : F == FT_MXFP4 ? 17 : F == FT_Q4_1 ? 20 : F == FT_Q5_0 ? 22
+                       : F == FT_Q5_1 ? 24 : 18;
+      // header bytes (scale, offset, fifth bits) before the codes
+      constexpr int HB = F == FT_MXFP4 ? 1 : F == FT_Q4_1 ? 4 : F == FT_Q5_0 ? 6 : F == FT_Q5_1 ? 8 : 2;
+      constexpr bool OFS = F == FT_Q4_1 || F == FT_Q5_1;   // w = d*q + m
 #pragma unroll
       for (int blk = 0; blk < CE / 32; ++blk) {
-        const uint32_t wb = (uint32_t)(col * CB + BB * blk);
+        const uint32_t wb = (uint32_t)(col * SLOT + BB * blk);
         float dw;
         if constexpr (F == FT_MXFP4) dw = e8m0_half(wl[wb]);   // codes enter doubled: 2^(e-128)
         else dw = lds_h2f(wl, wb);
@@ -315,6 +326,17 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
           const uint64_t q = lds_u64(wl, wb + HB + 8 * (kq & 1));
           const uint64_t nib = (q >> (4 * (kq >> 1))) & 0x0F0F0F0F0F0F0F0Full;
           b = (uint64_t)e2m1x2_bytes((uint32_t)nib) | ((uint64_t)e2m1x2_bytes((uint32_t)(nib >> 32)) << 32);
+        } else if constexpr (F == FT_Q4_1 || F == FT_Q5_0 || F == FT_Q5_1) {
+          // nibbles as Q4_0's; the fifth bits of elements 8kq..8kq+7 are byte kq of qh
+          const uint64_t q = lds_u64(wl, wb + HB + 8 * (kq & 1));
+          uint64_t x = (q >> (4 * (kq >> 1))) & 0x0F0F0F0F0F0F0F0Full;
+          if constexpr (F != FT_Q4_1) {
+            const uint32_t hb = wl[wb + HB - 4 + kq];
+            x |= ((uint64_t)spread4(hb) | ((uint64_t)spread4(hb >> 4) << 32)) << 4;
+          }
+          if constexpr (F == FT_Q5_0)   // q - 16 as int8 (q <= 31)
+            x = (x + 0x7070707070707070ull) ^ 0x8080808080808080ull;
+          b = x;
         } else {
           // elements 8kq..8kq+7: low nibbles of bytes 0..7 (kq 0) or 8..15 (kq 1),
           // high nibbles of the same (kq 2, 3); as int8 n - 8
@@ -327,11 +349,22 @@ mmvq_mfma_kernel(const uint8_t* __restrict__ W, int64_t n, int64_t k, int64_t ro
         const uint64_t ar = lds_u64(al, arow_off + (uint32_t)(36 * blk + 4 + 8 * kq));
         const uint64_t a = arow ? ar : 0ull;
         const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)b, zi, 0, 0, 0);
+        if constexpr (OFS) {   // + m * (activation code sum), the sum from an all-ones operand
+          const float m = lds_h2f(wl, wb + 2);
+          const v4i S = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)a, (long)0x0101010101010101ll, zi, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(36 * blk));
-          const float dx = sv[r] ? dxr : 0.0f;
-          acc[r] = fmaf((float)D[r], dw * dx, acc[r]);
+          for (int r = 0; r < NR; ++r) {
+            const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(36 * blk));
+            const float dx = sv[r] ? dxr : 0.0f;
+            acc[r] = fmaf(dx, fmaf(dw, (float)D[r], m * (float)S[r]), acc[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const float dxr = lds_h2f(al, s_off[r] + (uint32_t)(36 * blk));
+            const float dx = sv[r] ? dxr : 0.0f;
+            acc[r] = fmaf((float)D[r], dw * dx, acc[r]);
+          }
         }
       }
     }
@@ -405,7 +438,7 @@ static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
 // 2..8 tokens, K a whole number of chunks, every weight format x Q8_1
 static bool is_mmvq_mfma_format(int w) {
   return w == FT_Q4_0 || w == FT_Q8_0 || w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4 ||
-         w == FT_Q2_K || w == FT_Q3_K;
+         w == FT_Q2_K || w == FT_Q3_K || w == FT_Q4_1 || w == FT_Q5_0 || w == FT_Q5_1;
 }
 
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t) {
@@ -426,6 +459,9 @@ hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st) {
     case FT_MXFP4: return launch_mfma_f<FT_MXFP4>(a, k, st);
     case FT_Q2_K: return launch_mfma_f<FT_Q2_K>(a, k, st);
     case FT_Q3_K: return launch_mfma_f<FT_Q3_K>(a, k, st);
+    case FT_Q4_1: return launch_mfma_f<FT_Q4_1>(a, k, st);
+    case FT_Q5_0: return launch_mfma_f<FT_Q5_0>(a, k, st);
+    case FT_Q5_1: return launch_mfma_f<FT_Q5_1>(a, k, st);
     default: return hipErrorInvalidValue;
   }
 }
