@@ -128,9 +128,8 @@ ft_status ft_dequant(ft_type w, const void* blocks, int64_t rows, int64_t k, flo
    integer dots per block followed by an fp32 scale combine.  Any t >= 0 (t = 0 is a
    no-op); batches beyond 8 tokens are processed 8 at a time.  Supported (w, act):
    every weight type x FT_Q8_1.  From 2-5 tokens on (the threshold depends on the
-   format and on k) every format but Q2_K and Q3_K runs on the int8 matrix cores when
-   k is a multiple of 256 (512 for MXFP4); the result is the same integer dots
-   either way. */
+   format and on k) every format runs on the int8 matrix cores when k is a multiple
+   of 256 (512 for MXFP4); the result is the same integer dots either way. */
 ft_status ft_mul_mat_vec_q(ft_type w, const void* W, int64_t n, int64_t k,
                            ft_type act, const void* xq, int64_t t,
                            float* y, int64_t ldy, ft_stream_t stream);
