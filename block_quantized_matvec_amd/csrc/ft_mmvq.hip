@@ -135,9 +135,11 @@ int ftk_num_cus() {
 }
 
 // Several tokens go to the int8 MFMA kernels (ft_mmvq_mfma.hip) when K is a whole
-// number of chunks: Q4_0 / Q4_K / Q6_K / MXFP4 from 3 tokens on, and at 2 tokens on
-// rows of more than 128 units; Q8_0 / Q5_K from 5 tokens on, and at 3-4 tokens on
-// rows of more than 128 units.  The rest stay on the per-wave dot4 ring.  Measured
+// number of chunks: from 5 tokens on for rows of at most 128 units, and on longer
+// rows from 2 tokens on (Q4_0 / Q4_K / Q6_K / MXFP4) or 3 (Q8_0 / Q5_K).  The rest
+// stay on the per-wave dot4 ring.  With every weight copy out of the last-level
+// cache, 4 tokens on 14336 x 4096 take (dot4 vs MFMA, us) Q4_K 10.9 / 12.6, Q4_0
+// 12.0 / 12.6, MXFP4 13.9 / 15.2, Q6_K 19.2 / 19.6.  Earlier measurements
 // (dot4 vs MFMA, us): 2 tokens, 14336 x 4096: Q8_0 12.0 / 14.9, Q4_K 8.7 / 10.4,
 // Q4_0 9.4 / 10.4; 4096 x 14336: Q8_0 13.2 / 13.7, Q4_K 11.3 / 9.7, Q4_0 12.7 /
 // 10.1.  4 tokens, 14336 x 4096: Q8_0 13.1 / 15.2, Q4_K 10.8 / 10.4, Q4_0 12.1 /
@@ -182,9 +184,8 @@ hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   const bool lng = units_of(a.w, k) > 128;
   const bool late = a.w == FT_Q2_K || a.w == FT_Q3_K || a.w == FT_Q4_1 || a.w == FT_Q5_0 || a.w == FT_Q5_1;
   const bool mfma = mt ? a.t >= mt
-                       : late ? a.t >= 5
-                       : (a.w == FT_Q8_0 || a.w == FT_Q5_K ? a.t >= 5 || (a.t >= 3 && lng)
-                                                             : a.t >= 3 || (a.t == 2 && lng));
+                       : late || !lng ? a.t >= 5
+                       : (a.w == FT_Q8_0 || a.w == FT_Q5_K ? a.t >= 3 : a.t >= 2);
   if (mfma && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t)) return ftk_launch_mmvq_mfma(a, k, st);
   if (a.act == FT_Q8_1) {
     switch (a.w) {
