@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libft.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ft_api.cpp", "ft_quant.hip", "ft_mmvq.hip", "ft_mmvq_kq.hip", "ft_mmvq_mfma.hip", "ft_moe.hip", "ft_moe_fp4.hip", "ft_grouped.hip",
+SOURCES = ["ft_mmvq_kq.hip", "ft_mmvq_kq_b.hip", "ft_mmvq_kq_c.hip", "ft_mmvq_kq_d.hip", "ft_mmvq.hip",
+           "ft_api.cpp", "ft_quant.hip", "ft_mmvq_mfma.hip", "ft_moe.hip", "ft_moe_fp4.hip", "ft_grouped.hip",
            "ft_probe.hip"]
 
 CFLAGS = [
@@ -51,7 +52,7 @@ def _compile(src: str) -> str:
 
 def build(jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2) // 2))
+    jobs = jobs or min(len(SOURCES), max(1, min(os.cpu_count() or 2, 16)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

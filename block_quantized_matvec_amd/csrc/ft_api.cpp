@@ -108,8 +108,13 @@ SortScratch sort_layout(int64_t n_expert, int64_t t, int topk, size_t xf8_bytes 
 size_t xf8_bytes_of(int w, int64_t rows, int64_t k) { return w == FT_MXFP4 ? (size_t)rows * (k / 256) * 512 : 0; }
 
 bool mmvq_pair(int w, int a) { return a == FT_Q8_1 && is_weight(w); }
-bool moe_pair(int w, int a) { return (w == FT_Q4_K && a == FT_Q8_1) || (w == FT_MXFP4 && a == FT_Q8_K); }
-bool moe_tile_pair(int w, int a) { return w == FT_MXFP4 && a == FT_Q8_K; }
+// the direct route: Q4_K x Q8_1 on dot4, MXFP4 x Q8_K on the FP4 MFMA; the sorted
+// tiles: every grouped-GEMM format x Q8_K
+bool moe_direct_pair(int w, int a) { return (w == FT_Q4_K && a == FT_Q8_1) || (w == FT_MXFP4 && a == FT_Q8_K); }
+bool moe_tile_pair(int w, int a) {
+  return a == FT_Q8_K && (w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4);
+}
+bool moe_pair(int w, int a) { return moe_direct_pair(w, a) || moe_tile_pair(w, a); }
 // the tile route splits x, then h, into FP8 halves in one buffer
 size_t moe_xf8_bytes(int w, int64_t hidden, int64_t inter, int64_t t, int topk) {
   const size_t a = xf8_bytes_of(w, t, hidden), b = xf8_bytes_of(w, t * topk, inter);
@@ -232,43 +237,51 @@ size_t ft_grouped_scratch_bytes(ft_type w, int64_t n_expert, int64_t k, int64_t 
   return sort_layout(n_expert, t, topk, xf8_bytes_of(w, x_per_pair ? t * topk : t, k)).total;
 }
 
-ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const void* w_down, int64_t n_expert,
-                       int64_t hidden, int64_t inter, ft_type act, const float* x, int64_t t,
-                       const int32_t* expert_ids, const float* expert_w, int topk, float* y, const ft_moe_opts* opts,
-                       ft_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of ft_moe_q_vec; on FT_OK, *tiles says which route runs and
+// *need the scratch bytes it takes.
+ft_status moe_check(ft_type w, const void* w_gate, const void* w_up, const void* w_down, int64_t n_expert,
+                    int64_t hidden, int64_t inter, ft_type act, const float* x, int64_t t,
+                    const int32_t* expert_ids, const float* expert_w, int topk, float* y, const ft_moe_opts& o,
+                    bool* tiles, size_t* need) {
   if (!is_weight(w) || !is_act(act) || !moe_pair(w, act)) return FT_ERR_UNSUPPORTED;
   if (n_expert < 1 || hidden < 0 || inter < 0 || t < 0) return FT_ERR_INVALID_ARG;
   if (topk < 1 || topk > 8 || topk > n_expert) return FT_ERR_SHAPE;
   if (hidden % kElems[w] || hidden % kElems[act] || inter % kElems[w] || inter % kElems[act]) return FT_ERR_SHAPE;
   if (hidden == 0 || inter == 0 || hidden > 16384 || inter > 16384) return FT_ERR_SHAPE;
+  if (o.route < 0 || o.route > 2 || o.direct_max_t < 0) return FT_ERR_INVALID_ARG;
+  const bool tile_ok = moe_tile_pair(w, act), direct_ok = moe_direct_pair(w, act);
+  if ((o.route == 2 && !tile_ok) || (o.route == 1 && !direct_ok)) return FT_ERR_UNSUPPORTED;
+  // default threshold: up to 8 tokens (one launch chunk of the direct MXFP4 kernels)
+  // the direct route wins on MI355X (measured per layer: t = 8: 284 vs 290 us; t = 9:
+  // 317 vs 298 us for the sorted tiles); pairs with no direct kernels take the tiles
+  const int64_t dmax = o.direct_max_t > 0 ? o.direct_max_t : 8;
+  *tiles = o.route == 2 || (o.route == 0 && (!direct_ok || (tile_ok && t > dmax)));
+  // the sort behind the tiles holds one counter per expert in LDS
+  if (*tiles && n_expert > 8192) return FT_ERR_SHAPE;
   if (t == 0) return FT_OK;
   if (!w_gate || !w_up || !w_down || !x || !expert_ids || !expert_w || !y) return FT_ERR_INVALID_ARG;
   if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(x) || !aligned16(y))
     return FT_ERR_ALIGNMENT;
-  ft_moe_opts o = {};
-  if (opts) o = *opts;
-  if (o.route < 0 || o.route > 2 || o.direct_max_t < 0) return FT_ERR_INVALID_ARG;
-  // sorted-tile route: token->expert sort + grouped MFMA GEMMs (MXFP4 x Q8_K)
-  const bool tile_ok = moe_tile_pair(w, act);
-  if (o.route == 2 && !tile_ok) return FT_ERR_UNSUPPORTED;
-  // default threshold: up to 8 tokens (one launch chunk of the direct MXFP4 kernels)
-  // the direct route wins on MI355X (measured per layer: t = 8: 284 vs 290 us; t = 9:
-  // 317 vs 298 us for the sorted tiles)
-  const int64_t dmax = o.direct_max_t > 0 ? o.direct_max_t : 8;
-  const bool tiles = o.route == 2 || (o.route == 0 && tile_ok && t > dmax);
   if ((o.tap_g && !aligned16(o.tap_g)) || (o.tap_u && !aligned16(o.tap_u)) || (o.tap_h && !aligned16(o.tap_h)) ||
       (o.tap_hq && !aligned16(o.tap_hq)) || (o.tap_down && !aligned16(o.tap_down)) ||
       (o.in_hq && !aligned16(o.in_hq)))
     return FT_ERR_ALIGNMENT;
+  *need = moe_layout(w, act, hidden, inter, t, topk).total +
+          (*tiles ? sort_layout(n_expert, t, topk, moe_xf8_bytes(w, hidden, inter, t, topk)).total : 0);
+  return FT_OK;
+}
 
-  hipStream_t st = hs(stream);
+// The layer on checked arguments, its scratch at b (moe_check's `need` bytes).
+ft_status moe_run(ft_type w, const void* w_gate, const void* w_up, const void* w_down, int64_t n_expert,
+                  int64_t hidden, int64_t inter, ft_type act, const float* x, int64_t t,
+                  const int32_t* expert_ids, const float* expert_w, int topk, float* y, const ft_moe_opts& o,
+                  bool tiles, uint8_t* b, hipStream_t st) {
   const MoeScratch L = moe_layout(w, act, hidden, inter, t, topk);
   const SortScratch S = sort_layout(n_expert, t, topk, moe_xf8_bytes(w, hidden, inter, t, topk));
-  void* base = nullptr;
-  ft_status s = pool_get(st, L.total + (tiles ? S.total : 0), &base);
-  if (s != FT_OK) return s;
-  uint8_t* b = (uint8_t*)base;
-
   MoeArgs a = {};
   a.w = w;
   a.act = act;
@@ -348,6 +361,29 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
   if (e == hipSuccess) e = ftk_launch_moe_down(a, st);
   if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const void* w_down, int64_t n_expert,
+                       int64_t hidden, int64_t inter, ft_type act, const float* x, int64_t t,
+                       const int32_t* expert_ids, const float* expert_w, int topk, float* y, const ft_moe_opts* opts,
+                       ft_stream_t stream) {
+  ft_moe_opts o = {};
+  if (opts) o = *opts;
+  bool tiles = false;
+  size_t need = 0;
+  ft_status s = moe_check(w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, t, expert_ids, expert_w, topk,
+                          y, o, &tiles, &need);
+  if (s != FT_OK || t == 0) return s;
+  hipStream_t st = hs(stream);
+  void* base = nullptr;
+  s = pool_get(st, need, &base);
+  if (s != FT_OK) return s;
+  return moe_run(w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, t, expert_ids, expert_w, topk, y, o,
+                 tiles, (uint8_t*)base, st);
 }
 
 ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t n, int64_t k, ft_type act,

@@ -51,14 +51,12 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-#ifndef GM_WAVES_OPT
-#define GM_WAVES_OPT 4
-#endif
-constexpr int GM_WAVES = GM_WAVES_OPT;
+constexpr int GM_WAVES = 4;
 constexpr int GM_THREADS = 64 * GM_WAVES;
 // 16-row MFMA groups per wave (they share every A-operand read); Q6_K's two
-// MFMAs and two scales per group need the registers of a second group
-template <int F> struct GRg { static constexpr int RG = F == FT_Q6_K ? 1 : 2; };
+// MFMAs and two scales per group need the registers of a second group, except in
+// the fused gate/up form, whose two groups are the gate and up rows
+template <int F, bool GLU> struct GRg { static constexpr int RG = (F == FT_Q6_K && !GLU) ? 1 : 2; };
 
 // One 256-element superblock of a weight row: BYTES in HBM; SLOT bytes in LDS
 // (room for a misaligned start; SLOT/16 odd keeps the 16 rows of an MFMA group on
@@ -73,7 +71,7 @@ template <> struct GSb<FT_MXFP4> { static constexpr int BYTES = 136, SLOT = 176;
 // the all-zero tile of the Q6_K half masks.
 // MXFP4 tiles hold the FP8 halves instead: [PT][2 k-steps][lo, hi][2 16-byte
 // halves][64 lanes] x 16 B, and need no code sums.
-template <int F, int PT> struct GLds {
+template <int F, int PT, int RG> struct GLds {
   static constexpr bool FP4 = F == FT_MXFP4;
   static constexpr int GSTR = 544;                       // bytes per 32-element group (512 + bank pad)
   static constexpr int TSTR = FP4 ? 8192 : 8 * GSTR;     // bytes per pair tile
@@ -81,7 +79,7 @@ template <int F, int PT> struct GLds {
   static constexpr int BSUM = CODES + PT * TSTR;         // [PT][64 lanes] x 4 fp16
   static constexpr int DX = BSUM + (FP4 ? 0 : PT * 512); // [PT][16 pairs] fp32
   static constexpr int WT = DX + PT * 64;                // [waves][16*RG rows][SLOT]
-  static constexpr int BUF = WT + GM_WAVES * 16 * GRg<F>::RG * GSb<F>::SLOT;
+  static constexpr int BUF = WT + GM_WAVES * 16 * RG * GSb<F>::SLOT;
   static constexpr int ZTILE = BUF;                      // the zero tile
   static constexpr int TOTAL = ZTILE + (F == FT_Q6_K ? TSTR : 0);
 };
@@ -194,9 +192,9 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
                     float* __restrict__ y, float* __restrict__ g_tap, float* __restrict__ u_tap,
                     int64_t row_tiles, int64_t total, int64_t per_xcd) {
   using SB = GSb<F>;
-  using LY = GLds<F, PT>;
+  constexpr int RG = GRg<F, GLU>::RG;
+  using LY = GLds<F, PT, RG>;
   constexpr int NCH = SB::SLOT / 16;                   // 16-byte chunks per row slot
-  constexpr int RG = GRg<F>::RG;
   static_assert(!GLU || RG == 2, "the fused gate/up form takes two row groups");
   constexpr int WROWS = 16 * RG;                       // weight rows per wave
   constexpr int OROWS = GLU ? 16 : WROWS;              // output rows per wave
@@ -501,12 +499,13 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
 
 template <int F, int PT, bool GLU>
 static hipError_t launch_gm(const GroupedArgs& a, hipStream_t st) {
-  const int rows = (GLU ? 16 : 16 * GRg<F>::RG) * GM_WAVES;
+  constexpr int RG = GRg<F, GLU>::RG;
+  const int rows = (GLU ? 16 : 16 * RG) * GM_WAVES;
   const int64_t row_tiles = (a.n + rows - 1) / rows;
   const int64_t total = row_tiles * a.n_expert;
   const int64_t per = (total + 7) / 8;
   const int64_t row_bytes = a.k / 256 * GSb<F>::BYTES;
-  const size_t lds = (size_t)GLds<F, PT>::TOTAL;
+  const size_t lds = (size_t)GLds<F, PT, RG>::TOTAL;
   hipLaunchKernelGGL((grouped_mfma_kernel<F, PT, GLU>), dim3((unsigned)(per * 8)), dim3(GM_THREADS), lds, st,
                      (const uint8_t*)a.W, (const uint8_t*)a.W2, a.n, row_bytes, (int)(a.k / 256),
                      (const uint8_t*)a.xq, (int64_t)(a.k / 256 * 292), (const uint8_t*)a.xf8, a.x_per_pair, a.topk,
@@ -536,7 +535,12 @@ hipError_t ftk_launch_grouped(const GroupedArgs& a, hipStream_t st) {
   if (a.act != FT_Q8_K || a.k % 256) return hipErrorInvalidValue;
   if (a.w == FT_MXFP4 && !a.xf8) return hipErrorInvalidValue;   // needs the FP8 halves
   if (a.W2) {   // fused gate/up + SwiGLU
-    if (a.w == FT_MXFP4) return grouped_f<FT_MXFP4, true>(a, st);
+    switch (a.w) {
+      case FT_Q4_K: return grouped_f<FT_Q4_K, true>(a, st);
+      case FT_Q5_K: return grouped_f<FT_Q5_K, true>(a, st);
+      case FT_Q6_K: return grouped_f<FT_Q6_K, true>(a, st);
+      case FT_MXFP4: return grouped_f<FT_MXFP4, true>(a, st);
+    }
     return hipErrorInvalidValue;
   }
   switch (a.w) {

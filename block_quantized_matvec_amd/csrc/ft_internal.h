@@ -33,6 +33,12 @@ struct MmvqPlan {
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out);
 // dot4 matvec of Q5_K / Q6_K / MXFP4 x Q8_1 (ft_mmvq_kq.hip)
 hipError_t ftk_launch_mmvq_kq(const MmvqArgs& a, int64_t k, hipStream_t st);
+hipError_t ftk_launch_mmvq_dot4_mxfp4(const MmvqArgs& a, int64_t k, hipStream_t st);
+hipError_t ftk_launch_mmvq_dot4_q2_k(const MmvqArgs& a, int64_t k, hipStream_t st);
+hipError_t ftk_launch_mmvq_dot4_q3_k(const MmvqArgs& a, int64_t k, hipStream_t st);
+hipError_t ftk_launch_mmvq_dot4_q4_1(const MmvqArgs& a, int64_t k, hipStream_t st);
+hipError_t ftk_launch_mmvq_dot4_q5_0(const MmvqArgs& a, int64_t k, hipStream_t st);
+hipError_t ftk_launch_mmvq_dot4_q5_1(const MmvqArgs& a, int64_t k, hipStream_t st);
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st);
 // int8-MFMA matvec for 2..8 tokens (K % 256 == 0; Q4_0, Q8_0, Q4_K x Q8_1)
 bool ftk_mmvq_mfma_ok(int w, int act, int64_t k, int t);
@@ -82,7 +88,7 @@ hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st);
 // y from the per-pair rows in dpair, slot order
 hipError_t ftk_launch_moe_combine(const MoeArgs& a, hipStream_t st);
 
-// grouped GEMM over expert-sorted pairs.  With W2 set (MXFP4 only) W and W2 are
+// grouped GEMM over expert-sorted pairs.  With W2 set W and W2 are
 // the gate and up banks and y receives silu(g) * u.
 struct GroupedArgs {
   int w, act;

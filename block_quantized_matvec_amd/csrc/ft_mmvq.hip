@@ -7,9 +7,6 @@
 // fewest idle lanes, at most 16 unit-token activation sets per lane; a tile is
 // as many whole rows as fit in CPL * 4 KiB and must give every row group a row;
 // the grid is a few workgroups per CU, each owning an equal share of rows.
-// FT_MMVQ_PLAN="lr,p,cpl,wgs_per_cu,mode,-,stages,rows" forces a plan (tuning
-// sweeps; 0 = choose; mode 1 = workgroup tiles, 3 = per-wave rings; rows 1 =
-// contiguous shares, 2 = interleaved).
 // Per-wave ring: units per lane cover the row in 64-unit segments.  Measured on
 // the 14336 x 4096 and 4096 x 14336 Q4_K / Q8_0 matrices at 1, 2 and 4 tokens
 // (grid of 1..4 workgroups per CU x 2..4 stages, contiguous or interleaved rows):
@@ -23,11 +20,9 @@
 // (Q4_K, K = 14336) 1 workgroup per CU, 4 stages, contiguous, except 1 token: 2
 // workgroups per CU, 2 stages (9.17 -> 8.84 us).  More waves or deeper rings
 // beyond these only add requests in flight.
-static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n, int force_p, int force_wpc,
-                          int force_st, int force_il, MmvqPlan* out) {
+static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out) {
   int P = 1;
   while (P * 64 < units_per_row) P *= 2;
-  if (force_p) P = force_p;
   if (P > 8 || P * 64 < units_per_row || P * tslot > 16) return 0;
   int wpc, stages, il;
   if (P >= 8) {
@@ -44,11 +39,6 @@ static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n
     il = 0;
     if (P <= 2) { wpc = 2; stages = 2; }
   }
-  if (force_st) stages = force_st;
-  if (stages < 2 || stages > 4) return 0;
-  if (force_wpc) wpc = force_wpc;
-  if (force_il) il = force_il - 1;   // FT_MMVQ_PLAN field 8: 1 contiguous, 2 interleaved
-  wpc = wpc < 1 ? 1 : (wpc > 10 ? 10 : wpc);
   const int64_t waves = (int64_t)ftk::num_cus() * wpc * 4;
   int64_t rpw = (n + waves - 1) / waves;
   if (rpw < 1) rpw = 1;
@@ -72,24 +62,15 @@ static int mmvq_plan_wave(int units_per_row, int tslot, int row_bytes, int64_t n
 int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPlan* out) {
   MmvqPlan best{};
   double best_cost = 1e30;
-  int force_lr = 0, force_p = 0, force_cpl = 0, force_wgs = 0, force_mode = 0, unused = 0, force_st = 0,
-      force_il = 0;
-  if (const char* e = getenv("FT_MMVQ_PLAN"))
-    sscanf(e, "%d,%d,%d,%d,%d,%d,%d,%d", &force_lr, &force_p, &force_cpl, &force_wgs, &force_mode, &unused,
-           &force_st, &force_il);
-  // mode 0 and 3: per-wave rings; 1: workgroup LDS tiles
-  if (force_mode == 0 || force_mode == 3)
-    if (mmvq_plan_wave(units_per_row, tslot, row_bytes, n, force_p, force_wgs, force_st, force_il, out)) return 1;
+  // per-wave rings first; workgroup LDS tiles for what they cannot hold
+  if (mmvq_plan_wave(units_per_row, tslot, row_bytes, n, out)) return 1;
   for (int cpl = 4; cpl <= 8; cpl += 4) {
-    if (force_cpl && cpl != force_cpl) continue;
     const int rt = (cpl * 4096 - 15) / row_bytes;
     if (rt < 1) continue;
     for (int L = 64; L <= 256; L *= 2) {
-      if (force_lr && L != force_lr) continue;
       const int G = ftk::MMVQ_THREADS / L;
       if (G > rt) continue;
       for (int P = 1; P <= 8; P *= 2) {
-        if (force_p && P != force_p) continue;
         if (P * L < units_per_row || P * tslot > 16) continue;
         const double waste = (double)(P * L - units_per_row) / (P * L);
         const int rows_per_group = rt / G;
@@ -109,8 +90,8 @@ int ftk_mmvq_plan(int units_per_row, int tslot, int row_bytes, int64_t n, MmvqPl
   }
   if (!best.lr) return 0;
   best.tslot = tslot;
-  best.stages = best.cpl == 8 ? 2 : (force_st == 2 ? 2 : 4);
-  const int wgs_per_cu = force_wgs ? force_wgs : 2;
+  best.stages = best.cpl == 8 ? 2 : 4;
+  const int wgs_per_cu = 2;
   const int64_t slots = (int64_t)ftk::num_cus() * wgs_per_cu;
   const int64_t tiles = (n + best.rows_per_tile - 1) / best.rows_per_tile;
   const int64_t grid = tiles < slots ? tiles : slots;
@@ -151,15 +132,6 @@ int ftk_num_cus() {
 // per-block unpack and combine), and so do Q4_1 / Q5_0 / Q5_1 (4 tokens 12.4 / 13.4,
 // 13.1 / 14.8, 13.5 / 21.1; 8 tokens 24.6 / 15.4, 26.7 / 16.3, 27.0 / 22.9 before
 // Q5_1's slot pad).
-// FT_MMVQ_MFMA_MIN_T = m sends every t >= m to MFMA and the rest to dot4 (tuning
-// sweeps).
-static int mfma_min_t() {   // 0: the automatic choice
-  static const int v = [] {
-    const char* e = getenv("FT_MMVQ_MFMA_MIN_T");
-    return e && atoi(e) > 0 ? atoi(e) : 0;
-  }();
-  return v;
-}
 
 static int64_t units_of(int w, int64_t k) {
   switch (w) {
@@ -180,12 +152,9 @@ static int64_t units_of(int w, int64_t k) {
 
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;
-  const int mt = mfma_min_t();
   const bool lng = units_of(a.w, k) > 128;
   const bool late = a.w == FT_Q2_K || a.w == FT_Q3_K || a.w == FT_Q4_1 || a.w == FT_Q5_0 || a.w == FT_Q5_1;
-  const bool mfma = mt ? a.t >= mt
-                       : late || !lng ? a.t >= 5
-                       : (a.w == FT_Q8_0 || a.w == FT_Q5_K ? a.t >= 3 : a.t >= 2);
+  const bool mfma = late || !lng ? a.t >= 5 : (a.w == FT_Q8_0 || a.w == FT_Q5_K ? a.t >= 3 : a.t >= 2);
   if (mfma && ftk_mmvq_mfma_ok(a.w, a.act, k, a.t)) return ftk_launch_mmvq_mfma(a, k, st);
   if (a.act == FT_Q8_1) {
     switch (a.w) {

@@ -419,17 +419,12 @@ static hipError_t launch_mfma_kp(const MmvqArgs& a, int64_t k, hipStream_t st) {
 // 4096 at 8 tokens with 2 / 4 / 8 parts: Q8_0 16.5 / 18.3 / 19.3 us, Q4_K 13.3 /
 // 12.3 / 11.9 us; 4096 x 14336 needs 8 (2 parts: 2-3x slower).  512-element chunks
 // or a second register buffer cost more in occupancy than they gain in
-// contiguity.  FT_MMVQ_MFMA_KP = 2, 4 or 8 forces the parts (tuning sweeps).
+// contiguity.
 template <int F>
 static hipError_t launch_mfma_f(const MmvqArgs& a, int64_t k, hipStream_t st) {
-  static const int force_kp = [] { const char* e = getenv("FT_MMVQ_MFMA_KP"); return e ? atoi(e) : 0; }();
   const int64_t groups = (a.n + 15) / 16;
   const bool many = groups * 4 >= (int64_t)ftk_num_cus() * 8;
-  const int kp = force_kp == 2 || force_kp == 4 || force_kp == 8 ? force_kp
-                 : many && MvGeo<F>::CB >= 256 && F == FT_Q8_0 ? 2
-                                                            : 8;
-  if (kp == 2) return launch_mfma_kp<F, 2>(a, k, st);
-  if (kp == 4) return launch_mfma_kp<F, 4>(a, k, st);
+  if (many && MvGeo<F>::CB >= 256 && F == FT_Q8_0) return launch_mfma_kp<F, 2>(a, k, st);
   return launch_mfma_kp<F, 8>(a, k, st);
 }
 

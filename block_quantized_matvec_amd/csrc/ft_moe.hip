@@ -598,8 +598,7 @@ static bool moe_plan(int units_per_row, int row_bytes, int64_t rows, int slots, 
   if (pl.p > 8) return false;
   pl.rows_per_tile = (MOE_CPL * 4096 - 15) / row_bytes;
   if (pl.rows_per_tile < 1) return false;
-  int wpc = 2;   // FT_MOE_WPC overrides (tuning sweeps)
-  if (const char* ev = getenv("FT_MOE_WPC")) wpc = atoi(ev) > 0 ? atoi(ev) : 2;
+  const int wpc = 2;
   const int64_t target = (int64_t)wpc * ftk_num_cus();
   int64_t x = (target + slots - 1) / slots;
   if (x < 1) x = 1;
@@ -945,18 +944,12 @@ moe_ring_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t h
 // CU, 2 stages, contiguous), 3 tokens 46.7 -> 40.5 and 4 tokens 48.2 -> 47.9 (3 per
 // CU, 2 stages, interleaved); 3 stages were slower throughout.  The direct kernels
 // are bound by latency (expert ids, then the first weight bytes), not by the
-// stream.  FT_MOE_RING = "wpc,stages,rows" overrides (tuning sweeps; 0 = choose;
-// rows 1 = contiguous, 2 = interleaved), "off" keeps the workgroup-tile kernels.
+// stream.
 struct RingPlan { int lr, stages, groups_per_wave, wgs; int64_t group_stride; };
 
 static bool moe_ring_plan(int units, int64_t rows, int slots, int tslot, RingPlan& pl) {
-  static const char* env = getenv("FT_MOE_RING");
-  if (units > 64 || (env && strcmp(env, "off") == 0)) return false;
-  int wpc = 0, st = 0, il = 0;
-  if (env) sscanf(env, "%d,%d,%d", &wpc, &st, &il);
-  if (wpc <= 0) wpc = tslot >= 4 ? 3 : 2;
-  if (st < 2 || st > 4) st = 2;
-  il = il == 0 ? (tslot >= 4 ? 1 : 0) : il - 1;
+  if (units > 64) return false;
+  const int wpc = tslot >= 4 ? 3 : 2, st = 2, il = tslot >= 4 ? 1 : 0;
   pl.lr = 16;
   while (pl.lr < units) pl.lr *= 2;
   pl.stages = st;

@@ -407,21 +407,15 @@ static hipError_t fp4_gate_up_kq(const MoeArgs& a, int c0, int tc, hipStream_t s
 // gate/up K parts: 2 (each row's K in two halves: one cache line shared per row)
 // when that still gives two workgroups per CU, else 4 (more workgroups, three
 // shared lines per row; measured at 1 token: 46.4 vs 47.6 us per layer, at 2-8
-// tokens 2 parts win by 5-10%).  FT_MOE_FP4_KQ = 2, 4 or 8 forces it (sweeps).
+// tokens 2 parts win by 5-10%).
 hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
-  static const int force = [] {
-    const char* e = getenv("FT_MOE_FP4_KQ");
-    return e ? atoi(e) : 0;
-  }();
   const int cs = fp4_chunk(a.hidden, 2);
   if (cs < 1 || a.hidden % 256 || a.inter % 256) return hipErrorInvalidValue;
   for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
     const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
     const int64_t wgs2 = a.inter / (16 * MF_WAVES / 2) * tc * a.topk;
-    const int kq = force == 2 || force == 4 || force == 8 ? force : (wgs2 >= 2 * (int64_t)ftk_num_cus() ? 2 : 4);
-    const hipError_t err = kq == 2   ? fp4_gate_up_kq<2>(a, (int)c0, tc, st)
-                           : kq == 8 ? fp4_gate_up_kq<8>(a, (int)c0, tc, st)
-                                     : fp4_gate_up_kq<4>(a, (int)c0, tc, st);
+    const hipError_t err = wgs2 >= 2 * (int64_t)ftk_num_cus() ? fp4_gate_up_kq<2>(a, (int)c0, tc, st)
+                                                               : fp4_gate_up_kq<4>(a, (int)c0, tc, st);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

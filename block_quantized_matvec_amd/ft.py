@@ -189,11 +189,9 @@ def moe_sort(ids: torch.Tensor, n_expert: int, stream=None):
     return counts, offsets, pairs
 
 
-def moe_q_vec(w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: int, act: str,
-              x: torch.Tensor, ids: torch.Tensor, expert_w: torch.Tensor, out: torch.Tensor | None = None,
-              route: int = 0, taps: dict | None = None, in_hq: torch.Tensor | None = None,
-              stream=None) -> torch.Tensor:
-    """taps: optional dict of preallocated device tensors g, u, h, hq, down."""
+def _moe(entry: str, w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: int, act: str,
+         x: torch.Tensor, ids: torch.Tensor, expert_w: torch.Tensor, out, route: int, taps, in_hq,
+         direct_max_t: int, stream) -> torch.Tensor:
     for nm, tt in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down), ("x", x), ("ids", ids),
                    ("expert_w", expert_w)):
         _dev(tt, nm)
@@ -202,11 +200,20 @@ def moe_q_vec(w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: i
     if out is None:
         out = torch.empty((t, hidden), dtype=torch.float32, device=x.device)
     taps = taps or {}
-    opts = _MoeOpts(route, 0, *(_ptr(taps.get(k)) for k in ("g", "u", "h", "hq", "down")), _ptr(in_hq))
-    _check(lib().ft_moe_q_vec(TYPES[w], _ptr(w_gate), _ptr(w_up), _ptr(w_down), n_expert, hidden, inter,
-                              TYPES[act], _ptr(x), t, _ptr(ids), _ptr(expert_w), topk, _ptr(out),
-                              ctypes.byref(opts), _stream(stream)), "ft_moe_q_vec")
+    opts = _MoeOpts(route, direct_max_t, *(_ptr(taps.get(k)) for k in ("g", "u", "h", "hq", "down")), _ptr(in_hq))
+    _check(getattr(lib(), entry)(TYPES[w], _ptr(w_gate), _ptr(w_up), _ptr(w_down), n_expert, hidden, inter,
+                                 TYPES[act], _ptr(x), t, _ptr(ids), _ptr(expert_w), topk, _ptr(out),
+                                 ctypes.byref(opts), _stream(stream)), entry)
     return out
+
+
+def moe_q_vec(w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: int, act: str,
+              x: torch.Tensor, ids: torch.Tensor, expert_w: torch.Tensor, out: torch.Tensor | None = None,
+              route: int = 0, taps: dict | None = None, in_hq: torch.Tensor | None = None,
+              direct_max_t: int = 0, stream=None) -> torch.Tensor:
+    """taps: optional dict of preallocated device tensors g, u, h, hq, down."""
+    return _moe("ft_moe_q_vec", w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, ids, expert_w, out,
+                route, taps, in_hq, direct_max_t, stream)
 
 
 def grouped_gemm_q(w: str, W: torch.Tensor, n_expert: int, n: int, k: int, act: str, xq: torch.Tensor,

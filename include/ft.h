@@ -150,10 +150,12 @@ ft_status ft_moe_sort(const int32_t* ids, int64_t t, int topk, int64_t n_expert,
 
 /* Options of ft_moe_q_vec; pass NULL for defaults. */
 typedef struct {
-  int route;          /* 0 auto, 1 force the direct route, 2 force sorted tiles
-                         (tiles: (MXFP4, Q8_K) only, else FT_ERR_UNSUPPORTED) */
+  int route;          /* 0 auto, 1 force the direct route ((Q4_K, Q8_1) and (MXFP4,
+                         Q8_K) only), 2 force sorted tiles (every (w, Q8_K) pair);
+                         a route the pair lacks gives FT_ERR_UNSUPPORTED */
   int direct_max_t;   /* auto route: direct for t <= direct_max_t (0 = default 8),
-                         sorted tiles above it where supported */
+                         sorted tiles above it where supported; pairs without a
+                         direct route take the tiles at every t */
   float* tap_g;       /* nullable [t*topk][inter] fp32: gate projections */
   float* tap_u;       /* nullable [t*topk][inter] fp32: up projections */
   float* tap_h;       /* nullable [t*topk][inter] fp32: silu(g)*u */
@@ -170,8 +172,11 @@ typedef struct {
      h = silu(g)*u, hhat = act-quantized h, d = W_down[e].hhat,
    and y[i] = sum over s (in slot order) of expert_w[i][s] * d.  y: [t][hidden] fp32.
    The topk ids of one token must be distinct (as top-k routing makes them).
-   Supported (w, act): (Q4_K, Q8_1), (MXFP4, Q8_K).  topk 1..8.
-   Routes [P4 Summary: tiny batches direct, larger ones on expert-sorted tiles]:
+   Supported (w, act): (Q4_K, Q8_1) and (MXFP4, Q8_K) on both routes; (Q4_K, Q8_K),
+   (Q5_K, Q8_K), (Q6_K, Q8_K) on the sorted tiles.  topk 1..8; n_expert <= 8192 on
+   the sorted tiles.
+   Routes [P4 Summary: tiny batches direct, larger ones on expert-sorted tiles;
+   P3 What changed: the grouped keep-quant op over expert_ids]:
    direct = one workgroup per selected expert and row tile, tokens in VGPRs;
    sorted tiles = token->expert sort, one fused gate/up + SwiGLU grouped MFMA GEMM,
    h quantize, grouped down GEMM, slot-order combine.  Both give the same result
@@ -197,8 +202,10 @@ ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t 
    and 32 otherwise: the sum over each sub-block of the weight's integer code (n-8 for
    Q4_0, q for Q8_0, the 4/5-bit n for Q4_K/Q5_K, q6-32 for Q6_K, twice the E2M1 value
    for MXFP4, the 2-bit q for Q2_K, the 3-bit q-4 for Q3_K) times the activation's
-   int8 code.  Computed by the same unpack and dot core as the
-   matvec kernels. */
+   int8 code.  Computed with the unpack and v_dot4 core of the dot4 matvec kernels
+   (one and two tokens); the int8-MFMA matvec, the grouped GEMM and the FP4-MFMA
+   MoE kernels form the same integers on the matrix cores and are checked for
+   them through exactly representable outputs instead. */
 ft_status ft_debug_block_dots(ft_type w, const void* W, int64_t n, int64_t k,
                               ft_type act, const void* xq, int64_t t,
                               int32_t* partials, ft_stream_t stream);

@@ -48,7 +48,7 @@ def test_block_sizes():
 
 def test_capability_table():
     expect_mmvq = {(w, "Q8_1") for w in W}
-    expect_moe = {("Q4_K", "Q8_1"), ("MXFP4", "Q8_K")}
+    expect_moe = {("Q4_K", "Q8_1"), ("MXFP4", "Q8_K"), ("Q4_K", "Q8_K"), ("Q5_K", "Q8_K"), ("Q6_K", "Q8_K")}
     expect_grp = {("Q4_K", "Q8_K"), ("Q5_K", "Q8_K"), ("Q6_K", "Q8_K"), ("MXFP4", "Q8_K")}
     for w in W:
         for a in A:
@@ -122,15 +122,24 @@ def test_moe_route_options_refused_on_host():
     T = ft.TYPES
     fake = ctypes.c_void_p(1 << 20)
 
-    def call(w, a, route, dmax=0):
+    def call(w, a, route, dmax=0, n_expert=4, t=1):
         o = ft._MoeOpts(route, dmax, None, None, None, None, None, None)
-        return L.ft_moe_q_vec(T[w], fake, fake, fake, 4, 256, 256, T[a], fake, 1, fake, fake, 2, fake,
+        return L.ft_moe_q_vec(T[w], fake, fake, fake, n_expert, 256, 256, T[a], fake, t, fake, fake, 2, fake,
                               ctypes.byref(o), None)
 
     assert call("Q4_K", "Q8_1", 2) == ST["FT_ERR_UNSUPPORTED"]
     assert call("Q4_K", "Q8_1", 3) == ST["FT_ERR_INVALID_ARG"]
     assert call("MXFP4", "Q8_K", -1) == ST["FT_ERR_INVALID_ARG"]
     assert call("MXFP4", "Q8_K", 0, dmax=-2) == ST["FT_ERR_INVALID_ARG"]
+    # K-quant experts x Q8_K have no direct kernels: the direct route is refused
+    for w in ("Q4_K", "Q5_K", "Q6_K"):
+        assert call(w, "Q8_K", 1) == ST["FT_ERR_UNSUPPORTED"]
+    # the sorted tiles take at most 8192 experts (forced, or chosen by the auto
+    # route above direct_max_t, or for a pair without direct kernels); the direct
+    # route has no such limit
+    assert call("MXFP4", "Q8_K", 2, n_expert=9000) == ST["FT_ERR_SHAPE"]
+    assert call("MXFP4", "Q8_K", 0, n_expert=9000, t=9) == ST["FT_ERR_SHAPE"]
+    assert call("Q5_K", "Q8_K", 0, n_expert=9000) == ST["FT_ERR_SHAPE"]
 
 
 def test_status_strings():

@@ -53,6 +53,14 @@ CASES = {
     # rows of 68 units: both stages take the workgroup-tile kernels, not the rings
     "q4k_wide": dict(w="Q4_K", a="Q8_1", hidden=4352, inter=4352, E=3, topk=2),
     "mxfp4_small": dict(w="MXFP4", a="Q8_K", hidden=512, inter=512, E=5, topk=3),
+    # K-quant experts x Q8_K on the sorted tiles (grouped gate/up + SwiGLU, h
+    # quantize, grouped down, combine)
+    "q4k8k_small": dict(w="Q4_K", a="Q8_K", hidden=512, inter=768, E=6, topk=2),
+    "q5k_small": dict(w="Q5_K", a="Q8_K", hidden=768, inter=512, E=5, topk=3),
+    "q6k_small": dict(w="Q6_K", a="Q8_K", hidden=512, inter=256, E=7, topk=4),
+    # the grouped-GEMM workload's layer: hidden 4096, 128 experts of 1536, top-8
+    "q5k_c4": dict(w="Q5_K", a="Q8_K", hidden=4096, inter=1536, E=128, topk=8),
+    "q6k_c4": dict(w="Q6_K", a="Q8_K", hidden=4096, inter=1536, E=128, topk=8),
 }
 
 _banks = {}
@@ -184,6 +192,15 @@ def test_moe_mxfp4_small_tiles_shared_experts():
     _run_stages("mxfp4_small", 6, route=2, dup=True)
 
 
+@pytest.mark.parametrize("t", [200, 64])
+def test_moe_mxfp4_small_tiles_hot_expert(t):
+    """Skewed routing on the sorted tiles: every token picks one expert (t pairs on
+    it, several passes of the grouped kernels over its weights: at t = 200 the
+    kernel holds 64 pairs per pass, at t = 64 32); every pair is compared."""
+    log(f"moe mxfp4_small tiles hot expert t={t}")
+    _run_stages("mxfp4_small", t, route=2, dup=True)
+
+
 @pytest.mark.parametrize("t,route", [(1, 2), (4, 2), (5, 0), (9, 0), (12, 0)])
 def test_moe_mxfp4_tiles(t, route):
     """Full-size MXFP4 bank (hidden 4096, 256 experts of 2048): route 0 takes the
@@ -214,17 +231,100 @@ def test_moe_mxfp4_tiles_sampled(t):
     xq = oracle.quantize(c["a"], x)
     flat = ids.reshape(-1)
     pairs = np.unique(np.concatenate([np.arange(4), np.arange(np_ - 4, np_), g.choice(np_, 12, replace=False)]))
-    for p in pairs:
+    # the oracle's gate/up stage on the sampled pairs alone: one token per pair
+    # (its token's quantized x), top-1 routing to the pair's expert
+    rg_all, ru_all, rh_all = oracle.moe_gate_up(c["w"], wg, wu, E, H, I, c["a"],
+                                                np.ascontiguousarray(xq[pairs // K]),
+                                                np.ascontiguousarray(flat[pairs][:, None]))
+    for j, p in enumerate(pairs):
         e = flat[p]
-        rg = oracle.matvec(c["w"], np.ascontiguousarray(wg[e]), I, H, c["a"], xq[p // K][None], 1)[0]
-        ru = oracle.matvec(c["w"], np.ascontiguousarray(wu[e]), I, H, c["a"], xq[p // K][None], 1)[0]
-        check_fp32(gg[p], rg, f"g pair {p}")
-        check_fp32(uu[p], ru, f"u pair {p}")
-        rh = (rg / (1.0 + np.exp(-rg)) * ru)
-        check_fp32(hh[p], rh, f"h pair {p}")
+        check_fp32(gg[p], rg_all[j], f"g pair {p}")
+        check_fp32(uu[p], ru_all[j], f"u pair {p}")
+        check_fp32(hh[p], rh_all[j], f"h pair {p}")
         assert np.array_equal(hq[p], oracle.quantize(c["a"], hh[p][None])[0]), f"hq pair {p}"
         rd = oracle.matvec(c["w"], np.ascontiguousarray(wd[e]), H, I, c["a"], hq[p][None], 1)[0]
         check_fp32(dd[p], rd, f"down pair {p}")
+    check_fp32(y, oracle.moe_combine(dd, ew), "combine")
+
+
+@pytest.mark.parametrize("name", ["q4k8k_small", "q5k_small", "q6k_small"])
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 5, 9, 32])
+def test_moe_kq_tiles_small(name, t):
+    """K-quant experts on the sorted tiles at every t (the auto route takes them:
+    these pairs have no direct kernels); stage taps against the oracle."""
+    log(f"moe {name} tiles t={t}")
+    _run_stages(name, t, route=2 if t % 2 else 0)
+
+
+@pytest.mark.parametrize("name", ["q4k8k_small", "q5k_small", "q6k_small"])
+def test_moe_kq_tiles_hot_expert(name):
+    """Skewed routing: every token picks one expert (several passes of the grouped
+    kernels over its weights); every pair is compared stage by stage."""
+    log(f"moe {name} tiles hot expert t=160")
+    _run_stages(name, 160, route=2, dup=True)
+
+
+@pytest.mark.parametrize("name", ["q4k8k_small", "q6k_small"])
+def test_moe_kq_tiles_repeated_expert(name):
+    _run_stages(name, 6, route=2, rep=True)
+
+
+def test_moe_kq_no_direct_route():
+    c = CASES["q5k_small"]
+    wg, wu, wd, dwg, dwu, dwd = _bank("q5k_small")
+    x = dev(synth.activations(2, c["hidden"], synth.rng(307)))
+    ids = dev(synth.expert_ids(2, c["E"], c["topk"], synth.rng(308)))
+    ew = dev(synth.expert_weights(2, c["topk"], synth.rng(309)))
+    with pytest.raises(ft.FtError, match="FT_ERR_UNSUPPORTED"):
+        ft.moe_q_vec(c["w"], dwg, dwu, dwd, c["E"], c["hidden"], c["inter"], c["a"], x, ids, ew, route=1)
+
+
+@pytest.mark.parametrize("name,t,hot", [("q5k_c4", 32, False), ("q5k_c4", 512, False), ("q6k_c4", 128, False),
+                                        ("q6k_c4", 512, True)])
+def test_moe_kq_tiles_sampled(name, t, hot):
+    """The grouped-GEMM workload as a whole layer (hidden 4096, 128 experts of 1536,
+    top-8) at 32-512 tokens; the oracle checks a sample of pairs stage by stage (g,
+    u, h, quantized h, down) and the whole combine.  hot: every token's slot 0 on
+    one expert, whose pairs are all in the sample."""
+    c = CASES[name]
+    wg, wu, wd, dwg, dwu, dwd = _bank(name)
+    g = synth.rng(310, t, hot)
+    H, I, E, K = c["hidden"], c["inter"], c["E"], c["topk"]
+    x = synth.activations(t, H, g)
+    ids = synth.expert_ids(t, E, K, g)
+    if hot:
+        e0 = 3
+        for i in range(t):
+            hit = np.nonzero(ids[i] == e0)[0]
+            if len(hit):
+                ids[i, hit[0]] = ids[i, 0]
+            ids[i, 0] = e0
+    ew = synth.expert_weights(t, K, g)
+    np_ = t * K
+    taps = {"g": torch.empty(np_, I, device="cuda"), "u": torch.empty(np_, I, device="cuda"),
+            "h": torch.empty(np_, I, device="cuda"),
+            "hq": torch.empty(np_, ft.row_bytes(c["a"], I), dtype=torch.uint8, device="cuda"),
+            "down": torch.empty(np_, H, device="cuda")}
+    log(f"moe {name} tiles sampled t={t} hot={hot}")
+    y = host(ft.moe_q_vec(c["w"], dwg, dwu, dwd, E, H, I, c["a"], dev(x), dev(ids), dev(ew), route=0, taps=taps))
+    gg, uu, hh, hq, dd = (host(taps[k]) for k in ("g", "u", "h", "hq", "down"))
+    xq = oracle.quantize(c["a"], x)
+    flat = ids.reshape(-1)
+    pick = [np.arange(4), np.arange(np_ - 4, np_), g.choice(np_, 12, replace=False)]
+    if hot:
+        pick.append(np.nonzero(flat == 3)[0][:: max(1, t // 48)])
+    pairs = np.unique(np.concatenate(pick))
+    rg_all, ru_all, rh_all = oracle.moe_gate_up(c["w"], wg, wu, E, H, I, c["a"],
+                                                np.ascontiguousarray(xq[pairs // K]),
+                                                np.ascontiguousarray(flat[pairs][:, None]))
+    rd_all = oracle.moe_down(c["w"], wd, E, H, I, c["a"], np.ascontiguousarray(hq[pairs]),
+                             np.ascontiguousarray(flat[pairs][:, None]))
+    for j, p in enumerate(pairs):
+        check_fp32(gg[p], rg_all[j], f"g pair {p}")
+        check_fp32(uu[p], ru_all[j], f"u pair {p}")
+        check_fp32(hh[p], rh_all[j], f"h pair {p}")
+        assert np.array_equal(hq[p], oracle.quantize(c["a"], hh[p][None])[0]), f"hq pair {p}"
+        check_fp32(dd[p], rd_all[j], f"down pair {p}")
     check_fp32(y, oracle.moe_combine(dd, ew), "combine")
 
 
