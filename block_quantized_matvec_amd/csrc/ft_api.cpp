@@ -363,6 +363,31 @@ ft_status moe_run(ft_type w, const void* w_gate, const void* w_up, const void* w
   return hip_status(e);
 }
 
+// --------------------------------------------------------------------------
+// fixed scratch of ft_moe_q_vec_noalloc: a device array of every GPU the library
+// runs on, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is a stand-in, not a device address): the address
+// comes from hipGetSymbolAddress once per device and is kept here.
+// --------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[FT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+
+ft_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FT_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FT_ERR_HIP;
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return FT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +409,25 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
   if (s != FT_OK) return s;
   return moe_run(w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, t, expert_ids, expert_w, topk, y, o,
                  tiles, (uint8_t*)base, st);
+}
+
+ft_status ft_moe_q_vec_noalloc(ft_type w, const void* w_gate, const void* w_up, const void* w_down,
+                               int64_t n_expert, int64_t hidden, int64_t inter, ft_type act, const float* x,
+                               int64_t t, const int32_t* expert_ids, const float* expert_w, int topk, float* y,
+                               const ft_moe_opts* opts, ft_stream_t stream) {
+  ft_moe_opts o = {};
+  if (opts) o = *opts;
+  bool tiles = false;
+  size_t need = 0;
+  ft_status s = moe_check(w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, t, expert_ids, expert_w, topk,
+                          y, o, &tiles, &need);
+  if (s != FT_OK || t == 0) return s;
+  if (need > (size_t)FT_NOALLOC_SCRATCH_BYTES) return FT_ERR_SHAPE;
+  void* base = nullptr;
+  s = static_scratch(&base);
+  if (s != FT_OK) return s;
+  return moe_run(w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, t, expert_ids, expert_w, topk, y, o,
+                 tiles, (uint8_t*)base, hs(stream));
 }
 
 ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t n, int64_t k, ft_type act,

@@ -55,6 +55,11 @@ EXPORTS = {
                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(_MoeOpts), ctypes.c_void_p]),
+    "ft_moe_q_vec_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(_MoeOpts),
+                                            ctypes.c_void_p]),
     "ft_grouped_gemm_q": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
@@ -214,6 +219,15 @@ def moe_q_vec(w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: i
     """taps: optional dict of preallocated device tensors g, u, h, hq, down."""
     return _moe("ft_moe_q_vec", w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, ids, expert_w, out,
                 route, taps, in_hq, direct_max_t, stream)
+
+
+def moe_q_vec_noalloc(w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: int, act: str,
+                      x: torch.Tensor, ids: torch.Tensor, expert_w: torch.Tensor, out: torch.Tensor | None = None,
+                      route: int = 0, taps: dict | None = None, in_hq: torch.Tensor | None = None,
+                      direct_max_t: int = 0, stream=None) -> torch.Tensor:
+    """As moe_q_vec, with the library's fixed per-GPU scratch instead of the stream's pool."""
+    return _moe("ft_moe_q_vec_noalloc", w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, ids, expert_w,
+                out, route, taps, in_hq, direct_max_t, stream)
 
 
 def grouped_gemm_q(w: str, W: torch.Tensor, n_expert: int, n: int, k: int, act: str, xq: torch.Tensor,

@@ -187,6 +187,23 @@ ft_status ft_moe_q_vec(ft_type w, const void* w_gate, const void* w_up, const vo
                        const int32_t* expert_ids, const float* expert_w, int topk,
                        float* y, const ft_moe_opts* opts, ft_stream_t stream);
 
+/* The same layer for callers that cannot allocate device memory (code under HIP
+   graph capture, serving loops that must not call hipMalloc, harnesses that forbid
+   it).  Arguments, routes, results and errors as ft_moe_q_vec; its scratch is a
+   fixed device array of FT_NOALLOC_SCRATCH_BYTES per GPU, held by the library until
+   the process ends, instead of the stream's pool.  A problem whose scratch
+   (ft_moe_scratch_bytes) exceeds that size is refused with FT_ERR_SHAPE before
+   anything is enqueued.  Calls on one GPU share that array: calls that may overlap
+   on one GPU (different streams) race and must be ordered by the caller.  Nothing
+   in the array needs to start at zero.  The first call on a device looks the
+   array's address up (hipGetSymbolAddress) and keeps it. */
+#define FT_NOALLOC_SCRATCH_BYTES (32u << 20)
+ft_status ft_moe_q_vec_noalloc(ft_type w, const void* w_gate, const void* w_up, const void* w_down,
+                               int64_t n_expert, int64_t hidden, int64_t inter,
+                               ft_type act, const float* x, int64_t t,
+                               const int32_t* expert_ids, const float* expert_w, int topk,
+                               float* y, const ft_moe_opts* opts, ft_stream_t stream);
+
 /* Grouped keep-quant expert GEMM [P3 What changed: grouped over expert_ids].
    W: [n_expert][n][k/blk] blocks; xq: act blocks, [t][k/blk_a] when x_per_pair = 0
    (every slot of a token reads its token's row) or [t*topk][k/blk_a] when 1.

@@ -152,3 +152,19 @@ def test_scratch_sizes_are_monotone():
     a = ft.moe_scratch_bytes("Q4_K", "Q8_1", 128, 2048, 768, 1, 8)
     b = ft.moe_scratch_bytes("Q4_K", "Q8_1", 128, 2048, 768, 4, 8)
     assert 0 < a < b
+
+
+def test_moe_noalloc_refusals_on_host():
+    """ft_moe_q_vec_noalloc validates as ft_moe_q_vec and refuses a problem whose
+    scratch exceeds its fixed array before anything is enqueued (no GPU needed)."""
+    L = ft.lib()
+    T = ft.TYPES
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.ft_moe_q_vec_noalloc(T["Q5_0"], fake, fake, fake, 4, 256, 256, T["Q8_1"], fake, 1, fake, fake, 2,
+                                  fake, None, None) == ST["FT_ERR_UNSUPPORTED"]
+    assert L.ft_moe_q_vec_noalloc(T["Q4_K"], fake, fake, fake, 4, 256, 256, T["Q8_1"], fake, 1, fake, fake, 9,
+                                  fake, None, None) == ST["FT_ERR_SHAPE"]
+    H, I, E, K, t = 4096, 256, 8, 8, 1024
+    assert ft.moe_scratch_bytes("Q4_K", "Q8_1", E, H, I, t, K) > 32 << 20
+    assert L.ft_moe_q_vec_noalloc(T["Q4_K"], fake, fake, fake, E, H, I, T["Q8_1"], fake, t, fake, fake, K,
+                                  fake, None, None) == ST["FT_ERR_SHAPE"]
