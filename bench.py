@@ -10,8 +10,14 @@ whole path (activation quantize + quantized matvec) over all 16 cases.  Weights
 are resident in HBM before timing; every case rotates over enough distinct
 weight copies that no launch can be served from the 256 MB last-level cache.
 
-Other workloads (--workload): q4_0_matvec, moe_q4k, moe_mxfp4, grouped_kq, and
-formats (every weight format x Q8_1 at W 14336x4096, 1/2/4/8 tokens; no CPU leg).
+The same line carries the rest of the metric under its own keys: routed-MoE layer
+tokens/s for the Q4_K layer (1-4 tokens), the MXFP4 layer (1-512 tokens) and the
+K-quant layer on the sorted tiles (512 tokens), and the grouped keep-quant GEMM
+(512 tokens, Q5_K/Q6_K), each with its effective weight GB/s and HBM fraction.
+
+Other workloads (--workload): q4_0_matvec, moe_q4k, moe_mxfp4, moe_kq_layer,
+grouped_kq, and formats (every weight format x Q8_1 at W 14336x4096, 1/2/4/8
+tokens; no CPU leg).
 """
 from __future__ import annotations
 
@@ -22,6 +28,8 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MOE_DTYPE = ("i8 x i8 -> i32 (v_dot4 on the Q4_K direct route, int8 MFMA on the K-quant tiles), "
+             "E2M1 x FP8 halves of the i8 codes on the FP4 MFMA (MXFP4), f32 scale combine")
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
@@ -62,8 +70,10 @@ def _args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_decode",
-                    choices=["dense_decode", "q4_0_matvec", "moe_q4k", "moe_mxfp4", "grouped_kq", "counters",
-                             "ceilings", "formats"])
+                    choices=["dense_decode", "q4_0_matvec", "moe_q4k", "moe_mxfp4", "moe_kq_layer", "grouped_kq",
+                             "counters", "ceilings", "formats"])
+    ap.add_argument("--dense-only", action="store_true",
+                    help="dense_decode without the MoE and grouped-GEMM parts of the line")
     ap.add_argument("--copies", type=int, default=0, help="weight copies per matrix (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=str, default="", help="comma list overriding the token counts")
@@ -92,7 +102,7 @@ def main():
         sys.exit(1)
     ft.lib()
     fn = {"dense_decode": bench_dense, "formats": bench_dense, "q4_0_matvec": bench_q4_0, "moe_q4k": bench_moe,
-          "moe_mxfp4": bench_moe, "grouped_kq": bench_grouped, "counters": run_counters,
+          "moe_mxfp4": bench_moe, "moe_kq_layer": bench_moe, "grouped_kq": bench_grouped, "counters": run_counters,
           "ceilings": lambda a, n, t, f, s: measure_ceilings(t, f)}[args.workload]
     out = fn(args, np, torch, ft, synth)
     print(json.dumps(out), flush=True)
@@ -202,20 +212,44 @@ def _time_graph_median(torch, g, reps=7):
     return ts[len(ts) // 2]
 
 
-def _cpu_baseline(fn, sample_desc, unit, work, min_seconds=10.0):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline(fn, sample_desc, unit, work, min_seconds=10.0, one_thread_seconds=4.0):
     """Time the oracle (as it stands) on the host cores: repeat fn until about
-    min_seconds of CPU work, report work per second."""
+    min_seconds of CPU work with all the threads it has, report work per second;
+    then the same on one thread for about one_thread_seconds."""
     import oracle
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        fn()
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": round(reps * work / dt, 4), "unit": unit, "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{reps} x {sample_desc}", "seconds": round(dt, 2)}
+
+    def timed(limit):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= limit:
+                return reps, dt
+
+    threads = oracle.threads()
+    reps, dt = timed(min_seconds)
+    oracle.set_threads(1)
+    try:
+        reps1, dt1 = timed(one_thread_seconds)
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(reps * work / dt, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x {sample_desc}", "seconds": round(dt, 2), "cpu_model": _cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "one_thread": {"value": round(reps1 * work / dt1, 4), "sample": f"{reps1} x {sample_desc}",
+                           "seconds": round(dt1, 2)}}
 
 
 # ---------------------------------------------------------------------------
@@ -242,17 +276,24 @@ def bench_dense(args, np, torch, ft, synth):
     for key in dev:
         base = dev[key][0]
         dev[key] += [base.clone() for _ in range(ncp[key] - 1)]
-    xs = {(k, t): synth.activations(t, k, g) for (_, _, k) in mats for t in tokens}
-    dxs = {key: torch.from_numpy(v).cuda() for key, v in xs.items()}
-    xq = {(k, t): torch.empty((t, ft.row_bytes("Q8_1", k)), dtype=torch.uint8, device="cuda")
-          for (k, t) in xs}
+    # the activations of every token count at one K are the rows of one [sum t][K]
+    # matrix, quantized by one launch per step; a case reads its rows
+    ks = sorted({k for (_, _, k) in mats})
+    row0 = {t: sum(tokens[:i]) for i, t in enumerate(tokens)}
+    nrows = sum(tokens)
+    xall = {k: synth.activations(nrows, k, g) for k in ks}
+    dxall = {k: torch.from_numpy(v).cuda() for k, v in xall.items()}
+    xqall = {k: torch.empty((nrows, ft.row_bytes("Q8_1", k)), dtype=torch.uint8, device="cuda") for k in ks}
+    xs = {(k, t): xall[k][row0[t]:row0[t] + t] for k in ks for t in tokens}
+    xq = {(k, t): xqall[k][row0[t]:row0[t] + t] for k in ks for t in tokens}
     cases = [(fmt, n, k, t) for (fmt, n, k) in mats for t in tokens]
     ys = {c: torch.empty((c[3], c[1]), dtype=torch.float32, device="cuda") for c in cases}
 
     def step(j):
         """one pass of the path over every case, weight copy j"""
+        for k in ks:
+            ft.quantize_act("Q8_1", dxall[k], out=xqall[k])
         for (fmt, n, k, t) in cases:
-            ft.quantize_act("Q8_1", dxs[(k, t)], out=xq[(k, t)])
             cp = dev[(fmt, n, k)]
             ft.mul_mat_vec_q(fmt, cp[j % len(cp)], n, k, "Q8_1", xq[(k, t)], t, out=ys[(fmt, n, k, t)])
 
@@ -301,13 +342,14 @@ def bench_dense(args, np, torch, ft, synth):
         "n_gpus": 1, "steps": steps_done, "warmup": args.warmup,
         "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 dot4 -> i32, f32 scale combine",
+        "dtype": "i8 x i8 -> i32 (v_dot4 at 1-4 tokens, int8 MFMA from 2-5 tokens), f32 scale combine",
         "data": "synthetic (seeded GGUF blocks, N(0,1) activations)",
         "config": {"workload": (f"decode matvec, every weight format ({'/'.join(cfg['formats'])}), "
                                 "W 14336x4096" if fmts_only else
                                 "dense decode matvec: Q8_0 and Q4_K, W 14336x4096 and 4096x14336")
-                               + f", batch {'/'.join(map(str, tokens))}, Q8_1 activations; step = quantize + "
-                               "matvec for all cases, replayed as a HIP graph",
+                               + f", batch {'/'.join(map(str, tokens))}, Q8_1 activations; step = one Q8_1 "
+                               "quantize launch per K (all token counts' rows) + the matvec of every case, "
+                               "replayed as a HIP graph",
                    "cases": len(cases),
                    "weight_copies_per_matrix": {f"{f} {n}x{k}": c for (f, n, k), c in ncp.items()},
                    "weight_bytes_per_step": total_w},
@@ -318,6 +360,18 @@ def bench_dense(args, np, torch, ft, synth):
         "cases": per_case,
     }
     _add_ceilings(out, torch, ft)
+    if not fmts_only and not args.dense_only:
+        # the rest of the metric: routed-MoE layer tokens/s and the grouped GEMM
+        del dev, dxall, xqall, xq, ys, g_steps
+        torch.cuda.empty_cache()
+        out["moe_q4k"] = moe_results(args, np, torch, ft, synth, synth.MOE_Q4K, list(synth.MOE_Q4K["tokens"]))
+        torch.cuda.empty_cache()
+        out["moe_mxfp4"] = moe_results(args, np, torch, ft, synth, synth.MOE_MXFP4, list(synth.MOE_MXFP4["tokens"]))
+        torch.cuda.empty_cache()
+        out["grouped_kq"] = grouped_results(args, np, torch, ft, synth)
+        torch.cuda.empty_cache()
+        out["moe_kq_layer"] = moe_results(args, np, torch, ft, synth, synth.MOE_KQ_LAYER,
+                                          list(synth.MOE_KQ_LAYER["tokens"]))
     if not args.no_cpu_baseline and not fmts_only:
         import oracle
         xqs = {key: oracle.quantize("Q8_1", v) for key, v in xs.items()}
@@ -386,17 +440,18 @@ def bench_q4_0(args, np, torch, ft, synth):
 # ---------------------------------------------------------------------------
 # routed MoE layer, tokens/s
 # ---------------------------------------------------------------------------
-def bench_moe(args, np, torch, ft, synth):
-    c = synth.MOE_Q4K if args.workload == "moe_q4k" else synth.MOE_MXFP4
+def moe_results(args, np, torch, ft, synth, c, tokens, route=0):
+    """Layer time per token count: a HIP graph of 2 x (layer banks) steps, each
+    route (fresh logits) + the layer, each on another copy of the expert banks."""
     fmt, act, H, I, E, topk = c["fmt"], c["act"], c["hidden"], c["inter"], c["n_expert"], c["topk"]
-    tokens = [int(x) for x in args.tokens.split(",")] if args.tokens else list(c["tokens"])
-    g = synth.rng(7, 3 if fmt == "Q4_K" else 5)
+    g = synth.rng(7, {"Q4_K": 3, "MXFP4": 5}.get(fmt, 6), H)
     wg = synth.expert_bank(fmt, E, I, H, g)
     wu = synth.expert_bank(fmt, E, I, H, g)
     wd = synth.expert_bank(fmt, E, H, I, g)
     layer_bytes = wg.nbytes + wu.nbytes + wd.nbytes
     layers = args.copies or max(2, min(8, int(-(-(2 << 30) // layer_bytes))))
     banks = [(torch.from_numpy(wg).cuda(), torch.from_numpy(wu).cuda(), torch.from_numpy(wd).cuda())]
+    del wg, wu, wd
     for _ in range(layers - 1):
         banks.append(tuple(b.clone() for b in banks[0]))
     per_expert = layer_bytes // E
@@ -414,34 +469,43 @@ def bench_moe(args, np, torch, ft, synth):
             for i in range(G):
                 wgb, wub, wdb = banks[i % layers]
                 ft.moe_route(logits[i], topk, ids=ids[i], w=w[i])
-                ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, ids[i], w[i], out=y, route=args.route)
+                ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, ids[i], w[i], out=y, route=route)
 
         gs = _graph(torch, steps)
         sec = _time_graph(torch, gs, max(1, args.steps // G)) / G
         idh = ids.cpu().numpy()
         u = float(np.mean([len(np.unique(idh[i])) for i in range(G)]))
-        tiles_ok = (fmt, act) == ("MXFP4", "Q8_K")
-        route = "sorted tiles" if tiles_ok and (args.route == 2 or (args.route == 0 and t > 8)) else "direct"
-        results.append({"tokens": t, "route": route, "tok_per_s": round(t / sec, 1), "layer_us": round(sec * 1e6, 2),
+        direct_ok = (fmt, act) in (("Q4_K", "Q8_1"), ("MXFP4", "Q8_K"))
+        tiles = route == 2 or (route == 0 and (not direct_ok or t > 8))
+        results.append({"tokens": t, "route": "sorted tiles" if tiles else "direct",
+                        "tok_per_s": round(t / sec, 1), "layer_us": round(sec * 1e6, 2),
                         "unique_experts": round(u, 2),
                         "weight_GBps": round(u * per_expert / sec / 1e9, 1),
                         "hbm_frac": round(u * per_expert / sec / 1e9 / HBM_PEAK_GBS, 4)})
-        del gs
-    head = results[0]
+        del gs, x, logits, ids, w, y
+    del banks
+    return {"workload": f"routed MoE layer {fmt} x {act}: hidden {H}, {E} experts of {I}, top-{topk}; step = "
+                        "route + layer (quantize, gate/up+SwiGLU, quantize h, down, combine), HIP graph",
+            "metric": "routed-MoE layer tokens/s", "dtype": MOE_DTYPE, "layer_banks": layers,
+            "per_tokens": results}
+
+
+def bench_moe(args, np, torch, ft, synth):
+    c = {"moe_q4k": synth.MOE_Q4K, "moe_mxfp4": synth.MOE_MXFP4, "moe_kq_layer": synth.MOE_KQ_LAYER}[args.workload]
+    tokens = [int(x) for x in args.tokens.split(",")] if args.tokens else list(c["tokens"])
+    r = moe_results(args, np, torch, ft, synth, c, tokens, route=args.route)
+    head = r["per_tokens"][0]
     out = {
         "metric": "routed-MoE layer tokens/s", "value": head["tok_per_s"], "unit": "tokens/s",
-        "n_gpus": 1, "steps": G * max(1, args.steps // G), "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(head["layer_us"] / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 (dot4 direct route, MFMA sorted tiles) -> i32, f32 scale combine",
-        "data": "synthetic (router logits redrawn every step)",
-        "config": {"workload": f"routed MoE layer {fmt} x {act}: hidden {H}, {E} experts of {I}, top-{topk}; "
-                               "step = route + quantize + gate/up+SwiGLU + quantize + down + combine, HIP graph",
-                   "tokens": tokens, "layer_banks": layers},
+        "dtype": MOE_DTYPE, "data": "synthetic (router logits redrawn every step)",
+        "config": {"workload": r["workload"], "tokens": tokens, "layer_banks": r["layer_banks"]},
         "roofline": {"bound": "hbm", "kernel": "whole MoE layer (unique experts' weight bytes / layer time)",
                      "achieved": head["weight_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["hbm_frac"], "traffic": None},
-        "per_tokens": results,
+        "per_tokens": r["per_tokens"],
     }
     return _add_ceilings(out, torch, ft)
 
@@ -449,7 +513,9 @@ def bench_moe(args, np, torch, ft, synth):
 # ---------------------------------------------------------------------------
 # grouped keep-quant expert GEMM, 512 tokens
 # ---------------------------------------------------------------------------
-def bench_grouped(args, np, torch, ft, synth):
+def grouped_results(args, np, torch, ft, synth):
+    """Each grouped GEMM case (sort + GEMM per call) in a HIP graph over 4 weight
+    copies and 4 routings."""
     c = synth.GROUPED_KQ
     T, H, I, E, topk = c["tokens"], c["hidden"], c["inter"], c["n_expert"], c["topk"]
     g = synth.rng(7, 4)
@@ -467,27 +533,34 @@ def bench_grouped(args, np, torch, ft, synth):
             ids_pool = [torch.from_numpy(synth.expert_ids(T, E, topk, g)).cuda() for _ in range(copies)]
             y = torch.empty((T * topk, n), device="cuda")
             ft.scratch_reserve(1 << 20)
-            gg = _graph(torch, lambda: [ft.grouped_gemm_q(fmt, dWs[i], E, n, k, "Q8_K", xq, per_pair, ids_pool[i], out=y)
-                                        for i in range(copies)])
+            gg = _graph(torch, lambda: [ft.grouped_gemm_q(fmt, dWs[i], E, n, k, "Q8_K", xq, per_pair, ids_pool[i],
+                                                          out=y) for i in range(copies)])
             us = _time_graph(torch, gg, max(1, args.steps // copies)) / copies * 1e6
             ops = 2.0 * T * topk * n * k
             alg = W.nbytes + xq.numel() + y.numel() * 4
             results.append({"case": f"{fmt} {proj} {n}x{k}", "us": round(us, 2),
+                            "weight_GBps": round(W.nbytes / us / 1e3, 1),
                             "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
                             "int8_TOPS": round(ops / us / 1e6, 2),
                             "mfma_frac": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)})
-            del dWs, dW, gg
-    head = results[0]
+            del dWs, dW, gg, W, x, xq, y
+    return {"workload": f"grouped keep-quant GEMM: {T} tokens, hidden {H}, {E} experts of {I}, top-{topk}, "
+                        "Q5_K/Q6_K x Q8_K (sort + GEMM per call), HIP graph",
+            "cases": results}
+
+
+def bench_grouped(args, np, torch, ft, synth):
+    r = grouped_results(args, np, torch, ft, synth)
+    head = r["cases"][0]
     out = {
         "metric": "grouped expert GEMM int8 TOP/s", "value": head["int8_TOPS"], "unit": "TOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us"] / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 -> i32, f32 scale combine", "data": "synthetic",
-        "config": {"workload": f"grouped keep-quant GEMM: {T} tokens, hidden {H}, {E} experts of {I}, "
-                               f"top-{topk}, Q5_K/Q6_K x Q8_K (sort + GEMM per launch), HIP graph"},
+        "dtype": "i8 x i8 -> i32 on int8 MFMA, f32 scale combine", "data": "synthetic",
+        "config": {"workload": r["workload"]},
         "roofline": {"bound": "hbm", "kernel": head["case"], "achieved": round(head["hbm_frac"] * HBM_PEAK_GBS, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["hbm_frac"], "traffic": None},
-        "cases": results,
+        "cases": r["cases"],
     }
     return _add_ceilings(out, torch, ft, tops=head["int8_TOPS"])
 

@@ -99,6 +99,8 @@ MOE_Q4K = dict(fmt="Q4_K", act="Q8_1", hidden=2048, inter=768, n_expert=128, top
                tokens=(1, 2, 3, 4))
 GROUPED_KQ = dict(formats=("Q5_K", "Q6_K"), act="Q8_K", tokens=512, hidden=4096,
                   inter=1536, n_expert=128, topk=8)
+# the grouped-GEMM workload's shapes as a whole routed layer on the sorted tiles
+MOE_KQ_LAYER = dict(fmt="Q5_K", act="Q8_K", hidden=4096, inter=1536, n_expert=128, topk=8, tokens=(512,))
 MOE_MXFP4 = dict(fmt="MXFP4", act="Q8_K", hidden=4096, inter=2048, n_expert=256, topk=8,
                  tokens=(1, 2, 3, 4, 5, 32, 128, 512))
 

@@ -24,7 +24,10 @@ FMT = {"Q4_0": 0, "Q8_0": 1, "Q4_K": 2, "Q5_K": 3, "Q6_K": 4, "MXFP4": 5, "Q8_1"
 WEIGHT_FORMATS = ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K", "Q4_1", "Q5_0", "Q5_1")
 ACT_FORMATS = ("Q8_1", "Q8_K")
 
-_BUILD_CMD = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+# -O3 with the x86-64-v3 level (AVX2) rather than -march=native: the library is
+# built in one place and may run on another host's CPU.  No contraction and no
+# fast-math, so vectorisation cannot change a result.
+_BUILD_CMD = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
               "-Wall", "-shared", "-fPIC", SRC_PATH, "-o", LIB_PATH, "-lm"]
 
 
@@ -50,7 +53,7 @@ def lib() -> ctypes.CDLL:
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         sig = {
             "or_block_elems": (I, [I]), "or_block_bytes": (I, [I]), "or_sub_elems": (I, [I]),
-            "or_threads": (I, []),
+            "or_threads": (I, []), "or_set_threads": (None, [I]),
             "or_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
             "or_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
             "or_f32_to_f16_range": (None, [ctypes.c_uint32, ctypes.c_uint32, P]),
@@ -98,6 +101,10 @@ def sub_elems(fmt: str) -> int:
 
 def threads() -> int:
     return lib().or_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().or_set_threads(n)
 
 
 def row_bytes(fmt: str, k: int) -> int:

@@ -57,6 +57,14 @@ int or_threads(void) {
 #endif
 }
 
+void or_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* binary16                                                                  */
 /* ------------------------------------------------------------------------ */

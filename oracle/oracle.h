@@ -42,6 +42,7 @@ int    or_block_elems(int fmt);            /* 32 or 256, 0 for unknown */
 int    or_block_bytes(int fmt);            /* bytes per block, 0 for unknown */
 int    or_sub_elems(int wfmt);             /* elements per integer partial: 16 for Q2_K, Q3_K, Q6_K, else 32 */
 int    or_threads(void);                   /* OpenMP threads the oracle will use */
+void   or_set_threads(int n);              /* use n OpenMP threads from now on (n > 0) */
 
 /* IEEE binary16 <-> binary32, written by hand (round to nearest even). */
 float    or_f16_to_f32(uint16_t h);
