@@ -24,7 +24,8 @@ constexpr int kElems[kTypes] = {32, 32, 256, 256, 256, 32, 32, 256, 256, 256, 32
 constexpr int kBytes[kTypes] = {18, 34, 144, 176, 210, 17, 36, 292, 84, 110, 20, 22, 24};
 
 bool is_weight(int t) { return (t >= FT_Q4_0 && t <= FT_MXFP4) || (t >= FT_Q2_K && t <= FT_Q5_1); }
-bool is_act(int t) { return t == FT_Q8_1 || t == FT_Q8_K; }
+// Q8_0 is a weight format and, with the same block layout, an activation format
+bool is_act(int t) { return t == FT_Q8_1 || t == FT_Q8_K || t == FT_Q8_0; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int64_t row_bytes_of(int type, int64_t k) { return k / kElems[type] * kBytes[type]; }
 
@@ -107,7 +108,11 @@ SortScratch sort_layout(int64_t n_expert, int64_t t, int topk, size_t xf8_bytes 
 }
 size_t xf8_bytes_of(int w, int64_t rows, int64_t k) { return w == FT_MXFP4 ? (size_t)rows * (k / 256) * 512 : 0; }
 
-bool mmvq_pair(int w, int a) { return a == FT_Q8_1 && is_weight(w); }
+// every weight format x Q8_1 or Q8_0; the grouped-GEMM formats x Q8_K
+bool mmvq_pair(int w, int a) {
+  return ((a == FT_Q8_1 || a == FT_Q8_0) && is_weight(w)) ||
+         (a == FT_Q8_K && (w == FT_Q4_K || w == FT_Q5_K || w == FT_Q6_K || w == FT_MXFP4));
+}
 // the direct route: Q4_K x Q8_1 on dot4, MXFP4 x Q8_K on the FP4 MFMA; the sorted
 // tiles: every grouped-GEMM format x Q8_K
 bool moe_direct_pair(int w, int a) { return (w == FT_Q4_K && a == FT_Q8_1) || (w == FT_MXFP4 && a == FT_Q8_K); }
@@ -189,6 +194,16 @@ ft_status ft_mul_mat_vec_q(ft_type w, const void* W, int64_t n, int64_t k, ft_ty
   if (!W || !xq || !y) return FT_ERR_INVALID_ARG;
   if (k == 0) return FT_ERR_SHAPE;
   if (!aligned16(W) || !aligned16(xq) || !aligned16(y)) return FT_ERR_ALIGNMENT;
+  if (act == FT_Q8_0) {   // the Q8_1 layout of the same blocks, in the stream's pool
+    void* rp = nullptr;
+    const int64_t nblk = t * (k / 32);
+    const ft_status ps = pool_get(hs(stream), align256((size_t)nblk * 36), &rp);
+    if (ps != FT_OK) return ps;
+    const hipError_t e = ftk_launch_repack_q8_0(xq, nblk, rp, hs(stream));
+    if (e != hipSuccess) return FT_ERR_HIP;
+    xq = rp;
+    act = FT_Q8_1;
+  }
   MmvqArgs a;
   a.w = w;
   a.act = act;
@@ -477,6 +492,16 @@ ft_status ft_debug_block_dots(ft_type w, const void* W, int64_t n, int64_t k, ft
   if (n == 0 || t == 0 || k == 0) return FT_OK;
   if (!W || !xq || !partials) return FT_ERR_INVALID_ARG;
   if (!aligned16(W) || !aligned16(xq)) return FT_ERR_ALIGNMENT;
+  if (act == FT_Q8_0) {   // as the matvec: the Q8_1 layout of the same blocks
+    void* rp = nullptr;
+    const int64_t nblk = t * (k / 32);
+    const ft_status ps = pool_get(hs(stream), align256((size_t)nblk * 36), &rp);
+    if (ps != FT_OK) return ps;
+    const hipError_t e = ftk_launch_repack_q8_0(xq, nblk, rp, hs(stream));
+    if (e != hipSuccess) return FT_ERR_HIP;
+    xq = rp;
+    act = FT_Q8_1;
+  }
   return hip_status(ftk_launch_block_dots(w, W, n, k, act, xq, t, partials, hs(stream)));
 }
 

@@ -48,6 +48,10 @@ hipError_t ftk_launch_mmvq_mfma(const MmvqArgs& a, int64_t k, hipStream_t st);
 hipError_t ftk_launch_probe(int which, const void* buf, int64_t bytes, int64_t iters, uint32_t* out, hipStream_t st);
 hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
                                hipStream_t st);
+// Q8_0 activation blocks -> the Q8_1 layout (same d and codes), nblocks blocks
+hipError_t ftk_launch_repack_q8_0(const void* src, int64_t nblocks, void* dst, hipStream_t st);
+// dot4 matvec of Q4_K / Q5_K / Q6_K / MXFP4 x Q8_K (ft_mmvq_q8k.hip)
+hipError_t ftk_launch_mmvq_q8k(const MmvqArgs& a, int64_t k, hipStream_t st);
 // Q8_K rows [rows][k/256] -> FP8 halves for the FP4 MFMA, 512 bytes per superblock
 hipError_t ftk_launch_fp8_split(const void* xq, int64_t rows, int64_t k, void* out, hipStream_t st);
 hipError_t ftk_launch_dequant(int w, const void* blocks, int64_t rows, int64_t k, float* out,

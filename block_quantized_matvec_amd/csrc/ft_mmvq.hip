@@ -152,6 +152,7 @@ static int64_t units_of(int w, int64_t k) {
 
 hipError_t ftk_launch_mmvq(const MmvqArgs& a, int64_t k, hipStream_t st) {
   using namespace ftk;
+  if (a.act == FT_Q8_K) return ftk_launch_mmvq_q8k(a, k, st);
   const bool lng = units_of(a.w, k) > 128;
   const bool late = a.w == FT_Q2_K || a.w == FT_Q3_K || a.w == FT_Q4_1 || a.w == FT_Q5_0 || a.w == FT_Q5_1;
   const bool mfma = late || !lng ? a.t >= 5 : (a.w == FT_Q8_0 || a.w == FT_Q5_K ? a.t >= 3 : a.t >= 2);

@@ -1,10 +1,10 @@
-// ft_quant.hip -- activation quantizers (Q8_1, Q8_K), weight dequantization and
-// the integer-partials debug tap.
+// ft_quant.hip -- activation quantizers (Q8_1, Q8_0, Q8_K), weight dequantization
+// and the integer-partials debug tap.
 //
 // Quantizers: vllm.cpp PR #523 (What changed: Q8_0 / Q8_K activation quantizers)
 // and ds4 PR #656 (Summary: Q8 prequant of activations).  The arithmetic is
 // decided in fp32 so that the result is bit-identical on any IEEE device:
-// amax, d = amax/127 (stored as fp16 for Q8_1, fp32 for Q8_K), q = clamp(round
+// amax, d = amax/127 (stored as fp16 for Q8_1 and Q8_0, fp32 for Q8_K), q = clamp(round
 // half away from zero of x/d against the stored d, +-127), with the IEEE
 // correctly rounded division.
 // Dequantization: FreeToken PR #136 (Summary: Q4_0 dequantization) and the packed
@@ -39,6 +39,68 @@ quant_q8_1_kernel(const float* __restrict__ x, int64_t total_blocks, int64_t nb,
     for (int j = 0; j < 8; ++j) v[j] = xp[j];
   }
   q8_1_part(v, l4, xq + gb * 36);
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0: the Q8_1 arithmetic (fp16 d = amax/127, codes against the stored d) in
+// the 34-byte block without the sum field: fp16 d at byte 0, the 32 codes from
+// byte 2 (each lane's eight codes go out as four 16-bit stores).
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+quant_q8_0_kernel(const float* __restrict__ x, int64_t total_blocks, int64_t nb, int64_t ldx,
+                  uint8_t* __restrict__ xq) {
+  const int64_t gb = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int l4 = threadIdx.x & 3;
+  if (gb >= total_blocks) return;  // uniform over the block's four lanes
+  const int64_t r = gb / nb, b = gb % nb;
+  const float* xp = x + r * ldx + b * 32 + 8 * l4;
+  float v[8];
+  if constexpr (VEC) {
+    const float4 a = ((const float4*)xp)[0], c = ((const float4*)xp)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = xp[j];
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
+  a = fmaxf(a, xchg<1>(a));
+  a = fmaxf(a, xchg<2>(a));
+  uint32_t dh = f2h_bits(a / 127.0f);
+  const float d = h2f(dh);
+  uint8_t* ob = xq + gb * 34;
+  uint16_t* o = (uint16_t*)(ob + 2 + 8 * l4);
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const uint32_t lo = (uint32_t)(uint8_t)(int8_t)q8_code(v[j], d);
+    const uint32_t hi = (uint32_t)(uint8_t)(int8_t)q8_code(v[j + 1], d);
+    o[j >> 1] = (uint16_t)(lo | (hi << 8));
+  }
+  if (l4 == 0) *(uint16_t*)ob = (uint16_t)(d == 0.0f ? 0u : dh);
+}
+
+// Q8_0 activation blocks (34 bytes) -> the Q8_1 layout (36 bytes: d, s = fp16(d *
+// sum of codes), the same codes) that the matvec kernels read with aligned dword
+// loads; the dots use d and the codes only, so the result is the Q8_0 one.  One
+// thread per block.
+__global__ void __launch_bounds__(256)
+repack_q8_0_kernel(const uint8_t* __restrict__ src, int64_t nblocks, uint8_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nblocks) return;
+  const uint16_t* s = (const uint16_t*)(src + i * 34);   // 34 is even: 2-byte aligned
+  uint32_t* o = (uint32_t*)(dst + i * 36);
+  const uint32_t dh = s[0];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = (uint32_t)s[1 + 2 * j] | ((uint32_t)s[2 + 2 * j] << 16);
+    sum = dot4(w, 0x01010101u, sum);
+    o[1 + j] = w;
+  }
+  o[0] = dh | (f2h_bits(h2f(dh) * (float)sum) << 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -250,7 +312,13 @@ using namespace ftk;
 hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k, int64_t ldx, void* xq,
                                hipStream_t st) {
   const bool vec = ((uintptr_t)x & 15) == 0 && (ldx & 3) == 0;
-  if (act == FT_Q8_1) {
+  if (act == FT_Q8_0) {
+    const int64_t total = rows * (k / 32);
+    if (total == 0) return hipSuccess;
+    const dim3 grid((unsigned)((total + 63) / 64));
+    if (vec) hipLaunchKernelGGL(quant_q8_0_kernel<true>, grid, dim3(256), 0, st, x, total, k / 32, ldx, (uint8_t*)xq);
+    else hipLaunchKernelGGL(quant_q8_0_kernel<false>, grid, dim3(256), 0, st, x, total, k / 32, ldx, (uint8_t*)xq);
+  } else if (act == FT_Q8_1) {
     const int64_t total = rows * (k / 32);
     if (total == 0) return hipSuccess;
     const dim3 grid((unsigned)((total + 63) / 64));
@@ -263,6 +331,13 @@ hipError_t ftk_launch_quantize(int act, const float* x, int64_t rows, int64_t k,
     if (vec) hipLaunchKernelGGL(quant_q8_k_kernel<true>, grid, dim3(256), 0, st, x, total, k / 256, ldx, (uint8_t*)xq);
     else hipLaunchKernelGGL(quant_q8_k_kernel<false>, grid, dim3(256), 0, st, x, total, k / 256, ldx, (uint8_t*)xq);
   }
+  return hipGetLastError();
+}
+
+hipError_t ftk_launch_repack_q8_0(const void* src, int64_t nblocks, void* dst, hipStream_t st) {
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(repack_q8_0_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, st,
+                     (const uint8_t*)src, nblocks, (uint8_t*)dst);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ BLOCK = {  # name: (elements, bytes)
     "Q2_K": (256, 84), "Q3_K": (256, 110), "Q4_1": (32, 20), "Q5_0": (32, 22), "Q5_1": (32, 24),
 }
 WEIGHT_FORMATS = ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K", "Q4_1", "Q5_0", "Q5_1")
-ACT_FORMATS = ("Q8_1", "Q8_K")
+ACT_FORMATS = ("Q8_1", "Q8_K", "Q8_0")   # Q8_0: also a weight format, same layout
 
 
 def rng(*seed) -> np.random.Generator:

@@ -54,7 +54,7 @@ typedef void* ft_stream_t; /* a hipStream_t */
 /* block formats */
 typedef enum {
   FT_Q4_0 = 0,  /* 32 weights: fp16 d, 16 B nibbles; w = d*(n-8)            18 B */
-  FT_Q8_0 = 1,  /* 32 weights: fp16 d, 32 int8; w = d*q                      34 B */
+  FT_Q8_0 = 1,  /* 32 weights (or activations): fp16 d, 32 int8; w = d*q     34 B */
   FT_Q4_K = 2,  /* 256: fp16 d, fp16 dmin, 12 B of 6-bit scales/mins, 128 B nibbles;
                    w = d*sc_j*n - dmin*m_j per 32-element sub-block j       144 B */
   FT_Q5_K = 3,  /* 256: as Q4_K plus 32 B of fifth bits                     176 B */
@@ -106,9 +106,10 @@ const char* ft_version(void);
 
 /* Activation quantizer [P3 What changed: Q8_0/Q8_K quantizers; P4: Q8 prequant].
    x: [rows][k] fp32 with row stride ldx (elements) >= k.  xq: [rows][k/blk] blocks
-   of `act` (FT_Q8_1 or FT_Q8_K), written in full.
+   of `act` (FT_Q8_1, FT_Q8_0 or FT_Q8_K), written in full.
    Q8_1 per 32-block: d = fp16(amax/127); q = clamp(round_half_away(x/d), -127, 127)
    against the stored d (q = 0 when d is 0); s = fp16(d * sum q).
+   Q8_0 per 32-block: d and q as Q8_1, no s (fp16 d at byte 0, codes from byte 2).
    Q8_K per 256-block: d = amax/127 in fp32; q as above; bsums[g] = sum of q over
    elements 16g..16g+15. */
 ft_status ft_quantize_act(ft_type act, const float* x, int64_t rows, int64_t k, int64_t ldx,
@@ -127,9 +128,14 @@ ft_status ft_dequant(ft_type w, const void* blocks, int64_t rows, int64_t k, flo
    y: [t][ldy] fp32, ldy >= n, y[i][r] = sum_k w[r][k] * xhat[i][k], computed as exact
    integer dots per block followed by an fp32 scale combine.  Any t >= 0 (t = 0 is a
    no-op); batches beyond 8 tokens are processed 8 at a time.  Supported (w, act):
-   every weight type x FT_Q8_1.  From 2-5 tokens on (the threshold depends on the
-   format and on k) every format runs on the int8 matrix cores when k is a multiple
-   of 256 (512 for MXFP4); the result is the same integer dots either way. */
+   every weight type x FT_Q8_1 and x FT_Q8_0; (Q4_K, Q5_K, Q6_K, MXFP4) x FT_Q8_K
+   [P3 What changed: the non-grouped op with Q8_0 / Q8_K activations].  With
+   FT_Q8_1 or FT_Q8_0, from 2-5 tokens on (the threshold depends on the format and
+   on k) every format runs on the int8 matrix cores when k is a multiple of 256 (512
+   for MXFP4); the result is the same integer dots either way.  FT_Q8_0 activations
+   are first copied into the Q8_1 block layout (same d and codes) in the stream's
+   scratch pool, so under graph capture the pool must hold t*(k/32)*36 bytes
+   (FT_ERR_NO_SCRATCH otherwise).  FT_Q8_K runs on the dot4 kernels at every t. */
 ft_status ft_mul_mat_vec_q(ft_type w, const void* W, int64_t n, int64_t k,
                            ft_type act, const void* xq, int64_t t,
                            float* y, int64_t ldy, ft_stream_t stream);
@@ -219,7 +225,8 @@ ft_status ft_grouped_gemm_q(ft_type w, const void* W, int64_t n_expert, int64_t 
    and 32 otherwise: the sum over each sub-block of the weight's integer code (n-8 for
    Q4_0, q for Q8_0, the 4/5-bit n for Q4_K/Q5_K, q6-32 for Q6_K, twice the E2M1 value
    for MXFP4, the 2-bit q for Q2_K, the 3-bit q-4 for Q3_K) times the activation's
-   int8 code.  Computed with the unpack and v_dot4 core of the dot4 matvec kernels
+   int8 code (act: FT_Q8_1, FT_Q8_0 -- through its Q8_1 layout, as the matvec --
+   or FT_Q8_K).  Computed with the unpack and v_dot4 core of the dot4 matvec kernels
    (one and two tokens); the int8-MFMA matvec, the grouped GEMM and the FP4-MFMA
    MoE kernels form the same integers on the matrix cores and are checked for
    them through exactly representable outputs instead. */

@@ -22,7 +22,7 @@ SRC_PATH = os.path.join(_DIR, "oracle.c")
 FMT = {"Q4_0": 0, "Q8_0": 1, "Q4_K": 2, "Q5_K": 3, "Q6_K": 4, "MXFP4": 5, "Q8_1": 6, "Q8_K": 7,
        "Q2_K": 8, "Q3_K": 9, "Q4_1": 10, "Q5_0": 11, "Q5_1": 12}
 WEIGHT_FORMATS = ("Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K", "Q4_1", "Q5_0", "Q5_1")
-ACT_FORMATS = ("Q8_1", "Q8_K")
+ACT_FORMATS = ("Q8_1", "Q8_K", "Q8_0")
 
 # -O3 with the x86-64-v3 level (AVX2) rather than -march=native: the library is
 # built in one place and may run on another host's CPU.  No contraction and no

@@ -306,14 +306,13 @@ static void wscale(int fmt, const uint8_t* b, int e, double* scale, double* mn) 
   }
 }
 
-/* activation blocks: int8 code and fp64 scale of element e */
-/* both activation formats keep their int8 codes from byte 4 on */
+/* activation blocks: int8 code and fp64 scale of element e.  Q8_1 and Q8_K keep
+   their codes from byte 4 on, Q8_0 (fp16 d, no sum field) from byte 2. */
 static int acode(int afmt, const uint8_t* b, int e) {
-  (void)afmt;
-  return (int)(int8_t)b[4 + e];
+  return (int)(int8_t)b[(afmt == OR_Q8_0 ? 2 : 4) + e];
 }
 static double ascale(int afmt, const uint8_t* b) {
-  if (afmt == OR_Q8_1) return f16d(b);
+  if (afmt == OR_Q8_1 || afmt == OR_Q8_0) return f16d(b);
   float d;
   memcpy(&d, b, 4);
   return (double)d;
@@ -329,7 +328,8 @@ double or_elem(int fmt, const uint8_t* b, int e) {
 }
 
 static int is_weight(int f) { return (f >= OR_Q4_0 && f <= OR_MXFP4) || (f >= OR_Q2_K && f <= OR_Q5_1); }
-static int is_act(int f) { return f == OR_Q8_1 || f == OR_Q8_K; }
+/* Q8_0 is both: a weight format and, in the same layout, an activation format */
+static int is_act(int f) { return f == OR_Q8_1 || f == OR_Q8_K || f == OR_Q8_0; }
 
 void or_dequant_f32(int fmt, const uint8_t* blocks, int64_t rows, int64_t k, float* out) {
   int be = or_block_elems(fmt), bb = or_block_bytes(fmt);
@@ -372,6 +372,29 @@ static void quant_q8_1_block(const float* x, uint8_t* out) {
   wr16(out + 2, or_f32_to_f16(d * (float)sum));
 }
 
+/* Q8_0 of one 32-block: the Q8_1 scale and codes, d = fp16(amax/127) and q =
+   clamp(round(x/d)) against the stored d, in a block without the sum field (d at
+   byte 0, codes from byte 2). */
+static void quant_q8_0_block(const float* x, uint8_t* out) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; i++) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  uint16_t dh = or_f32_to_f16(amax / 127.0f);
+  float d = or_f16_to_f32(dh);
+  for (int i = 0; i < 32; i++) {
+    int q = 0;
+    if (d != 0.0f) {
+      float v = roundf(x[i] / d);
+      q = v > 127.0f ? 127 : (v < -127.0f ? -127 : (int)v);
+    }
+    out[2 + i] = (uint8_t)(int8_t)q;
+  }
+  if (d == 0.0f) dh = 0;
+  wr16(out, dh);
+}
+
 /* Q8_K of one 256-block: d = amax/127 in fp32 (kept, positive);
    q = clamp(round(x/d)); bsums[g] = sum of q over elements 16g..16g+15. */
 static void quant_q8_k_block(const float* x, uint8_t* out) {
@@ -408,6 +431,7 @@ void or_quantize(int afmt, const float* x, int64_t rows, int64_t k, int64_t ldx,
       const float* xb = x + r * ldx + i * be;
       uint8_t* ob = out + (r * nb + i) * bb;
       if (afmt == OR_Q8_1) quant_q8_1_block(xb, ob);
+      else if (afmt == OR_Q8_0) quant_q8_0_block(xb, ob);
       else quant_q8_k_block(xb, ob);
     }
 }

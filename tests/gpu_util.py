@@ -37,3 +37,23 @@ def check_fp32(y, r, what="", rel=REL, nmse=NMSE):
 
 def log(msg):
     print(msg, flush=True)
+
+
+def abs_terms(wfmt, W, n, k, afmt, xq, t):
+    """[t][n] sum over k of |w * xhat| (fp64, from the oracle's exact values): the
+    scale of the rounding an fp32 sum of the products may carry."""
+    import oracle
+    w = oracle.dequant(wfmt, W, n, k).astype(np.float64)
+    x = oracle.dequant(afmt, xq, t, k).astype(np.float64)
+    return np.abs(x) @ np.abs(w).T
+
+
+def check_fp32_small(y, r, terms, what="", rel=REL):
+    """The per-output form of the fp32 bar for a compared set too small for a
+    normwise maximum to mean anything (a single output is its own maximum, and
+    heavy cancellation leaves it far below its terms): |y - r| <= rel * sum|terms|."""
+    y = np.asarray(y, np.float64)
+    r = np.asarray(r, np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    bad = np.abs(y - r) > rel * np.asarray(terms)
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond {rel} of their term sums"

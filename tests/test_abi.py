@@ -18,7 +18,7 @@ from block_quantized_matvec_amd import ft
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 W = ["Q4_0", "Q8_0", "Q4_K", "Q5_K", "Q6_K", "MXFP4", "Q2_K", "Q3_K", "Q4_1", "Q5_0", "Q5_1"]
-A = ["Q8_1", "Q8_K"]
+A = ["Q8_1", "Q8_K", "Q8_0"]
 ST = {v: k for k, v in ft.STATUS.items()}
 
 
@@ -47,7 +47,8 @@ def test_block_sizes():
 
 
 def test_capability_table():
-    expect_mmvq = {(w, "Q8_1") for w in W}
+    expect_mmvq = ({(w, "Q8_1") for w in W} | {(w, "Q8_0") for w in W} |
+                   {(w, "Q8_K") for w in ("Q4_K", "Q5_K", "Q6_K", "MXFP4")})
     expect_moe = {("Q4_K", "Q8_1"), ("MXFP4", "Q8_K"), ("Q4_K", "Q8_K"), ("Q5_K", "Q8_K"), ("Q6_K", "Q8_K")}
     expect_grp = {("Q4_K", "Q8_K"), ("Q5_K", "Q8_K"), ("Q6_K", "Q8_K"), ("MXFP4", "Q8_K")}
     for w in W:
@@ -58,6 +59,7 @@ def test_capability_table():
             assert ft.supported("block_dots", w, a)
         assert ft.supported("dequant", w, "Q8_1")
     assert ft.supported("quantize", "Q4_0", "Q8_1") and ft.supported("quantize", "Q4_0", "Q8_K")
+    assert ft.supported("quantize", "Q4_0", "Q8_0")
     assert not ft.supported("quantize", "Q4_0", "Q4_0")
     assert not ft.supported("dequant", "Q8_1", "Q8_1")
 

@@ -117,12 +117,13 @@ def test_extreme_codes(wfmt):
     for afmt in synth.ACT_FORMATS:
         abe, abb = synth.BLOCK[afmt]
         xq = np.zeros((1, k // abe * abb), np.uint8).reshape(-1, abb)
-        if afmt == "Q8_1":
+        if afmt in ("Q8_1", "Q8_0"):
             xq[:, 0:2] = np.array([1.0], np.float16).view(np.uint8)
         else:
             xq[:, 0:4] = np.array([1.0], np.float32).view(np.uint8)
         codes = np.where(np.arange(abe) % 2 == 0, -128, 127).astype(np.int8)
-        xq[:, 4:4 + abe] = codes.view(np.uint8)
+        c0 = 2 if afmt == "Q8_0" else 4    # Q8_0 has no sum field: codes from byte 2
+        xq[:, c0:c0 + abe] = codes.view(np.uint8)
         got = oracle.block_dots(wfmt, W, 1, k, afmt, xq, 1)
         ref = brute.block_dots(wfmt, W, 1, k, afmt, xq, 1, oracle.sub_elems(wfmt))
         assert np.array_equal(got.astype(np.int64), ref)

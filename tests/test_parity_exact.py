@@ -106,6 +106,9 @@ def dyadic_act(afmt, t, k, g, qmax):
             s = (d * q[i].astype(np.float64).sum(axis=1)).astype(np.float16)
             out[i, :, 2:4] = s.view(np.uint8).reshape(nb, 2)
             out[i, :, 4:36] = q[i].view(np.uint8)
+        elif afmt == "Q8_0":
+            out[i, :, 0:2] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+            out[i, :, 2:34] = q[i].view(np.uint8)
         else:
             out[i, :, 0:4] = np.frombuffer(np.float32(d).tobytes(), np.uint8)
             out[i, :, 4:260] = q[i].view(np.uint8)
@@ -171,6 +174,24 @@ def test_mmvq_exact(w, rows, t):
     assert_exact_bound(w, "Q8_1", q)
     y = host(ft.mul_mat_vec_q(w, dev(W), n, k, "Q8_1", dev(xq), t))
     ref = oracle.matvec(w, W, n, k, "Q8_1", xq, t)
+    bad = np.argwhere(y != ref)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[0]}: {y[tuple(bad[0])]!r} vs {ref[tuple(bad[0])]!r}"
+
+
+@pytest.mark.parametrize("w,a", [(w, "Q8_0") for w in ("Q4_0", "Q8_0", "Q4_K", "Q6_K", "MXFP4", "Q3_K")] +
+                         [(w, "Q8_K") for w in ("Q4_K", "Q5_K", "Q6_K", "MXFP4")])
+@pytest.mark.parametrize("t", [1, 2, 5, 8])
+def test_mmvq_exact_other_activations(w, a, t):
+    """Q8_0 activations (through their Q8_1 layout, dot4 and MFMA) and Q8_K
+    activations (dot4 at every t), long rows."""
+    n, k = 70, _long_k(w)
+    log(f"mmvq exact {w} x {a} n={n} k={k} t={t}")
+    g = synth.rng(904, MMVQ_FORMATS.index(w), a == "Q8_K", t)
+    W = dyadic_weights(w, n, k, g)
+    xq, q = dyadic_act(a, t, k, g, qmax=4)
+    assert_exact_bound(w, a, q)
+    y = host(ft.mul_mat_vec_q(w, dev(W), n, k, a, dev(xq), t))
+    ref = oracle.matvec(w, W, n, k, a, xq, t)
     bad = np.argwhere(y != ref)
     assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[0]}: {y[tuple(bad[0])]!r} vs {ref[tuple(bad[0])]!r}"
 

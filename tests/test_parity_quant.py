@@ -15,7 +15,7 @@ def _gpu():
     need_gpu()
 
 
-@pytest.mark.parametrize("act", ["Q8_1", "Q8_K"])
+@pytest.mark.parametrize("act", ["Q8_1", "Q8_K", "Q8_0"])
 @pytest.mark.parametrize("rows,k", [(1, 256), (3, 2048), (17, 4096), (5, 14336), (512, 4096)])
 def test_quantize_bit_exact(act, rows, k):
     log(f"quantize {act} rows={rows} k={k}")
@@ -25,7 +25,7 @@ def test_quantize_bit_exact(act, rows, k):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("act", ["Q8_1", "Q8_K"])
+@pytest.mark.parametrize("act", ["Q8_1", "Q8_K", "Q8_0"])
 @pytest.mark.parametrize("pad", [1, 3, 4])
 def test_quantize_strided_rows(act, pad):
     """rows k + pad floats apart (ldx = k + pad): a row stride that is not a
