@@ -466,10 +466,11 @@ def moe_results(args, np, torch, ft, synth, c, tokens, route=0):
         ft.scratch_reserve(ft.moe_scratch_bytes(fmt, act, E, H, I, t, topk))
 
         def steps():
+            # the layer routes from the step's logits itself (ids / w come back as outputs)
             for i in range(G):
                 wgb, wub, wdb = banks[i % layers]
-                ft.moe_route(logits[i], topk, ids=ids[i], w=w[i])
-                ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, ids[i], w[i], out=y, route=route)
+                ft.moe_q_vec(fmt, wgb, wub, wdb, E, H, I, act, x, None, None, out=y, route=route, logits=logits[i],
+                             topk=topk, ids_out=ids[i], w_out=w[i])
 
         gs = _graph(torch, steps)
         sec = _time_graph(torch, gs, max(1, args.steps // G)) / G
@@ -485,7 +486,8 @@ def moe_results(args, np, torch, ft, synth, c, tokens, route=0):
         del gs, x, logits, ids, w, y
     del banks
     return {"workload": f"routed MoE layer {fmt} x {act}: hidden {H}, {E} experts of {I}, top-{topk}; step = "
-                        "route + layer (quantize, gate/up+SwiGLU, quantize h, down, combine), HIP graph",
+                        "one ft_moe_q_vec call from the router logits (route, quantize, gate/up+SwiGLU, quantize h, "
+                        "down, combine), HIP graph",
             "metric": "routed-MoE layer tokens/s", "dtype": MOE_DTYPE, "layer_banks": layers,
             "per_tokens": results}
 

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["ft_mmvq_kq.hip", "ft_mmvq_kq_b.hip", "ft_mmvq_kq_c.hip", "ft_mmvq_kq_d.hip", "ft_mmvq_q8k.hip", "ft_mmvq.hip",
-           "ft_api.cpp", "ft_quant.hip", "ft_mmvq_mfma.hip", "ft_moe.hip", "ft_moe_fp4.hip", "ft_grouped.hip",
+           "ft_api.cpp", "ft_quant.hip", "ft_mmvq_mfma.hip", "ft_moe.hip", "ft_moe_fused.hip", "ft_moe_fp4.hip", "ft_grouped.hip",
            "ft_probe.hip"]
 
 CFLAGS = [

@@ -69,7 +69,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // scratch layout of ft_moe_q_vec
 struct MoeScratch {
-  size_t xq, h, hq, d, total;
+  size_t xq, h, hq, d, ids, w, tab, total;
 };
 MoeScratch moe_layout(int w, int act, int64_t hidden, int64_t inter, int64_t t, int topk) {
   (void)w;
@@ -83,6 +83,12 @@ MoeScratch moe_layout(int w, int act, int64_t hidden, int64_t inter, int64_t t, 
   off += align256((size_t)t * topk * row_bytes_of(act, inter));
   s.d = off;
   off += align256((size_t)t * topk * hidden * sizeof(float));
+  s.ids = off;   // the routing when the layer routes from logits
+  off += align256((size_t)t * topk * 4);
+  s.w = off;
+  off += align256((size_t)t * topk * 4);
+  s.tab = off;   // the fused Q4_K layer's routing table (its first launch -> its second)
+  off += align256(ftk_moe_fused_table_bytes());
   s.total = off;
   return s;
 }
@@ -277,8 +283,10 @@ ft_status moe_check(ft_type w, const void* w_gate, const void* w_up, const void*
   *tiles = o.route == 2 || (o.route == 0 && (!direct_ok || (tile_ok && t > dmax)));
   // the sort behind the tiles holds one counter per expert in LDS
   if (*tiles && n_expert > 8192) return FT_ERR_SHAPE;
+  if (o.logits && n_expert > 1024) return FT_ERR_SHAPE;   // the router's limit
   if (t == 0) return FT_OK;
-  if (!w_gate || !w_up || !w_down || !x || !expert_ids || !expert_w || !y) return FT_ERR_INVALID_ARG;
+  if (!w_gate || !w_up || !w_down || !x || !y) return FT_ERR_INVALID_ARG;
+  if (!o.logits && (!expert_ids || !expert_w)) return FT_ERR_INVALID_ARG;
   if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(x) || !aligned16(y))
     return FT_ERR_ALIGNMENT;
   if ((o.tap_g && !aligned16(o.tap_g)) || (o.tap_u && !aligned16(o.tap_u)) || (o.tap_h && !aligned16(o.tap_h)) ||
@@ -319,9 +327,28 @@ ft_status moe_run(ft_type w, const void* w_gate, const void* w_up, const void* w
   a.hq_tap = o.tap_hq;
   a.in_hq = o.in_hq;
   a.dpair = o.tap_down ? o.tap_down : (float*)(b + L.d);
+  a.d_tap = o.tap_down;
+  a.h_tap = o.tap_h;
   a.y = y;
 
   hipError_t e = hipSuccess;
+  a.logits = nullptr;
+  a.ids_out = o.ids_out;
+  a.w_out = o.w_out;
+  const bool fused = !tiles && ftk_moe_fused_ok(w, act, hidden, inter, topk);
+  if (o.logits && fused && ftk_moe_fused_routes(n_expert)) {
+    a.logits = o.logits;   // the fused layer routes itself
+    a.ids = nullptr;
+    a.ew = nullptr;
+  } else if (o.logits) {   // route first, into the caller's outputs or scratch
+    int32_t* ri = o.ids_out ? o.ids_out : (int32_t*)(b + L.ids);
+    float* rw = o.w_out ? o.w_out : (float*)(b + L.w);
+    e = ftk_launch_route(o.logits, t, n_expert, topk, ri, rw, st);
+    if (e != hipSuccess) return FT_ERR_HIP;
+    a.ids = ri;
+    a.ew = rw;
+    expert_ids = ri;
+  }
   if (tiles) {
     e = ftk_launch_quantize(act, x, t, hidden, hidden, (void*)a.xq, st);
     uint8_t* sb = b + L.total;
@@ -370,8 +397,10 @@ ft_status moe_run(ft_type w, const void* w_gate, const void* w_up, const void* w
     if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
     return hip_status(e);
   }
-  // direct route: gate/up (quantizes x itself), down (quantizes each expert's h
-  // rows itself, or reads in_hq), slot-order combine
+  // direct route, Q4_K x Q8_1 shapes that fit: the whole layer in one launch
+  if (fused) return hip_status(ftk_launch_moe_fused(a, b + L.tab, st));
+  // otherwise gate/up (quantizes x itself), down (quantizes each expert's h rows
+  // itself, or reads in_hq), slot-order combine
   e = ftk_launch_moe_gate_up(a, st);
   if (e == hipSuccess) e = ftk_launch_moe_down(a, st);
   if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);

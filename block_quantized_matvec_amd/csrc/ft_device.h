@@ -643,6 +643,111 @@ __device__ __forceinline__ void q8_k_part(const float (&v)[16], int l16, uint8_t
 }
 
 // ---------------------------------------------------------------------------
+// router (ds4 PR #656 Summary; the routing semantics as read from the pages):
+// one wave per token.  Top-k with ties going to the lower expert index, then a
+// softmax over the selected logits in slot order.
+//  * logits become order-preserving unsigned keys (-0 first folded into +0, so
+//    that they tie as they compare equal);
+//  * the k-th largest key T is found bit by bit, from the top: the largest T with
+//    at least k keys >= T (each step is MAXE ballots and population counts);
+//  * the keys above T and, in expert order, the first k - #(> T) keys equal to T
+//    are the selection; its k entries go to LDS in expert order, and each of the
+//    first k lanes ranks one entry against the others (value, then index).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t route_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float route_val(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One token's routing by one wave, in two calls so that the logits can be in
+// flight while the wave does other work: route_load reads them (lane l holds
+// experts l, l + 64, ...), route_select picks the winners.  s_key / s_idx / s_ex:
+// 8 words each of LDS for this wave; the k winners go to ids[0..k) / w[0..k) in
+// slot order (LDS or global).
+template <int MAXE>
+__device__ __forceinline__ void route_load(const float* __restrict__ l, int n_expert, int lane, float (&raw)[MAXE]) {
+#pragma unroll
+  for (int i = 0; i < MAXE; ++i) {
+    const int e = lane + 64 * i;
+    raw[i] = e < n_expert ? l[e] : 0.0f;
+  }
+}
+template <int MAXE>   // logits per lane (n_expert <= 64 * MAXE)
+__device__ __forceinline__ void route_select(const float (&raw)[MAXE], int n_expert, int topk, int lane,
+                                             uint32_t* s_key, int* s_idx, float* s_ex, int32_t* ids, float* w) {
+  uint32_t key[MAXE];
+#pragma unroll
+  for (int i = 0; i < MAXE; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < n_expert ? route_key(raw[i]) : 0u;   // 0 is below every logit's key
+  }
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < MAXE; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    if (cnt >= topk) T = c;
+  }
+  int ngt = 0;
+#pragma unroll
+  for (int i = 0; i < MAXE; ++i) ngt += __popcll(__ballot(key[i] > T));
+  const int need = topk - ngt;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int eq_before = 0, sel_before = 0;
+#pragma unroll
+  for (int i = 0; i < MAXE; ++i) {
+    const bool eq = key[i] == T;
+    const uint64_t beq = __ballot(eq);
+    const bool sel = key[i] > T || (eq && eq_before + __popcll(beq & below) < need);
+    const uint64_t bsel = __ballot(sel);
+    if (sel) {
+      const int p = sel_before + __popcll(bsel & below);
+      s_key[p] = key[i];
+      s_idx[p] = lane + 64 * i;
+    }
+    eq_before += __popcll(beq);
+    sel_before += __popcll(bsel);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  int rank = 0, mi = 0;
+  float ex = 0.0f;
+  if (lane < topk) {
+    const uint32_t mk = s_key[lane];
+    mi = s_idx[lane];
+    uint32_t top = mk;
+    for (int q = 0; q < topk; ++q) {
+      const uint32_t kq = s_key[q];
+      rank += kq > mk || (kq == mk && s_idx[q] < mi);
+      top = kq > top ? kq : top;
+    }
+    ex = expf(route_val(mk) - route_val(top));
+    s_ex[rank] = ex;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  if (lane < topk) {
+    float den = 0.0f;
+    for (int q = 0; q < topk; ++q) den += s_ex[q];
+    ids[rank] = mi;
+    w[rank] = ex / den;
+  }
+}
+template <int MAXE>
+__device__ __forceinline__ void route_token(const float* __restrict__ l, int n_expert, int topk, int lane,
+                                            uint32_t* s_key, int* s_idx, float* s_ex, int32_t* ids, float* w) {
+  float raw[MAXE];
+  route_load<MAXE>(l, n_expert, lane, raw);
+  route_select<MAXE>(raw, n_expert, topk, lane, s_key, s_idx, s_ex, ids, w);
+}
+
+// ---------------------------------------------------------------------------
 // routed-MoE helpers (direct route)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int clamp_id(int e, int64_t n_expert) {

@@ -73,6 +73,9 @@ struct MoeArgs {
   int topk;
   const int32_t* ids;
   const float* ew;
+  const float* logits;   // nullable: the fused layer routes from these itself (ids / ew unused)
+  int32_t* ids_out;      // nullable: that routing
+  float* w_out;
   const float* x;      // [t][hidden] fp32 (the direct route quantizes it in its gate/up prologue)
   const void* xq;      // quantized x [t][hidden/blk_a] (sorted-tile route)
   float* h;            // [t*topk][inter]
@@ -82,8 +85,17 @@ struct MoeArgs {
   void* hq_tap;        // nullable: the direct route writes quantized h here
   const void* in_hq;   // nullable: the direct route's down stage reads these blocks instead
   float* dpair;        // [t*topk][hidden] per-pair down projections
+  float* d_tap;        // nullable: the caller's tap for dpair (the fused layer writes no dpair otherwise)
+  float* h_tap;        // nullable: the caller's tap for h (the fused layer writes no h otherwise)
   float* y;            // [t][hidden]
 };
+// the whole Q4_K x Q8_1 layer in two launches per 4-token chunk (ft_moe_fused.hip):
+// shapes it takes, and the launch; table: ftk_moe_fused_table_bytes() of scratch
+// the first launch hands the routing to the second in
+size_t ftk_moe_fused_table_bytes();
+bool ftk_moe_fused_ok(int w, int act, int64_t hidden, int64_t inter, int topk);
+bool ftk_moe_fused_routes(int64_t n_expert);   // the fused layer can route this many experts itself
+hipError_t ftk_launch_moe_fused(const MoeArgs& a, void* table, hipStream_t st);
 hipError_t ftk_launch_moe_gate_up(const MoeArgs& a, hipStream_t st);
 hipError_t ftk_launch_moe_down(const MoeArgs& a, hipStream_t st);
 // MXFP4 x Q8_K direct-route stages on the FP4 MFMA (hidden, inter multiples of 256)

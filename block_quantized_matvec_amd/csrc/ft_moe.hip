@@ -32,24 +32,8 @@ namespace ftk {
 constexpr int MOE_THREADS = 256;
 
 // ---------------------------------------------------------------------------
-// router: one wave per token.  Top-k with ties going to the lower expert index,
-// then a softmax over the selected logits in slot order.
-//  * logits become order-preserving unsigned keys (-0 first folded into +0, so
-//    that they tie as they compare equal);
-//  * the k-th largest key T is found bit by bit, from the top: the largest T with
-//    at least k keys >= T (each step is MAXE ballots and population counts);
-//  * the keys above T and, in expert order, the first k - #(> T) keys equal to T
-//    are the selection; its k entries go to LDS in expert order, and each of the
-//    first k lanes ranks one entry against the others (value, then index).
+// router: one wave per token (route_token, ft_device.h)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t route_key(float f) {
-  const uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float route_val(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
 template <int MAXE>   // logits per lane (n_expert <= 64 * MAXE)
 __global__ void __launch_bounds__(256)
 route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk, int32_t* __restrict__ ids,
@@ -60,67 +44,8 @@ route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
   if (tok >= t) return;
-  const float* l = logits + tok * n_expert;
-  uint32_t key[MAXE];
-#pragma unroll
-  for (int i = 0; i < MAXE; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < n_expert ? route_key(l[e]) : 0u;   // 0 is below every logit's key
-  }
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = T | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < MAXE; ++i) cnt += __popcll(__ballot(key[i] >= c));
-    if (cnt >= topk) T = c;
-  }
-  int ngt = 0;
-#pragma unroll
-  for (int i = 0; i < MAXE; ++i) ngt += __popcll(__ballot(key[i] > T));
-  const int need = topk - ngt;
-  const uint64_t below = (1ull << lane) - 1ull;
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int i = 0; i < MAXE; ++i) {
-    const bool eq = key[i] == T;
-    const uint64_t beq = __ballot(eq);
-    const bool sel = key[i] > T || (eq && eq_before + __popcll(beq & below) < need);
-    const uint64_t bsel = __ballot(sel);
-    if (sel) {
-      const int p = sel_before + __popcll(bsel & below);
-      s_key[wave][p] = key[i];
-      s_idx[wave][p] = lane + 64 * i;
-    }
-    eq_before += __popcll(beq);
-    sel_before += __popcll(bsel);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  int rank = 0, mi = 0;
-  float ex = 0.0f;
-  if (lane < topk) {
-    const uint32_t mk = s_key[wave][lane];
-    mi = s_idx[wave][lane];
-    uint32_t top = mk;
-    for (int q = 0; q < topk; ++q) {
-      const uint32_t kq = s_key[wave][q];
-      rank += kq > mk || (kq == mk && s_idx[wave][q] < mi);
-      top = kq > top ? kq : top;
-    }
-    ex = expf(route_val(mk) - route_val(top));
-    s_ex[wave][rank] = ex;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  if (lane < topk) {
-    float den = 0.0f;
-    for (int q = 0; q < topk; ++q) den += s_ex[wave][q];
-    ids[tok * topk + rank] = mi;
-    w[tok * topk + rank] = ex / den;
-  }
+  route_token<MAXE>(logits + tok * n_expert, n_expert, topk, lane, s_key[wave], s_idx[wave], s_ex[wave],
+                    ids + tok * topk, w + tok * topk);
 }
 
 // ---------------------------------------------------------------------------

@@ -31,7 +31,8 @@ class FtError(RuntimeError):
 class _MoeOpts(ctypes.Structure):
     _fields_ = [("route", ctypes.c_int), ("direct_max_t", ctypes.c_int),
                 ("tap_g", ctypes.c_void_p), ("tap_u", ctypes.c_void_p), ("tap_h", ctypes.c_void_p),
-                ("tap_hq", ctypes.c_void_p), ("tap_down", ctypes.c_void_p), ("in_hq", ctypes.c_void_p)]
+                ("tap_hq", ctypes.c_void_p), ("tap_down", ctypes.c_void_p), ("in_hq", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("ids_out", ctypes.c_void_p), ("w_out", ctypes.c_void_p)]
 
 
 EXPORTS = {
@@ -195,17 +196,20 @@ def moe_sort(ids: torch.Tensor, n_expert: int, stream=None):
 
 
 def _moe(entry: str, w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: int, act: str,
-         x: torch.Tensor, ids: torch.Tensor, expert_w: torch.Tensor, out, route: int, taps, in_hq,
-         direct_max_t: int, stream) -> torch.Tensor:
+         x: torch.Tensor, ids, expert_w, out, route: int, taps, in_hq, direct_max_t: int, stream,
+         logits=None, topk=None, ids_out=None, w_out=None) -> torch.Tensor:
     for nm, tt in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down), ("x", x), ("ids", ids),
-                   ("expert_w", expert_w)):
-        _dev(tt, nm)
+                   ("expert_w", expert_w), ("logits", logits), ("ids_out", ids_out), ("w_out", w_out)):
+        if tt is not None:
+            _dev(tt, nm)
     t = x.shape[0]
-    topk = ids.shape[1]
+    if topk is None:
+        topk = ids.shape[1]
     if out is None:
         out = torch.empty((t, hidden), dtype=torch.float32, device=x.device)
     taps = taps or {}
-    opts = _MoeOpts(route, direct_max_t, *(_ptr(taps.get(k)) for k in ("g", "u", "h", "hq", "down")), _ptr(in_hq))
+    opts = _MoeOpts(route, direct_max_t, *(_ptr(taps.get(k)) for k in ("g", "u", "h", "hq", "down")), _ptr(in_hq),
+                    _ptr(logits), _ptr(ids_out), _ptr(w_out))
     _check(getattr(lib(), entry)(TYPES[w], _ptr(w_gate), _ptr(w_up), _ptr(w_down), n_expert, hidden, inter,
                                  TYPES[act], _ptr(x), t, _ptr(ids), _ptr(expert_w), topk, _ptr(out),
                                  ctypes.byref(opts), _stream(stream)), entry)
@@ -213,12 +217,15 @@ def _moe(entry: str, w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, i
 
 
 def moe_q_vec(w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: int, act: str,
-              x: torch.Tensor, ids: torch.Tensor, expert_w: torch.Tensor, out: torch.Tensor | None = None,
+              x: torch.Tensor, ids, expert_w, out: torch.Tensor | None = None,
               route: int = 0, taps: dict | None = None, in_hq: torch.Tensor | None = None,
-              direct_max_t: int = 0, stream=None) -> torch.Tensor:
-    """taps: optional dict of preallocated device tensors g, u, h, hq, down."""
+              direct_max_t: int = 0, stream=None, logits=None, topk=None, ids_out=None,
+              w_out=None) -> torch.Tensor:
+    """taps: optional dict of preallocated device tensors g, u, h, hq, down.  With
+    logits ([t][n_expert]) the layer routes itself (ids / expert_w may be None;
+    topk is then required) and ids_out / w_out receive the routing."""
     return _moe("ft_moe_q_vec", w, w_gate, w_up, w_down, n_expert, hidden, inter, act, x, ids, expert_w, out,
-                route, taps, in_hq, direct_max_t, stream)
+                route, taps, in_hq, direct_max_t, stream, logits, topk, ids_out, w_out)
 
 
 def moe_q_vec_noalloc(w: str, w_gate, w_up, w_down, n_expert: int, hidden: int, inter: int, act: str,

@@ -168,6 +168,11 @@ typedef struct {
   void* tap_hq;       /* nullable [t*topk][inter/blk_a] blocks: quantized h */
   float* tap_down;    /* nullable [t*topk][hidden] fp32: per-pair down projections */
   const void* in_hq;  /* nullable: use these quantized h blocks for the down stage */
+  const float* logits;/* nullable [t][n_expert] router logits (n_expert <= 1024): the layer
+                         routes each token itself, as ft_moe_route, and expert_ids /
+                         expert_w are not read (they may be NULL) */
+  int32_t* ids_out;   /* nullable [t][topk]: receives that routing's ids ... */
+  float* w_out;       /* nullable [t][topk]: ... and weights */
 } ft_moe_opts;
 
 /* Routed-MoE layer [P1: routed MoE vector kernel; P4: gate/up, SwiGLU, down].

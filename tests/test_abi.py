@@ -125,7 +125,7 @@ def test_moe_route_options_refused_on_host():
     fake = ctypes.c_void_p(1 << 20)
 
     def call(w, a, route, dmax=0, n_expert=4, t=1):
-        o = ft._MoeOpts(route, dmax, None, None, None, None, None, None)
+        o = ft._MoeOpts(route, dmax, None, None, None, None, None, None, None, None, None)
         return L.ft_moe_q_vec(T[w], fake, fake, fake, n_expert, 256, 256, T[a], fake, t, fake, fake, 2, fake,
                               ctypes.byref(o), None)
 

@@ -77,12 +77,15 @@ def _bank(name):
     return _banks[name]
 
 
-def _run_stages(name, t, route, seed=0, dup=False, rep=False):
+def _run_stages(name, t, route, seed=0, dup=False, rep=False, from_logits=False):
     c = CASES[name]
     wg, wu, wd, dwg, dwu, dwd = _bank(name)
     g = synth.rng(303, t, seed)
     x = synth.activations(t, c["hidden"], g)
     ids = synth.expert_ids(t, c["E"], c["topk"], g)
+    if from_logits:
+        logits = synth.logits(t, c["E"], g)
+        ids, rw = oracle.route(logits, c["topk"])
     if rep:
         # slot 1 repeats slot 0's expert in every token: both pairs get the same
         # h and d, each with its own weight in the combine
@@ -101,8 +104,17 @@ def _run_stages(name, t, route, seed=0, dup=False, rep=False):
             "h": torch.empty(np_, I, device="cuda"),
             "hq": torch.empty(np_, ft.row_bytes(c["a"], I), dtype=torch.uint8, device="cuda"),
             "down": torch.empty(np_, H, device="cuda")}
-    y = ft.moe_q_vec(c["w"], dwg, dwu, dwd, c["E"], H, I, c["a"], dev(x), dev(ids), dev(ew),
-                     route=route, taps=taps)
+    if from_logits:
+        ids_out = torch.empty((t, c["topk"]), dtype=torch.int32, device="cuda")
+        w_out = torch.empty((t, c["topk"]), device="cuda")
+        y = ft.moe_q_vec(c["w"], dwg, dwu, dwd, c["E"], H, I, c["a"], dev(x), None, None, route=route, taps=taps,
+                         logits=dev(logits), topk=c["topk"], ids_out=ids_out, w_out=w_out)
+        assert np.array_equal(host(ids_out), ids), "routing ids differ from the oracle's"
+        check_fp32(host(w_out), rw, "routing weights", rel=1e-6, nmse=1e-12)
+        ew = host(w_out)
+    else:
+        y = ft.moe_q_vec(c["w"], dwg, dwu, dwd, c["E"], H, I, c["a"], dev(x), dev(ids), dev(ew),
+                         route=route, taps=taps)
     xq = oracle.quantize(c["a"], x)
     rg, ru, rh = oracle.moe_gate_up(c["w"], wg, wu, c["E"], H, I, c["a"], xq, ids)
     check_fp32(host(taps["g"]), rg, "g")
@@ -326,6 +338,17 @@ def test_moe_kq_tiles_sampled(name, t, hot):
         assert np.array_equal(hq[p], oracle.quantize(c["a"], hh[p][None])[0]), f"hq pair {p}"
         check_fp32(dd[p], rd_all[j], f"down pair {p}")
     check_fp32(y, oracle.moe_combine(dd, ew), "combine")
+
+
+@pytest.mark.parametrize("name,t,route", [("q4k", 1, 0), ("q4k", 4, 0), ("q4k", 6, 1), ("q4k_small", 3, 1),
+                                          ("q4k_wide", 2, 1), ("mxfp4_small", 5, 0), ("mxfp4_small", 12, 0),
+                                          ("q5k_small", 9, 0)])
+def test_moe_routes_from_logits(name, t, route):
+    """The layer routes each token itself from router logits (in the fused Q4_K
+    launch, else through the router first): its ids equal the oracle's routing
+    bit for bit, its weights within 1e-6, and every stage matches the oracle."""
+    log(f"moe {name} from logits t={t} route={route}")
+    _run_stages(name, t, route=route, from_logits=True)
 
 
 def test_moe_end_to_end_reported():

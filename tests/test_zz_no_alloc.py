@@ -32,7 +32,7 @@ def _gpu():
 
 def _call(entry, c, banks, x, ids, ew, y, hq_tap):
     name, w, a, H, I, E, K, route = c[:8]
-    opts = ft._MoeOpts(route, 0, None, None, None, ft._ptr(hq_tap), None, None)
+    opts = ft._MoeOpts(route, 0, None, None, None, ft._ptr(hq_tap), None, None, None, None, None)
     st = getattr(ft.lib(), entry)(ft.TYPES[w], *(ft._ptr(b) for b in banks), E, H, I, ft.TYPES[a], ft._ptr(x),
                                   x.shape[0], ft._ptr(ids), ft._ptr(ew), K, ft._ptr(y), ctypes.byref(opts),
                                   ft._stream())
