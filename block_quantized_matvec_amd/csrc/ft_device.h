@@ -548,9 +548,10 @@ __device__ __forceinline__ float unit_combine(const Unit<F>& u, const ActUnit<F>
 // from zero of x/d against the stored d, +-127), IEEE correctly rounded division.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int q8_code(float v, float d) {
-  if (d == 0.0f) return 0;
-  const float rq = roundf(v / d);
-  return rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
+  // branch-free (the code is 0 for d = 0), so a block's divisions can overlap
+  const float rq = roundf(v / (d == 0.0f ? 1.0f : d));
+  const int q = rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
+  return d == 0.0f ? 0 : q;
 }
 
 // ---------------------------------------------------------------------------
@@ -648,11 +649,10 @@ __device__ __forceinline__ void q8_k_part(const float (&v)[16], int l16, uint8_t
 // softmax over the selected logits in slot order.
 //  * logits become order-preserving unsigned keys (-0 first folded into +0, so
 //    that they tie as they compare equal);
-//  * the k-th largest key T is found bit by bit, from the top: the largest T with
-//    at least k keys >= T (each step is MAXE ballots and population counts);
-//  * the keys above T and, in expert order, the first k - #(> T) keys equal to T
-//    are the selection; its k entries go to LDS in expert order, and each of the
-//    first k lanes ranks one entry against the others (value, then index).
+//  * k rounds of a wave-wide arg-max: round r takes the largest key not yet
+//    taken, the lowest expert index among equal keys, as slot r;
+//  * slot r's weight is exp(l_r - l_0) / sum_q exp(l_q - l_0), the sum taken in
+//    slot order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t route_key(float f) {
   const uint32_t u = __float_as_uint(f + 0.0f);
@@ -662,89 +662,88 @@ __device__ __forceinline__ float route_val(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// the maximum of v over the wave, in every lane
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);           // (own, partner) either way
+  v = max(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(r32[0], r32[1]);
+}
+
 // One token's routing by one wave, in two calls so that the logits can be in
 // flight while the wave does other work: route_load reads them (lane l holds
-// experts l, l + 64, ...), route_select picks the winners.  s_key / s_idx / s_ex:
-// 8 words each of LDS for this wave; the k winners go to ids[0..k) / w[0..k) in
-// slot order (LDS or global).
+// experts l*MAXE .. l*MAXE + MAXE - 1, so expert order is lane order), and
+// route_select picks the winners; ids[0..k) / w[0..k) receive them in slot order
+// (LDS or global).  Each lane keeps the best of its keys not yet taken (higher
+// key, then lower expert); a round is one wave max over those, the lowest lane
+// holding it wins, and only that lane looks at its keys again.
 template <int MAXE>
 __device__ __forceinline__ void route_load(const float* __restrict__ l, int n_expert, int lane, float (&raw)[MAXE]) {
 #pragma unroll
   for (int i = 0; i < MAXE; ++i) {
-    const int e = lane + 64 * i;
+    const int e = lane * MAXE + i;
     raw[i] = e < n_expert ? l[e] : 0.0f;
   }
 }
 template <int MAXE>   // logits per lane (n_expert <= 64 * MAXE)
 __device__ __forceinline__ void route_select(const float (&raw)[MAXE], int n_expert, int topk, int lane,
-                                             uint32_t* s_key, int* s_idx, float* s_ex, int32_t* ids, float* w) {
+                                             int32_t* ids, float* w) {
   uint32_t key[MAXE];
+  uint32_t open = 0;               // bit i: key[i] is an expert not yet taken
 #pragma unroll
   for (int i = 0; i < MAXE; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < n_expert ? route_key(raw[i]) : 0u;   // 0 is below every logit's key
+    key[i] = route_key(raw[i]);
+    if (lane * MAXE + i < n_expert) open |= 1u << i;
   }
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = T | (1u << b);
-    int cnt = 0;
+  // this lane's best open key (bk) and its index (bs); bs = -1: none open
+  uint32_t bk = 0;
+  int bs = -1;
+  auto rescan = [&]() {
+    bk = 0;
+    bs = -1;
 #pragma unroll
-    for (int i = 0; i < MAXE; ++i) cnt += __popcll(__ballot(key[i] >= c));
-    if (cnt >= topk) T = c;
-  }
-  int ngt = 0;
-#pragma unroll
-  for (int i = 0; i < MAXE; ++i) ngt += __popcll(__ballot(key[i] > T));
-  const int need = topk - ngt;
-  const uint64_t below = (1ull << lane) - 1ull;
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int i = 0; i < MAXE; ++i) {
-    const bool eq = key[i] == T;
-    const uint64_t beq = __ballot(eq);
-    const bool sel = key[i] > T || (eq && eq_before + __popcll(beq & below) < need);
-    const uint64_t bsel = __ballot(sel);
-    if (sel) {
-      const int p = sel_before + __popcll(bsel & below);
-      s_key[p] = key[i];
-      s_idx[p] = lane + 64 * i;
+    for (int i = 0; i < MAXE; ++i) {
+      const bool better = ((open >> i) & 1) && (bs < 0 || key[i] > bk);
+      bk = better ? key[i] : bk;
+      bs = better ? i : bs;
     }
-    eq_before += __popcll(beq);
-    sel_before += __popcll(bsel);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  int rank = 0, mi = 0;
-  float ex = 0.0f;
-  if (lane < topk) {
-    const uint32_t mk = s_key[lane];
-    mi = s_idx[lane];
-    uint32_t top = mk;
-    for (int q = 0; q < topk; ++q) {
-      const uint32_t kq = s_key[q];
-      rank += kq > mk || (kq == mk && s_idx[q] < mi);
-      top = kq > top ? kq : top;
+  };
+  rescan();
+  uint32_t my_key = 0;             // lane r < k: slot r's key and expert
+  int my_idx = 0;
+  for (int r = 0; r < topk; ++r) {
+    const uint32_t mx = wave_umax(bk);
+    const uint64_t b = __ballot(bs >= 0 && bk == mx);
+    const int wl = (int)__builtin_ctzll(b);
+    const int ws = __builtin_amdgcn_readlane(bs, wl);
+    if (lane == r) {
+      my_key = mx;
+      my_idx = wl * MAXE + ws;
     }
-    ex = expf(route_val(mk) - route_val(top));
-    s_ex[rank] = ex;
+    if (lane == wl) {
+      open &= ~(1u << ws);
+      rescan();
+    }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const uint32_t top = __builtin_amdgcn_readlane(my_key, 0);
+  const float ex = lane < topk ? expf(route_val(my_key) - route_val(top)) : 0.0f;
+  float den = 0.0f;
+  for (int q = 0; q < topk; ++q) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), q));
   if (lane < topk) {
-    float den = 0.0f;
-    for (int q = 0; q < topk; ++q) den += s_ex[q];
-    ids[rank] = mi;
-    w[rank] = ex / den;
+    ids[lane] = my_idx;
+    w[lane] = ex / den;
   }
 }
 template <int MAXE>
 __device__ __forceinline__ void route_token(const float* __restrict__ l, int n_expert, int topk, int lane,
-                                            uint32_t* s_key, int* s_idx, float* s_ex, int32_t* ids, float* w) {
+                                            int32_t* ids, float* w) {
   float raw[MAXE];
   route_load<MAXE>(l, n_expert, lane, raw);
-  route_select<MAXE>(raw, n_expert, topk, lane, s_key, s_idx, s_ex, ids, w);
+  route_select<MAXE>(raw, n_expert, topk, lane, ids, w);
 }
 
 // ---------------------------------------------------------------------------

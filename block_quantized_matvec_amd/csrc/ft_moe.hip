@@ -38,14 +38,10 @@ template <int MAXE>   // logits per lane (n_expert <= 64 * MAXE)
 __global__ void __launch_bounds__(256)
 route_kernel(const float* __restrict__ logits, int64_t t, int n_expert, int topk, int32_t* __restrict__ ids,
              float* __restrict__ w) {
-  __shared__ uint32_t s_key[4][8];
-  __shared__ int s_idx[4][8];
-  __shared__ float s_ex[4][8];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t tok = (int64_t)blockIdx.x * 4 + wave;
   if (tok >= t) return;
-  route_token<MAXE>(logits + tok * n_expert, n_expert, topk, lane, s_key[wave], s_idx[wave], s_ex[wave],
-                    ids + tok * topk, w + tok * topk);
+  route_token<MAXE>(logits + tok * n_expert, n_expert, topk, lane, ids + tok * topk, w + tok * topk);
 }
 
 // ---------------------------------------------------------------------------

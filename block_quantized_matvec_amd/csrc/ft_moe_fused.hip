@@ -9,9 +9,10 @@
 // few microseconds of HBM time, and latency decides: each launch pays its start,
 // the latency of the first weight bytes and a tail.  Separate route, gate/up,
 // down and combine launches paid that four times.  Here:
-//   K1  every workgroup routes the chunk's tokens itself from the logits (one
-//       wave per token, the router's code) or reads the given ids, and builds the
-//       table of unique experts.  It takes (expert, 32-row block) tasks of the
+//   K1  every workgroup routes the chunk's tokens itself from the logits (the
+//       whole workgroup ranks the keys in parallel: a wave-serial top-k costs
+//       microseconds of dependent instructions) or reads the given ids, and
+//       builds the table of unique experts.  It takes (expert, 32-row block) tasks of the
 //       gate and up banks; each wave streams its rows through its own LDS-DMA
 //       ring, SwiGLU follows the 64-lane reduction, the block's 32 h values per
 //       token meet in LDS and are quantized to one Q8_1 block there (h itself
@@ -37,9 +38,9 @@ constexpr int FU_WAVES = 8;
 constexpr int FU_THREADS = 64 * FU_WAVES;
 constexpr int FU_S = 4;                    // ring stages per wave
 constexpr int FU_MAXU = 32;                // unique experts of a 4-token chunk at top-8
-constexpr int FU_MAXE = 4;                 // logits per lane of the in-kernel router (<= 256 experts)
+constexpr int FU_MAXE = 256;               // experts the in-kernel router takes
 constexpr int FU_STG = 8;                  // tasks (K1) / row blocks (K2) staged in LDS between stores
-constexpr int FU_TAB = 4368;               // LDS bytes: expert table, routing, h and down values, staging
+constexpr int FU_TAB = 4240;               // LDS bytes: expert table, routing, h and down values, staging
 
 // the chunk's routing and unique-expert table as K1 hands it to K2 (global scratch)
 struct FuTable {
@@ -60,7 +61,8 @@ struct FusedArgs {
   const float* x;        // [t][hidden] (this chunk)
   const int32_t* ids;    // [t][topk] (unless routed here)
   const float* ew;       // [t][topk] (unless routed here)
-  const float* logits;   // nullable [t][n_expert]: route here (n_expert <= 64 * FU_MAXE)
+  const float* logits;   // nullable [t][n_expert]: route here (n_expert <= FU_MAXE)
+  int rc;                // router: threads per (token, expert) key (1, 2, 4 or 8; t * n_expert * rc <= 512)
   int32_t* ids_out;      // nullable [t][topk]: the routing, written by workgroup 0
   float* w_out;          // nullable [t][topk]
   int t, topk;
@@ -86,10 +88,10 @@ struct FuLds {
   float* s_d;        // [2][T][8][GB] (two row blocks in turn)
   int32_t* s_ids;    // [4][8]
   float* s_w;        // [4][8]
-  uint32_t* s_rk;    // [4][8] router scratch
-  int* s_ri;
-  float* s_rx;
   uint8_t* stg;      // K1: [FU_STG][T] Q8_1 blocks of h; K2: [FU_STG][T][GB] outputs
+  uint32_t* s_selk;  // [4][8] router: the winners' keys
+  int32_t* s_ep;     // [32] the experts of the chunk's pairs
+  uint8_t* rings;    // the ring area (K1's router keys before the rings start)
   uint8_t* ring;     // this wave's
 };
 __device__ __forceinline__ FuLds fu_lds(int xbytes, int wave, int sb) {
@@ -105,11 +107,11 @@ __device__ __forceinline__ FuLds fu_lds(int xbytes, int wave, int sb) {
   L.s_d = (float*)(tab + 1552);
   L.s_ids = (int32_t*)(tab + 2576);
   L.s_w = (float*)(tab + 2704);
-  L.s_rk = (uint32_t*)(tab + 2832);
-  L.s_ri = (int*)(tab + 2960);
-  L.s_rx = (float*)(tab + 3088);
-  L.stg = tab + 3216;                      // 1152 bytes
-  L.ring = tab + FU_TAB + wave * (FU_S * sb + 16);
+  L.stg = tab + 2832;                      // 1152 bytes
+  L.s_selk = (uint32_t*)(tab + 3984);
+  L.s_ep = (int32_t*)(tab + 4112);
+  L.rings = tab + FU_TAB;
+  L.ring = L.rings + wave * (FU_S * sb + 16);
   return L;
 }
 
@@ -167,54 +169,138 @@ moe_q4k_gate_up_kernel(FusedArgs a) {
   const FuLds L = fu_lds(T * xrb, wave, SB);
   const Reader<const uint32_t*> rr{(const uint32_t*)L.ring};
 
-  // the given routing (wave 0, lane p: pair p), then x, then the logits of the
-  // token this wave routes (the last waves route, token i on wave FU_WAVES-1-i):
-  // every load is in flight before the first use
+  // the given routing (wave 0, lane p: pair p), then x, then the router logits
+  // (element q = tid + FU_THREADS * k of the chunk's [t][n_expert]): every load is
+  // in flight before the first use
   int id_in = 0;
   float w_in = 0.0f;
   if (!a.logits && wave == 0 && lane < npairs) {
     id_in = a.ids[lane];
     w_in = a.ew[lane];
   }
-  const int xgroups = (int)(H / 8);   // <= FU_THREADS
+  // x in groups of 8 elements: group p of the chunk (token p / xg) on thread
+  // p mod FU_THREADS, so all waves share the quantization (xg is a multiple of 4:
+  // a block's four groups stay on four aligned lanes)
+  const int xg = (int)(H / 8), nxg = a.t * xg;   // xg <= FU_THREADS
   float xv[T][8];
+  int xo[T];                                       // LDS offset of the group's block part
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    if (i < a.t && tid < xgroups) {
-      const float4* p = (const float4*)(a.x + (int64_t)i * H + 8 * tid);
-      const float4 f0 = p[0], f1 = p[1];
-      xv[i][0] = f0.x; xv[i][1] = f0.y; xv[i][2] = f0.z; xv[i][3] = f0.w;
-      xv[i][4] = f1.x; xv[i][5] = f1.y; xv[i][6] = f1.z; xv[i][7] = f1.w;
+  for (int k = 0; k < T; ++k) {
+    const int p = tid + FU_THREADS * k;
+    xo[k] = -1;
+    if (p < nxg) {
+      const int i = p / xg, gi = p - i * xg;
+      xo[k] = i * xrb + (gi >> 2) * 36;
+      const float4* src = (const float4*)(a.x + (int64_t)i * H + 8 * gi);
+      const float4 f0 = src[0], f1 = src[1];
+      xv[k][0] = f0.x; xv[k][1] = f0.y; xv[k][2] = f0.z; xv[k][3] = f0.w;
+      xv[k][4] = f1.x; xv[k][5] = f1.y; xv[k][6] = f1.z; xv[k][7] = f1.w;
     } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) xv[i][q] = 0.0f;
+      for (int q = 0; q < 8; ++q) xv[k][q] = 0.0f;
     }
   }
-  const int rt = FU_WAVES - 1 - wave;
-  const bool router = a.logits != nullptr && rt < a.t;
-  float raw[FU_MAXE];
-  if (router) route_load<FU_MAXE>(a.logits + (int64_t)rt * a.n_expert, (int)a.n_expert, lane, raw);
+  const int E = (int)a.n_expert, ne = a.logits ? a.t * E : 0;   // ne <= 4 * FU_MAXE
+  constexpr int RK = 4 * FU_MAXE / FU_THREADS;
+  float lr[RK];
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int q = tid + FU_THREADS * k;
+    lr[k] = q < ne ? a.logits[q] : 0.0f;
+  }
 
   // quantize x into LDS (Q8_1), the arithmetic of ft_quantize_act, while the
-  // logits arrive; then route
+  // logits arrive
 #pragma unroll
-  for (int i = 0; i < T; ++i)
-    if (i < a.t && tid < xgroups) q8_1_part(xv[i], tid & 3, L.xreg + i * xrb + (tid >> 2) * 36);
-  if (router)
-    route_select<FU_MAXE>(raw, (int)a.n_expert, a.topk, lane, L.s_rk + 8 * rt, L.s_ri + 8 * rt, L.s_rx + 8 * rt,
-                          L.s_ids + 8 * rt, L.s_w + 8 * rt);
+  for (int k = 0; k < T; ++k)
+    if (xo[k] >= 0) q8_1_part(xv[k], tid & 3, L.xreg + xo[k]);
+
+  // the router (same selection and weights as ft_moe_route), spread over the
+  // workgroup: each (token, expert) gets the 64-bit key (order-preserving logit
+  // key, then the complement of the expert index), so keys are distinct and
+  // "greater" means larger logit, or equal logit and lower index; an expert's
+  // slot is the number of its token's keys above its own (rc threads per expert
+  // count a share each), and slots below k are the winners
+  if (a.logits) {
+    uint64_t* s_ck = (uint64_t*)L.rings;                       // [t][E] keys
+    uint32_t* s_rank = (uint32_t*)(L.rings + 8 * 4 * FU_MAXE);  // [t][E] keys above
+#pragma unroll
+    for (int k = 0; k < RK; ++k) {
+      const int q = tid + FU_THREADS * k;
+      if (q < ne) {
+        const int e = q % E;
+        s_ck[q] = ((uint64_t)route_key(lr[k]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+        s_rank[q] = 0;
+      }
+    }
+    lds_barrier();
+    // a wave takes 64 consecutive keys and one share of the keys they are compared
+    // with, so its lanes read the same LDS words together (broadcast reads)
+    const int rc = a.rc, epp = FU_THREADS / rc, c = tid / epp;
+    for (int q0 = 0; q0 < ne; q0 += epp) {
+      const int q = q0 + tid % epp;
+      if (q < ne) {
+        const int i = q / E;
+        const uint64_t me = s_ck[q];
+        const uint64_t* row = s_ck + i * E;
+        const int f0 = c * E / rc, f1 = (c + 1) * E / rc;
+        uint32_t above = 0;
+#pragma unroll 8
+        for (int f = f0; f < f1; ++f) above += row[f] > me ? 1u : 0u;
+        if (rc == 1) s_rank[q] = above;
+        else atomicAdd(&s_rank[q], above);
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < RK; ++k) {
+      const int q = tid + FU_THREADS * k;
+      if (q < ne) {
+        const int r = (int)s_rank[q];
+        if (r < a.topk) {
+          const int i = q / E;
+          L.s_ids[8 * i + r] = q - i * E;
+          L.s_selk[8 * i + r] = (uint32_t)(s_ck[q] >> 32);
+        }
+      }
+    }
+  }
   lds_barrier();
 
-  // the chunk's unique experts, each with its tokens and (token, slot) pairs (lane
-  // p holds pair p; its first occurrence owns the expert)
+  // wave 0: the routing weights (logits) and the chunk's unique experts, each with
+  // its tokens and (token, slot) pairs (lane p holds pair p; its first occurrence
+  // owns the expert)
   if (wave == 0) {
     const int ti = lane / a.topk, ki = lane - ti * a.topk;
-    int ep = -1;
-    if (lane < npairs) ep = clamp_id(a.logits ? L.s_ids[8 * ti + ki] : id_in, a.n_expert);
+    const bool pv = lane < npairs;
+    int ep = 0;
+    float wv = 0.0f;
+    if (a.logits) {
+      float ex = 0.0f;
+      if (pv) {
+        ep = L.s_ids[8 * ti + ki];
+        ex = expf(route_val(L.s_selk[8 * ti + ki]) - route_val(L.s_selk[8 * ti]));
+      }
+      float den = 0.0f;   // this lane's token's sum, slot order
+      for (int i = 0; i < a.t; ++i) {
+        float di = 0.0f;
+        for (int kk = 0; kk < a.topk; ++kk)
+          di += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), i * a.topk + kk));
+        den = i == ti ? di : den;
+      }
+      if (pv) wv = ex / den;
+    } else if (pv) {
+      ep = clamp_id(id_in, a.n_expert);
+      wv = w_in;
+    }
+    if (pv) L.s_ep[lane] = ep;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     uint64_t same = 0;   // pairs naming the same expert as this lane's
-    for (int j = 0; j < npairs; ++j)
-      if (__builtin_amdgcn_readlane(ep, j) == ep) same |= 1ull << j;
-    const bool first = lane < npairs && (same & ((1ull << lane) - 1)) == 0;
+    for (int j = 0; j < npairs; ++j) same |= (uint64_t)(L.s_ep[j] == ep) << j;
+    if (!pv) same = 0;
+    const bool first = pv && (same & ((1ull << lane) - 1)) == 0;
     const uint64_t firsts = __ballot(first);
     const int nu = __popcll(firsts);
     if (first) {
@@ -238,11 +324,10 @@ moe_q4k_gate_up_kernel(FusedArgs a) {
     if (lane == 0) L.s_misc[0] = nu;
     if (blockIdx.x == 0) {
       if (lane == 0) a.table->nu = nu;
-      if (lane < npairs) {   // the routing for K2 and the caller
-        const float wv = a.logits ? L.s_w[8 * ti + ki] : w_in;
+      if (pv) {   // the routing for K2 and the caller
         a.table->ids[lane] = ep;
         a.table->w[lane] = wv;
-        if (a.logits && a.ids_out) a.ids_out[lane] = L.s_ids[8 * ti + ki];
+        if (a.logits && a.ids_out) a.ids_out[lane] = ep;
         if (a.logits && a.w_out) a.w_out[lane] = wv;
       }
     }
@@ -584,7 +669,7 @@ using namespace ftk;
 
 size_t ftk_moe_fused_table_bytes() { return sizeof(FuTable); }
 
-bool ftk_moe_fused_routes(int64_t n_expert) { return n_expert <= 64 * FU_MAXE; }
+bool ftk_moe_fused_routes(int64_t n_expert) { return n_expert <= FU_MAXE; }
 
 bool ftk_moe_fused_ok(int w, int act, int64_t hidden, int64_t inter, int topk) {
   if (w != FT_Q4_K || act != FT_Q8_1 || topk > 8) return false;
@@ -614,6 +699,8 @@ hipError_t ftk_launch_moe_fused(const MoeArgs& a, void* table, hipStream_t st) {
     fa.ids_out = a.ids_out ? a.ids_out + p0 : nullptr;
     fa.w_out = a.w_out ? a.w_out + p0 : nullptr;
     fa.t = tc;
+    fa.rc = 1;
+    while (fa.rc < 8 && (int64_t)tc * a.n_expert * fa.rc * 2 <= FU_THREADS) fa.rc *= 2;
     fa.topk = a.topk;
     fa.h_tap = a.h_tap ? a.h_tap + p0 * a.inter : nullptr;
     fa.g_tap = a.g_tap ? a.g_tap + p0 * a.inter : nullptr;

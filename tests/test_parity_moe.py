@@ -37,6 +37,37 @@ def test_route_ties():
     check_fp32(host(w), rw, rel=1e-6, nmse=1e-12)
 
 
+def _edge_logits(e):
+    """Rows that stress the key order and the tie rule: signed zeros, infinities,
+    the largest and smallest magnitudes, all-equal rows and winners in the last
+    64-expert slice."""
+    rows = []
+    r = np.full(e, -1.0, np.float32)
+    r[np.arange(0, e, 7)] = -0.0
+    r[np.arange(3, e, 11)] = 0.0
+    rows.append(r)                                          # -0 and +0 tie: index order
+    r = np.full(e, -np.inf, np.float32)
+    r[[e - 1, e // 2, 1]] = [np.float32(3e38), -np.float32(3e38), np.float32(1e-45)]
+    rows.append(r)                                          # infinities, extreme magnitudes
+    rows.append(np.full(e, 0.25, np.float32))               # all equal: the first k indices
+    r = np.linspace(-1.0, 1.0, e).astype(np.float32)
+    rows.append(r)                                          # winners at the highest indices
+    r = np.zeros(e, np.float32)
+    r[e - 9:] = 5.0
+    r[2] = 5.0
+    rows.append(r)                                          # a tie spanning the last slice
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("e,topk", [(8, 8), (64, 8), (100, 8), (128, 8), (200, 6), (256, 8), (1000, 4)])
+def test_route_edge_values(e, topk):
+    l = _edge_logits(e)
+    ids, w = ft.moe_route(dev(l), topk)
+    rid, rw = oracle.route(l, topk)
+    assert np.array_equal(host(ids), rid)
+    check_fp32(host(w), rw, "route weights", rel=1e-6, nmse=1e-12)
+
+
 @pytest.mark.parametrize("t,e,topk", [(1, 128, 8), (5, 256, 8), (512, 128, 8), (700, 64, 3), (4096, 256, 8),
                                       (1, 1, 1), (3000, 8, 8), (2048, 8192, 8)])
 def test_sort(t, e, topk):
