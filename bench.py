@@ -78,6 +78,10 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=str, default="", help="comma list overriding the token counts")
     ap.add_argument("--route", type=int, default=0, help="MoE route: 0 auto, 1 direct, 2 sorted tiles")
+    ap.add_argument("--counters-scope", default="all", choices=["all", "headline"],
+                    help="--workload counters: every kernel the counter summaries cover, or the headline only")
+    ap.add_argument("--counters-summary", nargs="+", metavar="CSV",
+                    help="per-kernel table of rocprofv3 --pmc CSVs of `--workload counters`")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of `--workload counters` into "
                          "profiles/traffic.json and exit")
@@ -88,6 +92,9 @@ def main():
     args = _args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return
+    if args.counters_summary:
+        counters_summary(args.counters_summary)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -342,7 +349,8 @@ def bench_dense(args, np, torch, ft, synth):
         "n_gpus": 1, "steps": steps_done, "warmup": args.warmup,
         "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8 x i8 -> i32 (v_dot4 at 1-4 tokens, int8 MFMA from 2-5 tokens), f32 scale combine",
+        "dtype": ("i8 x i8 -> i32 (v_dot4 ring at 1 token and on 4096-long rows up to 4 tokens; int8 MFMA at "
+                  "8 tokens and on 14336-long rows from 2 tokens, Q8_0 from 3), f32 scale combine"),
         "data": "synthetic (seeded GGUF blocks, N(0,1) activations)",
         "config": {"workload": (f"decode matvec, every weight format ({'/'.join(cfg['formats'])}), "
                                 "W 14336x4096" if fmts_only else
@@ -571,11 +579,15 @@ def bench_grouped(args, np, torch, ft, synth):
 # counter runs: a device copy of known size (calibration) and the headline kernel
 # ---------------------------------------------------------------------------
 def run_counters(args, np, torch, ft, synth):
+    """The counter workload: calibration copies, then the headline matvec, the Q4_K
+    MoE layer at 1 and 4 tokens, the MXFP4 MoE layer at 1 token and the Q5_K grouped
+    GEMM (each kernel is named apart in the counter CSVs)."""
     a = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
+    del a, b
     n, k = 14336, 4096
     g = synth.rng(7, 1)
     W = torch.from_numpy(synth.weights("Q4_K", n, k, g)).cuda()
@@ -585,7 +597,81 @@ def run_counters(args, np, torch, ft, synth):
     for i in range(20):
         ft.mul_mat_vec_q("Q4_K", Ws[i % 8], n, k, "Q8_1", xq, 1, out=y)
     torch.cuda.synchronize()
-    return {"counters_run": "copy 256 MiB x3, mmvq Q4_K 14336x4096 t=1 x20"}
+    del Ws, W
+    if args.counters_scope == "headline":
+        return {"counters_run": "copy 256 MiB x3, mmvq Q4_K 14336x4096 t=1 x20"}
+    # routed MoE layers from router logits (two bank copies, so each call reads HBM)
+    for c, tokens, reps in ((synth.MOE_Q4K, (1, 4), 8), (synth.MOE_MXFP4, (1,), 4)):
+        fmt, act, H, I, E, topk = c["fmt"], c["act"], c["hidden"], c["inter"], c["n_expert"], c["topk"]
+        gg = synth.rng(8, E)
+        bank = [torch.from_numpy(synth.expert_bank(fmt, E, I, H, gg)).cuda(),
+                torch.from_numpy(synth.expert_bank(fmt, E, I, H, gg)).cuda(),
+                torch.from_numpy(synth.expert_bank(fmt, E, H, I, gg)).cuda()]
+        banks = [bank, [t.clone() for t in bank]] if fmt == "Q4_K" else [bank]
+        for t in tokens:
+            x = torch.from_numpy(synth.activations(t, H, gg)).cuda()
+            yy = torch.empty((t, H), device="cuda")
+            for i in range(reps):
+                lg = torch.from_numpy(synth.logits(t, E, gg)).cuda()
+                ft.moe_q_vec(fmt, *banks[i % len(banks)], E, H, I, act, x, None, None, out=yy, logits=lg, topk=topk)
+            torch.cuda.synchronize()
+        del banks, bank
+    # grouped GEMM, Q5_K gate-shaped bank (one projection, sort + GEMM per call)
+    c = synth.GROUPED_KQ
+    T, H, I, E, topk = c["tokens"], c["hidden"], c["inter"], c["n_expert"], c["topk"]
+    gg = synth.rng(9)
+    Wg = torch.from_numpy(synth.expert_bank("Q5_K", E, I, H, gg)).cuda()
+    Wgs = [Wg, Wg.clone()]
+    xg = ft.quantize_act("Q8_K", torch.from_numpy(synth.activations(T, H, gg)).cuda())
+    yg = torch.empty((T * topk, I), device="cuda")
+    for i in range(4):
+        ids = torch.from_numpy(synth.expert_ids(T, E, topk, gg)).cuda()
+        ft.grouped_gemm_q("Q5_K", Wgs[i % 2], E, I, H, "Q8_K", xg, False, ids, out=yg)
+    torch.cuda.synchronize()
+    return {"counters_run": "copy 256 MiB x3, mmvq Q4_K 14336x4096 t=1 x20, MoE Q4_K t=1 x8 and t=4 x8, "
+                            "MoE MXFP4 t=1 x4, grouped Q5_K 512 tokens x4"}
+
+
+def counters_summary(csvs):
+    """Per-kernel means of every counter in rocprofv3 --pmc CSVs of `--workload
+    counters` (FETCH_SIZE / WRITE_SIZE scaled by the calibration copies, in MB per
+    dispatch); markdown on stdout."""
+    import csv
+    import statistics
+    per = {}
+    scale = {}
+    for path in csvs:
+        rs = list(csv.DictReader(open(path)))
+        for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+            cp = sorted((r for r in rs if r["Counter_Name"] == cname and "copyBuffer" in r["Kernel_Name"]),
+                        key=lambda r: int(r["Dispatch_Id"]))[:3]
+            if cp:
+                scale[cname] = COPY_BYTES / (statistics.median(float(r["Counter_Value"]) for r in cp) * 1024)
+        for r in rs:
+            per.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    names = sorted({kn for kn, _ in per})
+    counters = sorted({cn for _, cn in per})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---:|" + "---:|" * len(counters))
+    for kn in names:
+        if "copyBuffer" in kn or "elementwise" in kn:
+            continue
+        cells, nd = [], 0
+        for cn in counters:
+            vs = per.get((kn, cn))
+            if not vs:
+                cells.append("")
+                continue
+            nd = max(nd, len(vs))
+            m = statistics.mean(vs)
+            if cn in scale:
+                cells.append(f"{m * 1024 * scale[cn] / 1e6:.3f} MB")
+            else:
+                cells.append(f"{m:.4g}")
+        short = kn if len(kn) < 90 else kn[:87] + "..."
+        print(f"| `{short}` | {nd} | " + " | ".join(cells) + " |")
+    print()
+    print("scales: " + ", ".join(f"{k} x{v:.4f}" for k, v in scale.items()))
 
 
 def traffic_from(fetch_csv, write_csv):

@@ -6,7 +6,8 @@
 // the block scale, in 512-element chunks; Q4_1 / Q5_0 / Q5_1 as Q4_0 with their
 // fifth bits and the offset m from a second MFMA against an all-ones operand).
 //
-// ggml-cuda "mul_mat_vec_q" (the pages' MMVQ path, ds4 PR #656 Summary): a block's
+// The int8-activation quantized matvec (FreeToken PR #136, Summary: the
+// production ggml_mul_mat_vec_a8 kernel and its numerical tests): a block's
 // integer dot product of weight and activation codes, then the fp32 scale
 // combine.  MI355X design for more than one token:
 //  * the tokens are rows of the MFMA A operand (up to 16; 2..8 here) and 16 weight

@@ -16,9 +16,9 @@
 //       gate and up banks; each wave streams its rows through its own LDS-DMA
 //       ring, SwiGLU follows the 64-lane reduction, the block's 32 h values per
 //       token meet in LDS and are quantized to one Q8_1 block there (h itself
-//       never goes out unless tapped).  Then each workgroup reads the down rows
-//       its K2 counterpart will stream first, so that they sit in the cache
-//       hierarchy when K2 starts (workgroup w lands on the same XCD in both).
+//       never goes out unless tapped).  (Reading the down rows K2 streams first
+//       at the end of K1, to have them cached, was measured: it made the layer
+//       0.6-0.9 us slower, the K1 tail longer than what K2 saved.)
 //   K2  a workgroup owns blocks of output rows for every selected expert; each
 //       wave takes some of the experts; the (token, slot) down values meet in LDS
 //       and the combine is summed there in slot order, so no per-pair rows go out
@@ -146,15 +146,15 @@ __device__ __forceinline__ void wait_stages(int k) {
 // written out after the loop (or when the staging area is full).
 
 // K1: routing, unique experts, gate/up + SwiGLU, Q8_1 blocks of h.
-// T: token slots (1, 2, 4); LRA / LRB: lanes per gate/up row and per down row
-// (powers of two >= the row's 64-element units, at most 64).
-template <int T, int LRA, int LRB>
+// T: token slots (1, 2, 4); LRA: lanes per gate/up row (a power of two >= the
+// row's 64-element units, at most 64).
+template <int T, int LRA>
 __global__ void __launch_bounds__(FU_THREADS)
 moe_q4k_gate_up_kernel(FusedArgs a) {
   using FT = Fmt<FT_Q4_K>;
   constexpr int CPW = SegGeo<FT_Q4_K>::CPW;   // 16-byte DMA chunks per lane per stage
   constexpr int SB = CPW * 1024;              // bytes per ring stage
-  constexpr int GA = 64 / LRA, GB = 64 / LRB; // rows per stage
+  constexpr int GA = 64 / LRA;                // rows per stage
   constexpr int GPW = 32 / GA / FU_WAVES;     // groups per wave in a 32-row task
   constexpr int NTT = 2 * GPW;                // tiles per wave and task (gate, up)
   constexpr int MA = 2 * T;
@@ -163,7 +163,7 @@ moe_q4k_gate_up_kernel(FusedArgs a) {
   const int P = (int)gridDim.x;
   const int64_t H = a.hidden, I = a.inter;
   const int xrb = (int)(H / 32 * 36), hrb = (int)(I / 32 * 36);
-  const int rba = (int)(H / 256 * 144), rbb = (int)(I / 256 * 144);   // row bytes (multiples of 16)
+  const int rba = (int)(H / 256 * 144);       // row bytes (a multiple of 16)
   const int npairs = a.t * a.topk;
   const int nblk = (int)(I / 32);
   const FuLds L = fu_lds(T * xrb, wave, SB);
@@ -447,20 +447,6 @@ moe_q4k_gate_up_kernel(FusedArgs a) {
     }
   }
 
-  // read the down rows K2's workgroup blockIdx.x will stream first (into this
-  // wave's free ring; the bytes are not used here), so that they are cached
-  const int nrb = (int)((H + GB - 1) / GB);
-  const int my_rb = (int)blockIdx.x < nrb ? (nrb - (int)blockIdx.x + P - 1) / P : 0;
-  const int nuw = wave < nu ? (nu - wave + FU_WAVES - 1) / FU_WAVES : 0;
-  const int ntb = my_rb * nuw < FU_S ? my_rb * nuw : FU_S;
-  for (int j = 0; j < ntb; ++j) {
-    const int rb = (int)blockIdx.x + (j / nuw) * P;
-    const int u = wave + FU_WAVES * (j % nuw);
-    const int e = __builtin_amdgcn_readfirstlane(L.s_ue[u]);
-    const int64_t r0 = (int64_t)rb * GB;
-    const int nrows = (int)(H - r0 < GB ? H - r0 : GB);
-    fu_issue<CPW>(a.wd + ((int64_t)e * H + r0) * rbb, nrows * rbb, L.ring + j * SB, lane);
-  }
   if (!a.in_hq && my_tasks > 0) {
     lds_barrier();
     flush_hq(j0, my_tasks - 1);
@@ -629,13 +615,13 @@ static int lanes_for(int64_t units) {
   return lr;
 }
 
-template <int T, int LRA, int LRB>
+template <int T, int LRA>
 static hipError_t launch_k1(const FusedArgs& fa, hipStream_t st) {
   const size_t lds = k1_lds<T>(fa.hidden);
-  static const bool attr = hipFuncSetAttribute((const void*)moe_q4k_gate_up_kernel<T, LRA, LRB>,
+  static const bool attr = hipFuncSetAttribute((const void*)moe_q4k_gate_up_kernel<T, LRA>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
   if (lds > 65536 && !attr) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((moe_q4k_gate_up_kernel<T, LRA, LRB>), dim3((unsigned)ftk_num_cus()), dim3(FU_THREADS), lds, st,
+  hipLaunchKernelGGL((moe_q4k_gate_up_kernel<T, LRA>), dim3((unsigned)ftk_num_cus()), dim3(FU_THREADS), lds, st,
                      fa);
   return hipGetLastError();
 }
@@ -651,12 +637,7 @@ static hipError_t launch_k2(const FusedArgs& fa, hipStream_t st) {
 
 template <int T>
 static hipError_t fused_t(const FusedArgs& fa, int lra, int lrb, hipStream_t st) {
-  hipError_t e = hipErrorInvalidValue;
-#define FU_A(A, B) \
-  if (lra == A && lrb == B) e = launch_k1<T, A, B>(fa, st);
-  FU_A(16, 16) FU_A(16, 32) FU_A(16, 64) FU_A(32, 16) FU_A(32, 32) FU_A(32, 64) FU_A(64, 16) FU_A(64, 32)
-  FU_A(64, 64)
-#undef FU_A
+  hipError_t e = lra == 16 ? launch_k1<T, 16>(fa, st) : lra == 32 ? launch_k1<T, 32>(fa, st) : launch_k1<T, 64>(fa, st);
   if (e != hipSuccess) return e;
   if (lrb == 16) return launch_k2<T, 16>(fa, st);
   if (lrb == 32) return launch_k2<T, 32>(fa, st);
