@@ -280,6 +280,15 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
     u32x4 pa[NAI];
     float pdx[NAI];
     u32x4 pw[NWI];
+    // each weight chunk's row start in global memory (null: the chunk is idle)
+    const uint8_t* wrs[NWI];
+#pragma unroll
+    for (int i = 0; i < NWI; ++i) {
+      const int c = lane + 64 * i;
+      const int r = c / NCH;
+      const int64_t row = slot_row(r);
+      wrs[i] = (r < WROWS && row < n) ? slot_src(r) + row * row_bytes : nullptr;
+    }
     auto fetch = [&](int sb) {
 #pragma unroll
       for (int i = 0; i < NAI; ++i) {
@@ -297,16 +306,13 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
       }
 #pragma unroll
       for (int i = 0; i < NWI; ++i) {
-        const int c = lane + 64 * i;
-        const int r = c / NCH, ch = c % NCH;
-        const int64_t row = slot_row(r);
-        if (r < WROWS && row < n) {
-          const uint8_t* src = slot_src(r);
-          const int64_t off = row * row_bytes + (int64_t)sb * SB::BYTES;
-          const int sh = SB::ALIGNED ? 0 : (int)((uintptr_t)(src + off) & 15);
+        const int ch = (lane + 64 * i) % NCH;
+        if (wrs[i]) {
+          const uint8_t* sp = wrs[i] + (int64_t)sb * SB::BYTES;
+          const int sh = SB::ALIGNED ? 0 : (int)((uintptr_t)sp & 15);
           const int nch = (sh + SB::BYTES + 15) >> 4;
           // plain loads: the line that straddles two superblocks is read again by the next step
-          if (ch < nch) pw[i] = *((const u32x4*)(src + (off - sh)) + ch);
+          if (SB::ALIGNED || ch < nch) pw[i] = *((const u32x4*)(sp - sh) + ch);
         }
       }
     };
@@ -343,11 +349,8 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
         }
       }
 #pragma unroll
-      for (int i = 0; i < NWI; ++i) {
-        const int c = lane + 64 * i;
-        const int r = c / NCH, ch = c % NCH;
-        if (r < WROWS && slot_row(r) < n) *(u32x4*)(B + wslot + r * SB::SLOT + 16 * ch) = pw[i];
-      }
+      for (int i = 0; i < NWI; ++i)
+        if (wrs[i]) *(u32x4*)(B + wslot + 16 * (lane + 64 * i)) = pw[i];   // slot r, chunk ch: 16 * (r * NCH + ch)
     };
 
     v4f acc[PT][RG];
