@@ -397,7 +397,7 @@ ft_status moe_run(ft_type w, const void* w_gate, const void* w_up, const void* w
     if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
     return hip_status(e);
   }
-  // direct route, Q4_K x Q8_1 shapes that fit: the whole layer in one launch
+  // direct route, Q4_K x Q8_1 shapes that fit: the whole layer in two launches per 4-token chunk
   if (fused) return hip_status(ftk_launch_moe_fused(a, b + L.tab, st));
   // otherwise gate/up (quantizes x itself), down (quantizes each expert's h rows
   // itself, or reads in_hq), slot-order combine

@@ -171,7 +171,9 @@ def test_q4_0_matvec_full_size():
 @pytest.mark.parametrize("t", [1, 2, 4, 8])
 def test_dense_decode_full_size_sampled(w, n, k, t):
     """Full dense-decode shapes in the bench's launch configuration; the oracle
-    computes a sample of rows (every row of two tiles plus scattered rows)."""
+    computes a sample of rows: the first 64 and last 40 rows, the rows on both sides
+    of every multiple of 16 .. 1024 that the kernels' row shares fall on (a sample
+    of them), and scattered rows."""
     log(f"dense decode {w} {n}x{k} t={t}")
     g = synth.rng(204, n, k, t)
     W = synth.weights(w, n, k, g)
@@ -180,6 +182,9 @@ def test_dense_decode_full_size_sampled(w, n, k, t):
     xq = oracle.quantize("Q8_1", x)
     assert np.array_equal(host(xq_gpu), xq)
     y = host(ft.mul_mat_vec_q(w, dev(W), n, k, "Q8_1", xq_gpu, t))
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 40, n), g.choice(n, 200, replace=False)]))
+    edges = np.concatenate([np.arange(s, n, s * 7) for s in (16, 64, 256, 1024)])
+    edges = np.concatenate([edges - 1, edges])
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 40, n), edges[(edges >= 0) & (edges < n)],
+                                     g.choice(n, 200, replace=False)]))
     ref = oracle.matvec(w, np.ascontiguousarray(W[rows]), len(rows), k, "Q8_1", xq, t)
     check_fp32(y[:, rows], ref, f"{w} {n}x{k} t={t}")

@@ -83,6 +83,9 @@ CASES = {
     "q4k_small": dict(w="Q4_K", a="Q8_1", hidden=512, inter=256, E=6, topk=2),
     # rows of 68 units: both stages take the workgroup-tile kernels, not the rings
     "q4k_wide": dict(w="Q4_K", a="Q8_1", hidden=4352, inter=4352, E=3, topk=2),
+    # the two-launch layer's largest gate/up rows (64 lanes per row, one row per
+    # ring stage) and 32 lanes per down row
+    "q4k_h4096": dict(w="Q4_K", a="Q8_1", hidden=4096, inter=1536, E=16, topk=8),
     "mxfp4_small": dict(w="MXFP4", a="Q8_K", hidden=512, inter=512, E=5, topk=3),
     # K-quant experts x Q8_K on the sorted tiles (grouped gate/up + SwiGLU, h
     # quantize, grouped down, combine)
@@ -380,6 +383,14 @@ def test_moe_routes_from_logits(name, t, route):
     bit for bit, its weights within 1e-6, and every stage matches the oracle."""
     log(f"moe {name} from logits t={t} route={route}")
     _run_stages(name, t, route=route, from_logits=True)
+
+
+@pytest.mark.parametrize("t,from_logits", [(1, True), (3, False), (4, True), (6, True)])
+def test_moe_q4k_two_launch_shapes(t, from_logits):
+    """The two-launch Q4_K layer at hidden 4096 (gate/up rows of 64 units) and
+    intermediate 1536 (down rows of 24 units), one and several 4-token chunks."""
+    log(f"moe q4k_h4096 t={t} logits={from_logits}")
+    _run_stages("q4k_h4096", t, route=1, from_logits=from_logits)
 
 
 def test_moe_end_to_end_reported():
