@@ -746,6 +746,91 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int n_e
   route_select<MAXE>(raw, n_expert, topk, lane, ids, w);
 }
 
+// The same selection by a whole workgroup of NT threads, for the t tokens of a
+// chunk (ne = t * n_expert keys, element q = token q / n_expert).  Each (token,
+// expert) gets a 64-bit key: the order-preserving logit key above the complement
+// of the expert index, so keys are distinct and "greater" means larger logit, or
+// equal logit and lower index; a key with r < k keys of its token above it is
+// slot r.  Each wave takes 64 consecutive keys and one of rc shares of the keys
+// they are compared with, so its lanes read the same LDS words together
+// (broadcast reads); the shares meet through LDS atomics.  lr[j]: the logit of
+// element tid + NT * j (loaded by the caller, early).  s_ck / s_rank: 12 * ne
+// bytes of LDS.  Out: s_ids[8 * i + r] (expert of token i's slot r) and s_selk
+// (its logit key).  Every thread of the workgroup calls it (two barriers inside;
+// the caller's next barrier publishes the output).
+template <int NT, int RK>
+__device__ __forceinline__ void wg_route_rank(const float (&lr)[RK], int ne, int n_expert, int topk, int rc,
+                                              uint64_t* s_ck, uint32_t* s_rank, int32_t* s_ids, uint32_t* s_selk) {
+  const int tid = threadIdx.x, E = n_expert;
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int q = tid + NT * k;
+    if (q < ne) {
+      const int e = q % E;
+      s_ck[q] = ((uint64_t)route_key(lr[k]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+      s_rank[q] = 0;
+    }
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const int epp = NT / rc, c = tid / epp;
+  for (int q0 = 0; q0 < ne; q0 += epp) {
+    const int q = q0 + tid % epp;
+    if (q < ne) {
+      const int i = q / E;
+      const uint64_t me = s_ck[q];
+      const uint64_t* row = s_ck + i * E;
+      const int f0 = c * E / rc, f1 = (c + 1) * E / rc;
+      uint32_t above = 0;
+#pragma unroll 8
+      for (int f = f0; f < f1; ++f) above += row[f] > me ? 1u : 0u;
+      if (rc == 1) s_rank[q] = above;
+      else atomicAdd(&s_rank[q], above);
+    }
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < RK; ++k) {
+    const int q = tid + NT * k;
+    if (q < ne) {
+      const int r = (int)s_rank[q];
+      if (r < topk) {
+        const int i = q / E;
+        s_ids[8 * i + r] = q - i * E;
+        s_selk[8 * i + r] = (uint32_t)(s_ck[q] >> 32);
+      }
+    }
+  }
+}
+
+// The routing weights of the chunk from wg_route_rank's output, by one wave: lane
+// p < t * topk (pair p = token p / topk, slot p % topk) gets its expert and weight
+// (the router's softmax: exp of the logit minus the token's slot-0 logit, over
+// their sum in slot order).  Every lane of the wave calls it.
+__device__ __forceinline__ void route_pair_weights(const int32_t* s_ids, const uint32_t* s_selk, int t, int topk,
+                                                   int lane, int& ep, float& wv) {
+  const int ti = lane / topk, ki = lane - ti * topk;
+  const bool pv = lane < t * topk;
+  float ex = 0.0f;
+  ep = 0;
+  if (pv) {
+    ep = s_ids[8 * ti + ki];
+    ex = expf(route_val(s_selk[8 * ti + ki]) - route_val(s_selk[8 * ti]));
+  }
+  float den = 0.0f;
+  for (int i = 0; i < t; ++i) {
+    float di = 0.0f;
+    for (int kk = 0; kk < topk; ++kk) di += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), i * topk + kk));
+    den = i == ti ? di : den;
+  }
+  wv = pv ? ex / den : 0.0f;
+}
+
 // ---------------------------------------------------------------------------
 // routed-MoE helpers (direct route)
 // ---------------------------------------------------------------------------
@@ -757,10 +842,10 @@ __device__ __forceinline__ int clamp_id(int e, int64_t n_expert) {
 // of token i naming e in bits 8i.. of smask.  Returns false if an earlier slot
 // already names e (that workgroup owns the expert).  Lane p reads pair p (one load
 // per lane, t_real * topk <= 64); every lane of the wave must call it.
-__device__ __forceinline__ bool expert_tokens(const int32_t* __restrict__ ids, int slot, int t_real, int topk,
-                                              int64_t n_expert, int& e, uint32_t& mask, uint64_t& smask) {
+// ep: this lane's pair's expert (lane p = pair p; -1 past the pairs).
+__device__ __forceinline__ bool expert_tokens_of(int ep, int slot, int t_real, int topk, int& e, uint32_t& mask,
+                                                 uint64_t& smask) {
   const int p = threadIdx.x & 63, npairs = t_real * topk;
-  const int ep = p < npairs ? clamp_id(ids[p], n_expert) : -1;
   e = __builtin_amdgcn_readlane(ep, slot);
   const uint64_t same = __ballot(p < npairs && ep == e);
   if (same & ((1ull << slot) - 1)) return false;
@@ -772,6 +857,12 @@ __device__ __forceinline__ bool expert_tokens(const int32_t* __restrict__ ids, i
     if (b) mask |= 1u << i;
   }
   return true;
+}
+__device__ __forceinline__ bool expert_tokens(const int32_t* __restrict__ ids, int slot, int t_real, int topk,
+                                              int64_t n_expert, int& e, uint32_t& mask, uint64_t& smask) {
+  const int p = threadIdx.x & 63, npairs = t_real * topk;
+  const int ep = p < npairs ? clamp_id(ids[p], n_expert) : -1;
+  return expert_tokens_of(ep, slot, t_real, topk, e, mask, smask);
 }
 
 // index of the j-th set bit of m

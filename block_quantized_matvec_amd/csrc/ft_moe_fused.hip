@@ -221,74 +221,20 @@ moe_q4k_gate_up_kernel(FusedArgs a) {
   // "greater" means larger logit, or equal logit and lower index; an expert's
   // slot is the number of its token's keys above its own (rc threads per expert
   // count a share each), and slots below k are the winners
-  if (a.logits) {
-    uint64_t* s_ck = (uint64_t*)L.rings;                       // [t][E] keys
-    uint32_t* s_rank = (uint32_t*)(L.rings + 8 * 4 * FU_MAXE);  // [t][E] keys above
-#pragma unroll
-    for (int k = 0; k < RK; ++k) {
-      const int q = tid + FU_THREADS * k;
-      if (q < ne) {
-        const int e = q % E;
-        s_ck[q] = ((uint64_t)route_key(lr[k]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-        s_rank[q] = 0;
-      }
-    }
-    lds_barrier();
-    // a wave takes 64 consecutive keys and one share of the keys they are compared
-    // with, so its lanes read the same LDS words together (broadcast reads)
-    const int rc = a.rc, epp = FU_THREADS / rc, c = tid / epp;
-    for (int q0 = 0; q0 < ne; q0 += epp) {
-      const int q = q0 + tid % epp;
-      if (q < ne) {
-        const int i = q / E;
-        const uint64_t me = s_ck[q];
-        const uint64_t* row = s_ck + i * E;
-        const int f0 = c * E / rc, f1 = (c + 1) * E / rc;
-        uint32_t above = 0;
-#pragma unroll 8
-        for (int f = f0; f < f1; ++f) above += row[f] > me ? 1u : 0u;
-        if (rc == 1) s_rank[q] = above;
-        else atomicAdd(&s_rank[q], above);
-      }
-    }
-    lds_barrier();
-#pragma unroll
-    for (int k = 0; k < RK; ++k) {
-      const int q = tid + FU_THREADS * k;
-      if (q < ne) {
-        const int r = (int)s_rank[q];
-        if (r < a.topk) {
-          const int i = q / E;
-          L.s_ids[8 * i + r] = q - i * E;
-          L.s_selk[8 * i + r] = (uint32_t)(s_ck[q] >> 32);
-        }
-      }
-    }
-  }
+  if (a.logits)
+    wg_route_rank<FU_THREADS, RK>(lr, ne, E, a.topk, a.rc, (uint64_t*)L.rings, (uint32_t*)(L.rings + 8 * 4 * FU_MAXE),
+                                  L.s_ids, L.s_selk);
   lds_barrier();
 
   // wave 0: the routing weights (logits) and the chunk's unique experts, each with
   // its tokens and (token, slot) pairs (lane p holds pair p; its first occurrence
   // owns the expert)
   if (wave == 0) {
-    const int ti = lane / a.topk, ki = lane - ti * a.topk;
     const bool pv = lane < npairs;
     int ep = 0;
     float wv = 0.0f;
     if (a.logits) {
-      float ex = 0.0f;
-      if (pv) {
-        ep = L.s_ids[8 * ti + ki];
-        ex = expf(route_val(L.s_selk[8 * ti + ki]) - route_val(L.s_selk[8 * ti]));
-      }
-      float den = 0.0f;   // this lane's token's sum, slot order
-      for (int i = 0; i < a.t; ++i) {
-        float di = 0.0f;
-        for (int kk = 0; kk < a.topk; ++kk)
-          di += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), i * a.topk + kk));
-        den = i == ti ? di : den;
-      }
-      if (pv) wv = ex / den;
+      route_pair_weights(L.s_ids, L.s_selk, a.t, a.topk, lane, ep, wv);
     } else if (pv) {
       ep = clamp_id(id_in, a.n_expert);
       wv = w_in;
