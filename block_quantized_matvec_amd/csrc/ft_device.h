@@ -811,9 +811,10 @@ __device__ __forceinline__ void wg_route_rank(const float (&lr)[RK], int ne, int
 // The routing weights of the chunk from wg_route_rank's output, by one wave: lane
 // p < t * topk (pair p = token p / topk, slot p % topk) gets its expert and weight
 // (the router's softmax: exp of the logit minus the token's slot-0 logit, over
-// their sum in slot order).  Every lane of the wave calls it.
-__device__ __forceinline__ void route_pair_weights(const int32_t* s_ids, const uint32_t* s_selk, int t, int topk,
-                                                   int lane, int& ep, float& wv) {
+// their sum in slot order; every lane sums its token's row from s_ex, 64 floats of
+// LDS, so no lane waits on another's chain).  Every lane of the wave calls it.
+__device__ __forceinline__ void route_pair_weights(const int32_t* s_ids, const uint32_t* s_selk, float* s_ex, int t,
+                                                   int topk, int lane, int& ep, float& wv) {
   const int ti = lane / topk, ki = lane - ti * topk;
   const bool pv = lane < t * topk;
   float ex = 0.0f;
@@ -821,13 +822,14 @@ __device__ __forceinline__ void route_pair_weights(const int32_t* s_ids, const u
   if (pv) {
     ep = s_ids[8 * ti + ki];
     ex = expf(route_val(s_selk[8 * ti + ki]) - route_val(s_selk[8 * ti]));
+    s_ex[lane] = ex;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   float den = 0.0f;
-  for (int i = 0; i < t; ++i) {
-    float di = 0.0f;
-    for (int kk = 0; kk < topk; ++kk) di += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), i * topk + kk));
-    den = i == ti ? di : den;
-  }
+  if (pv)
+    for (int kk = 0; kk < topk; ++kk) den += s_ex[ti * topk + kk];
   wv = pv ? ex / den : 0.0f;
 }
 

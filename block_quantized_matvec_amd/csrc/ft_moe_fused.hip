@@ -234,17 +234,22 @@ moe_q4k_gate_up_kernel(FusedArgs a) {
     int ep = 0;
     float wv = 0.0f;
     if (a.logits) {
-      route_pair_weights(L.s_ids, L.s_selk, a.t, a.topk, lane, ep, wv);
+      route_pair_weights(L.s_ids, L.s_selk, (float*)L.rings, a.t, a.topk, lane, ep, wv);
     } else if (pv) {
       ep = clamp_id(id_in, a.n_expert);
       wv = w_in;
     }
-    if (pv) L.s_ep[lane] = ep;
+    if (lane < 32) L.s_ep[lane] = pv ? ep : -1 - lane;   // no two idle entries match
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    uint64_t same = 0;   // pairs naming the same expert as this lane's
-    for (int j = 0; j < npairs; ++j) same |= (uint64_t)(L.s_ep[j] == ep) << j;
+    uint64_t same = 0;   // pairs naming the same expert as this lane's (all 32 entries, 4 per read)
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+      const int4 q = *(const int4*)(L.s_ep + j);
+      same |= ((uint64_t)(q.x == ep) << j) | ((uint64_t)(q.y == ep) << (j + 1)) | ((uint64_t)(q.z == ep) << (j + 2)) |
+              ((uint64_t)(q.w == ep) << (j + 3));
+    }
     if (!pv) same = 0;
     const bool first = pv && (same & ((1ull << lane) - 1)) == 0;
     const uint64_t firsts = __ballot(first);
