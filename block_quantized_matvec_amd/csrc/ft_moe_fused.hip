@@ -489,14 +489,18 @@ moe_q4k_down_kernel(FusedArgs a) {
       const int u = wave + FU_WAVES * ui;
       const uint32_t mask = __builtin_amdgcn_readfirstlane(L.s_um[u]);
       const uint64_t smask = L.s_us[u];
+      // the h-hat units of the tokens that picked this expert (the other tokens'
+      // slots are never read: their combines are skipped below)
       ActUnit<FT_Q4_K> act[T];
 #pragma unroll
       for (int i = 0; i < T; ++i) {
-        if (uv && ((mask >> i) & 1)) {
-          const int p0 = i * a.topk + (int)__builtin_ctzll((smask >> (8 * i)) & 0xFFull);
-          load_act_unit<FT_Q4_K, FT_Q8_1>(L.xreg + p0 * hrb, un / FT::UPB, un % FT::UPB, act[i]);
-        } else {
-          zero_act_unit<FT_Q4_K>(act[i]);
+        if ((mask >> i) & 1) {
+          if (uv) {
+            const int p0 = i * a.topk + (int)__builtin_ctzll((smask >> (8 * i)) & 0xFFull);
+            load_act_unit<FT_Q4_K, FT_Q8_1>(L.xreg + p0 * hrb, un / FT::UPB, un % FT::UPB, act[i]);
+          } else {
+            zero_act_unit<FT_Q4_K>(act[i]);
+          }
         }
       }
       wait_tiles<CPW, FU_S>(issued - 1 - cur);
