@@ -494,7 +494,7 @@ moe_q4k_down_kernel(FusedArgs a) {
       ActUnit<FT_Q4_K> act[T];
 #pragma unroll
       for (int i = 0; i < T; ++i) {
-        if ((mask >> i) & 1) {
+        if (T == 1 || ((mask >> i) & 1)) {   // one token: it picked every expert of the table
           if (uv) {
             const int p0 = i * a.topk + (int)__builtin_ctzll((smask >> (8 * i)) & 0xFFull);
             load_act_unit<FT_Q4_K, FT_Q8_1>(L.xreg + p0 * hrb, un / FT::UPB, un % FT::UPB, act[i]);
