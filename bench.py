@@ -40,15 +40,25 @@ COPY_BYTES = 256 << 20         # calibration copy for the FETCH_SIZE / WRITE_SIZ
 _HEADLINE_SRC = ("ft_mmvq.hip", "ft_mmvq_kernels.h", "ft_device.h", "ft_internal.h")
 
 
+def _code_only(text):
+    """C/C++ source without comments and blank lines (a comment edit does not change
+    the kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def _src_hash():
-    """Hash of the headline kernel's sources: traffic figures are void once it changes."""
+    """Hash of the headline kernel's code (sources without comments): traffic figures
+    are void once it changes."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_matvec_amd", "csrc")
-    for f in _HEADLINE_SRC:
-        h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "ft.h"), "rb").read())
+    paths = [os.path.join(csrc, f) for f in _HEADLINE_SRC] + [os.path.join(ROOT, "include", "ft.h")]
+    for path in paths:
+        h.update(os.path.basename(path).encode())
+        h.update(_code_only(open(path).read()).encode())
     return h.hexdigest()[:16]
 
 

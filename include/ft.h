@@ -188,7 +188,12 @@ typedef struct {
    the sorted tiles.
    Routes [P4 Summary: tiny batches direct, larger ones on expert-sorted tiles;
    P3 What changed: the grouped keep-quant op over expert_ids]:
-   direct = one workgroup per selected expert and row tile, tokens in VGPRs;
+   direct = the selected experts' rows streamed once per chunk of tokens, every token
+   that picked an expert served from the same bytes: for (Q4_K, Q8_1) with hidden
+   and inter multiples of 256 up to 4096 (inter up to about 1536), two launches per
+   4-token chunk (routing from the logits, x quantize, gate/up + SwiGLU, h quantize;
+   then down and the slot-order combine), otherwise one workgroup per selected
+   expert and row tile per stage, then a combine;
    sorted tiles = token->expert sort, one fused gate/up + SwiGLU grouped MFMA GEMM,
    h quantize, grouped down GEMM, slot-order combine.  Both give the same result
    up to fp32 rounding order. */
