@@ -101,6 +101,9 @@ hipError_t ftk_launch_moe_down(const MoeArgs& a, hipStream_t st);
 // MXFP4 x Q8_K direct-route stages on the FP4 MFMA (hidden, inter multiples of 256)
 hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st);
 hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st);
+// one token: MXFP4 down and the slot-order combine in one launch (y written; d only to d_tap)
+bool ftk_moe_fp4_down_combine_ok(const MoeArgs& a);
+hipError_t ftk_launch_moe_fp4_down_combine(const MoeArgs& a, hipStream_t st);
 // y from the per-pair rows in dpair, slot order
 hipError_t ftk_launch_moe_combine(const MoeArgs& a, hipStream_t st);
 

@@ -371,6 +371,90 @@ moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hi
   }
 }
 
+// One token: down and the weighted combine in one launch.  A workgroup owns 16
+// output rows for every slot: wave 2s + p takes slot s's expert over K part p (of
+// 2, odd parts walking downwards as above), so the slots' down values of a row
+// meet in LDS and are summed in slot order there (ft_moe_combine's arithmetic), and
+// no per-pair rows go out.  The prologue quantizes every slot's h row to Q8_K
+// (or takes in_hq) into FP8-half images, one per slot.  A slot repeating an earlier
+// slot's expert is computed again (same d, its own weight).
+constexpr int MF_DC_WAVES = 16;   // 8 slots x 2 K parts
+__global__ void __launch_bounds__(64 * MF_DC_WAVES)
+moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int64_t inter,
+                            const float* __restrict__ h, const uint8_t* __restrict__ in_hq,
+                            uint8_t* __restrict__ hq_tap, const int32_t* __restrict__ ids,
+                            const float* __restrict__ ew, int topk, float* __restrict__ d_tap,
+                            float* __restrict__ y) {
+  extern __shared__ u32x4 smem4[];
+  const int nsb = (int)(inter / 256);
+  uint8_t* act = (uint8_t*)smem4;                               // [8][2 * inter]
+  float* dx = (float*)(act + (size_t)8 * 2 * inter);            // [8][nsb][16]
+  float* s_d = dx + (size_t)8 * nsb * 16;                       // [8][16]
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int s = wave >> 1, kq = wave & 1, dir = kq ? -1 : 1;
+  const int hrb = nsb * 292;
+  const bool live = s < topk;
+  const int e = live ? clamp_id(ids[s], n_expert) : 0;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (lane & 15);
+  const int64_t row_bytes = inter / 32 * 17;
+  const uint32_t* const rowd[1] = {(const uint32_t*)(wd + ((int64_t)e * hidden + row) * row_bytes)};
+  const int sb0 = kq * nsb / 2, sb1 = (kq + 1) * nsb / 2;
+  Fp4Blk nx[1][2];
+  if (live) fp4_first<1>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);   // slots past topk stream nothing
+
+  // every slot's h row -> Q8_K codes -> FP8 halves (16 elements per thread)
+  for (int i = tid; i < 8 * nsb * 16; i += 64 * MF_DC_WAVES) dx[i] = 0.0f;
+  __syncthreads();
+  const int per_row = (int)(inter / 16), total = topk * per_row;
+  for (int idx = tid; idx < total; idx += 64 * MF_DC_WAVES) {   // a block's 16 lanes stay together
+    const int j = idx / per_row, c = idx - j * per_row, sb = c >> 4, l16 = c & 15;
+    uint32_t w[4];
+    int sm;
+    float d;
+    if (in_hq) {
+      const uint8_t* blk = in_hq + (int64_t)j * hrb + (int64_t)sb * 292;
+      const uint32_t* q = (const uint32_t*)(blk + 4 + 16 * l16);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) w[jj] = q[jj];
+      d = *(const float*)blk;
+      sm = *(const int16_t*)(blk + 260 + 2 * l16);
+    } else {
+      const float4* p = (const float4*)(h + (int64_t)j * inter) + 4 * c;
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = p[q];
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+      q8_k_codes(v, w, sm, d);
+    }
+    stage_codes(w, act + (int64_t)j * 2 * inter, inter, sb, l16);
+    if (l16 == 0) dx[(j * nsb + sb) * 16] = d;
+    if (hq_tap && blockIdx.x == 0) q8_k_store(w, sm, d, l16, hq_tap + (int64_t)j * hrb + sb * 292);
+  }
+  __syncthreads();
+
+  v4f acc[1] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+  if (live) fp4_rows<1>(rowd, sb0, sb1, dir, nx, act + (size_t)s * 2 * inter, inter, 1, 1u, dx + (size_t)s * nsb * 16, acc);
+  __syncthreads();   // the images are dead: the K-part sums reuse their LDS
+  if (fp4_reduce<1, 2>(acc, (float*)smem4)) {
+    // part-0 wave of slot s: lanes 0..15 hold row (lane & 15) of token 0
+    if (live && lane < 16) {
+      s_d[s * 16 + lane] = acc[0][0];
+      if (d_tap) d_tap[(int64_t)s * hidden + row] = acc[0][0];
+    }
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float sum = 0.0f;
+    for (int k = 0; k < topk; ++k) sum = fmaf(ew[k], s_d[k * 16 + tid], sum);
+    y[(int64_t)blockIdx.x * 16 + tid] = sum;
+  }
+}
+
 // LDS bytes of one launch: the activation image and scales, or the K-quarter
 // partials, whichever is larger
 static size_t fp4_lds(int t, int64_t k, int nm) {
@@ -419,6 +503,23 @@ hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+// one token, top-k <= 8: down + combine in one launch (hidden a multiple of 16)
+bool ftk_moe_fp4_down_combine_ok(const MoeArgs& a) {
+  return a.t == 1 && a.topk <= 8 && a.hidden % 16 == 0 && a.inter % 256 == 0 &&
+         (size_t)8 * 2 * a.inter + (size_t)8 * (a.inter / 256) * 16 * 4 + 8 * 16 * 4 <= 65536;
+}
+hipError_t ftk_launch_moe_fp4_down_combine(const MoeArgs& a, hipStream_t st) {
+  if (!ftk_moe_fp4_down_combine_ok(a)) return hipErrorInvalidValue;
+  const size_t img = (size_t)8 * 2 * a.inter + (size_t)8 * (a.inter / 256) * 16 * 4 + 8 * 16 * 4;
+  const size_t red = (size_t)MF_DC_WAVES * 64 * 4 * 4;
+  const int64_t hrb = a.inter / 256 * 292;
+  (void)hrb;
+  hipLaunchKernelGGL(moe_fp4_down_combine_kernel, dim3((unsigned)(a.hidden / 16)), dim3(64 * MF_DC_WAVES),
+                     img > red ? img : red, st, (const uint8_t*)a.w_down, a.n_expert, a.hidden, a.inter, a.h,
+                     (const uint8_t*)a.in_hq, (uint8_t*)a.hq_tap, a.ids, a.ew, a.topk, a.d_tap, a.y);
+  return hipGetLastError();
 }
 
 hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st) {
