@@ -245,6 +245,7 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
     };
     const uint8_t* xr[NAI];
     const uint8_t* xr8[NAI];
+    int xpi[NAI], xpv[NAI];
 #pragma unroll
     for (int i = 0; i < NAI; ++i) {
       int pi = (tid + GM_THREADS * i) / CPP;
@@ -253,13 +254,15 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
         fp4_item(tid + GM_THREADS * i, m, r, qa, spl);
         pi = 16 * m + spl;
       }
-      xr[i] = nullptr;
-      xr8[i] = nullptr;
-      if (pi < gm) {
-        const int64_t row = x_per_pair ? pairs[g0 + pi] : pairs[g0 + pi] / topk;
-        xr[i] = xq + row * xrow_bytes;
-        if constexpr (FP4) xr8[i] = xf8 + row * (int64_t)nsb * 512;
-      }
+      xpi[i] = pi;
+      xpv[i] = pairs[g0 + min(pi, gm - 1)];   // every pair index in flight at once
+    }
+#pragma unroll
+    for (int i = 0; i < NAI; ++i) {
+      const int64_t row = x_per_pair ? xpv[i] : xpv[i] / topk;
+      const bool live = xpi[i] < gm;
+      xr[i] = live ? xq + row * xrow_bytes : nullptr;
+      xr8[i] = (FP4 && live) ? xf8 + row * (int64_t)nsb * 512 : nullptr;
     }
     // chunk of the item: codes: su; MXFP4: the FP8 chunk c = 16p + 2j + h of region r
     // (r = 4*st + 2*pp + bh) and lane quarter qa: j = 4st + 2bh + (qa>>1), h = qa & 1
