@@ -117,6 +117,45 @@ __device__ __forceinline__ void fp4_first(const uint32_t* const (&rowd)[NM], int
   }
 }
 
+// One superblock sb of a wave's 16 rows (blocks cur, for each of NM matrices)
+// against the activation image at ap (this lane's token row, 16 * (lane >> 4) in;
+// arow: the lane's token is staged), added to acc with the superblock's scales.
+template <int NM>
+__device__ __forceinline__ void fp4_sb(const Fp4Blk (&cur)[NM][2], int sb, const uint8_t* ap, int64_t k, bool arow,
+                                       const float* dx, v4f (&acc)[NM]) {
+  const int b = (threadIdx.x & 63) >> 4;
+  const v4f zf = {0.f, 0.f, 0.f, 0.f};
+  v4f dd[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) dd[m] = zf;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    int e8[NM];
+    v8i bw[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) bw[m] = fp4_operand(cur[m][st], b, e8[m]);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+      if (arow) {
+        const uint8_t* q = ap + pp * k + 256 * sb + 128 * st;
+        a0 = *(const u32x4*)q;
+        a1 = *(const u32x4*)(q + 64);
+      }
+      const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        dd[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw[m], dd[m], 0, 4, 0, pp ? 131 : 127, 0,
+                                                                  e8[m]);
+    }
+  }
+  const v4f dxv = *(const v4f*)(dx + sb * 16 + 4 * b);
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[m][r] = fmaf(dxv[r], dd[m][r], acc[m][r]);
+}
+
 // The dot products of one wave: 16 rows (rowd[m] for each of NM matrices) over the
 // superblocks [sb0, sb1), walked upwards (dir = 1) or downwards (dir = -1), against
 // the activation image `act` (t_in tokens, those of tmask staged).  nx: the first
@@ -148,35 +187,7 @@ __device__ __forceinline__ void fp4_rows(const uint32_t* const (&rowd)[NM], int 
         fp4_fetch(rowd[m], 2 * sn + 1, b, nx[m][1]);
       }
     }
-    v4f dd[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) dd[m] = zf;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      int e8[NM];
-      v8i bw[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) bw[m] = fp4_operand(cur[m][st], b, e8[m]);
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-        if (arow) {
-          const uint8_t* q = ap + pp * k + 256 * sb + 128 * st;
-          a0 = *(const u32x4*)q;
-          a1 = *(const u32x4*)(q + 64);
-        }
-        const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-          dd[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw[m], dd[m], 0, 4, 0, pp ? 131 : 127, 0,
-                                                                    e8[m]);
-      }
-    }
-    const v4f dxv = *(const v4f*)(dx + sb * 16 + 4 * b);
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[m][r] = fmaf(dxv[r], dd[m][r], acc[m][r]);
+    fp4_sb<NM>(cur, sb, ap, k, arow, dx, acc);
   }
 }
 
@@ -379,6 +390,13 @@ moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hi
 // (or takes in_hq) into FP8-half images, one per slot.  A slot repeating an earlier
 // slot's expert is computed again (same d, its own weight).
 constexpr int MF_DC_WAVES = 16;   // 8 slots x 2 K parts
+// NW > 0: every superblock of a wave's K part (at most NW) is requested right after
+// the quantization, all at once, and each superblock's dot waits only for its own
+// loads (loads complete in order; every wave issues the same loads).  Requested
+// before the quantization, the loads of the whole layer's down matrices held up
+// the quantization behind their issue; one superblock of lookahead (NW = 0, longer
+// K parts) pays a full memory latency per superblock.
+template <int NW>
 __global__ void __launch_bounds__(64 * MF_DC_WAVES)
 moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int64_t inter,
                             const float* __restrict__ h, const uint8_t* __restrict__ in_hq,
@@ -394,13 +412,14 @@ moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, in
   const int s = wave >> 1, kq = wave & 1, dir = kq ? -1 : 1;
   const int hrb = nsb * 292;
   const bool live = s < topk;
-  const int e = live ? clamp_id(ids[s], n_expert) : 0;
+  // NW > 0: slots past topk read slot 0's rows (unused), so that every wave issues the same loads
+  const int e = live ? clamp_id(ids[s], n_expert) : (NW > 0 ? clamp_id(ids[0], n_expert) : 0);
   const int64_t row = (int64_t)blockIdx.x * 16 + (lane & 15);
   const int64_t row_bytes = inter / 32 * 17;
   const uint32_t* const rowd[1] = {(const uint32_t*)(wd + ((int64_t)e * hidden + row) * row_bytes)};
-  const int sb0 = kq * nsb / 2, sb1 = (kq + 1) * nsb / 2;
+  const int sb0 = kq * nsb / 2, sb1 = (kq + 1) * nsb / 2, n = sb1 - sb0;
   Fp4Blk nx[1][2];
-  if (live) fp4_first<1>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);   // slots past topk stream nothing
+  if (NW == 0 && live) fp4_first<1>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);   // slots past topk stream nothing
 
   // every slot's h row -> Q8_K codes -> FP8 halves (16 elements per thread)
   for (int i = tid; i < 8 * nsb * 16; i += 64 * MF_DC_WAVES) dx[i] = 0.0f;
@@ -435,10 +454,32 @@ moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, in
     if (l16 == 0) dx[(j * nsb + sb) * 16] = d;
     if (hq_tap && blockIdx.x == 0) q8_k_store(w, sm, d, l16, hq_tap + (int64_t)j * hrb + sb * 292);
   }
-  __syncthreads();
+  Fp4Blk wb[NW > 0 ? NW : 1][1][2];
+  if constexpr (NW > 0) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {   // superblock j in walk order (past the part: a valid one, unused)
+      int sb = dir > 0 ? sb0 + j : sb1 - 1 - j;
+      sb = sb < 0 ? 0 : (sb < nsb ? sb : nsb - 1);
+      fp4_fetch(rowd[0], 2 * sb, lane >> 4, wb[j][0][0]);
+      fp4_fetch(rowd[0], 2 * sb + 1, lane >> 4, wb[j][0][1]);
+    }
+    lds_barrier();   // (a barrier with a full fence would wait for those loads)
+  } else {
+    __syncthreads();
+  }
 
   v4f acc[1] = {{0.0f, 0.0f, 0.0f, 0.0f}};
-  if (live) fp4_rows<1>(rowd, sb0, sb1, dir, nx, act + (size_t)s * 2 * inter, inter, 1, 1u, dx + (size_t)s * nsb * 16, acc);
+  if constexpr (NW > 0) {
+    const int tok = lane & 15;
+    const uint8_t* ap = act + (size_t)s * 2 * inter + (int64_t)tok * 2 * inter + 16 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      if (live && j < n)
+        fp4_sb<1>(wb[j], dir > 0 ? sb0 + j : sb1 - 1 - j, ap, inter, tok == 0, dx + (size_t)s * nsb * 16, acc);
+    }
+  } else {
+    if (live) fp4_rows<1>(rowd, sb0, sb1, dir, nx, act + (size_t)s * 2 * inter, inter, 1, 1u, dx + (size_t)s * nsb * 16, acc);
+  }
   __syncthreads();   // the images are dead: the K-part sums reuse their LDS
   if (fp4_reduce<1, 2>(acc, (float*)smem4)) {
     // part-0 wave of slot s: lanes 0..15 hold row (lane & 15) of token 0
@@ -516,7 +557,11 @@ hipError_t ftk_launch_moe_fp4_down_combine(const MoeArgs& a, hipStream_t st) {
   const size_t red = (size_t)MF_DC_WAVES * 64 * 4 * 4;
   const int64_t hrb = a.inter / 256 * 292;
   (void)hrb;
-  hipLaunchKernelGGL(moe_fp4_down_combine_kernel, dim3((unsigned)(a.hidden / 16)), dim3(64 * MF_DC_WAVES),
+  const int nw = (int)(a.inter / 256 + 1) / 2;   // superblocks of a wave's K part, at most
+  auto kern = nw == 0 ? moe_fp4_down_combine_kernel<0> : nw <= 1 ? moe_fp4_down_combine_kernel<1>
+            : nw <= 2 ? moe_fp4_down_combine_kernel<2> : nw <= 4 ? moe_fp4_down_combine_kernel<4>
+            : moe_fp4_down_combine_kernel<0>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.hidden / 16)), dim3(64 * MF_DC_WAVES),
                      img > red ? img : red, st, (const uint8_t*)a.w_down, a.n_expert, a.hidden, a.inter, a.h,
                      (const uint8_t*)a.in_hq, (uint8_t*)a.hq_tap, a.ids, a.ew, a.topk, a.d_tap, a.y);
   return hipGetLastError();
