@@ -229,6 +229,23 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   uint8_t* act = (uint8_t*)smem4;                           // [t_real][2 * hidden]
   float* dx = (float*)(act + (size_t)t_real * 2 * hidden);  // [hidden / 256][16]
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  // the first quantization item's x (it needs no expert id): requested before the ids
+  // and the weights, so that the quantization waits for neither
+  const int per_row = (int)(hidden / 16), total = t_real * per_row;
+  float xv0[16];
+  {
+    const int idx = tid < total ? tid : 0;
+    const int r = idx / per_row, c = idx - r * per_row;
+    const float4* p = (const float4*)(x + (int64_t)r * hidden) + 4 * c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = p[q];
+      xv0[4 * q] = f.x;
+      xv0[4 * q + 1] = f.y;
+      xv0[4 * q + 2] = f.z;
+      xv0[4 * q + 3] = f.w;
+    }
+  }
   int e;
   uint32_t mask;
   uint64_t smask;
@@ -244,23 +261,28 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   Fp4Blk nx[2][2];
   fp4_first<2>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
 
-  // x -> Q8_K codes -> FP8 halves in LDS (16 elements per thread, 16 lanes per block)
+  // x -> Q8_K codes -> FP8 halves in LDS (16 elements per thread, 16 lanes per block),
+  // while the first superblock streams in
   for (int i = tid; i < nsb * 16; i += MF_THREADS) dx[i] = 0.0f;
-  __syncthreads();
-  const int per_row = (int)(hidden / 16), total = t_real * per_row;
+  lds_barrier();   // (a barrier with a full fence would wait for the weight loads)
   for (int idx0 = 0; idx0 < total; idx0 += MF_THREADS) {
     const int idx = idx0 + tid;
     if (idx < total) {   // the same for all 16 lanes of a block
       const int r = idx / per_row, c = idx - r * per_row;
-      const float4* p = (const float4*)(x + (int64_t)r * hidden) + 4 * c;
       float v[16];
+      if (idx0 == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = p[q];
-        v[4 * q] = f.x;
-        v[4 * q + 1] = f.y;
-        v[4 * q + 2] = f.z;
-        v[4 * q + 3] = f.w;
+        for (int q = 0; q < 16; ++q) v[q] = xv0[q];
+      } else {
+        const float4* p = (const float4*)(x + (int64_t)r * hidden) + 4 * c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = p[q];
+          v[4 * q] = f.x;
+          v[4 * q + 1] = f.y;
+          v[4 * q + 2] = f.z;
+          v[4 * q + 3] = f.w;
+        }
       }
       uint32_t w[4];
       int s;
