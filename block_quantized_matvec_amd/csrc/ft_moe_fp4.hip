@@ -224,7 +224,8 @@ __global__ void __launch_bounds__(MF_THREADS)
 moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t n_expert,
                        int64_t inter, int64_t hidden, const float* __restrict__ x, int t_real,
                        const int32_t* __restrict__ ids, int topk, float* __restrict__ h, float* __restrict__ gtap,
-                       float* __restrict__ utap) {
+                       float* __restrict__ utap, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
+                       float* __restrict__ w_out) {
   extern __shared__ u32x4 smem4[];
   uint8_t* act = (uint8_t*)smem4;                           // [t_real][2 * hidden]
   float* dx = (float*)(act + (size_t)t_real * 2 * hidden);  // [hidden / 256][16]
@@ -249,7 +250,25 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   int e;
   uint32_t mask;
   uint64_t smask;
-  if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
+  if (logits) {
+    // routed here (n_expert <= 256): wave i takes token i of the chunk, with the
+    // router's own selection and weights, into LDS; workgroup (0, 0) hands the
+    // routing on to the later stages and the caller
+    __shared__ int32_t s_rid[MF_MAXT * 8];
+    __shared__ float s_rw[MF_MAXT * 8];
+    if (wave < t_real) route_token<4>(logits + (int64_t)wave * n_expert, (int)n_expert, topk, lane,
+                                      s_rid + wave * topk, s_rw + wave * topk);
+    __syncthreads();
+    const int npairs = t_real * topk;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid < npairs) {
+      ids_out[tid] = s_rid[tid];
+      w_out[tid] = s_rw[tid];
+    }
+    const int ep = lane < npairs ? s_rid[lane] : -1;
+    if (!expert_tokens_of(ep, blockIdx.y, t_real, topk, e, mask, smask)) return;
+  } else {
+    if (!expert_tokens(ids, blockIdx.y, t_real, topk, n_expert, e, mask, smask)) return;
+  }
 
   constexpr int RG = MF_WAVES / KQ;
   const int nsb = (int)(hidden / 256), rg = wave / KQ, kq = wave % KQ, dir = (kq & 1) ? -1 : 1;
@@ -547,7 +566,10 @@ static hipError_t fp4_gate_up_kq(const MoeArgs& a, int c0, int tc, hipStream_t s
   hipLaunchKernelGGL(moe_fp4_gate_up_kernel<KQ>, grid, dim3(MF_THREADS), fp4_lds(tc, a.hidden, 2), st,
                      (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, a.hidden,
                      a.x + (size_t)c0 * a.hidden, tc, a.ids + p0, a.topk, a.h + p0 * a.inter,
-                     a.g_tap ? a.g_tap + p0 * a.inter : nullptr, a.u_tap ? a.u_tap + p0 * a.inter : nullptr);
+                     a.g_tap ? a.g_tap + p0 * a.inter : nullptr, a.u_tap ? a.u_tap + p0 * a.inter : nullptr,
+                     a.logits ? a.logits + (size_t)c0 * a.n_expert : nullptr,
+                     a.logits ? const_cast<int32_t*>(a.ids) + p0 : nullptr,
+                     a.logits ? const_cast<float*>(a.ew) + p0 : nullptr);
   return hipGetLastError();
 }
 

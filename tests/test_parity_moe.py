@@ -377,12 +377,13 @@ def test_moe_kq_tiles_sampled(name, t, hot):
 @pytest.mark.parametrize("name,t,route", [("q4k", 1, 0), ("q4k", 4, 0), ("q4k", 6, 1), ("q4k_small", 3, 1),
                                           ("q4k_wide", 2, 1), ("mxfp4_small", 5, 0), ("mxfp4_small", 12, 0),
                                           ("q5k_small", 9, 0), ("mxfp4_small", 1, 0), ("mxfp4_small", 3, 1),
-                                          ("mxfp4_small", 4, 1), ("mxfp4", 1, 1), ("mxfp4", 4, 1)])
+                                          ("mxfp4_small", 4, 1), ("mxfp4", 1, 1), ("mxfp4", 4, 1),
+                                          ("mxfp4_small", 2, 1), ("mxfp4", 2, 1)])
 def test_moe_routes_from_logits(name, t, route):
     """The layer routes each token itself from router logits (inside the first
-    launch of the Q4_K layer, else through the router first): its ids equal the
-    oracle's routing bit for bit, its weights within 1e-6, and every stage matches
-    the oracle."""
+    launch of the Q4_K layer and of the MXFP4 direct route at 1-2 tokens, else
+    through the router first): its ids equal the oracle's routing bit for bit, its
+    weights within 1e-6, and every stage matches the oracle."""
     log(f"moe {name} from logits t={t} route={route}")
     _run_stages(name, t, route=route, from_logits=True)
 
