@@ -230,6 +230,10 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   uint8_t* act = (uint8_t*)smem4;                           // [t_real][2 * hidden]
   float* dx = (float*)(act + (size_t)t_real * 2 * hidden);  // [hidden / 256][16]
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  // routed here: the logits first (loads complete in order: the selection then
+  // waits for nothing after them)
+  float raw[4];
+  if (logits && wave < t_real) route_load<4>(logits + (int64_t)wave * n_expert, (int)n_expert, lane, raw);
   // the first quantization item's x (it needs no expert id): requested before the ids
   // and the weights, so that the quantization waits for neither
   const int per_row = (int)(hidden / 16), total = t_real * per_row;
@@ -256,8 +260,7 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
     // routing on to the later stages and the caller
     __shared__ int32_t s_rid[MF_MAXT * 8];
     __shared__ float s_rw[MF_MAXT * 8];
-    if (wave < t_real) route_token<4>(logits + (int64_t)wave * n_expert, (int)n_expert, topk, lane,
-                                      s_rid + wave * topk, s_rw + wave * topk);
+    if (wave < t_real) route_select<4>(raw, (int)n_expert, topk, lane, s_rid + wave * topk, s_rw + wave * topk);
     __syncthreads();
     const int npairs = t_real * topk;
     if (blockIdx.x == 0 && blockIdx.y == 0 && tid < npairs) {
