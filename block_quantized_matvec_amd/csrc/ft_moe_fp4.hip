@@ -577,16 +577,17 @@ static hipError_t fp4_gate_up_kq(const MoeArgs& a, int c0, int tc, hipStream_t s
 }
 
 // gate/up K parts: 2 (each row's K in two halves: one cache line shared per row)
-// when that still gives two workgroups per CU, else 4 (more workgroups, three
-// shared lines per row; measured at 1 token: 46.4 vs 47.6 us per layer, at 2-8
-// tokens 2 parts win by 5-10%).
+// when that still gives a workgroup per CU, else 4 (more workgroups, three shared
+// lines per row).  At 1 token of the 256 x 2048 x 4096 layer (one workgroup per CU)
+// 2 parts measure 38.0-38.3 against 38.4-38.8 us per layer; at 2-8 tokens 2 parts
+// win by 5-10%.
 hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
   const int cs = fp4_chunk(a.hidden, 2);
   if (cs < 1 || a.hidden % 256 || a.inter % 256) return hipErrorInvalidValue;
   for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
     const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
     const int64_t wgs2 = a.inter / (16 * MF_WAVES / 2) * tc * a.topk;
-    const hipError_t err = wgs2 >= 2 * (int64_t)ftk_num_cus() ? fp4_gate_up_kq<2>(a, (int)c0, tc, st)
+    const hipError_t err = wgs2 >= (int64_t)ftk_num_cus() ? fp4_gate_up_kq<2>(a, (int)c0, tc, st)
                                                                : fp4_gate_up_kq<4>(a, (int)c0, tc, st);
     if (err != hipSuccess) return err;
   }
