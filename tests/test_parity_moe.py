@@ -95,6 +95,8 @@ CASES = {
     # the grouped-GEMM workload's layer: hidden 4096, 128 experts of 1536, top-8
     "q5k_c4": dict(w="Q5_K", a="Q8_K", hidden=4096, inter=1536, E=128, topk=8),
     "q6k_c4": dict(w="Q6_K", a="Q8_K", hidden=4096, inter=1536, E=128, topk=8),
+    # one superblock per row: K parts with no superblock, four experts on one router lane
+    "mxfp4_tiny": dict(w="MXFP4", a="Q8_K", hidden=256, inter=256, E=4, topk=2),
 }
 
 _banks = {}
@@ -378,7 +380,8 @@ def test_moe_kq_tiles_sampled(name, t, hot):
                                           ("q4k_wide", 2, 1), ("mxfp4_small", 5, 0), ("mxfp4_small", 12, 0),
                                           ("q5k_small", 9, 0), ("mxfp4_small", 1, 0), ("mxfp4_small", 3, 1),
                                           ("mxfp4_small", 4, 1), ("mxfp4", 1, 1), ("mxfp4", 4, 1),
-                                          ("mxfp4_small", 2, 1), ("mxfp4", 2, 1)])
+                                          ("mxfp4_small", 2, 1), ("mxfp4", 2, 1), ("mxfp4_tiny", 1, 1),
+                                          ("mxfp4_tiny", 2, 1), ("mxfp4_tiny", 3, 1)])
 def test_moe_routes_from_logits(name, t, route):
     """The layer routes each token itself from router logits (inside the first
     launch of the Q4_K layer and of the MXFP4 direct route at 1-2 tokens, else
