@@ -17,9 +17,10 @@
 //  * a workgroup of 8 waves owns 16-row groups of one expert, each split over K in
 //    KQ parts (summed in a fixed order through LDS); odd parts walk K downwards so
 //    that the cache line two parts share is fetched once;
-//  * each lane fetches its own block per k-step straight from global memory (five
-//    dwords: E8M0 byte + 16 code bytes at a 1..4 byte offset), one superblock
-//    ahead;
+//  * each lane takes its own block per k-step as five dwords (E8M0 byte + 16 code
+//    bytes at a 1..4 byte offset): in gate/up (K a multiple of 512) from the
+//    wave's LDS ring, filled by 16-byte global_load_lds over whole row pieces,
+//    else straight from global memory one superblock ahead;
 //  * the workgroup quantizes its activation rows to Q8_K itself (the arithmetic of
 //    ft_quantize_act) and keeps them in LDS as the FP8 halves in the operand's
 //    nibble order, with the Q8_K scale of every (token, superblock).
@@ -191,6 +192,94 @@ __device__ __forceinline__ void fp4_rows(const uint32_t* const (&rowd)[NM], int 
   }
 }
 
+// The K walk through a per-wave LDS ring (rows a whole number of 16-byte chunks:
+// K a multiple of 512).  A stage holds one superblock of the wave's 16 rows of
+// each of NM matrices: per row the 9 chunks from the 16-byte boundary at or below
+// the superblock's start (136 bytes at an offset of 0 or 8), 144 chunks per
+// matrix, moved by global_load_lds (16 bytes per lane, CPS loads per wave and
+// stage; lanes past the end re-read the last chunk).  Chunk cc of row r of matrix
+// m sits in slot 144m + 9r + cc, so the 16 rows a read touches fall in distinct
+// bank groups (9 is odd).  Lane (r, b) reads its 17-byte block of k-step st as the
+// two slots from 4st + b (the block starts at dword 2P + st of them, P = the
+// superblock's parity), i.e. the same five dwords the direct fetch takes.
+template <int NM>
+struct Fp4Ring {
+  static constexpr int CPS = (NM * 144 + 63) / 64;   // DMA loads per wave and stage
+  static constexpr int STAGE = CPS * 1024;           // LDS bytes of one stage
+  const uint8_t* p[CPS];                             // this lane's chunk of each load, at row offset 0
+  uint8_t* ring;
+  int sb0, sb1, dir, n, issued;
+  __device__ __forceinline__ void init(const uint8_t* const (&grp)[NM], int64_t row_bytes, uint8_t* ring_, int sb0_,
+                                       int sb1_, int dir_) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+      const int q = min(64 * c + lane, NM * 144 - 1), m = q / 144, rr = (q - 144 * m) / 9, cc = q - 144 * m - 9 * rr;
+      p[c] = grp[m] + rr * row_bytes + 16 * cc;
+    }
+    ring = ring_;
+    sb0 = sb0_;
+    sb1 = sb1_;
+    dir = dir_;
+    n = sb1 - sb0;
+    issued = 0;
+  }
+  __device__ __forceinline__ int sb_of(int it) const { return dir > 0 ? sb0 + it : sb1 - 1 - it; }
+  // the next superblock of the walk into its stage
+  template <int RS>
+  __device__ __forceinline__ void issue() {
+    const int64_t win = (int64_t)(136 * sb_of(issued)) & ~(int64_t)15;
+    uint8_t* dst = ring + (issued % RS) * STAGE;
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) lds_dma16(p[c] + win, dst + 1024 * c);
+    ++issued;
+  }
+};
+
+template <int NM, int RS>
+__device__ __forceinline__ void fp4_rows_ring(Fp4Ring<NM>& rg, const uint8_t* act, int64_t k, int t_in,
+                                              uint32_t tmask, const float* dx, v4f (&acc)[NM]) {
+  constexpr int CPS = Fp4Ring<NM>::CPS;
+  const int lane = threadIdx.x & 63, b = lane >> 4, tok = lane & 15, r = lane & 15;
+  const bool arow = tok < t_in && ((tmask >> tok) & 1);
+  const uint8_t* ap = act + (int64_t)tok * 2 * k + 16 * b;
+  const v4f zf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = zf;
+  for (int it = 0; it < rg.n; ++it) {
+    wait_tiles<CPS, RS>(rg.issued - 1 - it);
+    const uint8_t* stg = rg.ring + (it % RS) * Fp4Ring<NM>::STAGE;
+    const int sb = rg.sb_of(it);
+    const bool odd = sb & 1;
+    Fp4Blk cur[NM][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4* s = (const u32x4*)(stg + 16 * (144 * m + 9 * r + 4 * st + b));
+        const u32x4 u0 = s[0], u1 = s[1];
+        uint32_t* d = cur[m][st].d;   // dwords st .. st + 4 of the pair (odd: 2 further), named one by one
+        if (st == 0) {
+          d[0] = odd ? u0.z : u0.x;
+          d[1] = odd ? u0.w : u0.y;
+          d[2] = odd ? u1.x : u0.z;
+          d[3] = odd ? u1.y : u0.w;
+          d[4] = odd ? u1.z : u1.x;
+        } else {
+          d[0] = odd ? u0.w : u0.y;
+          d[1] = odd ? u1.x : u0.z;
+          d[2] = odd ? u1.y : u0.w;
+          d[3] = odd ? u1.z : u1.x;
+          d[4] = odd ? u1.w : u1.y;
+        }
+      }
+    fp4_sb<NM>(cur, sb, ap, k, arow, dx, acc);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): the stage is read
+    if (rg.issued < rg.n) rg.template issue<RS>();
+  }
+}
+
 // Sum the KQ K-parts of each row group (fixed order) through LDS `red`
 // ([row group][K part][64 lanes][NM * 4] fp32, wave = KQ * row group + part);
 // returns true in the waves of part 0, whose acc then holds the totals.
@@ -219,7 +308,7 @@ __device__ __forceinline__ bool fp4_reduce(v4f (&acc)[NM], float* red) {
 // gate/up + SwiGLU for 16 * 8 / KQ rows of the expert of slot blockIdx.y (KQ K parts
 // per 16-row group; odd parts walk their superblocks downwards, so that a cache line
 // shared by two neighbouring parts is read by both at about the same time)
-template <int KQ>
+template <int KQ, int RS>
 __global__ void __launch_bounds__(MF_THREADS)
 moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t n_expert,
                        int64_t inter, int64_t hidden, const float* __restrict__ x, int t_real,
@@ -281,7 +370,16 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
                                    (const uint32_t*)(wu + ((int64_t)e * inter + row) * row_bytes)};
   const int sb0 = kq * nsb / KQ, sb1 = (kq + 1) * nsb / KQ;
   Fp4Blk nx[2][2];
-  fp4_first<2>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
+  Fp4Ring<2> ring;
+  if constexpr (RS > 0) {   // the wave's ring follows the activation image and scales
+    const int64_t row0 = (int64_t)blockIdx.x * (16 * RG) + rg * 16;
+    const uint8_t* const grp[2] = {wg + ((int64_t)e * inter + row0) * row_bytes, wu + ((int64_t)e * inter + row0) * row_bytes};
+    const size_t roff = ((size_t)t_real * 2 * hidden + (size_t)nsb * 64 + 15) & ~(size_t)15;
+    ring.init(grp, row_bytes, (uint8_t*)smem4 + roff + (size_t)wave * RS * Fp4Ring<2>::STAGE, sb0, sb1, dir);
+    for (int j = 0; j < RS && j < ring.n; ++j) ring.template issue<RS>();
+  } else {
+    fp4_first<2>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
+  }
 
   // x -> Q8_K codes -> FP8 halves in LDS (16 elements per thread, 16 lanes per block),
   // while the first superblock streams in
@@ -317,7 +415,8 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   __syncthreads();
 
   v4f acc[2];
-  fp4_rows<2>(rowd, sb0, sb1, dir, nx, act, hidden, t_real, 0xFFu, dx, acc);
+  if constexpr (RS > 0) fp4_rows_ring<2, RS>(ring, act, hidden, t_real, 0xFFu, dx, acc);
+  else fp4_rows<2>(rowd, sb0, sb1, dir, nx, act, hidden, t_real, 0xFFu, dx, acc);
   __syncthreads();   // the activation image is dead: the reduction reuses its LDS
   if (!fp4_reduce<2, KQ>(acc, (float*)smem4)) return;
 
@@ -562,11 +661,21 @@ static int fp4_chunk(int64_t k, int nm) {
   return fp4_lds(cs, k, nm) > 65536 ? 0 : cs;
 }
 
-template <int KQ>
+template <int KQ, int RS>
 static hipError_t fp4_gate_up_kq(const MoeArgs& a, int c0, int tc, hipStream_t st) {
   const dim3 grid((unsigned)(a.inter / (16 * MF_WAVES / KQ)), (unsigned)(tc * a.topk));
   const size_t p0 = (size_t)c0 * a.topk;
-  hipLaunchKernelGGL(moe_fp4_gate_up_kernel<KQ>, grid, dim3(MF_THREADS), fp4_lds(tc, a.hidden, 2), st,
+  size_t lds = fp4_lds(tc, a.hidden, 2);
+  if (RS > 0) {
+    const size_t ring = (((size_t)tc * 2 * a.hidden + (size_t)(a.hidden / 256) * 64 + 15) & ~(size_t)15) +
+                        (size_t)MF_WAVES * RS * Fp4Ring<2>::STAGE;
+    lds = ring > lds ? ring : lds;
+    // (the kernel's static LDS, the routing, counts against the same 160 KiB)
+    static const bool attr = hipFuncSetAttribute((const void*)moe_fp4_gate_up_kernel<KQ, RS>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 159 * 1024) == hipSuccess;
+    if (!attr || lds > 159 * 1024) return hipErrorInvalidConfiguration;
+  }
+  hipLaunchKernelGGL((moe_fp4_gate_up_kernel<KQ, RS>), grid, dim3(MF_THREADS), lds, st,
                      (const uint8_t*)a.w_gate, (const uint8_t*)a.w_up, a.n_expert, a.inter, a.hidden,
                      a.x + (size_t)c0 * a.hidden, tc, a.ids + p0, a.topk, a.h + p0 * a.inter,
                      a.g_tap ? a.g_tap + p0 * a.inter : nullptr, a.u_tap ? a.u_tap + p0 * a.inter : nullptr,
@@ -580,15 +689,23 @@ static hipError_t fp4_gate_up_kq(const MoeArgs& a, int c0, int tc, hipStream_t s
 // when that still gives a workgroup per CU, else 4 (more workgroups, three shared
 // lines per row).  At 1 token of the 256 x 2048 x 4096 layer (one workgroup per CU)
 // 2 parts measure 38.0-38.3 against 38.4-38.8 us per layer; at 2-8 tokens 2 parts
-// win by 5-10%.
+// win by 5-10%.  With K a multiple of 512 the K walk runs on the LDS ring: 2 stages
+// per wave at 1 token (layer 38.2-38.4 -> 37.0-37.2 us), 1 stage from 2 tokens,
+// where the smaller ring keeps two workgroups per CU (2 / 4 / 8 tokens 69.4 / 130
+// / 235 -> 68.1-69.0 / 127.7-128.2 / 230-233 us; 2 stages there: no gain, 3 stages
+// at 1 token: no gain).  The same ring in the per-expert down launch was slower
+// (2-8 tokens +2-5%).
 hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
   const int cs = fp4_chunk(a.hidden, 2);
   if (cs < 1 || a.hidden % 256 || a.inter % 256) return hipErrorInvalidValue;
   for (int64_t c0 = 0; c0 < a.t; c0 += cs) {
     const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
     const int64_t wgs2 = a.inter / (16 * MF_WAVES / 2) * tc * a.topk;
-    const hipError_t err = wgs2 >= (int64_t)ftk_num_cus() ? fp4_gate_up_kq<2>(a, (int)c0, tc, st)
-                                                               : fp4_gate_up_kq<4>(a, (int)c0, tc, st);
+    const bool k2 = wgs2 >= (int64_t)ftk_num_cus();
+    hipError_t err;
+    if (a.hidden % 512) err = k2 ? fp4_gate_up_kq<2, 0>(a, (int)c0, tc, st) : fp4_gate_up_kq<4, 0>(a, (int)c0, tc, st);
+    else if (tc == 1) err = k2 ? fp4_gate_up_kq<2, 2>(a, (int)c0, tc, st) : fp4_gate_up_kq<4, 2>(a, (int)c0, tc, st);
+    else err = k2 ? fp4_gate_up_kq<2, 1>(a, (int)c0, tc, st) : fp4_gate_up_kq<4, 1>(a, (int)c0, tc, st);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -623,7 +740,7 @@ hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st) {
     const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
     const dim3 grid((unsigned)(a.hidden / (16 * MF_WAVES / MF_KQ_DN)), (unsigned)(tc * a.topk));
     const size_t p0 = (size_t)c0 * a.topk;
-    hipLaunchKernelGGL(moe_fp4_down_kernel<MF_KQ_DN>, grid, dim3(MF_THREADS), fp4_lds(tc, a.inter, 1), st,
+hipLaunchKernelGGL(moe_fp4_down_kernel<MF_KQ_DN>, grid, dim3(MF_THREADS), fp4_lds(tc, a.inter, 1), st,
                        (const uint8_t*)a.w_down, a.n_expert, a.hidden, a.inter, a.h + p0 * a.inter,
                        a.in_hq ? (const uint8_t*)a.in_hq + p0 * hrb : nullptr,
                        a.hq_tap ? (uint8_t*)a.hq_tap + p0 * hrb : nullptr, tc, a.ids + p0, a.topk,
