@@ -554,6 +554,31 @@ __device__ __forceinline__ int q8_code(float v, float d) {
   return d == 0.0f ? 0 : q;
 }
 
+// The same codes for N elements of one scale, without a division per element.
+// While |v / d| < 128, t = v * rcp(d) is within 1.5 * 2^-16 of v / d (v_rcp_f32
+// within 1 ulp, then the product's rounding) and the correctly rounded quotient
+// within 2^-18 of it, so the two round to the same integer unless t lies within
+// 2^-14 of a half-integer; larger quotients clamp to 127 either way.  A lane with
+// such an element, or with a scale outside [2^-100, 2^100] (zero included), takes
+// q8_code's division for all N.  Away from half-integers round-half-even
+// (v_rndne) and round-half-away agree.
+template <int N>
+__device__ __forceinline__ void q8_codes(const float (&v)[N], float d, int (&q)[N]) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  bool slow = !(d >= 0x1p-100f && d <= 0x1p100f);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float t = v[j] * r;
+    slow |= fabsf(__builtin_amdgcn_fractf(t) - 0.5f) <= 0x1p-14f;
+    const int k = (int)__builtin_rintf(t);
+    q[j] = k > 127 ? 127 : (k < -127 ? -127 : k);
+  }
+  if (slow) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) q[j] = q8_code(v[j], d);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 64-lane reductions
 // ---------------------------------------------------------------------------
@@ -587,9 +612,11 @@ __device__ __forceinline__ void q8_1_part(const float (&v)[8], int l4, uint8_t* 
   const float d = h2f(dh);
   uint32_t w[2] = {0u, 0u};
   int s = 0;
+  int qc[8];
+  q8_codes<8>(v, d, qc);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int q = q8_code(v[j], d);
+    const int q = qc[j];
     s += q;
     w[j >> 2] |= ((uint32_t)(uint8_t)(int8_t)q) << (8 * (j & 3));
   }
@@ -620,9 +647,11 @@ __device__ __forceinline__ void q8_k_codes(const float (&v)[16], uint32_t (&w)[4
   s = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = 0u;
+  int qc[16];
+  q8_codes<16>(v, d, qc);
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int q = q8_code(v[j], d);
+    const int q = qc[j];
     s += q;
     w[j >> 2] |= ((uint32_t)(uint8_t)(int8_t)q) << (8 * (j & 3));
   }

@@ -208,9 +208,9 @@ struct Fp4Ring {
   static constexpr int STAGE = CPS * 1024;           // LDS bytes of one stage
   const uint8_t* p[CPS];                             // this lane's chunk of each load, at row offset 0
   uint8_t* ring;
-  int sb0, sb1, dir, n, issued;
+  int sb0, sb1, dir, n, issued, spare;
   __device__ __forceinline__ void init(const uint8_t* const (&grp)[NM], int64_t row_bytes, uint8_t* ring_, int sb0_,
-                                       int sb1_, int dir_) {
+                                       int sb1_, int dir_, int nsb) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
@@ -223,12 +223,14 @@ struct Fp4Ring {
     dir = dir_;
     n = sb1 - sb0;
     issued = 0;
+    spare = sb0 < nsb ? sb0 : nsb - 1;
   }
   __device__ __forceinline__ int sb_of(int it) const { return dir > 0 ? sb0 + it : sb1 - 1 - it; }
-  // the next superblock of the walk into its stage
+  // the next superblock of the walk into its stage (past the walk: a valid one, unused,
+  // so that the first RS stages can be issued unconditionally)
   template <int RS>
   __device__ __forceinline__ void issue() {
-    const int64_t win = (int64_t)(136 * sb_of(issued)) & ~(int64_t)15;
+    const int64_t win = (int64_t)(136 * (issued < n ? sb_of(issued) : spare)) & ~(int64_t)15;
     uint8_t* dst = ring + (issued % RS) * STAGE;
 #pragma unroll
     for (int c = 0; c < CPS; ++c) lds_dma16(p[c] + win, dst + 1024 * c);
@@ -323,23 +325,59 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   // waits for nothing after them)
   float raw[4];
   if (logits && wave < t_real) route_load<4>(logits + (int64_t)wave * n_expert, (int)n_expert, lane, raw);
-  // the first quantization item's x (it needs no expert id): requested before the ids
-  // and the weights, so that the quantization waits for neither
+  // the x of this thread's first two quantization items (they need no expert id):
+  // requested before the ids and the weights, so that the quantization waits for
+  // neither
   const int per_row = (int)(hidden / 16), total = t_real * per_row;
-  float xv0[16];
-  {
-    const int idx = tid < total ? tid : 0;
+  float xv[2][16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j == 1 && total <= MF_THREADS) break;   // (uniform; the wait before the quantization is explicit)
+    const int idx = min(tid + j * MF_THREADS, total - 1);
     const int r = idx / per_row, c = idx - r * per_row;
     const float4* p = (const float4*)(x + (int64_t)r * hidden) + 4 * c;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 f = p[q];
-      xv0[4 * q] = f.x;
-      xv0[4 * q + 1] = f.y;
-      xv0[4 * q + 2] = f.z;
-      xv0[4 * q + 3] = f.w;
+      xv[j][4 * q] = f.x;
+      xv[j][4 * q + 1] = f.y;
+      xv[j][4 * q + 2] = f.z;
+      xv[j][4 * q + 3] = f.w;
     }
   }
+  // x -> Q8_K codes -> FP8 halves in LDS (16 elements per thread, 16 lanes per block)
+  const int nsb = (int)(hidden / 256);
+  auto quantize = [&]() {
+    for (int idx0 = 0; idx0 < total; idx0 += MF_THREADS) {
+      const int idx = idx0 + tid;
+      if (idx < total) {   // the same for all 16 lanes of a block
+        const int r = idx / per_row, c = idx - r * per_row;
+        float v[16];
+        if (idx0 < 2 * MF_THREADS) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) v[q] = idx0 == 0 ? xv[0][q] : xv[1][q];
+        } else {
+          const float4* p = (const float4*)(x + (int64_t)r * hidden) + 4 * c;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 f = p[q];
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
+          }
+        }
+        uint32_t w[4];
+        int s;
+        float d;
+        q8_k_codes(v, w, s, d);
+        stage_codes(w, act + (int64_t)r * 2 * hidden, hidden, c >> 4, c & 15);
+        if ((c & 15) == 0) dx[(c >> 4) * 16 + r] = d;
+      }
+    }
+  };
+  for (int i = tid; i < nsb * 16; i += MF_THREADS) dx[i] = 0.0f;
+  lds_barrier();
   int e;
   uint32_t mask;
   uint64_t smask;
@@ -363,7 +401,7 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   }
 
   constexpr int RG = MF_WAVES / KQ;
-  const int nsb = (int)(hidden / 256), rg = wave / KQ, kq = wave % KQ, dir = (kq & 1) ? -1 : 1;
+  const int rg = wave / KQ, kq = wave % KQ, dir = (kq & 1) ? -1 : 1;
   const int64_t row = (int64_t)blockIdx.x * (16 * RG) + rg * 16 + (lane & 15);
   const int64_t row_bytes = hidden / 32 * 17;
   const uint32_t* const rowd[2] = {(const uint32_t*)(wg + ((int64_t)e * inter + row) * row_bytes),
@@ -375,44 +413,17 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
     const int64_t row0 = (int64_t)blockIdx.x * (16 * RG) + rg * 16;
     const uint8_t* const grp[2] = {wg + ((int64_t)e * inter + row0) * row_bytes, wu + ((int64_t)e * inter + row0) * row_bytes};
     const size_t roff = ((size_t)t_real * 2 * hidden + (size_t)nsb * 64 + 15) & ~(size_t)15;
-    ring.init(grp, row_bytes, (uint8_t*)smem4 + roff + (size_t)wave * RS * Fp4Ring<2>::STAGE, sb0, sb1, dir);
-    for (int j = 0; j < RS && j < ring.n; ++j) ring.template issue<RS>();
+    ring.init(grp, row_bytes, (uint8_t*)smem4 + roff + (size_t)wave * RS * Fp4Ring<2>::STAGE, sb0, sb1, dir, nsb);
+#pragma unroll
+    for (int j = 0; j < RS; ++j) ring.template issue<RS>();   // a fixed count: the compiler's waits stay exact
   } else {
     fp4_first<2>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
   }
-
-  // x -> Q8_K codes -> FP8 halves in LDS (16 elements per thread, 16 lanes per block),
-  // while the first superblock streams in
-  for (int i = tid; i < nsb * 16; i += MF_THREADS) dx[i] = 0.0f;
-  lds_barrier();   // (a barrier with a full fence would wait for the weight loads)
-  for (int idx0 = 0; idx0 < total; idx0 += MF_THREADS) {
-    const int idx = idx0 + tid;
-    if (idx < total) {   // the same for all 16 lanes of a block
-      const int r = idx / per_row, c = idx - r * per_row;
-      float v[16];
-      if (idx0 == 0) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) v[q] = xv0[q];
-      } else {
-        const float4* p = (const float4*)(x + (int64_t)r * hidden) + 4 * c;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 f = p[q];
-          v[4 * q] = f.x;
-          v[4 * q + 1] = f.y;
-          v[4 * q + 2] = f.z;
-          v[4 * q + 3] = f.w;
-        }
-      }
-      uint32_t w[4];
-      int s;
-      float d;
-      q8_k_codes(v, w, s, d);
-      stage_codes(w, act + (int64_t)r * 2 * hidden, hidden, c >> 4, c & 15);
-      if ((c & 15) == 0) dx[(c >> 4) * 16 + r] = d;
-    }
-  }
-  __syncthreads();
+  // quantize while the first superblocks stream in (quantizing before the weight
+  // requests, during the routing, measured slower at 1-2 tokens)
+  if constexpr (RS > 0) wait_vm<RS * Fp4Ring<2>::CPS>();   // x is in (loads complete in order)
+  quantize();
+  lds_barrier();   // the image is complete (a barrier with a full fence would wait for the weight loads)
 
   v4f acc[2];
   if constexpr (RS > 0) fp4_rows_ring<2, RS>(ring, act, hidden, t_real, 0xFFu, dx, acc);

@@ -73,10 +73,12 @@ quant_q8_0_kernel(const float* __restrict__ x, int64_t total_blocks, int64_t nb,
   const float d = h2f(dh);
   uint8_t* ob = xq + gb * 34;
   uint16_t* o = (uint16_t*)(ob + 2 + 8 * l4);
+  int qc[8];
+  q8_codes<8>(v, d, qc);
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
-    const uint32_t lo = (uint32_t)(uint8_t)(int8_t)q8_code(v[j], d);
-    const uint32_t hi = (uint32_t)(uint8_t)(int8_t)q8_code(v[j + 1], d);
+    const uint32_t lo = (uint32_t)(uint8_t)(int8_t)qc[j];
+    const uint32_t hi = (uint32_t)(uint8_t)(int8_t)qc[j + 1];
     o[j >> 1] = (uint16_t)(lo | (hi << 8));
   }
   if (l4 == 0) *(uint16_t*)ob = (uint16_t)(d == 0.0f ? 0u : dh);
