@@ -412,7 +412,7 @@ ft_status moe_run(ft_type w, const void* w_gate, const void* w_up, const void* w
   // itself, or reads in_hq), slot-order combine
   e = ftk_launch_moe_gate_up(a, st);
   if (e == hipSuccess && w == FT_MXFP4 && ftk_moe_fp4_down_combine_ok(a))
-    return hip_status(ftk_launch_moe_fp4_down_combine(a, st));   // one token: down + combine
+    return hip_status(ftk_launch_moe_fp4_down_combine(a, st));   // 1-2 tokens: down + combine
   if (e == hipSuccess) e = ftk_launch_moe_down(a, st);
   if (e == hipSuccess) e = ftk_launch_moe_combine(a, st);
   return hip_status(e);

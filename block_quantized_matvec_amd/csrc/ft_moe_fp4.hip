@@ -536,13 +536,15 @@ moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hi
   }
 }
 
-// One token: down and the weighted combine in one launch.  A workgroup owns 16
-// output rows for every slot: wave 2s + p takes slot s's expert over K part p (of
-// 2, odd parts walking downwards as above), so the slots' down values of a row
-// meet in LDS and are summed in slot order there (ft_moe_combine's arithmetic), and
-// no per-pair rows go out.  The prologue quantizes every slot's h row to Q8_K
-// (or takes in_hq) into FP8-half images, one per slot.  A slot repeating an earlier
-// slot's expert is computed again (same d, its own weight).
+// Down and the weighted combine in one launch.  Workgroup (x, i) owns 16 * R output
+// rows of token i for every slot of that token: wave 2s + p takes slot s's expert
+// over K part p (of 2, odd parts walking downwards as above) for its R row groups,
+// so the slots' down values of a row meet in LDS and are summed in slot order there
+// (ft_moe_combine's arithmetic), and no per-pair rows go out.  The prologue
+// quantizes the token's h rows, one per slot, to Q8_K (or takes in_hq) into
+// FP8-half images.  A slot repeating an earlier slot's expert, in this token or
+// another, is computed again (same d, its own weight): the tokens' workgroups are
+// independent.
 constexpr int MF_DC_WAVES = 16;   // 8 slots x 2 K parts
 // NW > 0: every superblock of a wave's K part (at most NW) is requested right after
 // the quantization, all at once, and each superblock's dot waits only for its own
@@ -550,7 +552,7 @@ constexpr int MF_DC_WAVES = 16;   // 8 slots x 2 K parts
 // before the quantization, the loads of the whole layer's down matrices held up
 // the quantization behind their issue; one superblock of lookahead (NW = 0, longer
 // K parts) pays a full memory latency per superblock.
-template <int NW>
+template <int NW, int R>
 __global__ void __launch_bounds__(64 * MF_DC_WAVES)
 moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int64_t inter,
                             const float* __restrict__ h, const uint8_t* __restrict__ in_hq,
@@ -561,19 +563,22 @@ moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, in
   const int nsb = (int)(inter / 256);
   uint8_t* act = (uint8_t*)smem4;                               // [8][2 * inter]
   float* dx = (float*)(act + (size_t)8 * 2 * inter);            // [8][nsb][16]
-  float* s_d = dx + (size_t)8 * nsb * 16;                       // [8][16]
+  float* s_d = dx + (size_t)8 * nsb * 16;                       // [8][16 * R]
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int s = wave >> 1, kq = wave & 1, dir = kq ? -1 : 1;
   const int hrb = nsb * 292;
+  const int64_t p0 = (int64_t)blockIdx.y * topk;                // the token's first pair
   const bool live = s < topk;
   // NW > 0: slots past topk read slot 0's rows (unused), so that every wave issues the same loads
-  const int e = live ? clamp_id(ids[s], n_expert) : (NW > 0 ? clamp_id(ids[0], n_expert) : 0);
-  const int64_t row = (int64_t)blockIdx.x * 16 + (lane & 15);
+  const int e = live ? clamp_id(ids[p0 + s], n_expert) : (NW > 0 ? clamp_id(ids[p0], n_expert) : 0);
+  const int64_t row = (int64_t)blockIdx.x * (16 * R) + (lane & 15);   // + 16 r for row group r
   const int64_t row_bytes = inter / 32 * 17;
-  const uint32_t* const rowd[1] = {(const uint32_t*)(wd + ((int64_t)e * hidden + row) * row_bytes)};
   const int sb0 = kq * nsb / 2, sb1 = (kq + 1) * nsb / 2, n = sb1 - sb0;
-  Fp4Blk nx[1][2];
-  if (NW == 0 && live) fp4_first<1>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);   // slots past topk stream nothing
+  const uint32_t* rowd[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rowd[r] = (const uint32_t*)(wd + ((int64_t)e * hidden + row + 16 * r) * row_bytes);
+  Fp4Blk nx[R][2];
+  if (NW == 0 && live) fp4_first<R>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);   // slots past topk stream nothing
 
   // every slot's h row -> Q8_K codes -> FP8 halves (16 elements per thread)
   for (int i = tid; i < 8 * nsb * 16; i += 64 * MF_DC_WAVES) dx[i] = 0.0f;
@@ -585,14 +590,14 @@ moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, in
     int sm;
     float d;
     if (in_hq) {
-      const uint8_t* blk = in_hq + (int64_t)j * hrb + (int64_t)sb * 292;
+      const uint8_t* blk = in_hq + (p0 + j) * hrb + (int64_t)sb * 292;
       const uint32_t* q = (const uint32_t*)(blk + 4 + 16 * l16);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) w[jj] = q[jj];
       d = *(const float*)blk;
       sm = *(const int16_t*)(blk + 260 + 2 * l16);
     } else {
-      const float4* p = (const float4*)(h + (int64_t)j * inter) + 4 * c;
+      const float4* p = (const float4*)(h + (p0 + j) * inter) + 4 * c;
       float v[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -606,47 +611,55 @@ moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, in
     }
     stage_codes(w, act + (int64_t)j * 2 * inter, inter, sb, l16);
     if (l16 == 0) dx[(j * nsb + sb) * 16] = d;
-    if (hq_tap && blockIdx.x == 0) q8_k_store(w, sm, d, l16, hq_tap + (int64_t)j * hrb + sb * 292);
+    if (hq_tap && blockIdx.x == 0) q8_k_store(w, sm, d, l16, hq_tap + (p0 + j) * hrb + sb * 292);
   }
-  Fp4Blk wb[NW > 0 ? NW : 1][1][2];
+  Fp4Blk wb[NW > 0 ? NW : 1][R][2];
   if constexpr (NW > 0) {
 #pragma unroll
     for (int j = 0; j < NW; ++j) {   // superblock j in walk order (past the part: a valid one, unused)
       int sb = dir > 0 ? sb0 + j : sb1 - 1 - j;
       sb = sb < 0 ? 0 : (sb < nsb ? sb : nsb - 1);
-      fp4_fetch(rowd[0], 2 * sb, lane >> 4, wb[j][0][0]);
-      fp4_fetch(rowd[0], 2 * sb + 1, lane >> 4, wb[j][0][1]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        fp4_fetch(rowd[r], 2 * sb, lane >> 4, wb[j][r][0]);
+        fp4_fetch(rowd[r], 2 * sb + 1, lane >> 4, wb[j][r][1]);
+      }
     }
     lds_barrier();   // (a barrier with a full fence would wait for those loads)
   } else {
     __syncthreads();
   }
 
-  v4f acc[1] = {{0.0f, 0.0f, 0.0f, 0.0f}};
+  v4f acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (NW > 0) {
     const int tok = lane & 15;
     const uint8_t* ap = act + (size_t)s * 2 * inter + (int64_t)tok * 2 * inter + 16 * (lane >> 4);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       if (live && j < n)
-        fp4_sb<1>(wb[j], dir > 0 ? sb0 + j : sb1 - 1 - j, ap, inter, tok == 0, dx + (size_t)s * nsb * 16, acc);
+        fp4_sb<R>(wb[j], dir > 0 ? sb0 + j : sb1 - 1 - j, ap, inter, tok == 0, dx + (size_t)s * nsb * 16, acc);
     }
   } else {
-    if (live) fp4_rows<1>(rowd, sb0, sb1, dir, nx, act + (size_t)s * 2 * inter, inter, 1, 1u, dx + (size_t)s * nsb * 16, acc);
+    if (live) fp4_rows<R>(rowd, sb0, sb1, dir, nx, act + (size_t)s * 2 * inter, inter, 1, 1u, dx + (size_t)s * nsb * 16, acc);
   }
   __syncthreads();   // the images are dead: the K-part sums reuse their LDS
-  if (fp4_reduce<1, 2>(acc, (float*)smem4)) {
-    // part-0 wave of slot s: lanes 0..15 hold row (lane & 15) of token 0
+  if (fp4_reduce<R, 2>(acc, (float*)smem4)) {
+    // part-0 wave of slot s: lanes 0..15 hold row (lane & 15) of each row group
     if (live && lane < 16) {
-      s_d[s * 16 + lane] = acc[0][0];
-      if (d_tap) d_tap[(int64_t)s * hidden + row] = acc[0][0];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        s_d[s * 16 * R + 16 * r + lane] = acc[r][0];
+        if (d_tap) d_tap[(p0 + s) * hidden + row + 16 * r] = acc[r][0];
+      }
     }
   }
   __syncthreads();
-  if (tid < 16) {
+  if (tid < 16 * R) {
     float sum = 0.0f;
-    for (int k = 0; k < topk; ++k) sum = fmaf(ew[k], s_d[k * 16 + tid], sum);
-    y[(int64_t)blockIdx.x * 16 + tid] = sum;
+    for (int k = 0; k < topk; ++k) sum = fmaf(ew[p0 + k], s_d[k * 16 * R + tid], sum);
+    y[(int64_t)blockIdx.y * hidden + (int64_t)blockIdx.x * 16 * R + tid] = sum;
   }
 }
 
@@ -722,25 +735,38 @@ hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
   return hipSuccess;
 }
 
-// one token, top-k <= 8: down + combine in one launch (hidden a multiple of 16)
+// down + combine in one launch at 1-2 tokens (top-k <= 8): workgroup (x, i) takes
+// 16 * R rows of token i, R = 1 at one token (a workgroup per CU), 2 at two (the
+// quantization of a token's h rows shared by twice the rows; 256 workgroups
+// again).  Against the per-expert down launch and the combine launch: 2 tokens
+// 68.1-68.6 -> 64.0-64.3 us per layer; 3, 5 and 8 tokens (1.5, 2.5 and 4 rounds
+// of workgroups) were 3-8 us slower and 4 tokens even, so from 3 tokens the layer
+// keeps the two launches.
+constexpr int MF_DC_MAXT = 2;
+static size_t fp4_dc_lds(int64_t inter, int r) {
+  const size_t img = (size_t)8 * 2 * inter + (size_t)8 * (inter / 256) * 16 * 4 + (size_t)8 * 16 * r * 4;
+  const size_t red = (size_t)MF_DC_WAVES * 64 * r * 4 * 4;
+  return img > red ? img : red;
+}
 bool ftk_moe_fp4_down_combine_ok(const MoeArgs& a) {
-  return a.t == 1 && a.topk <= 8 && a.hidden % 16 == 0 && a.inter % 256 == 0 &&
-         (size_t)8 * 2 * a.inter + (size_t)8 * (a.inter / 256) * 16 * 4 + 8 * 16 * 4 <= 65536;
+  const int r = a.t == 1 ? 1 : 2;
+  return a.t >= 1 && a.t <= MF_DC_MAXT && a.topk <= 8 && a.hidden % (16 * r) == 0 && a.inter % 256 == 0 &&
+         fp4_dc_lds(a.inter, r) <= 65536;
+}
+template <int R>
+static hipError_t fp4_down_combine_r(const MoeArgs& a, hipStream_t st) {
+  const int nw = (int)(a.inter / 256 + 1) / 2;   // superblocks of a wave's K part, at most
+  auto kern = nw == 0 ? moe_fp4_down_combine_kernel<0, R> : nw <= 1 ? moe_fp4_down_combine_kernel<1, R>
+            : nw <= 2 ? moe_fp4_down_combine_kernel<2, R> : nw <= 4 ? moe_fp4_down_combine_kernel<4, R>
+            : moe_fp4_down_combine_kernel<0, R>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.hidden / (16 * R)), (unsigned)a.t), dim3(64 * MF_DC_WAVES),
+                     fp4_dc_lds(a.inter, R), st, (const uint8_t*)a.w_down, a.n_expert, a.hidden, a.inter, a.h,
+                     (const uint8_t*)a.in_hq, (uint8_t*)a.hq_tap, a.ids, a.ew, a.topk, a.d_tap, a.y);
+  return hipGetLastError();
 }
 hipError_t ftk_launch_moe_fp4_down_combine(const MoeArgs& a, hipStream_t st) {
   if (!ftk_moe_fp4_down_combine_ok(a)) return hipErrorInvalidValue;
-  const size_t img = (size_t)8 * 2 * a.inter + (size_t)8 * (a.inter / 256) * 16 * 4 + 8 * 16 * 4;
-  const size_t red = (size_t)MF_DC_WAVES * 64 * 4 * 4;
-  const int64_t hrb = a.inter / 256 * 292;
-  (void)hrb;
-  const int nw = (int)(a.inter / 256 + 1) / 2;   // superblocks of a wave's K part, at most
-  auto kern = nw == 0 ? moe_fp4_down_combine_kernel<0> : nw <= 1 ? moe_fp4_down_combine_kernel<1>
-            : nw <= 2 ? moe_fp4_down_combine_kernel<2> : nw <= 4 ? moe_fp4_down_combine_kernel<4>
-            : moe_fp4_down_combine_kernel<0>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.hidden / 16)), dim3(64 * MF_DC_WAVES),
-                     img > red ? img : red, st, (const uint8_t*)a.w_down, a.n_expert, a.hidden, a.inter, a.h,
-                     (const uint8_t*)a.in_hq, (uint8_t*)a.hq_tap, a.ids, a.ew, a.topk, a.d_tap, a.y);
-  return hipGetLastError();
+  return a.t == 1 ? fp4_down_combine_r<1>(a, st) : fp4_down_combine_r<2>(a, st);
 }
 
 hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st) {

@@ -194,8 +194,9 @@ typedef struct {
    4-token chunk (routing from the logits, x quantize, gate/up + SwiGLU, h quantize;
    then down and the slot-order combine), otherwise one workgroup per selected
    expert and row tile per stage, then a combine; for (MXFP4, Q8_K) the gate/up
-   launch routes 1-2 tokens from the logits itself, and at 1 token down and the
-   combine are one launch;
+   launch routes 1-2 tokens from the logits itself, and at 1-2 tokens down and the
+   combine are one launch whose workgroups each take one token's rows (an expert
+   both tokens picked is read once per token there);
    sorted tiles = token->expert sort, one fused gate/up + SwiGLU grouped MFMA GEMM,
    h quantize, grouped down GEMM, slot-order combine.  Both give the same result
    up to fp32 rounding order. */

@@ -187,7 +187,8 @@ def test_moe_repeated_expert_in_token(name, t, route):
 
 
 @pytest.mark.parametrize("name,t,route", [("q4k", 1, 1), ("q4k", 4, 1), ("mxfp4", 3, 1), ("mxfp4", 5, 2),
-                                          ("mxfp4_small", 6, 2), ("mxfp4", 1, 1), ("mxfp4_small", 1, 1)])
+                                          ("mxfp4_small", 6, 2), ("mxfp4", 1, 1), ("mxfp4_small", 1, 1),
+                                          ("mxfp4", 2, 1), ("mxfp4_small", 2, 1)])
 def test_moe_down_from_given_hq(name, t, route):
     """The down stage and the combine alone: the quantized h rows come from the
     oracle (in_hq), so the check does not depend on the GPU's gate/up."""

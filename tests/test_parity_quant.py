@@ -58,6 +58,32 @@ def test_quantize_edge_values(act):
     assert np.array_equal(got, oracle.quantize(act, x))
 
 
+@pytest.mark.parametrize("act", ["Q8_1", "Q8_K", "Q8_0"])
+def test_quantize_near_half_integers(act):
+    """Quotients v / d within a few ulps of a half-integer, on both sides, for scales
+    that are not powers of two: the quantizers take the code from a reciprocal
+    product and fall back to the division near half-integers, so these are the
+    elements where the two could part; every code must equal the oracle's."""
+    be = synth.BLOCK[act][0]
+    g = synth.rng(103)
+    blocks = []
+    for amax in (100.0, 3.3, 0.0123, 7770.0, 1.0 / 3.0):
+        d32 = np.float32(amax) / np.float32(127.0)
+        d = np.float32(np.float16(d32)) if act in ("Q8_1", "Q8_0") else d32
+        for _ in range(6):
+            k = g.integers(-127, 127, be)
+            v = (k.astype(np.float32) + np.float32(0.5)) * d
+            for i, steps in enumerate(g.integers(-4, 5, be)):
+                for _ in range(abs(int(steps))):
+                    v[i] = np.nextafter(v[i], np.float32(np.inf if steps > 0 else -np.inf), dtype=np.float32)
+            v = np.clip(v, -np.float32(amax), np.float32(amax)).astype(np.float32)
+            v[0] = np.float32(amax)
+            blocks.append(v)
+    x = np.stack(blocks).astype(np.float32)
+    got = host(ft.quantize_act(act, dev(x)))
+    assert np.array_equal(got, oracle.quantize(act, x))
+
+
 @pytest.mark.parametrize("fmt", synth.WEIGHT_FORMATS)
 @pytest.mark.parametrize("rows,k", [(1, 256), (7, 512), (33, 1536)])
 def test_dequant_bit_exact(fmt, rows, k):
