@@ -347,11 +347,14 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   }
   // x -> Q8_K codes -> FP8 halves in LDS (16 elements per thread, 16 lanes per block)
   const int nsb = (int)(hidden / 256);
-  auto quantize = [&]() {
+  // Only the tokens of tm (the expert's), compacted in token order: row j of the
+  // image and of the MFMA's A operand is the j-th token of tm.
+  auto quantize = [&](uint32_t tm) {
     for (int idx0 = 0; idx0 < total; idx0 += MF_THREADS) {
       const int idx = idx0 + tid;
-      if (idx < total) {   // the same for all 16 lanes of a block
-        const int r = idx / per_row, c = idx - r * per_row;
+      const int r = idx / per_row, c = idx - r * per_row;
+      if (idx < total && ((tm >> r) & 1)) {   // the same for all 16 lanes of a block
+        const int jr = __popc(tm & ((1u << r) - 1));
         float v[16];
         if (idx0 < 2 * MF_THREADS) {
 #pragma unroll
@@ -371,8 +374,8 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
         int s;
         float d;
         q8_k_codes(v, w, s, d);
-        stage_codes(w, act + (int64_t)r * 2 * hidden, hidden, c >> 4, c & 15);
-        if ((c & 15) == 0) dx[(c >> 4) * 16 + r] = d;
+        stage_codes(w, act + (int64_t)jr * 2 * hidden, hidden, c >> 4, c & 15);
+        if ((c & 15) == 0) dx[(c >> 4) * 16 + jr] = d;
       }
     }
   };
@@ -422,20 +425,22 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
   // quantize while the first superblocks stream in (quantizing before the weight
   // requests, during the routing, measured slower at 1-2 tokens)
   if constexpr (RS > 0) wait_vm<RS * Fp4Ring<2>::CPS>();   // x is in (loads complete in order)
-  quantize();
+  quantize(mask);
+  const int ntok = __popc(mask);
   lds_barrier();   // the image is complete (a barrier with a full fence would wait for the weight loads)
 
   v4f acc[2];
-  if constexpr (RS > 0) fp4_rows_ring<2, RS>(ring, act, hidden, t_real, 0xFFu, dx, acc);
-  else fp4_rows<2>(rowd, sb0, sb1, dir, nx, act, hidden, t_real, 0xFFu, dx, acc);
+  if constexpr (RS > 0) fp4_rows_ring<2, RS>(ring, act, hidden, ntok, 0xFFu, dx, acc);
+  else fp4_rows<2>(rowd, sb0, sb1, dir, nx, act, hidden, ntok, 0xFFu, dx, acc);
   __syncthreads();   // the activation image is dead: the reduction reuses its LDS
   if (!fp4_reduce<2, KQ>(acc, (float*)smem4)) return;
 
   const int b = lane >> 4;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int i = 4 * b + r;
-    if (i < t_real && ((mask >> i) & 1)) {
+    const int j = 4 * b + r;   // compacted row -> the token
+    if (j < ntok) {
+      const int i = nth_bit(mask, j);
       const float g = acc[0][r], u = acc[1][r], hv = g / (1.0f + expf(-g)) * u;
       for (int k = 0; k < topk; ++k) {
         if ((smask >> (8 * i + k)) & 1) {
