@@ -202,6 +202,12 @@ __device__ __forceinline__ void fp4_rows(const uint32_t* const (&rowd)[NM], int 
 // bank groups (9 is odd).  Lane (r, b) reads its 17-byte block of k-step st as the
 // two slots from 4st + b (the block starts at dword 2P + st of them, P = the
 // superblock's parity), i.e. the same five dwords the direct fetch takes.
+// The ring's loads keep the default cache policy (lds_dma16_cached): two
+// neighbouring superblock windows of a row share a 16-byte chunk (the 9-chunk
+// windows overlap), and with the streaming (nt) hint that line was fetched again
+// for the second window (the launch fetched 1.36x its weight bytes; cached, 1.02x:
+// 1 token 35.6 -> 33.5 us, 2 tokens 63.6-64.1 -> 56.3-56.7 us, 4 tokens
+// 122.8-124.1 -> 105.5-106 us).
 template <int NM>
 struct Fp4Ring {
   static constexpr int CPS = (NM * 144 + 63) / 64;   // DMA loads per wave and stage
@@ -233,7 +239,7 @@ struct Fp4Ring {
     const int64_t win = (int64_t)(136 * (issued < n ? sb_of(issued) : spare)) & ~(int64_t)15;
     uint8_t* dst = ring + (issued % RS) * STAGE;
 #pragma unroll
-    for (int c = 0; c < CPS; ++c) lds_dma16(p[c] + win, dst + 1024 * c);
+    for (int c = 0; c < CPS; ++c) lds_dma16_cached(p[c] + win, dst + 1024 * c);
     ++issued;
   }
 };

@@ -117,14 +117,15 @@ __device__ __forceinline__ FuLds fu_lds(int xbytes, int wave, int sb) {
 
 // One ring stage: `nbytes` (<= CPW KiB) from src (16-byte aligned) into dst, CPW
 // 16-byte loads per lane (lanes past the end re-read the last chunk), so every
-// stage is exactly CPW loads of this wave.
+// stage is exactly CPW loads of this wave.  Default cache policy: against the
+// streaming hint the layer measured 0.1-0.4 us shorter at 1 and 3 tokens.
 template <int CPW>
 __device__ __forceinline__ void fu_issue(const uint8_t* src, int nbytes, uint8_t* dst, int lane) {
   const int nch = (nbytes + 15) >> 4;
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int ch = lane + 64 * c < nch ? lane + 64 * c : nch - 1;
-    lds_dma16(src + 16 * ch, dst + 1024 * c);
+    lds_dma16_cached(src + 16 * ch, dst + 1024 * c);
   }
 }
 
@@ -445,7 +446,7 @@ moe_q4k_down_kernel(FusedArgs a) {
   const uint8_t* hsrc = a.in_hq ? a.in_hq : a.hq;
   const int nq = npairs * hrb / 16;
   for (int c = wave; c * 64 < nq; c += FU_WAVES)
-    if (c * 64 + lane < nq) lds_dma16(hsrc + 16 * (c * 64 + lane), L.xreg + 1024 * c);
+    if (c * 64 + lane < nq) lds_dma16_cached(hsrc + 16 * (c * 64 + lane), L.xreg + 1024 * c);
 
   const int nrb = (int)((H + GB - 1) / GB);
   const int my_rb = (int)blockIdx.x < nrb ? (nrb - (int)blockIdx.x + P - 1) / P : 0;
