@@ -464,7 +464,7 @@ moe_fp4_gate_up_kernel(const uint8_t* __restrict__ wg, const uint8_t* __restrict
 // every slot naming it.  hhat of the expert's tokens is quantized here from the
 // first slot's h row (or taken from in_hq); the workgroup of row block 0 writes
 // the Q8_K blocks to hq_tap for every slot naming the expert.
-template <int KQ>
+template <int KQ, int RS>
 __global__ void __launch_bounds__(MF_THREADS)
 moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hidden, int64_t inter,
                     const float* __restrict__ h, const uint8_t* __restrict__ in_hq, uint8_t* __restrict__ hq_tap,
@@ -485,7 +485,17 @@ moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hi
   const uint32_t* const rowd[1] = {(const uint32_t*)(wd + ((int64_t)e * hidden + row) * row_bytes)};
   const int sb0 = kq * nsb / KQ, sb1 = (kq + 1) * nsb / KQ;
   Fp4Blk nx[1][2];
-  fp4_first<1>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
+  Fp4Ring<1> ring;
+  if constexpr (RS > 0) {   // the wave's ring follows the activation images and scales
+    const int64_t row0 = (int64_t)blockIdx.x * (16 * RG) + rg * 16;
+    const uint8_t* const grp[1] = {wd + ((int64_t)e * hidden + row0) * row_bytes};
+    const size_t roff = ((size_t)t_real * 2 * inter + (size_t)nsb * 64 + 15) & ~(size_t)15;
+    ring.init(grp, row_bytes, (uint8_t*)smem4 + roff + (size_t)wave * RS * Fp4Ring<1>::STAGE, sb0, sb1, dir, nsb);
+#pragma unroll
+    for (int j = 0; j < RS; ++j) ring.template issue<RS>();
+  } else {
+    fp4_first<1>(rowd, dir > 0 ? sb0 : sb1 - 1, nsb, nx);
+  }
   const int hrb = nsb * 292;
   auto first_pair = [&](int i) { return i * topk + __ffs((unsigned)(smask >> (8 * i)) & 0xFFu) - 1; };
   const bool tap = hq_tap && blockIdx.x == 0;
@@ -532,7 +542,8 @@ moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hi
   __syncthreads();
 
   v4f acc[1];
-  fp4_rows<1>(rowd, sb0, sb1, dir, nx, act, inter, t_real, mask, dx, acc);
+  if constexpr (RS > 0) fp4_rows_ring<1, RS>(ring, act, inter, t_real, mask, dx, acc);
+  else fp4_rows<1>(rowd, sb0, sb1, dir, nx, act, inter, t_real, mask, dx, acc);
   __syncthreads();
   if (!fp4_reduce<1, KQ>(acc, (float*)smem4)) return;
 
@@ -788,7 +799,22 @@ hipError_t ftk_launch_moe_fp4_down(const MoeArgs& a, hipStream_t st) {
     const int tc = (int)(a.t - c0 < cs ? a.t - c0 : cs);
     const dim3 grid((unsigned)(a.hidden / (16 * MF_WAVES / MF_KQ_DN)), (unsigned)(tc * a.topk));
     const size_t p0 = (size_t)c0 * a.topk;
-hipLaunchKernelGGL(moe_fp4_down_kernel<MF_KQ_DN>, grid, dim3(MF_THREADS), fp4_lds(tc, a.inter, 1), st,
+    // K walk on the LDS ring (one stage per wave, cached loads) up to 5 tokens:
+    // 3 / 4 / 5 tokens 87.1-88.7 / 107.7-107.8 / 130.0-130.3 -> 86.1-86.4 /
+    // 104.9-105.7 / 128.5-128.6 us per layer; at 8 tokens its LDS halves the
+    // workgroups per CU (191 -> 197 us), and two stages were slower throughout
+    size_t lds = fp4_lds(tc, a.inter, 1);
+    const bool ring = a.inter % 512 == 0 && tc <= 5;
+    if (ring) {
+      const size_t r = (((size_t)tc * 2 * a.inter + (size_t)(a.inter / 256) * 64 + 15) & ~(size_t)15) +
+                       (size_t)MF_WAVES * Fp4Ring<1>::STAGE;
+      lds = r > lds ? r : lds;
+      static const bool attr = hipFuncSetAttribute((const void*)moe_fp4_down_kernel<MF_KQ_DN, 1>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, 159 * 1024) == hipSuccess;
+      if (!attr || lds > 159 * 1024) return hipErrorInvalidConfiguration;
+    }
+    auto kern = ring ? moe_fp4_down_kernel<MF_KQ_DN, 1> : moe_fp4_down_kernel<MF_KQ_DN, 0>;
+    hipLaunchKernelGGL(kern, grid, dim3(MF_THREADS), lds, st,
                        (const uint8_t*)a.w_down, a.n_expert, a.hidden, a.inter, a.h + p0 * a.inter,
                        a.in_hq ? (const uint8_t*)a.in_hq + p0 * hrb : nullptr,
                        a.hq_tap ? (uint8_t*)a.hq_tap + p0 * hrb : nullptr, tc, a.ids + p0, a.topk,
