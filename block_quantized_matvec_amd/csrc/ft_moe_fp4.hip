@@ -568,6 +568,13 @@ moe_fp4_down_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, int64_t hi
 // another, is computed again (same d, its own weight): the tokens' workgroups are
 // independent.
 constexpr int MF_DC_WAVES = 16;   // 8 slots x 2 K parts
+// byte offset of the down + combine launch's s_d: past the images and scales and
+// past fp4_reduce's K-part sums
+__host__ __device__ inline size_t fp4_dc_sd_off(int64_t inter, int r) {
+  const size_t img = (size_t)8 * 2 * inter + (size_t)8 * (inter / 256) * 16 * 4;
+  const size_t red = (size_t)MF_DC_WAVES * 64 * r * 4 * 4;
+  return img > red ? img : red;
+}
 // NW > 0: every superblock of a wave's K part (at most NW) is requested right after
 // the quantization, all at once, and each superblock's dot waits only for its own
 // loads (loads complete in order; every wave issues the same loads).  Requested
@@ -585,7 +592,9 @@ moe_fp4_down_combine_kernel(const uint8_t* __restrict__ wd, int64_t n_expert, in
   const int nsb = (int)(inter / 256);
   uint8_t* act = (uint8_t*)smem4;                               // [8][2 * inter]
   float* dx = (float*)(act + (size_t)8 * 2 * inter);            // [8][nsb][16]
-  float* s_d = dx + (size_t)8 * nsb * 16;                       // [8][16 * R]
+  // s_d [8][16 * R] past both the images and the K-part sums (fp4_reduce's area from
+  // offset 0): a part-0 wave writes it while others still read their partners' sums
+  float* s_d = (float*)smem4 + fp4_dc_sd_off(inter, R) / 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int s = wave >> 1, kq = wave & 1, dir = kq ? -1 : 1;
   const int hrb = nsb * 292;
@@ -765,11 +774,7 @@ hipError_t ftk_launch_moe_fp4_gate_up(const MoeArgs& a, hipStream_t st) {
 // of workgroups) were 3-8 us slower and 4 tokens even, so from 3 tokens the layer
 // keeps the two launches.
 constexpr int MF_DC_MAXT = 2;
-static size_t fp4_dc_lds(int64_t inter, int r) {
-  const size_t img = (size_t)8 * 2 * inter + (size_t)8 * (inter / 256) * 16 * 4 + (size_t)8 * 16 * r * 4;
-  const size_t red = (size_t)MF_DC_WAVES * 64 * r * 4 * 4;
-  return img > red ? img : red;
-}
+static size_t fp4_dc_lds(int64_t inter, int r) { return fp4_dc_sd_off(inter, r) + (size_t)8 * 16 * r * 4; }
 bool ftk_moe_fp4_down_combine_ok(const MoeArgs& a) {
   const int r = a.t == 1 ? 1 : 2;
   return a.t >= 1 && a.t <= MF_DC_MAXT && a.topk <= 8 && a.hidden % (16 * r) == 0 && a.inter % 256 == 0 &&
