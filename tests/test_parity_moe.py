@@ -97,6 +97,9 @@ CASES = {
     "q6k_c4": dict(w="Q6_K", a="Q8_K", hidden=4096, inter=1536, E=128, topk=8),
     # one superblock per row: K parts with no superblock, four experts on one router lane
     "mxfp4_tiny": dict(w="MXFP4", a="Q8_K", hidden=256, inter=256, E=4, topk=2),
+    # 6 superblocks per row: the LDS-ring walks' K parts hold 3 (the upper part starts
+    # at an odd superblock and walks down through both parities)
+    "mxfp4_mid": dict(w="MXFP4", a="Q8_K", hidden=1536, inter=1536, E=16, topk=4),
 }
 
 _banks = {}
@@ -228,6 +231,16 @@ def test_moe_q4k_layer(t):
 def test_moe_mxfp4_direct(t):
     log(f"moe mxfp4 t={t}")
     _run_stages("mxfp4", t, route=1)
+
+
+@pytest.mark.parametrize("t,from_logits", [(1, True), (2, True), (3, False), (5, False), (8, False)])
+def test_moe_mxfp4_direct_odd_parts(t, from_logits):
+    """The direct route's LDS-ring K walks with 3 superblocks per K part (hidden and
+    inter 1536): odd parts start on an odd superblock; 1-2 tokens routed inside the
+    gate/up launch with down and combine in one launch, 3-5 tokens on the per-expert
+    down ring, 8 without it."""
+    log(f"moe mxfp4_mid t={t} logits={from_logits}")
+    _run_stages("mxfp4_mid", t, route=1, from_logits=from_logits)
 
 
 @pytest.mark.parametrize("t", [1, 3, 5, 9, 40])
