@@ -503,6 +503,306 @@ grouped_mfma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W
   }
 }
 
+// 4 bytes per lane by direct-to-LDS load, default cache policy (the pairs' Q8_K d)
+__device__ __forceinline__ void lds_dma4_cached(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// The K-quant kernel with every operand staged by direct-to-LDS loads.  Same
+// contraction as above; what differs is the staging:
+//  * two LDS stages, one barrier per superblock: superblock sb+1 of the weights
+//    and activations is in flight (global_load_lds) while sb is computed, and no
+//    VGPR holds staged data;
+//  * each pair's Q8_K superblock lands as stored (codes, group sums, d) in a
+//    304-byte slot from the 16-byte boundary at or below its start, so a lane
+//    reads its A operand at the superblock's offset in the slot; the min / offset
+//    term takes the format's 16-element group sums as stored (exact in fp16);
+//    wave 0 also moves the pairs' d into a dense array;
+//  * the occupied pair tiles of a pass run interleaved (one code path per tile
+//    count), so the MFMAs of different tiles hide each other's latency.
+// Two stages of 37 KB (Q5_K, 3 tiles) keep two workgroups per CU.
+// ---------------------------------------------------------------------------
+template <int F, int PT, int RG> struct GDLds {
+  static constexpr int XS = 304;                                     // one 292-byte Q8_K superblock, 16-byte aligned down
+  static constexpr int WT = 0;                                       // [waves][16*RG rows][SLOT]
+  static constexpr int X = WT + GM_WAVES * 16 * RG * GSb<F>::SLOT;   // [PT*16 pairs][XS]
+  static constexpr int DX = X + PT * 16 * XS;                        // [PT*16] fp32 d
+  static constexpr int STAGE = DX + PT * 64;
+  static constexpr int ZERO = 2 * STAGE;                             // Q6_K: 256 zero bytes (half masks)
+  static constexpr int TOTAL = ZERO + (F == FT_Q6_K ? 256 : 0);
+  static_assert(STAGE % 16 == 0, "");
+};
+
+template <int N> struct GIc { static constexpr int value = N; };
+
+template <int F, int PT, bool GLU>
+__global__ void __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+grouped_dma_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ W2, int64_t n, int64_t row_bytes,
+                   int nsb, const uint8_t* __restrict__ xq, int64_t xrow_bytes, int x_per_pair, int topk,
+                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
+                   float* __restrict__ y, float* __restrict__ g_tap, float* __restrict__ u_tap,
+                   int64_t row_tiles, int64_t total, int64_t per_xcd) {
+  using SB = GSb<F>;
+  constexpr int RG = GRg<F, GLU>::RG;
+  using LY = GDLds<F, PT, RG>;
+  constexpr int NCH = SB::SLOT / 16;                   // 16-byte chunks per weight slot
+  static_assert(!GLU || RG == 2, "the fused gate/up form takes two row groups");
+  static_assert(F == FT_Q4_K || F == FT_Q5_K || F == FT_Q6_K, "K-quant weights");
+  constexpr int WROWS = 16 * RG;
+  constexpr int OROWS = GLU ? 16 : WROWS;
+  constexpr int NWI = (WROWS * NCH + 63) / 64;         // weight chunks per lane
+  constexpr int XCH = LY::XS / 16;                     // 16-byte chunks per activation slot
+  constexpr int NXI = (PT * 16 * XCH + GM_THREADS - 1) / GM_THREADS;   // activation chunks per lane
+  constexpr bool KQ = F == FT_Q4_K || F == FT_Q5_K;
+  extern __shared__ u32x4 gsm[];
+  uint8_t* L = (uint8_t*)gsm;
+
+  const int64_t bid = blockIdx.x;
+  const int64_t item = (bid & 7) * per_xcd + (bid >> 3);
+  if (item >= total) return;
+  const int e = (int)(item / row_tiles);
+  const int64_t tile = item % row_tiles;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  if (p0 >= p1) return;
+
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int q = lane >> 4, rl = lane & 15;
+  const int64_t wrow0 = tile * (OROWS * GM_WAVES) + (int64_t)wave * OROWS;
+  const uint8_t* wexp = W + (int64_t)e * n * row_bytes;
+  const uint8_t* wexp2 = GLU ? W2 + (int64_t)e * n * row_bytes : wexp;
+  auto slot_src = [&](int r) { return (GLU && r >= 16) ? wexp2 : wexp; };
+  auto slot_row = [&](int r) { return wrow0 + (GLU ? (r & 15) : r); };
+  const int wslot = LY::WT + wave * WROWS * SB::SLOT;
+  const v4f zf = {0.0f, 0.0f, 0.0f, 0.0f};
+  const v4i zi = {0, 0, 0, 0};
+  if constexpr (F == FT_Q6_K) {   // published by the first barrier of the superblock loop
+    if (tid < 16) ((u32x4*)(L + LY::ZERO))[tid] = (u32x4){0u, 0u, 0u, 0u};
+  }
+  // this lane's weight chunks: row start (null: idle)
+  const uint8_t* wrs[NWI];
+#pragma unroll
+  for (int i = 0; i < NWI; ++i) {
+    const int c = lane + 64 * i;
+    const int r = c / NCH;
+    const int64_t row = slot_row(r);
+    wrs[i] = (r < WROWS && row < n) ? slot_src(r) + row * row_bytes : nullptr;
+  }
+  auto xrow_of = [&](int p) -> const uint8_t* {
+    const int64_t row = x_per_pair ? pairs[p] : pairs[p] / topk;
+    return xq + row * xrow_bytes;
+  };
+
+  for (int g0 = p0; g0 < p1; g0 += PT * 16) {
+    const int gm = min(PT * 16, p1 - g0);
+    const int npt = (gm + 15) >> 4;
+    // activation chunks: instruction i of wave w moves items 64*(GM_WAVES*i + w) + lane,
+    // item = pair * XCH + chunk, to X + 16 * item
+    const uint8_t* xrs[NXI];   // pair row start + 16 * chunk (null: idle)
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) {
+      const int it = 64 * (GM_WAVES * i + wave) + lane;
+      const int pi = it / XCH;
+      xrs[i] = (it < PT * 16 * XCH && pi < gm) ? xrow_of(g0 + pi) + 16 * (it - pi * XCH) : nullptr;
+    }
+    // wave 0: pair `lane`'s row, for its d
+    const uint8_t* drs = (wave == 0 && lane < gm) ? xrow_of(g0 + lane) : nullptr;
+    // the low address bits of the lane's own pair row in each tile (its superblock's offset in the slot)
+    uint32_t xlo[PT];
+#pragma unroll
+    for (int m = 0; m < PT; ++m) {
+      const int pi = 16 * m + rl;
+      xlo[m] = pi < gm ? (uint32_t)(uintptr_t)xrow_of(g0 + pi) : 0u;
+    }
+
+    auto issue = [&](int sb, int s) {
+      uint8_t* B = L + s * LY::STAGE;
+#pragma unroll
+      for (int i = 0; i < NWI; ++i) {
+        const int ch = (lane + 64 * i) % NCH;
+        if (wrs[i]) {
+          const uint8_t* sp = wrs[i] + (int64_t)sb * SB::BYTES;
+          const int sh = SB::ALIGNED ? 0 : (int)((uintptr_t)sp & 15);
+          // chunks that overlap the superblock (16-byte aligned: never past the buffer's last line)
+          if (SB::ALIGNED || ch < ((sh + SB::BYTES + 15) >> 4)) lds_dma16_cached(sp - sh + 16 * ch, B + wslot + 1024 * i);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NXI; ++i) {
+        if (xrs[i]) {
+          const uint8_t* sp = xrs[i] + (int64_t)sb * 292;
+          lds_dma16_cached(sp - ((uintptr_t)sp & 15), B + LY::X + 1024 * (GM_WAVES * i + wave));
+        }
+      }
+      if (drs) lds_dma4_cached(drs + (int64_t)sb * 292, B + LY::DX);
+    };
+
+    v4f acc[PT][RG];
+#pragma unroll
+    for (int m = 0; m < PT; ++m)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) acc[m][rg] = zf;
+
+    issue(0, 0);
+    for (int sb = 0; sb < nsb; ++sb) {
+      wait_vm<0>();    // this wave's loads of superblock sb have landed
+      lds_barrier();   // everyone's have; everyone is done with superblock sb-1's stage
+      if (sb + 1 < nsb) issue(sb + 1, (sb + 1) & 1);
+      const uint8_t* B = L + (sb & 1) * LY::STAGE;
+
+      GW<F> w[RG];
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const int r = rg * 16 + rl;
+        uint32_t o = 0;
+        if constexpr (!SB::ALIGNED)
+          o = (uint32_t)((uintptr_t)(slot_src(r) + slot_row(r) * row_bytes + (int64_t)sb * SB::BYTES) & 15);
+        gw_decode<F>(B + wslot + r * SB::SLOT, o, q, w[rg]);
+      }
+
+      // tiles M0 .. M0+NT-1, interleaved
+      auto tiles = [&](auto m0c, auto ntc) {
+        constexpr int M0 = decltype(m0c)::value, NT = decltype(ntc)::value;
+        const uint8_t* ap[NT];   // the lane's codes (group 0, quarter q) in tile M0 + m
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+          ap[m] = B + LY::X + LY::XS * (16 * (M0 + m) + rl) + ((xlo[M0 + m] + 4u * (uint32_t)sb) & 15u) + 4 + 8 * q;
+        v4i isc[NT][RG];
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg) isc[m][rg] = zi;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // every MFMA of the group first, then the integer scale step of each
+          v4i dv[NT][RG], dh[NT][RG];
+#pragma unroll
+          for (int m = 0; m < NT; ++m) {
+            const uint32_t* cp = (const uint32_t*)(ap[m] + 32 * j);
+            long a0, a1 = 0;
+            if constexpr (F == FT_Q6_K) {
+              // the low half of a 32-element group (quarters 0, 1) is one sub-block and
+              // the high half the next; each MFMA reads zeros in the other half's lanes
+              const uint32_t* zp = (const uint32_t*)(L + LY::ZERO);
+              const uint32_t* c0 = q >= 2 ? zp : cp;
+              const uint32_t* c1 = q < 2 ? zp : cp;
+              a0 = (long)pk64(c0[0], c0[1]);
+              a1 = (long)pk64(c1[0], c1[1]);
+            } else {
+              a0 = (long)pk64(cp[0], cp[1]);
+            }
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+              dv[m][rg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a0, (long)w[rg].b[j], zi, 0, 0, 0);
+              if constexpr (F == FT_Q6_K) dh[m][rg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a1, (long)w[rg].b[j], zi, 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < NT; ++m) {
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+              if constexpr (KQ) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  isc[m][rg][r] += __mul24(dv[m][rg][r], w[rg].sc[j]);
+                  // one multiply-add per product: keep the compiler from regrouping the
+                  // chain into separate multiplies and three-way adds
+                  asm("" : "+v"(isc[m][rg][r]));
+                }
+              } else {
+                const int s0 = (int)(int8_t)((w[rg].scp[j >> 1] >> (16 * (j & 1))) & 0xFFu);
+                const int s1 = (int)(int8_t)((w[rg].scp[j >> 1] >> (16 * (j & 1) + 8)) & 0xFFu);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) isc[m][rg][r] += __mul24(dv[m][rg][r], s0) + __mul24(dh[m][rg][r], s1);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+          // the lane's four 16-element group sums (int16 as stored, exact in fp16)
+          const uint32_t* sp = (const uint32_t*)(ap[m] + 256);
+          const uint32_t s01 = sp[0], s23 = sp[1];
+          const v4h ba = {(_Float16)(int16_t)(s01 & 0xFFFFu), (_Float16)(int16_t)(s01 >> 16),
+                          (_Float16)(int16_t)(s23 & 0xFFFFu), (_Float16)(int16_t)(s23 >> 16)};
+          const v4f dx4 = *(const v4f*)(B + LY::DX + (M0 + m) * 64 + 16 * q);
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg) {
+            const v4f dm = __builtin_amdgcn_mfma_f32_16x16x16f16(ba, w[rg].mb, zf, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float t;
+              if constexpr (KQ) t = fmaf(-w[rg].dmin, dm[r], w[rg].d * (float)isc[m][rg][r]);
+              else t = w[rg].d * fmaf(-32.0f, dm[r], (float)isc[m][rg][r]);
+              acc[M0 + m][rg][r] = fmaf(dx4[r], t, acc[M0 + m][rg][r]);
+            }
+          }
+        }
+      };
+      if constexpr (F == FT_Q6_K) {
+        // two MFMAs and two scales per group: one tile at a time (registers)
+        tiles(GIc<0>{}, GIc<1>{});
+        if constexpr (PT >= 2) if (npt >= 2) tiles(GIc<1>{}, GIc<1>{});
+        if constexpr (PT >= 3) if (npt >= 3) tiles(GIc<2>{}, GIc<1>{});
+        if constexpr (PT >= 4) if (npt >= 4) tiles(GIc<3>{}, GIc<1>{});
+      } else {
+        if constexpr (PT >= 4) { if (npt >= 4) { tiles(GIc<0>{}, GIc<4>{}); continue; } }
+        if constexpr (PT >= 3) { if (npt >= 3) { tiles(GIc<0>{}, GIc<3>{}); continue; } }
+        if constexpr (PT >= 2) { if (npt >= 2) { tiles(GIc<0>{}, GIc<2>{}); continue; } }
+        tiles(GIc<0>{}, GIc<1>{});
+      }
+    }
+
+    // lane holds weight slots 16rg + rl for pairs 16m + 4q + r of the group
+#pragma unroll
+    for (int m = 0; m < PT; ++m) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pi = 16 * m + 4 * q + r;
+        if (pi < gm) {
+          const int64_t pr = pairs[g0 + pi];
+          if constexpr (GLU) {
+            const int64_t row = wrow0 + rl;
+            if (row < n) {
+              const float g = acc[m][0][r], u = acc[m][1][r];
+              y[pr * n + row] = g / (1.0f + expf(-g)) * u;
+              if (g_tap) g_tap[pr * n + row] = g;
+              if (u_tap) u_tap[pr * n + row] = u;
+            }
+          } else {
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+              const int64_t row = wrow0 + 16 * rg + rl;
+              if (row < n) y[pr * n + row] = acc[m][rg][r];
+            }
+          }
+        }
+      }
+    }
+    // the next pass overwrites both stages: everyone is done with the last one
+    lds_barrier();
+  }
+}
+
+template <int F, int PT, bool GLU>
+static hipError_t launch_gd(const GroupedArgs& a, hipStream_t st) {
+  constexpr int RG = GRg<F, GLU>::RG;
+  const int rows = (GLU ? 16 : 16 * RG) * GM_WAVES;
+  const int64_t row_tiles = (a.n + rows - 1) / rows;
+  const int64_t total = row_tiles * a.n_expert;
+  const int64_t per = (total + 7) / 8;
+  const int64_t row_bytes = a.k / 256 * GSb<F>::BYTES;
+  constexpr size_t lds = (size_t)GDLds<F, PT, RG>::TOTAL;
+  static const bool attr = hipFuncSetAttribute((const void*)grouped_dma_kernel<F, PT, GLU>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+  if (!attr) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((grouped_dma_kernel<F, PT, GLU>), dim3((unsigned)(per * 8)), dim3(GM_THREADS), lds, st,
+                     (const uint8_t*)a.W, (const uint8_t*)a.W2, a.n, row_bytes, (int)(a.k / 256),
+                     (const uint8_t*)a.xq, (int64_t)(a.k / 256 * 292), a.x_per_pair, a.topk, a.offsets, a.pairs,
+                     a.y, a.g_tap, a.u_tap, row_tiles, total, per);
+  return hipGetLastError();
+}
+
 template <int F, int PT, bool GLU>
 static hipError_t launch_gm(const GroupedArgs& a, hipStream_t st) {
   constexpr int RG = GRg<F, GLU>::RG;
@@ -520,6 +820,24 @@ static hipError_t launch_gm(const GroupedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+
+// The DMA-staged kernel for Q4_K / Q5_K up to 3 pair tiles, where two of its
+// workgroups fit a CU without spills; with its weight and activation loads on the
+// default cache policy (the 136-176-byte superblock windows of a row share
+// lines) it beats the register-staged kernel: Q5_K 1536x4096 gate/up at 512
+// tokens 224 -> 207-208 us, down 228 -> 220-221 us, the K-quant tile layer 600 ->
+// 577-579 us.  Q6_K stays on the register-staged kernel (down +2-4% on DMA).
+template <int F, bool GLU, int PT>
+static hipError_t launch_g(const GroupedArgs& a, hipStream_t st) {
+  if constexpr (F == FT_Q4_K || F == FT_Q5_K) {
+    if constexpr (PT <= 3) return launch_gd<F, PT, GLU>(a, st);
+    else return launch_gm<F, PT, GLU>(a, st);
+  } else {
+    return launch_gm<F, PT, GLU>(a, st);
+  }
+}
+
 // Pair tiles held per pass: room for an expert 2.5 standard deviations above the
 // mean pairs per expert of this batch (uniform routing gives a near-binomial
 // spread); a larger group takes a second pass over its weights.
@@ -527,10 +845,10 @@ template <int F, bool GLU>
 static hipError_t grouped_f(const GroupedArgs& a, hipStream_t st) {
   const double avg = (double)a.t * a.topk / (double)a.n_expert;
   const double hi = avg + 2.5 * sqrt(avg);
-  if (hi <= 16.0) return launch_gm<F, 1, GLU>(a, st);
-  if (hi <= 32.0) return launch_gm<F, 2, GLU>(a, st);
-  if (hi <= 48.0) return launch_gm<F, 3, GLU>(a, st);
-  return launch_gm<F, 4, GLU>(a, st);
+  if (hi <= 16.0) return launch_g<F, GLU, 1>(a, st);
+  if (hi <= 32.0) return launch_g<F, GLU, 2>(a, st);
+  if (hi <= 48.0) return launch_g<F, GLU, 3>(a, st);
+  return launch_g<F, GLU, 4>(a, st);
 }
 
 }  // namespace ftk
