@@ -176,6 +176,85 @@ sort_kernel(const int32_t* __restrict__ ids, int npairs, int n_expert, int chunk
   for (int e = tid; e < E; e += SORT_THREADS) counts[e] = offsets[e + 1] - offsets[e];
 }
 
+// The same stable sort for at most 16384 pairs and 512 experts, without the
+// per-pair count over its segment.  Wave w owns the consecutive pairs
+// [w * per, (w + 1) * per), 64 per round in pair order.  In a round the lanes that
+// hold the same expert find each other with one ballot per bit of the expert
+// index; a pair's rank among its wave's earlier pairs of that expert is the
+// wave's running count for it (one LDS row of E counters per wave) plus the
+// group's lanes below it, and the group's highest lane advances the count (the
+// wave's LDS read precedes its write).  Then each expert's per-wave counts become
+// starts in wave order, the totals are scanned into the offsets, and every pair
+// lands at offsets[e] + its wave's start + its rank.
+constexpr int SORTF_MAXE = 512;
+constexpr int SORTF_MAXR = 16;   // rounds per wave: 16 waves x 64 lanes x 16 = 16384 pairs
+
+__global__ void __launch_bounds__(SORT_THREADS)
+sort_fast_kernel(const int32_t* __restrict__ ids, int npairs, int n_expert, int nbits, int per,
+                 int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ pairs) {
+  constexpr int NW = SORT_THREADS / 64;
+  __shared__ int32_t cnt[NW * SORTF_MAXE];
+  __shared__ int32_t base[SORTF_MAXE];
+  __shared__ int wsum[NW + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int E = n_expert;
+  int32_t* my = cnt + wave * E;
+  for (int e = lane; e < E; e += 64) my[e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  const int p0 = wave * per;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int er[SORTF_MAXR], rk[SORTF_MAXR];
+#pragma unroll
+  for (int r = 0; r < SORTF_MAXR; ++r) {
+    er[r] = -1;
+    rk[r] = 0;
+    if (r * 64 < per) {
+      const int p = p0 + r * 64 + lane;
+      const bool v = p < npairs;
+      const int e = v ? clamp_e(ids[p], E) : 0;
+      uint64_t m = __ballot(v);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(v && bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (v) {
+        const int prev = my[e];
+        er[r] = e;
+        rk[r] = prev + __popcll(m & below);
+        if ((m >> lane) == 1ull) my[e] = prev + __popcll(m);   // highest lane of the group
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += SORT_THREADS) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+    base[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(
+      E, wsum, [&](int e) { return base[e]; },
+      [&](int e, int v) {
+        counts[e] = base[e];
+        offsets[e] = v;
+        base[e] = v;
+      });
+  if (tid == 0) offsets[E] = total;
+#pragma unroll
+  for (int r = 0; r < SORTF_MAXR; ++r) {
+    if (er[r] >= 0) {
+      const int d = base[er[r]] + cnt[wave * E + er[r]] + rk[r];
+      if (d < npairs) pairs[d] = p0 + r * 64 + lane;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // helpers shared by the expert kernels
 // ---------------------------------------------------------------------------
@@ -1030,6 +1109,14 @@ hipError_t ftk_launch_sort(const int32_t* ids, int64_t t, int topk, int64_t n_ex
                            int32_t* offsets, int32_t* pairs, hipStream_t st) {
   // LDS: max(4E, 2*ceil(E/2) + 2*(E+2) + 4*chunk) bytes, kept within 64 KiB
   const int64_t npairs = t * topk;
+  if (npairs >= 1 && npairs <= 16 * 64 * SORTF_MAXR && n_expert <= SORTF_MAXE) {
+    const int per = (int)(((npairs + 15) / 16 + 63) / 64 * 64);
+    int nbits = 0;
+    while ((1 << nbits) < n_expert) ++nbits;
+    hipLaunchKernelGGL(sort_fast_kernel, dim3(1), dim3(SORT_THREADS), 0, st, ids, (int)npairs, (int)n_expert, nbits,
+                       per, counts, offsets, pairs);
+    return hipGetLastError();
+  }
   const int64_t fixed = 4 * ((n_expert + 1) / 2) + 4 * ((n_expert + 2) / 2);
   int64_t chunk = (65536 - fixed) / 4;
   if (chunk > 65535) chunk = 65535;

@@ -69,9 +69,24 @@ def test_route_edge_values(e, topk):
 
 
 @pytest.mark.parametrize("t,e,topk", [(1, 128, 8), (5, 256, 8), (512, 128, 8), (700, 64, 3), (4096, 256, 8),
-                                      (1, 1, 1), (3000, 8, 8), (2048, 8192, 8)])
+                                      (1, 1, 1), (3000, 8, 8), (2048, 8192, 8), (2048, 512, 8), (2049, 512, 8),
+                                      (33, 2, 2), (2048, 513, 8)])
 def test_sort(t, e, topk):
     ids = synth.expert_ids(t, e, topk, synth.rng(301, t))
+    c, o, p = ft.moe_sort(dev(ids), e)
+    rc, ro, rp = oracle.sort_pairs(ids, e)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(o), ro) and np.array_equal(host(p), rp)
+
+
+@pytest.mark.parametrize("t,e,topk", [(512, 128, 8), (2048, 512, 8), (64, 3, 2), (1, 256, 8)])
+def test_sort_skewed(t, e, topk):
+    """Slot 0 of every token names expert e - 1 and slot 1 expert 0, so two
+    experts hold a third or more of the pairs (long runs of equal keys in every
+    64-pair round) and most experts few or none; the order within each expert's
+    segment must still be pair order."""
+    ids = synth.expert_ids(t, e, topk, synth.rng(302, t))
+    ids[:, 0] = e - 1
+    ids[:, 1] = 0
     c, o, p = ft.moe_sort(dev(ids), e)
     rc, ro, rp = oracle.sort_pairs(ids, e)
     assert np.array_equal(host(c), rc) and np.array_equal(host(o), ro) and np.array_equal(host(p), rp)
